@@ -1,0 +1,276 @@
+"""Pins for the CPU oracle (runs without a GPU).
+
+The sequential fp64 recurrence (oracle.scan / oracle.decode) is checked
+against things other than itself:
+  * hand-derived values (tests/golden/scalar_by_hand.json),
+  * the brute-force quadratic (duality) form, built from explicit decay
+    products ("Engineering hybrid state-space models", section 2),
+  * scipy.signal.lfilter in the linear time-invariant special case
+    (lesty.tech Mamba explainer, section 3, convolution mode),
+  * closed forms in the limits the explainer's section 4 describes
+    (dt -> 0 keeps the state, large dt flushes it), A = 0 (causal linear
+    attention, the blog's section 3 state S_t = S_{t-1} + k v^T), x = 0,
+  * algebraic invariants: linearity, group broadcast, packed sequences ==
+    separate runs, head permutation, prefill + decode == longer prefill.
+The fp64 chunked regrouping (oracle.chunked) is pinned against the
+sequential oracle for many chunk sizes, including ragged tails.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+import scipy.signal
+
+import oracle
+from oracle.chunked import chunked_scan
+from oracle.quadratic import quadratic_scan_sequence
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def rand_case(seed, L=23, H=4, P=3, N=5, G=2, nseq=1, init=True, A_scale=1.0):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((nseq, L, H, P))
+    dt = rng.uniform(0.01, 0.6, (nseq, L, H))
+    A = -rng.uniform(0.2, 3.0, H) * A_scale
+    B = rng.standard_normal((nseq, L, G, N))
+    C = rng.standard_normal((nseq, L, G, N))
+    D = rng.standard_normal(H)
+    h0 = rng.standard_normal((nseq, H, P, N)) if init else None
+    return x, dt, A, B, C, D, h0
+
+
+def close(a, b, tol=1e-12):
+    a = np.asarray(a)
+    b = np.asarray(b)
+    scale = max(1.0, float(np.max(np.abs(b))) if b.size else 1.0)
+    assert a.shape == b.shape
+    err = float(np.max(np.abs(a - b))) / scale if a.size else 0.0
+    assert err <= tol, err
+
+
+# ------------------------------------------------------------------ golden
+def test_golden_hand_values():
+    g = json.load(open(os.path.join(GOLDEN, "scalar_by_hand.json")))
+    L = len(g["dt"])
+    x = np.array(g["x"]).reshape(1, L, 1, 1)
+    dt = np.array(g["dt"]).reshape(1, L, 1)
+    B = np.array(g["B"]).reshape(1, L, 1, 2)
+    C = np.array(g["C"]).reshape(1, L, 1, 2)
+    for case in g["cases"]:
+        h0 = np.array(case["h0"]).reshape(1, 1, 1, 2)
+        y, fin = oracle.scan(x, dt, g["A"], B, C, g["D"], init=h0)
+        close(y.reshape(-1), case["y"], 1e-15)
+        close(fin.reshape(-1), case["final"], 1e-15)
+        if "decode" in case:
+            d = case["decode"]
+            yd, st = oracle.decode(fin.reshape(1, 1, 1, 2), np.full((1, 1, 1), d["x"]),
+                                   np.full((1, 1), d["dt"]), g["A"],
+                                   np.array(d["B"]).reshape(1, 1, 2),
+                                   np.array(d["C"]).reshape(1, 1, 2), g["D"])
+            close(yd.reshape(-1), [d["y"]], 1e-15)
+            close(st.reshape(-1), d["state"], 1e-15)
+
+
+# ------------------------------------------------------------------ quadratic form
+@pytest.mark.parametrize("seed", range(6))
+@pytest.mark.parametrize("init", [False, True])
+def test_matches_quadratic_form(seed, init):
+    L = [1, 2, 7, 23, 37, 64][seed]
+    x, dt, A, B, C, D, h0 = rand_case(seed, L=L, init=init)
+    y, fin = oracle.scan(x, dt, A, B, C, D, init=h0)
+    yq, fq = quadratic_scan_sequence(x[0], dt[0], A, B[0], C[0], D,
+                                     None if h0 is None else h0[0])
+    close(y[0], yq, 1e-12)
+    close(fin[0], fq, 1e-12)
+
+
+# ------------------------------------------------------------------ LTI == lfilter
+def test_lti_is_first_order_iir():
+    """Constant dt, B, C and zero h0: every (h, p) channel is the IIR filter
+    y = (B.C) * lfilter([dt], [1, -exp(dt*A)], x) + D x."""
+    rng = np.random.default_rng(7)
+    L, H, P, N = 50, 3, 4, 6
+    x = rng.standard_normal((1, L, H, P))
+    dtv = rng.uniform(0.05, 0.5, H)
+    dt = np.broadcast_to(dtv, (1, L, H)).copy()
+    A = -rng.uniform(0.1, 2.0, H)
+    b = rng.standard_normal(N)
+    c = rng.standard_normal(N)
+    B = np.broadcast_to(b, (1, L, 1, N)).copy()
+    C = np.broadcast_to(c, (1, L, 1, N)).copy()
+    D = rng.standard_normal(H)
+    y, _ = oracle.scan(x, dt, A, B, C, D)
+    for h in range(H):
+        filt = scipy.signal.lfilter([dtv[h]], [1.0, -np.exp(dtv[h] * A[h])], x[0, :, h, :], axis=0)
+        close(y[0, :, h, :], float(b @ c) * filt + D[h] * x[0, :, h, :], 1e-12)
+
+
+# ------------------------------------------------------------------ limits / closed forms
+def test_A_zero_is_causal_linear_attention():
+    x, dt, A, B, C, D, h0 = rand_case(3, L=30)
+    A = np.zeros_like(A)
+    y, fin = oracle.scan(x, dt, A, B, C, D, init=h0)
+    H = x.shape[2]
+    G = B.shape[2]
+    for h in range(H):
+        g = h // (H // G)
+        kv = (dt[0, :, h, None] * x[0, :, h, :])[:, :, None] * B[0, :, g, None, :]
+        S = h0[0, h][None] + np.cumsum(kv, axis=0)            # S_t = S_{t-1} + k v^T
+        yy = np.einsum("tpn,tn->tp", S, C[0, :, g, :]) + D[h] * x[0, :, h, :]
+        close(y[0, :, h, :], yy, 1e-12)
+        close(fin[0, h], S[-1], 1e-12)
+
+
+def test_memoryless_limit():
+    """exp(dt*A) underflows to exactly 0: only the current token remains."""
+    x, dt, A, B, C, D, h0 = rand_case(4, L=12)
+    A = np.full_like(A, -1e6)
+    y, fin = oracle.scan(x, dt, A, B, C, D, init=h0)
+    H = x.shape[2]
+    G = B.shape[2]
+    for h in range(H):
+        g = h // (H // G)
+        cb = np.sum(C[0, :, g, :] * B[0, :, g, :], axis=1)
+        close(y[0, :, h, :], (dt[0, :, h] * cb)[:, None] * x[0, :, h, :] + D[h] * x[0, :, h, :])
+        close(fin[0, h], dt[0, -1, h] * np.outer(x[0, -1, h], B[0, -1, g]))
+
+
+def test_dt_to_zero_keeps_state():
+    x, dt, A, B, C, D, h0 = rand_case(5, L=9)
+    dt = np.full_like(dt, 1e-30)
+    y, fin = oracle.scan(x, dt, A, B, C, D, init=h0)
+    H = x.shape[2]
+    G = B.shape[2]
+    for h in range(H):
+        g = h // (H // G)
+        close(y[0, :, h, :], C[0, :, g, :] @ h0[0, h].T + D[h] * x[0, :, h, :])
+    close(fin, h0)
+
+
+def test_zero_input_decays_initial_state():
+    x, dt, A, B, C, D, h0 = rand_case(6, L=15)
+    x = np.zeros_like(x)
+    y, fin = oracle.scan(x, dt, A, B, C, D, init=h0)
+    H = x.shape[2]
+    G = B.shape[2]
+    for h in range(H):
+        g = h // (H // G)
+        decay = np.exp(A[h] * np.cumsum(dt[0, :, h]))
+        close(y[0, :, h, :], decay[:, None] * (C[0, :, g, :] @ h0[0, h].T))
+        close(fin[0, h], decay[-1] * h0[0, h])
+
+
+# ------------------------------------------------------------------ invariants
+def test_linearity_in_x_and_h0():
+    x1, dt, A, B, C, D, h1 = rand_case(8)
+    x2, _, _, _, _, _, h2 = rand_case(9)
+    a, b = 0.7, -1.3
+    y, f = oracle.scan(a * x1 + b * x2, dt, A, B, C, D, init=a * h1 + b * h2)
+    y1, f1 = oracle.scan(x1, dt, A, B, C, D, init=h1)
+    y2, f2 = oracle.scan(x2, dt, A, B, C, D, init=h2)
+    close(y, a * y1 + b * y2)
+    close(f, a * f1 + b * f2)
+
+
+def test_group_broadcast_equals_expanded_heads():
+    x, dt, A, B, C, D, h0 = rand_case(10, H=6, G=3)
+    y, f = oracle.scan(x, dt, A, B, C, D, init=h0)
+    rep = 6 // 3
+    Be = np.repeat(B, rep, axis=2)
+    Ce = np.repeat(C, rep, axis=2)
+    ye, fe = oracle.scan(x, dt, A, Be, Ce, D, init=h0)
+    close(y, ye, 1e-14)
+    close(f, fe, 1e-14)
+
+
+def test_head_permutation_equivariance():
+    x, dt, A, B, C, D, h0 = rand_case(11, H=5, G=1)
+    perm = np.array([3, 0, 4, 1, 2])
+    y, f = oracle.scan(x, dt, A, B, C, D, init=h0)
+    yp, fp = oracle.scan(x[:, :, perm], dt[:, :, perm], A[perm], B, C, D[perm], init=h0[:, perm])
+    close(yp, y[:, :, perm], 0)
+    close(fp, f[:, perm], 0)
+
+
+def test_packed_sequences_equal_separate_runs():
+    rng = np.random.default_rng(12)
+    lens = [5, 0, 17, 1, 9]
+    H, P, N, G = 4, 3, 5, 2
+    T = sum(lens)
+    x = rng.standard_normal((T, H, P))
+    dt = rng.uniform(0.01, 0.5, (T, H))
+    A = -rng.uniform(0.2, 2, H)
+    B = rng.standard_normal((T, G, N))
+    C = rng.standard_normal((T, G, N))
+    D = rng.standard_normal(H)
+    h0 = rng.standard_normal((len(lens), H, P, N))
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    y, f = oracle.scan(x, dt, A, B, C, D, init=h0, cu_seqlens=cu)
+    for s, l in enumerate(lens):
+        a, b = cu[s], cu[s + 1]
+        ys, fs = oracle.scan(x[None, a:b], dt[None, a:b], A, B[None, a:b], C[None, a:b], D,
+                             init=h0[s:s + 1])
+        close(y[a:b], ys[0], 0)
+        close(f[s], fs[0], 0)
+    close(f[1], h0[1], 0)  # empty sequence: the state passes through
+
+
+def test_prefill_then_decode_equals_longer_prefill():
+    x, dt, A, B, C, D, h0 = rand_case(13, L=21)
+    y, f = oracle.scan(x, dt, A, B, C, D, init=h0)
+    L = x.shape[1]
+    k = 4
+    _, f_short = oracle.scan(x[:, :L - k], dt[:, :L - k], A, B[:, :L - k], C[:, :L - k], D,
+                             init=h0)
+    st = f_short
+    for t in range(L - k, L):
+        yd, st = oracle.decode(st, x[:, t], dt[:, t], A, B[:, t], C[:, t], D)
+        close(yd, y[:, t], 1e-13)
+    close(st, f, 1e-13)
+    # a one-token prefill is a decode step from the initial state
+    y1, f1 = oracle.scan(x[:, :1], dt[:, :1], A, B[:, :1], C[:, :1], D, init=h0)
+    yd, sd = oracle.decode(h0, x[:, 0], dt[:, 0], A, B[:, 0], C[:, 0], D)
+    close(y1[:, 0], yd, 0)
+    close(f1, sd, 0)
+
+
+def test_thread_count_does_not_change_result():
+    x, dt, A, B, C, D, h0 = rand_case(14, L=40, nseq=3)
+    y1, f1 = oracle.scan(x, dt, A, B, C, D, init=h0, nthreads=1)
+    y4, f4 = oracle.scan(x, dt, A, B, C, D, init=h0, nthreads=4)
+    assert np.array_equal(y1, y4) and np.array_equal(f1, f4)
+
+
+# ------------------------------------------------------------------ chunked regrouping
+@pytest.mark.parametrize("Q", [1, 2, 3, 4, 8, 16, 37, 50])
+def test_chunked_equals_sequential(Q):
+    x, dt, A, B, C, D, h0 = rand_case(15, L=37, nseq=2)
+    y, f = oracle.scan(x, dt, A, B, C, D, init=h0)
+    yc, fc = chunked_scan(x, dt, A, B, C, D, Q, init=h0)
+    close(yc, y, 1e-12)
+    close(fc, f, 1e-12)
+
+
+def test_chunked_packed_restart_at_sequence_start():
+    rng = np.random.default_rng(16)
+    lens = [7, 12, 0, 3]
+    H, P, N, G = 4, 2, 3, 2
+    T = sum(lens)
+    x = rng.standard_normal((T, H, P))
+    dt = rng.uniform(0.01, 0.5, (T, H))
+    A = -rng.uniform(0.2, 2, H)
+    B = rng.standard_normal((T, G, N))
+    C = rng.standard_normal((T, G, N))
+    D = rng.standard_normal(H)
+    h0 = rng.standard_normal((len(lens), H, P, N))
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    y, f = oracle.scan(x, dt, A, B, C, D, init=h0, cu_seqlens=cu)
+    yc, fc, inter = chunked_scan(x, dt, A, B, C, D, 4, init=h0, cu_seqlens=cu,
+                                 return_intermediates=True)
+    close(yc, y, 1e-12)
+    close(fc, f, 1e-12)
+    # chunks never straddle a sequence boundary
+    for c in inter:
+        assert cu[c["seq"]] <= c["start"] and c["start"] + c["len"] <= cu[c["seq"] + 1]
