@@ -1,0 +1,164 @@
+/*
+ * ssd.h -- C ABI of the MI355X (gfx950) Mamba-2 SSD selective-scan library.
+ *
+ * The operation ("Compiler-First State Space Duality and Portable O(1)
+ * Autoregressive Caching for Inference", abstract; recurrence as in
+ * "Engineering hybrid state-space models", innvotechnologies blog, section 2):
+ * per sequence, head h (group g = h / (H/G)) and token t,
+ *
+ *     S_t = exp(dt[t,h] * A[h]) * S_{t-1} + dt[t,h] * x[t,h,:] (outer) B[t,g,:]
+ *     y[t,h,:] = S_t C[t,g,:]  +  D[h] * x[t,h,:]
+ *
+ * with S a (P x N) fp32 state per (sequence, head).  Two entry points:
+ *   ssd_chunked_scan  -- prefill over whole sequences, computed chunk by chunk
+ *                        (the paper's fixed-size chunking); returns y and the
+ *                        state after each sequence's last token;
+ *   ssd_decode_step   -- the O(1) cached single-token step, updating the state
+ *                        in place (the paper's cached decode).
+ *
+ * Conventions shared by every entry point
+ *   - All tensor pointers are DEVICE pointers owned by the caller.  The library
+ *     never allocates or frees device memory, never synchronizes, and keeps no
+ *     global state: calls are reentrant and asynchronous on `stream` (a
+ *     hipStream_t passed as void*, NULL = the null stream).
+ *   - Tensors are dense row-major with the innermost index last, as listed per
+ *     argument.  Every tensor pointer must be 16-byte aligned.
+ *   - Validation runs on the host before any launch.  On any error nothing is
+ *     launched and nothing is written; the returned code says why and
+ *     ssd_last_error_detail() gives a sentence (thread-local).
+ *   - Inputs are not checked for NaN/Inf; such values propagate.
+ *   - dtype of x, B, C and y is ssd_shape.dtype (fp32 or bf16); dt, A, D and
+ *     every state tensor are always fp32.  Arithmetic is fp32 throughout;
+ *     bf16 values are widened exactly and y is rounded to nearest even.
+ */
+#ifndef SSD_MI355X_H
+#define SSD_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum ssd_status {
+    SSD_OK = 0,
+    SSD_ERR_NULL = -1,        /* a required pointer is NULL */
+    SSD_ERR_SHAPE = -2,       /* a size is out of range or inconsistent */
+    SSD_ERR_DTYPE = -3,       /* unknown dtype code */
+    SSD_ERR_ALIGN = -4,       /* a tensor pointer is not 16-byte aligned */
+    SSD_ERR_CHUNK = -5,       /* chunk not in {32, 64, 128, 256} */
+    SSD_ERR_WORKSPACE = -6,   /* workspace NULL or smaller than the query says */
+    SSD_ERR_HIP = -7,         /* the HIP runtime reported an error at launch */
+    SSD_ERR_UNSUPPORTED = -8, /* valid but outside what the kernels implement */
+    SSD_ERR_SEQLENS = -9      /* host copy of cu_seqlens is not a valid offset list */
+} ssd_status;
+
+typedef enum ssd_dtype { SSD_F32 = 0, SSD_BF16 = 1 } ssd_dtype;
+
+/*
+ * Problem description.
+ *   Dense batch (cu_seqlens == NULL): `batch` sequences of `seqlen` tokens;
+ *     token rows are indexed [batch, seqlen].
+ *   Packed variable-length batch (cu_seqlens != NULL): `batch` sequences packed
+ *     into one stream of `seqlen` = T tokens; sequence s owns rows
+ *     [cu_seqlens[s], cu_seqlens[s+1]).  Chunks restart at every sequence start
+ *     and never straddle two sequences; a zero-length sequence passes its
+ *     initial state through unchanged.
+ *   headdim P in [8, 128] and dstate N in [8, 256], both multiples of 8;
+ *   ngroups G >= 1 divides nheads H; head h reads B/C group h / (H/G).
+ *   chunks_per_segment: scheduling knob of ssd_chunked_scan (how many
+ *     consecutive chunks one workgroup walks while carrying the state);
+ *     0 = let the library choose.  It never changes the result beyond rounding.
+ */
+typedef struct ssd_shape {
+    int64_t batch;
+    int64_t seqlen;
+    int32_t nheads;
+    int32_t headdim;
+    int32_t dstate;
+    int32_t ngroups;
+    int32_t dtype;               /* ssd_dtype */
+    int32_t chunks_per_segment;  /* 0 = automatic */
+    const int32_t* cu_seqlens;      /* device int32 [batch+1], or NULL (dense) */
+    const int32_t* cu_seqlens_host; /* optional host copy; validated when given */
+} ssd_shape;
+
+/*
+ * Workspace bytes that ssd_chunked_scan needs for this shape and chunk size.
+ * Writes *bytes and returns SSD_OK, or an error code for an invalid shape.
+ */
+ssd_status ssd_chunked_scan_workspace_size(const ssd_shape* shape, int32_t chunk, size_t* bytes);
+
+/*
+ * Chunked prefill.  ("Compiler-First State Space Duality...", abstract:
+ * fixed-size chunking, einsum-dominated compute; chunk algebra as in the
+ * blog's section 2 duality Y = (M o CB^T) X with a 1-semiseparable mask M.)
+ *
+ *   x          [rows, H, P]  dtype      rows = batch*seqlen (dense) or T (packed)
+ *   dt         [rows, H]     fp32       step sizes, used as given (no activation)
+ *   A          [H]           fp32       per-head scalar decay rate
+ *   B, C       [rows, G, N]  dtype
+ *   D          [H]           fp32       skip coefficient
+ *   chunk      32, 64, 128 or 256 tokens
+ *   init_state [nseq, H, P, N] fp32, or NULL for zero initial states
+ *   y          [rows, H, P]  dtype      output; must not alias any input
+ *   final_state[nseq, H, P, N] fp32, or NULL (not written); may alias
+ *              init_state (each element is read before it is written)
+ *   workspace  device scratch of at least the queried size, owned by the
+ *              caller, contents undefined on entry and exit
+ *   stream     hipStream_t (as void*) the kernels are queued on
+ * Returns SSD_OK once the kernels are queued (asynchronous).
+ */
+ssd_status ssd_chunked_scan(const void* x, const float* dt, const float* A, const void* B,
+                            const void* C, const float* D, int32_t chunk,
+                            const float* init_state, void* y, float* final_state,
+                            const ssd_shape* shape, void* workspace, size_t workspace_bytes,
+                            void* stream);
+
+/*
+ * O(1) cached decode step, in place.  ("Compiler-First State Space
+ * Duality...", abstract: registered cache + cached decode whose cost does not
+ * depend on the sequence length; the state is a fixed (batch, heads,
+ * head_dim, state_dim) buffer as in the blog's section 3.)
+ *
+ *   state [batch, H, P, N] fp32   read and overwritten with the new state
+ *   x     [batch, H, P]  dtype    one token per sequence
+ *   dt    [batch, H]     fp32
+ *   A, D  [H]            fp32
+ *   B, C  [batch, G, N]  dtype
+ *   y     [batch, H, P]  dtype    output; must not alias any input
+ * shape->seqlen, shape->cu_seqlens and shape->chunks_per_segment are ignored.
+ */
+ssd_status ssd_decode_step(float* state, const void* x, const float* dt, const float* A,
+                           const void* B, const void* C, const float* D, void* y,
+                           const ssd_shape* shape, void* stream);
+
+/*
+ * Measurement helper, for benchmarks only: does what ssd_chunked_scan does,
+ * with a HIP event recorded on `stream` before and after every kernel stage,
+ * then waits for the last event and writes each stage's elapsed time in
+ * milliseconds to stage_ms[SSD_PREFILL_STAGES], in the order plan, cumsum,
+ * cb, chunk_state, state_passing, chunk_scan (0 for a stage that did not
+ * run).  Unlike ssd_chunked_scan it blocks the calling thread until the
+ * kernels finish.  Same arguments and errors as ssd_chunked_scan, plus
+ * SSD_ERR_NULL when stage_ms is NULL.
+ */
+#define SSD_PREFILL_STAGES 6
+ssd_status ssd_chunked_scan_profiled(const void* x, const float* dt, const float* A,
+                                     const void* B, const void* C, const float* D, int32_t chunk,
+                                     const float* init_state, void* y, float* final_state,
+                                     const ssd_shape* shape, void* workspace,
+                                     size_t workspace_bytes, void* stream, float* stage_ms);
+
+/* Static English name of a status code. */
+const char* ssd_status_string(int32_t status);
+
+/* Thread-local sentence describing the last error returned on this thread. */
+const char* ssd_last_error_detail(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SSD_MI355X_H */

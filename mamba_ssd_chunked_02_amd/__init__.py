@@ -1,0 +1,256 @@
+"""MI355X (gfx950) Mamba-2 SSD selective scan: Python binding of libssd_mi355x.so.
+
+The binding only marshals arguments: every step of the scan runs in the HIP
+kernels behind the C ABI of ``include/ssd.h``.  PyTorch supplies device
+memory and the current stream; nothing here computes on the CPU, and there is
+no fallback: if the library is missing or a call fails, an exception says so.
+
+    y, final_state = chunked_scan(x, dt, A, B, C, D, chunk, init_state=None,
+                                  cu_seqlens=None)
+    y = decode_step(state, x, dt, A, B, C, D)          # state updated in place
+
+Shapes: dense x [b, L, H, P], dt [b, L, H], B/C [b, L, G, N]; packed
+(``cu_seqlens`` int32 [nseq+1]) x [T, H, P], dt [T, H], B/C [T, G, N].
+A, D [H]; states [nseq, H, P, N] fp32.  x/B/C/y share one dtype (float32 or
+bfloat16); dt, A, D and states are float32.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence, Tuple
+
+__all__ = ["chunked_scan", "decode_step", "workspace_size", "SsdError", "library_path", "load"]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_NAME = "libssd_mi355x.so"
+_lib = None
+
+SSD_F32 = 0
+SSD_BF16 = 1
+
+
+class SsdError(RuntimeError):
+    """A status other than SSD_OK from the C ABI."""
+
+    def __init__(self, status: int, what: str, detail: str):
+        super().__init__("%s failed: %s (%d): %s" % (what, _status_name(status), status, detail))
+        self.status = status
+
+
+class _Shape(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64), ("nheads", ctypes.c_int32),
+                ("headdim", ctypes.c_int32), ("dstate", ctypes.c_int32),
+                ("ngroups", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("chunks_per_segment", ctypes.c_int32), ("cu_seqlens", ctypes.c_void_p),
+                ("cu_seqlens_host", ctypes.c_void_p)]
+
+
+def library_path() -> str:
+    return os.path.join(_PKG, _LIB_NAME)
+
+
+def load():
+    """Load the HIP library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        path = library_path()
+        if not os.path.exists(path):
+            raise RuntimeError("%s is not built; run `python -m mamba_ssd_chunked_02_amd.build`"
+                               % path)
+        lib = ctypes.CDLL(path)
+        vp = ctypes.c_void_p
+        sp = ctypes.POINTER(_Shape)
+        lib.ssd_chunked_scan_workspace_size.argtypes = [sp, ctypes.c_int32,
+                                                        ctypes.POINTER(ctypes.c_size_t)]
+        lib.ssd_chunked_scan_workspace_size.restype = ctypes.c_int32
+        lib.ssd_chunked_scan.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_int32, vp, vp, vp, sp, vp,
+                                         ctypes.c_size_t, vp]
+        lib.ssd_chunked_scan.restype = ctypes.c_int32
+        lib.ssd_chunked_scan_profiled.argtypes = lib.ssd_chunked_scan.argtypes + [
+            ctypes.POINTER(ctypes.c_float)]
+        lib.ssd_chunked_scan_profiled.restype = ctypes.c_int32
+        lib.ssd_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, sp, vp]
+        lib.ssd_decode_step.restype = ctypes.c_int32
+        lib.ssd_status_string.argtypes = [ctypes.c_int32]
+        lib.ssd_status_string.restype = ctypes.c_char_p
+        lib.ssd_last_error_detail.argtypes = []
+        lib.ssd_last_error_detail.restype = ctypes.c_char_p
+        _lib = lib
+    return _lib
+
+
+def _status_name(st: int) -> str:
+    try:
+        return load().ssd_status_string(st).decode()
+    except Exception:  # pragma: no cover
+        return "status"
+
+
+def _check(st: int, what: str):
+    if st != 0:
+        raise SsdError(st, what, load().ssd_last_error_detail().decode())
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return SSD_F32
+    if t.dtype == torch.bfloat16:
+        return SSD_BF16
+    raise TypeError("x/B/C must be float32 or bfloat16, got %s" % t.dtype)
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    return t.data_ptr()
+
+
+def _need_cuda(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("tensors must live on the GPU")
+
+
+def _expect(t, shape, dtype, name):
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+    if t.dtype != dtype:
+        raise TypeError("%s has dtype %s, expected %s" % (name, t.dtype, dtype))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+def _stream_handle(t) -> int:
+    torch = _torch()
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def make_shape(x, B, cu_seqlens=None, cu_seqlens_host=None, chunks_per_segment: int = 0,
+               nseq: Optional[int] = None) -> Tuple[_Shape, object]:
+    """Build the C shape struct from tensors.  Returns (shape, keepalive)."""
+    sh = _Shape()
+    keep = None
+    if cu_seqlens is None:
+        b, L, H, P = x.shape
+        sh.batch, sh.seqlen = b, L
+    else:
+        T, H, P = x.shape
+        sh.batch = cu_seqlens.shape[0] - 1 if nseq is None else nseq
+        sh.seqlen = T
+        sh.cu_seqlens = cu_seqlens.data_ptr()
+        if cu_seqlens_host is not None:
+            import numpy as np
+            keep = np.ascontiguousarray(np.asarray(cu_seqlens_host, dtype=np.int32))
+            sh.cu_seqlens_host = keep.ctypes.data
+    sh.nheads, sh.headdim = H, P
+    sh.ngroups, sh.dstate = B.shape[-2], B.shape[-1]
+    sh.dtype = _dtype_code(x)
+    sh.chunks_per_segment = chunks_per_segment
+    return sh, keep
+
+
+def workspace_size(x, B, chunk: int, cu_seqlens=None, chunks_per_segment: int = 0) -> int:
+    sh, _ = make_shape(x, B, cu_seqlens, None, chunks_per_segment)
+    n = ctypes.c_size_t(0)
+    _check(load().ssd_chunked_scan_workspace_size(ctypes.byref(sh), int(chunk), ctypes.byref(n)),
+           "ssd_chunked_scan_workspace_size")
+    return int(n.value)
+
+
+STAGES = ("plan", "cumsum", "cb", "chunk_state", "state_passing", "chunk_scan")
+
+
+def chunked_scan(x, dt, A, B, C, D, chunk: int = 256, init_state=None, cu_seqlens=None, *,
+                 y=None, final_state=None, want_final: bool = True, workspace=None,
+                 chunks_per_segment: int = 0, cu_seqlens_host: Optional[Sequence[int]] = None,
+                 stage_ms: Optional[list] = None):
+    """Chunked prefill.  Returns (y, final_state or None).
+
+    ``cu_seqlens`` (packed batch) may be a GPU int32 tensor or a host sequence;
+    a host sequence is copied to the GPU and also validated on the host.
+    ``workspace`` (uint8 GPU tensor) is allocated when not given.
+    ``stage_ms``: when a list is given, the call goes through the measuring
+    entry point (it blocks until the kernels finish) and the list receives the
+    duration in ms of each stage named in ``STAGES``.
+    """
+    torch = _torch()
+    _need_cuda(x, dt, A, B, C, D, init_state)
+    host_cu = cu_seqlens_host
+    if cu_seqlens is not None and not (hasattr(cu_seqlens, "is_cuda") and cu_seqlens.is_cuda):
+        host_cu = list(int(v) for v in (cu_seqlens.tolist() if hasattr(cu_seqlens, "tolist")
+                                        else cu_seqlens))
+        cu_seqlens = torch.tensor(host_cu, dtype=torch.int32, device=x.device)
+    if cu_seqlens is not None and cu_seqlens.dtype != torch.int32:
+        raise TypeError("cu_seqlens must be int32")
+    sh, keep = make_shape(x, B, cu_seqlens, host_cu, chunks_per_segment)
+    nseq = sh.batch
+    H, P, N = sh.nheads, sh.headdim, sh.dstate
+    lead = tuple(x.shape[:-2])
+    _expect(dt, lead + (H,), torch.float32, "dt")
+    _expect(B, lead + (sh.ngroups, N), x.dtype, "B")
+    _expect(C, lead + (sh.ngroups, N), x.dtype, "C")
+    _expect(A, (H,), torch.float32, "A")
+    _expect(D, (H,), torch.float32, "D")
+    _expect(init_state, (nseq, H, P, N), torch.float32, "init_state")
+    _expect(y, tuple(x.shape), x.dtype, "y")
+    _expect(final_state, (nseq, H, P, N), torch.float32, "final_state")
+    if cu_seqlens is not None:
+        _expect(cu_seqlens, (nseq + 1,), torch.int32, "cu_seqlens")
+    if y is None:
+        y = torch.empty_like(x)
+    if final_state is None and want_final:
+        final_state = torch.empty((nseq, H, P, N), dtype=torch.float32, device=x.device)
+    lib = load()
+    nbytes = ctypes.c_size_t(0)
+    _check(lib.ssd_chunked_scan_workspace_size(ctypes.byref(sh), int(chunk), ctypes.byref(nbytes)),
+           "ssd_chunked_scan_workspace_size")
+    if workspace is None or workspace.numel() < nbytes.value:
+        workspace = torch.empty(int(nbytes.value), dtype=torch.uint8, device=x.device)
+    args = (_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), int(chunk), _ptr(init_state),
+            _ptr(y), _ptr(final_state), ctypes.byref(sh), _ptr(workspace), int(workspace.numel()),
+            _stream_handle(x))
+    if stage_ms is None:
+        _check(lib.ssd_chunked_scan(*args), "ssd_chunked_scan")
+    else:
+        out = (ctypes.c_float * len(STAGES))()
+        _check(lib.ssd_chunked_scan_profiled(*args, out), "ssd_chunked_scan_profiled")
+        stage_ms[:] = [float(v) for v in out]
+    del keep
+    return y, final_state
+
+
+def decode_step(state, x, dt, A, B, C, D, *, y=None):
+    """One cached decode step; ``state`` [b, H, P, N] fp32 is updated in place."""
+    torch = _torch()
+    _need_cuda(state, x, dt, A, B, C, D)
+    b, H, P = x.shape
+    G, N = B.shape[-2], B.shape[-1]
+    _expect(state, (b, H, P, N), torch.float32, "state")
+    _expect(dt, (b, H), torch.float32, "dt")
+    _expect(B, (b, G, N), x.dtype, "B")
+    _expect(C, (b, G, N), x.dtype, "C")
+    _expect(A, (H,), torch.float32, "A")
+    _expect(D, (H,), torch.float32, "D")
+    _expect(y, (b, H, P), x.dtype, "y")
+    sh = _Shape()
+    sh.batch, sh.seqlen = b, 1
+    sh.nheads, sh.headdim = H, P
+    sh.ngroups, sh.dstate = B.shape[-2], B.shape[-1]
+    sh.dtype = _dtype_code(x)
+    if y is None:
+        y = torch.empty_like(x)
+    st = load().ssd_decode_step(_ptr(state), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+                                _ptr(y), ctypes.byref(sh), _stream_handle(x))
+    _check(st, "ssd_decode_step")
+    return y

@@ -1,0 +1,318 @@
+// Host side of the C ABI declared in include/ssd.h: argument validation (pure
+// host code, before any launch), the chunk/segment plan, the workspace carve
+// and the kernel queueing.  Nothing here allocates, frees or synchronizes.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <algorithm>
+
+#include "ssd.h"
+#include "ssd_internal.h"
+
+#define SSD_API extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+thread_local char g_detail[320] = "";
+
+ssd_status fail(ssd_status st, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_detail, sizeof(g_detail), fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+ssd_status ok() {
+    g_detail[0] = '\0';
+    return SSD_OK;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+size_t up256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+constexpr size_t kMaxLds = 160 * 1024;  // LDS per CU on gfx950
+constexpr int kTargetWorkgroups = 2048;  // ~8 resident chunk-scan workgroups per CU
+
+struct Prepared {
+    ssd::Plan plan;
+    ssd::Layout lay;
+    int run_passing;
+};
+
+ssd_status check_head_dims(const ssd_shape* sh) {
+    if (sh->dtype != SSD_F32 && sh->dtype != SSD_BF16)
+        return fail(SSD_ERR_DTYPE, "dtype %d is neither SSD_F32 (0) nor SSD_BF16 (1)", sh->dtype);
+    if (sh->nheads < 1) return fail(SSD_ERR_SHAPE, "nheads must be >= 1 (got %d)", sh->nheads);
+    if (sh->ngroups < 1 || sh->nheads % sh->ngroups != 0)
+        return fail(SSD_ERR_SHAPE, "ngroups %d must be >= 1 and divide nheads %d", sh->ngroups,
+                    sh->nheads);
+    if (sh->headdim < 8 || sh->headdim > 128 || sh->headdim % 8 != 0)
+        return fail(SSD_ERR_SHAPE, "headdim %d must be a multiple of 8 in [8, 128]", sh->headdim);
+    if (sh->dstate < 8 || sh->dstate > 256 || sh->dstate % 8 != 0)
+        return fail(SSD_ERR_SHAPE, "dstate %d must be a multiple of 8 in [8, 256]", sh->dstate);
+    if (sh->batch < 0) return fail(SSD_ERR_SHAPE, "batch must be >= 0 (got %lld)", (long long)sh->batch);
+    return SSD_OK;
+}
+
+ssd_status prepare(const ssd_shape* sh, int32_t chunk, Prepared* out) {
+    if (!sh) return fail(SSD_ERR_NULL, "shape is NULL");
+    ssd_status st = check_head_dims(sh);
+    if (st != SSD_OK) return st;
+    if (chunk != 32 && chunk != 64 && chunk != 128 && chunk != 256)
+        return fail(SSD_ERR_CHUNK, "chunk %d is not one of 32, 64, 128, 256", chunk);
+    if (sh->seqlen < 0) return fail(SSD_ERR_SHAPE, "seqlen must be >= 0");
+    if (sh->chunks_per_segment < 0) return fail(SSD_ERR_SHAPE, "chunks_per_segment must be >= 0");
+    const bool packed = sh->cu_seqlens != nullptr;
+    const int64_t nseq = sh->batch;
+    const int64_t T = packed ? sh->seqlen : sh->batch * sh->seqlen;
+    if (sh->batch > (1 << 24) || sh->seqlen > ((int64_t)1 << 30) || T > ((int64_t)1 << 30))
+        return fail(SSD_ERR_SHAPE, "token count %lld exceeds the supported 2^30", (long long)T);
+    if (T * sh->nheads * (int64_t)sh->headdim > ((int64_t)1 << 40))
+        return fail(SSD_ERR_SHAPE, "tensor too large");
+    if (packed && sh->cu_seqlens_host) {
+        const int32_t* cu = sh->cu_seqlens_host;
+        if (cu[0] != 0) return fail(SSD_ERR_SEQLENS, "cu_seqlens[0] must be 0 (got %d)", cu[0]);
+        for (int64_t s = 0; s < nseq; ++s)
+            if (cu[s + 1] < cu[s])
+                return fail(SSD_ERR_SEQLENS, "cu_seqlens decreases at %lld", (long long)s);
+        if (cu[nseq] != T)
+            return fail(SSD_ERR_SEQLENS, "cu_seqlens[batch] = %d differs from seqlen %lld", cu[nseq],
+                        (long long)T);
+    }
+    if (!packed && sh->cu_seqlens_host)
+        return fail(SSD_ERR_SHAPE, "cu_seqlens_host given without the device cu_seqlens");
+    const size_t lds = ssd::chunk_scan_lds_bytes(sh->dtype, sh->headdim, sh->dstate, chunk);
+    if (lds > kMaxLds)
+        return fail(SSD_ERR_UNSUPPORTED,
+                    "headdim %d, dstate %d, chunk %d and dtype %d need %zu bytes of LDS (> %zu); "
+                    "use a smaller chunk",
+                    sh->headdim, sh->dstate, chunk, sh->dtype, lds, kMaxLds);
+
+    ssd::Plan& pl = out->plan;
+    pl = ssd::Plan{};
+    pl.H = sh->nheads;
+    pl.P = sh->headdim;
+    pl.N = sh->dstate;
+    pl.G = sh->ngroups;
+    pl.hpg = sh->nheads / sh->ngroups;
+    pl.Q = chunk;
+    pl.nseq = (int32_t)nseq;
+    pl.dense = packed ? 0 : 1;
+    pl.T = T;
+    pl.cu = sh->cu_seqlens;
+    if (!packed) {
+        pl.L = sh->seqlen;
+        pl.cpseq = (int32_t)((sh->seqlen + chunk - 1) / chunk);
+        int cps = sh->chunks_per_segment;
+        if (cps == 0) {
+            // enough segments per sequence to give ~kTargetWorkgroups chunk-scan workgroups
+            const int64_t pairs = std::max<int64_t>(1, nseq * sh->nheads);
+            int64_t want = (kTargetWorkgroups + pairs - 1) / pairs;
+            want = std::max<int64_t>(1, std::min<int64_t>(want, std::max(1, pl.cpseq)));
+            cps = (int)((std::max(1, pl.cpseq) + want - 1) / want);
+        }
+        pl.cps = std::max(1, std::min(cps, std::max(1, pl.cpseq)));
+        pl.spseq = pl.cpseq == 0 ? 0 : (pl.cpseq + pl.cps - 1) / pl.cps;
+        pl.nchunk_ub = (int32_t)(nseq * pl.cpseq);
+        pl.nseg_ub = (int32_t)(nseq * pl.spseq);
+        pl.nslot_ub = (int32_t)(nseq * std::max(0, pl.spseq - 1));
+        out->run_passing = (pl.spseq > 1 || (pl.cpseq == 0 && nseq > 0)) ? 1 : 0;
+    } else {
+        pl.L = 0;
+        const int64_t ub = nseq == 0 ? 0 : (T + nseq * (int64_t)(chunk - 1)) / chunk;
+        pl.nchunk_ub = (int32_t)ub;
+        int cps = sh->chunks_per_segment;
+        if (cps == 0) cps = (int)std::max<int64_t>(1, (ub * sh->nheads) / kTargetWorkgroups);
+        pl.cps = cps;
+        const int64_t sub = std::min<int64_t>(ub, (ub + nseq * (int64_t)(cps - 1)) / cps);
+        pl.nseg_ub = (int32_t)sub;
+        pl.nslot_ub = (int32_t)sub;
+        out->run_passing = nseq > 0 ? 1 : 0;
+    }
+
+    ssd::Layout& L = out->lay;
+    const size_t es = sh->dtype == SSD_BF16 ? 2 : 4;
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t at = off;
+        off += up256(bytes);
+        return at;
+    };
+    L.seq_tab = take(packed ? (size_t)nseq * 16 : 0);
+    L.chunk_tab = take(packed ? (size_t)pl.nchunk_ub * 16 : 0);
+    L.seg_tab = take(packed ? (size_t)pl.nseg_ub * 16 : 0);
+    L.cs = take((size_t)pl.nchunk_ub * pl.H * chunk * 4);
+    L.dtc = take((size_t)pl.nchunk_ub * pl.H * chunk * 4);
+    L.cb = take((size_t)pl.nchunk_ub * pl.G * chunk * chunk * 4);
+    L.bt = take((size_t)pl.nchunk_ub * pl.G * pl.N * chunk * es);
+    L.sbuf = take((size_t)pl.nslot_ub * pl.H * pl.P * pl.N * 4);
+    L.total = std::max<size_t>(off, 256);
+    return SSD_OK;
+}
+
+}  // namespace
+
+SSD_API const char* ssd_status_string(int32_t status) {
+    switch (status) {
+        case SSD_OK: return "ok";
+        case SSD_ERR_NULL: return "a required pointer is NULL";
+        case SSD_ERR_SHAPE: return "a size is out of range or inconsistent";
+        case SSD_ERR_DTYPE: return "unknown dtype";
+        case SSD_ERR_ALIGN: return "a tensor pointer is not 16-byte aligned";
+        case SSD_ERR_CHUNK: return "chunk must be 32, 64, 128 or 256";
+        case SSD_ERR_WORKSPACE: return "workspace missing or too small";
+        case SSD_ERR_HIP: return "HIP runtime error";
+        case SSD_ERR_UNSUPPORTED: return "valid but unsupported configuration";
+        case SSD_ERR_SEQLENS: return "cu_seqlens is not a valid offset list";
+        default: return "unknown status";
+    }
+}
+
+SSD_API const char* ssd_last_error_detail(void) { return g_detail; }
+
+SSD_API ssd_status ssd_chunked_scan_workspace_size(const ssd_shape* shape, int32_t chunk,
+                                                   size_t* bytes) {
+    if (!bytes) return fail(SSD_ERR_NULL, "bytes is NULL");
+    Prepared pr;
+    const ssd_status st = prepare(shape, chunk, &pr);
+    if (st != SSD_OK) return st;
+    *bytes = pr.lay.total;
+    return ok();
+}
+
+namespace {
+
+ssd_status scan_impl(const void* x, const float* dt, const float* A, const void* B, const void* C,
+                     const float* D, int32_t chunk, const float* init_state, void* y,
+                     float* final_state, const ssd_shape* shape, void* workspace,
+                     size_t workspace_bytes, void* stream, hipEvent_t* marks) {
+    Prepared pr;
+    ssd_status st = prepare(shape, chunk, &pr);
+    if (st != SSD_OK) return st;
+    const bool any_tokens = pr.plan.T > 0;
+    struct {
+        const void* p;
+        const char* name;
+        bool required;
+    } ptrs[] = {{x, "x", any_tokens},   {dt, "dt", any_tokens},     {A, "A", true},
+                {B, "B", any_tokens},   {C, "C", any_tokens},       {D, "D", true},
+                {y, "y", any_tokens},   {init_state, "init_state", false},
+                {final_state, "final_state", false},             {workspace, "workspace", true}};
+    for (auto& q : ptrs) {
+        if (!q.p && q.required) {
+            if (q.name[0] == 'w') return fail(SSD_ERR_WORKSPACE, "workspace is NULL");
+            return fail(SSD_ERR_NULL, "%s is NULL", q.name);
+        }
+        if (q.p && !aligned16(q.p)) return fail(SSD_ERR_ALIGN, "%s is not 16-byte aligned", q.name);
+    }
+    if (workspace_bytes < pr.lay.total)
+        return fail(SSD_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes,
+                    pr.lay.total);
+    if (y && (y == x || y == B || y == C || y == (const void*)dt))
+        return fail(SSD_ERR_SHAPE, "y aliases an input");
+    ssd::ScanArgs a;
+    a.x = x;
+    a.dt = dt;
+    a.A = A;
+    a.B = B;
+    a.C = C;
+    a.D = D;
+    a.init = init_state;
+    a.y = y;
+    a.final_state = final_state;
+    a.ws = (char*)workspace;
+    a.dtype = shape->dtype;
+    a.run_passing = pr.run_passing;
+    pr.plan.seq_tab = (int32_t*)(a.ws + pr.lay.seq_tab);
+    pr.plan.chunk_tab = (int32_t*)(a.ws + pr.lay.chunk_tab);
+    pr.plan.seg_tab = (int32_t*)(a.ws + pr.lay.seg_tab);
+    if (pr.plan.nseq == 0 && !marks) return ok();
+    const hipError_t err = ssd::launch_prefill(pr.plan, pr.lay, a, (hipStream_t)stream, marks);
+    if (err != hipSuccess)
+        return fail(SSD_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(err));
+    return ok();
+}
+
+}  // namespace
+
+SSD_API ssd_status ssd_chunked_scan(const void* x, const float* dt, const float* A, const void* B,
+                                    const void* C, const float* D, int32_t chunk,
+                                    const float* init_state, void* y, float* final_state,
+                                    const ssd_shape* shape, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
+    return scan_impl(x, dt, A, B, C, D, chunk, init_state, y, final_state, shape, workspace,
+                     workspace_bytes, stream, nullptr);
+}
+
+SSD_API ssd_status ssd_chunked_scan_profiled(const void* x, const float* dt, const float* A,
+                                             const void* B, const void* C, const float* D,
+                                             int32_t chunk, const float* init_state, void* y,
+                                             float* final_state, const ssd_shape* shape,
+                                             void* workspace, size_t workspace_bytes, void* stream,
+                                             float* stage_ms) {
+    if (!stage_ms) return fail(SSD_ERR_NULL, "stage_ms is NULL");
+    constexpr int kMarks = SSD_PREFILL_STAGES + 1;
+    hipEvent_t ev[kMarks] = {};
+    hipError_t err = hipSuccess;
+    int made = 0;
+    for (; made < kMarks && err == hipSuccess; ++made) err = hipEventCreate(&ev[made]);
+    ssd_status st = SSD_OK;
+    if (err != hipSuccess) {
+        st = fail(SSD_ERR_HIP, "hipEventCreate failed: %s", hipGetErrorString(err));
+        --made;
+    } else {
+        st = scan_impl(x, dt, A, B, C, D, chunk, init_state, y, final_state, shape, workspace,
+                       workspace_bytes, stream, ev);
+        if (st == SSD_OK) err = hipEventSynchronize(ev[kMarks - 1]);
+        for (int i = 0; st == SSD_OK && err == hipSuccess && i < SSD_PREFILL_STAGES; ++i)
+            err = hipEventElapsedTime(&stage_ms[i], ev[i], ev[i + 1]);
+        if (st == SSD_OK && err != hipSuccess)
+            st = fail(SSD_ERR_HIP, "event timing failed: %s", hipGetErrorString(err));
+    }
+    for (int i = 0; i < made; ++i) (void)hipEventDestroy(ev[i]);
+    return st;
+}
+
+SSD_API ssd_status ssd_decode_step(float* state, const void* x, const float* dt, const float* A,
+                                   const void* B, const void* C, const float* D, void* y,
+                                   const ssd_shape* shape, void* stream) {
+    if (!shape) return fail(SSD_ERR_NULL, "shape is NULL");
+    ssd_status st = check_head_dims(shape);
+    if (st != SSD_OK) return st;
+    const bool any = shape->batch > 0;
+    struct {
+        const void* p;
+        const char* name;
+        bool required;
+    } ptrs[] = {{state, "state", any}, {x, "x", any}, {dt, "dt", any}, {A, "A", true},
+                {B, "B", any},         {C, "C", any}, {D, "D", true},  {y, "y", any}};
+    for (auto& q : ptrs) {
+        if (!q.p && q.required) return fail(SSD_ERR_NULL, "%s is NULL", q.name);
+        if (q.p && !aligned16(q.p)) return fail(SSD_ERR_ALIGN, "%s is not 16-byte aligned", q.name);
+    }
+    if (y && (y == x || y == B || y == C || y == (const void*)state))
+        return fail(SSD_ERR_SHAPE, "y aliases an input");
+    if (shape->batch * (int64_t)shape->nheads * shape->headdim > ((int64_t)1 << 40))
+        return fail(SSD_ERR_SHAPE, "tensor too large");
+    ssd::DecodeArgs a;
+    a.state = state;
+    a.x = x;
+    a.dt = dt;
+    a.A = A;
+    a.B = B;
+    a.C = C;
+    a.D = D;
+    a.y = y;
+    a.batch = shape->batch;
+    a.H = shape->nheads;
+    a.P = shape->headdim;
+    a.N = shape->dstate;
+    a.G = shape->ngroups;
+    a.dtype = shape->dtype;
+    const hipError_t err = ssd::launch_decode(a, (hipStream_t)stream);
+    if (err != hipSuccess)
+        return fail(SSD_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(err));
+    return ok();
+}

@@ -1,0 +1,95 @@
+// Private declarations shared by the host ABI (ssd_api.cpp) and the kernel
+// launchers (ssd_prefill.hip, ssd_decode.hip).  Not part of the public ABI.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+namespace ssd {
+
+// Everything a prefill kernel needs to map its grid index to tokens.  Built
+// on the host; for a packed batch the tables are filled on the device by the
+// plan kernel from the device copy of cu_seqlens.
+//
+// Terminology: a *chunk* is <= Q consecutive tokens of one sequence (chunks
+// restart at every sequence start).  A *segment* is <= cps consecutive chunks
+// of one sequence that one chunk-scan workgroup walks while carrying the state
+// in registers.  Every segment except the last of its sequence owns one
+// *slot* of the segment-state buffer: chunk_state writes the segment's own
+// state there and state_passing overwrites it with the state entering the
+// next segment.
+struct Plan {
+    int32_t H, P, N, G, hpg, Q, cps;
+    int32_t nseq;
+    int32_t dense;     // 1: uniform batch, descriptors are arithmetic
+    int32_t pad0;
+    int64_t L;         // dense: tokens per sequence
+    int64_t T;         // total token rows
+    int32_t nchunk_ub; // grid bound of chunk-indexed launches (exact when dense)
+    int32_t nseg_ub;   // grid bound of segment-indexed launches (exact when dense)
+    int32_t nslot_ub;  // slots in the segment-state buffer
+    int32_t cpseq;     // dense: chunks per sequence
+    int32_t spseq;     // dense: segments per sequence
+    int32_t pad1;
+    const int32_t* cu; // packed: device cu_seqlens [nseq+1]
+    int32_t* seq_tab;  // packed: per sequence {chunk0, nchunks, seg0, slot0}
+    int32_t* chunk_tab;// packed: per chunk {seq, row0, len, seg}
+    int32_t* seg_tab;  // packed: per segment {seq, chunk0, nchunks, index in sequence}
+};
+
+// Byte offsets of the workspace regions (all 256-byte aligned).
+struct Layout {
+    size_t seq_tab, chunk_tab, seg_tab;  // int32 x4 entries
+    size_t cs;      // f32 [nchunk_ub][H][Q]   decay exponent sums dA_cs
+    size_t dtc;     // f32 [nchunk_ub][H][Q]   dt per chunk and head, 0 past the chunk end
+    size_t cb;      // f32 [nchunk_ub][G][Q][Q] C_t . B_k within each chunk
+    size_t bt;      // elem [nchunk_ub][G][N][Q] B transposed per chunk, 0 past the end
+    size_t sbuf;    // f32 [nslot_ub][H][P][N] segment states, then states passed on
+    size_t total;
+};
+
+struct ScanArgs {
+    const void* x;
+    const float* dt;
+    const float* A;
+    const void* B;
+    const void* C;
+    const float* D;
+    const float* init;
+    void* y;
+    float* final_state;
+    char* ws;
+    int32_t dtype;     // 0 f32, 1 bf16
+    int32_t run_passing; // launch chunk_state + state_passing
+};
+
+struct DecodeArgs {
+    float* state;
+    const void* x;
+    const float* dt;
+    const float* A;
+    const void* B;
+    const void* C;
+    const float* D;
+    void* y;
+    int64_t batch;
+    int32_t H, P, N, G;
+    int32_t dtype;
+};
+
+// LDS bytes the chunk-scan kernel needs (0 if the tile shape is not built).
+size_t chunk_scan_lds_bytes(int dtype, int P, int N, int Q);
+
+// Queue the prefill kernels.  Returns hipSuccess or the launch error.
+// When `marks` is non-NULL, an event is recorded before the first stage and
+// after each of the six stages (plan, cumsum, cb, chunk_state, state_passing,
+// chunk_scan), seven events in all.
+hipError_t launch_prefill(const Plan& plan, const Layout& lay, const ScanArgs& a,
+                          hipStream_t stream, hipEvent_t* marks = nullptr);
+
+// Queue the decode kernel.
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+
+}  // namespace ssd

@@ -1,0 +1,171 @@
+"""C-ABI checks that need no GPU: the library loads, exports every entry point
+that include/ssd.h declares, and rejects bad arguments on the host before any
+launch (fake, never-dereferenced device addresses are used)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import mamba_ssd_chunked_02_amd as ssd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ssd.h")
+
+OK, E_NULL, E_SHAPE, E_DTYPE, E_ALIGN, E_CHUNK, E_WS, E_HIP, E_UNSUP, E_SEQ = 0, -1, -2, -3, -4, -5, -6, -7, -8, -9
+FAKE = 0x7F0000000000  # 16-byte aligned, never dereferenced: validation fails first
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(ssd.library_path()):
+        import mamba_ssd_chunked_02_amd.build as b
+        b.build()
+    return ssd.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:ssd_status|const char\*)\s+(ssd_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ["ssd_chunked_scan", "ssd_decode_step", "ssd_chunked_scan_workspace_size",
+              "ssd_status_string", "ssd_last_error_detail"]:
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for n in declared_functions():
+        assert hasattr(lib, n), n
+
+
+def test_only_the_abi_is_exported(lib):
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", ssd.library_path()], capture_output=True,
+                         text=True).stdout
+    syms = {l.split()[-1] for l in out.splitlines() if l.strip()}
+    ours = {s for s in syms if s.startswith("ssd_")}
+    assert ours == set(declared_functions())
+
+
+def shape(**kw):
+    s = ssd._Shape()
+    d = dict(batch=1, seqlen=512, nheads=4, headdim=16, dstate=16, ngroups=1, dtype=0,
+             chunks_per_segment=0)
+    d.update(kw)
+    for k, v in d.items():
+        setattr(s, k, v)
+    return s
+
+
+def ws_size(lib, sh, chunk=64):
+    n = ctypes.c_size_t(0)
+    st = lib.ssd_chunked_scan_workspace_size(ctypes.byref(sh), chunk, ctypes.byref(n))
+    return st, n.value
+
+
+def test_workspace_size_valid(lib):
+    st, n = ws_size(lib, shape())
+    assert st == OK and n > 0
+    st2, n2 = ws_size(lib, shape(seqlen=1024))
+    assert st2 == OK and n2 > n
+    st3, n3 = ws_size(lib, shape(batch=8, seqlen=8192, nheads=80, headdim=64, dstate=128, dtype=1), 256)
+    assert st3 == OK and n3 < 2 ** 31
+
+
+@pytest.mark.parametrize("kw,chunk,code", [
+    (dict(dtype=7), 64, E_DTYPE),
+    (dict(nheads=0), 64, E_SHAPE),
+    (dict(nheads=6, ngroups=4), 64, E_SHAPE),
+    (dict(headdim=12), 64, E_SHAPE),
+    (dict(headdim=136), 64, E_SHAPE),
+    (dict(dstate=264), 64, E_SHAPE),
+    (dict(dstate=4), 64, E_SHAPE),
+    (dict(batch=-1), 64, E_SHAPE),
+    (dict(seqlen=-5), 64, E_SHAPE),
+    (dict(chunks_per_segment=-1), 64, E_SHAPE),
+    (dict(), 48, E_CHUNK),
+    (dict(), 512, E_CHUNK),
+    (dict(headdim=128, dstate=256, dtype=0), 256, E_UNSUP),
+])
+def test_shape_errors(lib, kw, chunk, code):
+    st, _ = ws_size(lib, shape(**kw), chunk)
+    assert st == code
+    assert lib.ssd_last_error_detail().decode()
+
+
+def test_null_shape_and_out(lib):
+    n = ctypes.c_size_t(0)
+    assert lib.ssd_chunked_scan_workspace_size(None, 64, ctypes.byref(n)) == E_NULL
+    sh = shape()
+    assert lib.ssd_chunked_scan_workspace_size(ctypes.byref(sh), 64, None) == E_NULL
+
+
+def test_cu_seqlens_host_validation(lib):
+    cu_dev = FAKE
+    for cu, code in [([0, 5, 3, 9], E_SEQ), ([1, 5, 9, 9], E_SEQ), ([0, 5, 7, 8], E_SEQ),
+                     ([0, 5, 7, 9], OK)]:
+        arr = (ctypes.c_int32 * 4)(*cu)
+        sh = shape(batch=3, seqlen=9)
+        sh.cu_seqlens = cu_dev
+        sh.cu_seqlens_host = ctypes.addressof(arr)
+        st, _ = ws_size(lib, sh)
+        assert st == code, cu
+
+
+def scan(lib, sh, chunk=64, ws_bytes=None, **ptrs):
+    p = dict(x=FAKE, dt=FAKE, A=FAKE, B=FAKE, C=FAKE, D=FAKE, init=None, y=FAKE + 4096,
+             final=None, ws=FAKE + 8192)
+    p.update(ptrs)
+    if ws_bytes is None:
+        ws_bytes = ws_size(lib, sh, chunk)[1]
+    return lib.ssd_chunked_scan(p["x"], p["dt"], p["A"], p["B"], p["C"], p["D"], chunk, p["init"],
+                                p["y"], p["final"], ctypes.byref(sh), p["ws"], ws_bytes, None)
+
+
+def test_scan_pointer_errors(lib):
+    sh = shape()
+    for name in ["x", "dt", "A", "B", "C", "D", "y"]:
+        assert scan(lib, sh, **{name: None}) == E_NULL, name
+    assert scan(lib, sh, ws=None) == E_WS
+    for name in ["x", "dt", "A", "B", "C", "D", "y", "init", "final", "ws"]:
+        assert scan(lib, sh, **{name: FAKE + 8}) == E_ALIGN, name
+    n = ws_size(lib, sh)[1]
+    assert scan(lib, sh, ws_bytes=n - 1) == E_WS
+    assert scan(lib, sh, y=FAKE) == E_SHAPE  # y aliases x
+
+
+def test_decode_errors(lib):
+    sh = shape(batch=2)
+
+    def dec(**kw):
+        p = dict(state=FAKE, x=FAKE + 16, dt=FAKE + 32, A=FAKE + 48, B=FAKE + 64, C=FAKE + 80,
+                 D=FAKE + 96, y=FAKE + 112)
+        p.update(kw)
+        return lib.ssd_decode_step(p["state"], p["x"], p["dt"], p["A"], p["B"], p["C"], p["D"],
+                                   p["y"], ctypes.byref(kw.get("sh", sh)), None)
+
+    for name in ["state", "x", "dt", "A", "B", "C", "D", "y"]:
+        assert dec(**{name: None}) == E_NULL
+        assert dec(**{name: FAKE + 8}) == E_ALIGN
+    assert dec(y=FAKE + 16) == E_SHAPE
+    bad = shape(batch=2, ngroups=3)
+    assert lib.ssd_decode_step(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE + 16,
+                               ctypes.byref(bad), None) == E_SHAPE
+    assert lib.ssd_decode_step(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None) == E_NULL
+
+
+def test_status_strings(lib):
+    for code in [OK, E_NULL, E_SHAPE, E_DTYPE, E_ALIGN, E_CHUNK, E_WS, E_HIP, E_UNSUP, E_SEQ]:
+        s = lib.ssd_status_string(code).decode()
+        assert s and s != "unknown status"
+    assert lib.ssd_status_string(123).decode() == "unknown status"
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(ssd, "_lib", None)
+    monkeypatch.setattr(ssd, "_PKG", str(tmp_path))
+    with pytest.raises(RuntimeError, match="not built"):
+        ssd.load()

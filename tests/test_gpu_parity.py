@@ -1,0 +1,261 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle on the
+same seeded inputs.  Small cases compare every element; full-size workloads
+compare sampled (sequence, head) pairs that the oracle recomputes."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import mamba_ssd_chunked_02_amd as ssd
+from mamba_ssd_chunked_02_amd import workloads as W
+from parity import assert_close, host, oracle_scan, tdev, to_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def run_gpu(inp, chunk=None, cps=0, want_final=True):
+    g = to_gpu(inp)
+    chunk = chunk or inp.wl.chunk
+    y, fin = ssd.chunked_scan(g["x"], g["dt"], g["A"], g["B"], g["C"], g["D"], chunk,
+                              init_state=g["init"], cu_seqlens=g.get("cu"),
+                              chunks_per_segment=cps, want_final=want_final)
+    torch.cuda.synchronize()
+    return host(y), None if fin is None else host(fin)
+
+
+def check_scan(inp, chunk=None, cps=0, what=""):
+    dt = inp.wl.dtype
+    say("case:", inp.wl.name, "chunk", chunk, "cps", cps, what)
+    y, fin = run_gpu(inp, chunk, cps)
+    yr, fr = oracle_scan(inp)
+    ey = assert_close(y, yr, dt, "y " + what)
+    ef = assert_close(fin, fr, dt, "final " + what)
+    return ey, ef
+
+
+# ------------------------------------------------------------------ tiny fp32 workload
+def test_tiny_fp32_prefill_and_decode():
+    wl = W.CONFIGS[0]
+    inp = W.generate(wl, W.SEED_BASE + 0)
+    say("case: tiny fp32 config with 16 decode steps")
+    g = to_gpu(inp)
+    y, fin = ssd.chunked_scan(g["x"], g["dt"], g["A"], g["B"], g["C"], g["D"], wl.chunk,
+                              init_state=g["init"])
+    yr, fr = oracle.scan(inp.x, inp.dt, inp.A, inp.B, inp.C, inp.D, init=inp.init)
+    assert_close(host(y), yr, "f32", "y")
+    assert_close(host(fin), fr, "f32", "final")
+    state = fin.clone()
+    ref_state = fr
+    for k, d in enumerate(inp.decode):
+        yd = ssd.decode_step(state, tdev(d["x"]), tdev(d["dt"]), g["A"], tdev(d["B"]), tdev(d["C"]),
+                             g["D"])
+        yref, ref_state = oracle.decode(ref_state, d["x"], d["dt"], inp.A, d["B"], d["C"], inp.D)
+        assert_close(host(yd), yref, "f32", "decode y step %d" % k)
+        assert_close(host(state), ref_state, "f32", "decode state step %d" % k)
+
+
+# ------------------------------------------------------------------ shapes, tiles, ragged tails
+SMALL = [
+    # (batch, L, H, P, N, G, chunk, dtype, init)
+    (1, 64, 4, 16, 16, 1, 64, "f32", 0.0),
+    (2, 700, 6, 64, 128, 2, 256, "bf16", 0.1),
+    (1, 1000, 4, 64, 128, 1, 128, "bf16", 0.1),
+    (3, 333, 4, 32, 64, 4, 64, "bf16", 0.1),
+    (2, 257, 4, 64, 64, 2, 32, "f32", 0.1),
+    (1, 300, 2, 128, 128, 1, 64, "bf16", 0.1),
+    (1, 130, 2, 8, 8, 2, 64, "f32", 0.1),
+    (2, 200, 3, 24, 40, 3, 32, "bf16", 0.1),
+    (1, 513, 2, 64, 256, 1, 128, "bf16", 0.1),
+    (1, 96, 2, 128, 256, 1, 32, "bf16", 0.1),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=lambda c: "b%d-L%d-H%d-P%d-N%d-G%d-Q%d-%s" % c[:8])
+def test_small_shapes(case):
+    b, L, H, P, N, G, Q, dt, iv = case
+    wl = W.small_workload(batch=b, seqlen=L, H=H, P=P, N=N, G=G, chunk=Q, dtype=dt, init_var=iv)
+    check_scan(W.generate(wl, 11 + L), what=str(case))
+
+
+@pytest.mark.parametrize("variant", ["slow", "A0", "x0"])
+def test_decay_variants(variant):
+    """Slow decay, A = 0 and x = 0 (initial-state path only) stress the state
+    passed between chunks, which strong decay would hide."""
+    wl = W.small_workload(batch=2, seqlen=900, H=4, P=64, N=128, G=2, chunk=128, dtype="bf16",
+                          init_var=0.1)
+    kw = dict(slow=dict(A_range=(-0.05, -0.001)), A0=dict(A_zero=True), x0=dict(x_zero=True))[variant]
+    inp = W.generate(wl, 21, **kw)
+    for cps in (0, 1, 3):
+        check_scan(inp, cps=cps, what=variant)
+
+
+@pytest.mark.parametrize("chunk", [32, 64, 128, 256])
+def test_chunk_sizes_agree(chunk):
+    wl = W.small_workload(batch=1, seqlen=777, H=4, P=64, N=64, G=1, chunk=chunk, dtype="f32",
+                          init_var=0.1)
+    inp = W.generate(wl, 31, A_range=(-0.2, -0.01))
+    check_scan(inp, chunk=chunk)
+
+
+@pytest.mark.parametrize("cps", [1, 2, 3, 5, 100])
+def test_segment_lengths_agree(cps):
+    wl = W.small_workload(batch=2, seqlen=1100, H=3, P=64, N=128, G=1, chunk=64, dtype="bf16",
+                          init_var=0.1)
+    inp = W.generate(wl, 41, A_range=(-0.1, -0.001))
+    check_scan(inp, cps=cps)
+
+
+def test_edge_lengths():
+    for L in (1, 31, 32, 33, 64, 65):
+        wl = W.small_workload(batch=2, seqlen=L, H=2, P=16, N=16, G=1, chunk=32, dtype="f32",
+                              init_var=0.1)
+        check_scan(W.generate(wl, 50 + L), what="L=%d" % L)
+
+
+def test_no_initial_state_equals_zero_initial_state():
+    wl = W.small_workload(batch=1, seqlen=300, H=2, P=64, N=64, G=1, chunk=64, dtype="bf16")
+    inp = W.generate(wl, 60)
+    g = to_gpu(inp)
+    y0, f0 = ssd.chunked_scan(g["x"], g["dt"], g["A"], g["B"], g["C"], g["D"], 64)
+    z = torch.zeros_like(f0)
+    y1, f1 = ssd.chunked_scan(g["x"], g["dt"], g["A"], g["B"], g["C"], g["D"], 64, init_state=z)
+    torch.cuda.synchronize()
+    assert torch.equal(y0, y1) and torch.equal(f0, f1)
+
+
+def test_final_state_may_alias_initial_state():
+    wl = W.small_workload(batch=2, seqlen=400, H=2, P=32, N=32, G=1, chunk=64, dtype="f32",
+                          init_var=0.1)
+    inp = W.generate(wl, 61)
+    g = to_gpu(inp)
+    st = g["init"].clone()
+    y, fin = ssd.chunked_scan(g["x"], g["dt"], g["A"], g["B"], g["C"], g["D"], 64, init_state=st,
+                              final_state=st, chunks_per_segment=2)
+    torch.cuda.synchronize()
+    yr, fr = oracle.scan(inp.x, inp.dt, inp.A, inp.B, inp.C, inp.D, init=inp.init)
+    assert_close(host(st), fr, "f32", "aliased final")
+    assert_close(host(y), yr, "f32", "y")
+
+
+# ------------------------------------------------------------------ packed variable-length batches
+@pytest.mark.parametrize("lens,G,cps", [
+    ((100, 0, 513, 1, 256), 2, 0),
+    ((300, 700, 64, 65), 4, 1),
+    ((1024, 3000, 7), 8, 3),
+    ((0, 0), 1, 0),
+])
+def test_packed_batches(lens, G, cps):
+    H = 8 if G in (1, 2, 4, 8) else G
+    wl = W.small_workload(seqlens=lens, H=H, P=64, N=128, G=G, chunk=256, dtype="bf16", init_var=0.1)
+    check_scan(W.generate(wl, 70 + sum(lens)), cps=cps, what="lens=%s" % (lens,))
+
+
+def test_packed_equals_separate_dense_runs():
+    lens = (200, 450, 31)
+    wl = W.small_workload(seqlens=lens, H=4, P=64, N=64, G=2, chunk=64, dtype="f32", init_var=0.1)
+    inp = W.generate(wl, 80)
+    y, fin = run_gpu(inp)
+    cu = inp.cu_seqlens
+    for s in range(len(lens)):
+        a, b = cu[s], cu[s + 1]
+        g = dict(x=tdev(inp.x[None, a:b]), dt=tdev(inp.dt[None, a:b]), B=tdev(inp.B[None, a:b]),
+                 C=tdev(inp.C[None, a:b]))
+        ys, fs = ssd.chunked_scan(g["x"], g["dt"], tdev(inp.A), g["B"], g["C"], tdev(inp.D), 64,
+                                  init_state=tdev(inp.init[s:s + 1]))
+        torch.cuda.synchronize()
+        assert_close(y[a:b], host(ys)[0], "f32", "seq %d y" % s)
+        assert_close(fin[s], host(fs)[0], "f32", "seq %d final" % s)
+
+
+# ------------------------------------------------------------------ cache semantics
+def test_prefill_then_decode_equals_longer_prefill():
+    wl = W.small_workload(batch=2, seqlen=600, H=4, P=64, N=128, G=1, chunk=256, dtype="f32",
+                          init_var=0.1)
+    inp = W.generate(wl, 90, A_range=(-0.3, -0.01))
+    g = to_gpu(inp)
+    L, k = 600, 5
+    y_full, f_full = ssd.chunked_scan(g["x"], g["dt"], g["A"], g["B"], g["C"], g["D"], 256,
+                                      init_state=g["init"])
+    sl = slice(0, L - k)
+    _, state = ssd.chunked_scan(g["x"][:, sl].contiguous(), g["dt"][:, sl].contiguous(), g["A"],
+                                g["B"][:, sl].contiguous(), g["C"][:, sl].contiguous(), g["D"], 256,
+                                init_state=g["init"])
+    for t in range(L - k, L):
+        yd = ssd.decode_step(state, g["x"][:, t].contiguous(), g["dt"][:, t].contiguous(), g["A"],
+                             g["B"][:, t].contiguous(), g["C"][:, t].contiguous(), g["D"])
+        assert_close(host(yd), host(y_full[:, t]), "f32", "decode vs prefill y at %d" % t)
+    assert_close(host(state), host(f_full), "f32", "decode vs prefill state")
+
+
+def test_decode_state_roundtrip_through_host_is_bitwise():
+    wl = W.small_workload(batch=3, seqlen=100, H=4, P=64, N=64, G=2, chunk=64, dtype="bf16",
+                          init_var=0.1, decode_steps=2)
+    inp = W.generate(wl, 91)
+    g = to_gpu(inp)
+    _, st = ssd.chunked_scan(g["x"], g["dt"], g["A"], g["B"], g["C"], g["D"], 64, init_state=g["init"])
+    st2 = st.cpu().cuda()
+    d = inp.decode[0]
+    args = (tdev(d["x"], "bf16"), tdev(d["dt"]), g["A"], tdev(d["B"], "bf16"), tdev(d["C"], "bf16"), g["D"])
+    y1 = ssd.decode_step(st, *args)
+    y2 = ssd.decode_step(st2, *args)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2) and torch.equal(st, st2)
+
+
+@pytest.mark.parametrize("P,N,dt", [(16, 16, "f32"), (64, 128, "bf16"), (32, 256, "bf16"), (128, 8, "f32"),
+                                    (24, 40, "bf16")])
+def test_decode_shapes(P, N, dt):
+    wl = W.small_workload(batch=5, seqlen=0, H=6, P=P, N=N, G=3, dtype=dt, init_var=0.1,
+                          decode_steps=3, decode_batch=5)
+    inp = W.generate(wl, 100 + P + N)
+    state = tdev(inp.init)
+    ref = inp.init.astype(np.float64)
+    A, D = tdev(inp.A), tdev(inp.D)
+    for k, d in enumerate(inp.decode):
+        y = ssd.decode_step(state, tdev(d["x"], dt), tdev(d["dt"]), A, tdev(d["B"], dt), tdev(d["C"], dt), D)
+        yr, ref = oracle.decode(ref, d["x"], d["dt"], inp.A, d["B"], d["C"], inp.D)
+        assert_close(host(y), yr, dt, "decode y %d" % k)
+        assert_close(host(state), ref, dt, "decode state %d" % k)
+
+
+# ------------------------------------------------------------------ robustness
+def test_deterministic_and_independent_of_workspace_contents():
+    wl = W.small_workload(batch=2, seqlen=700, H=4, P=64, N=128, G=2, chunk=128, dtype="bf16",
+                          init_var=0.1)
+    inp = W.generate(wl, 110)
+    g = to_gpu(inp)
+    nbytes = ssd.workspace_size(g["x"], g["B"], 128, chunks_per_segment=2)
+    ws = torch.full((nbytes // 4,), float("nan"), device="cuda").view(torch.uint8)
+    y_nan = torch.full_like(g["x"], float("nan"))
+    f_nan = torch.full((2, 4, 64, 128), float("nan"), device="cuda")
+    y1, f1 = ssd.chunked_scan(g["x"], g["dt"], g["A"], g["B"], g["C"], g["D"], 128, init_state=g["init"],
+                              y=y_nan, final_state=f_nan, workspace=ws, chunks_per_segment=2)
+    y2, f2 = ssd.chunked_scan(g["x"], g["dt"], g["A"], g["B"], g["C"], g["D"], 128, init_state=g["init"],
+                              chunks_per_segment=2)
+    torch.cuda.synchronize()
+    assert torch.isfinite(y1.float()).all() and torch.isfinite(f1).all()
+    assert torch.equal(y1, y2) and torch.equal(f1, f2)
+
+
+def test_empty_batch_is_a_no_op():
+    x = torch.zeros((0, 10, 2, 16), device="cuda")
+    y, fin = ssd.chunked_scan(x, torch.zeros((0, 10, 2), device="cuda"), torch.zeros(2, device="cuda"),
+                              torch.zeros((0, 10, 1, 16), device="cuda"),
+                              torch.zeros((0, 10, 1, 16), device="cuda"), torch.zeros(2, device="cuda"), 64)
+    torch.cuda.synchronize()
+    assert y.shape == x.shape and fin.shape == (0, 2, 16, 16)
+
+
+def test_binding_rejects_wrong_shapes():
+    x = torch.zeros((1, 64, 2, 16), device="cuda")
+    with pytest.raises(ValueError):
+        ssd.chunked_scan(x, torch.zeros((1, 64, 3), device="cuda"), torch.zeros(2, device="cuda"),
+                         torch.zeros((1, 64, 1, 16), device="cuda"), torch.zeros((1, 64, 1, 16), device="cuda"),
+                         torch.zeros(2, device="cuda"), 64)
