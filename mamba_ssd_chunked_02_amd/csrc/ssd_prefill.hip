@@ -78,7 +78,15 @@ __global__ __launch_bounds__(kThreads) void ssd_plan_kernel(Plan pl) {
         }
         __syncthreads();
     }
-    const int nchunks = s_carry[0], nsegs = s_carry[1];
+    int nchunks = s_carry[0], nsegs = s_carry[1];
+    if (nchunks > pl.nchunk_ub || nsegs > pl.nseg_ub) {
+        // the offsets describe more tokens than the stream holds (overlapping
+        // sequences): treat every sequence as empty rather than index past the
+        // workspace regions sized for T tokens
+        for (int s = tid; s < pl.nseq; s += kThreads) ((int4*)pl.seq_tab)[s] = make_int4(0, 0, 0, 0);
+        nchunks = 0;
+        nsegs = 0;
+    }
     // chunk and segment entries; the owning sequence is the last one whose
     // first index is <= the entry (empty sequences share it with a successor)
     for (int k = tid; k < pl.nchunk_ub; k += kThreads) {
