@@ -27,9 +27,10 @@
  *     launched and nothing is written; the returned code says why and
  *     ssd_last_error_detail() gives a sentence (thread-local).
  *   - Inputs are not checked for NaN/Inf; such values propagate.
- *   - dtype of x, B, C and y is ssd_shape.dtype (fp32 or bf16); dt, A, D and
- *     every state tensor are always fp32.  Arithmetic is fp32 throughout;
- *     bf16 values are widened exactly and y is rounded to nearest even.
+ *   - dtype of x, B and C is ssd_shape.dtype (fp32 or bf16); dtype of y is
+ *     ssd_shape.ydtype (fp32 by default); dt, A, D and every state tensor are
+ *     always fp32.  Accumulation is fp32; bf16 inputs are widened exactly; a
+ *     bf16 y is rounded to nearest even.
  */
 #ifndef SSD_MI355X_H
 #define SSD_MI355X_H
@@ -78,8 +79,10 @@ typedef struct ssd_shape {
     int32_t headdim;
     int32_t dstate;
     int32_t ngroups;
-    int32_t dtype;               /* ssd_dtype */
+    int32_t dtype;               /* ssd_dtype of x, B, C */
+    int32_t ydtype;              /* ssd_dtype of y (0 = SSD_F32, the default) */
     int32_t chunks_per_segment;  /* 0 = automatic */
+    int32_t reserved;            /* must be 0 */
     const int32_t* cu_seqlens;      /* device int32 [batch+1], or NULL (dense) */
     const int32_t* cu_seqlens_host; /* optional host copy; validated when given */
 } ssd_shape;
@@ -102,7 +105,7 @@ ssd_status ssd_chunked_scan_workspace_size(const ssd_shape* shape, int32_t chunk
  *   D          [H]           fp32       skip coefficient
  *   chunk      32, 64, 128 or 256 tokens
  *   init_state [nseq, H, P, N] fp32, or NULL for zero initial states
- *   y          [rows, H, P]  dtype      output; must not alias any input
+ *   y          [rows, H, P]  ydtype     output; must not alias any input
  *   final_state[nseq, H, P, N] fp32, or NULL (not written); may alias
  *              init_state (each element is read before it is written)
  *   workspace  device scratch of at least the queried size, owned by the
@@ -127,7 +130,7 @@ ssd_status ssd_chunked_scan(const void* x, const float* dt, const float* A, cons
  *   dt    [batch, H]     fp32
  *   A, D  [H]            fp32
  *   B, C  [batch, G, N]  dtype
- *   y     [batch, H, P]  dtype    output; must not alias any input
+ *   y     [batch, H, P]  ydtype   output; must not alias any input
  * shape->seqlen, shape->cu_seqlens and shape->chunks_per_segment are ignored.
  */
 ssd_status ssd_decode_step(float* state, const void* x, const float* dt, const float* A,

@@ -41,8 +41,9 @@ class SsdError(RuntimeError):
 class _Shape(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64), ("nheads", ctypes.c_int32),
                 ("headdim", ctypes.c_int32), ("dstate", ctypes.c_int32),
-                ("ngroups", ctypes.c_int32), ("dtype", ctypes.c_int32),
-                ("chunks_per_segment", ctypes.c_int32), ("cu_seqlens", ctypes.c_void_p),
+                ("ngroups", ctypes.c_int32), ("dtype", ctypes.c_int32), ("ydtype", ctypes.c_int32),
+                ("chunks_per_segment", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("cu_seqlens", ctypes.c_void_p),
                 ("cu_seqlens_host", ctypes.c_void_p)]
 
 
@@ -106,6 +107,15 @@ def _dtype_code(t) -> int:
     raise TypeError("x/B/C must be float32 or bfloat16, got %s" % t.dtype)
 
 
+def _dtype_code_of(dtype) -> int:
+    torch = _torch()
+    if dtype == torch.float32:
+        return SSD_F32
+    if dtype == torch.bfloat16:
+        return SSD_BF16
+    raise TypeError("y must be float32 or bfloat16, got %s" % dtype)
+
+
 def _ptr(t) -> Optional[int]:
     if t is None:
         return None
@@ -137,7 +147,7 @@ def _stream_handle(t) -> int:
 
 
 def make_shape(x, B, cu_seqlens=None, cu_seqlens_host=None, chunks_per_segment: int = 0,
-               nseq: Optional[int] = None) -> Tuple[_Shape, object]:
+               nseq: Optional[int] = None, y_dtype=None) -> Tuple[_Shape, object]:
     """Build the C shape struct from tensors.  Returns (shape, keepalive)."""
     sh = _Shape()
     keep = None
@@ -156,6 +166,7 @@ def make_shape(x, B, cu_seqlens=None, cu_seqlens_host=None, chunks_per_segment: 
     sh.nheads, sh.headdim = H, P
     sh.ngroups, sh.dstate = B.shape[-2], B.shape[-1]
     sh.dtype = _dtype_code(x)
+    sh.ydtype = SSD_F32 if y_dtype is None else _dtype_code_of(y_dtype)
     sh.chunks_per_segment = chunks_per_segment
     return sh, keep
 
@@ -174,7 +185,7 @@ STAGES = ("plan", "cumsum", "cb", "chunk_state", "state_passing", "chunk_scan")
 def chunked_scan(x, dt, A, B, C, D, chunk: int = 256, init_state=None, cu_seqlens=None, *,
                  y=None, final_state=None, want_final: bool = True, workspace=None,
                  chunks_per_segment: int = 0, cu_seqlens_host: Optional[Sequence[int]] = None,
-                 stage_ms: Optional[list] = None):
+                 stage_ms: Optional[list] = None, y_dtype=None):
     """Chunked prefill.  Returns (y, final_state or None).
 
     ``cu_seqlens`` (packed batch) may be a GPU int32 tensor or a host sequence;
@@ -183,6 +194,7 @@ def chunked_scan(x, dt, A, B, C, D, chunk: int = 256, init_state=None, cu_seqlen
     ``stage_ms``: when a list is given, the call goes through the measuring
     entry point (it blocks until the kernels finish) and the list receives the
     duration in ms of each stage named in ``STAGES``.
+    ``y_dtype``: torch.float32 (default) or torch.bfloat16.
     """
     torch = _torch()
     _need_cuda(x, dt, A, B, C, D, init_state)
@@ -193,7 +205,9 @@ def chunked_scan(x, dt, A, B, C, D, chunk: int = 256, init_state=None, cu_seqlen
         cu_seqlens = torch.tensor(host_cu, dtype=torch.int32, device=x.device)
     if cu_seqlens is not None and cu_seqlens.dtype != torch.int32:
         raise TypeError("cu_seqlens must be int32")
-    sh, keep = make_shape(x, B, cu_seqlens, host_cu, chunks_per_segment)
+    if y_dtype is None:
+        y_dtype = torch.float32 if y is None else y.dtype
+    sh, keep = make_shape(x, B, cu_seqlens, host_cu, chunks_per_segment, y_dtype=y_dtype)
     nseq = sh.batch
     H, P, N = sh.nheads, sh.headdim, sh.dstate
     lead = tuple(x.shape[:-2])
@@ -203,12 +217,12 @@ def chunked_scan(x, dt, A, B, C, D, chunk: int = 256, init_state=None, cu_seqlen
     _expect(A, (H,), torch.float32, "A")
     _expect(D, (H,), torch.float32, "D")
     _expect(init_state, (nseq, H, P, N), torch.float32, "init_state")
-    _expect(y, tuple(x.shape), x.dtype, "y")
+    _expect(y, tuple(x.shape), y_dtype, "y")
     _expect(final_state, (nseq, H, P, N), torch.float32, "final_state")
     if cu_seqlens is not None:
         _expect(cu_seqlens, (nseq + 1,), torch.int32, "cu_seqlens")
     if y is None:
-        y = torch.empty_like(x)
+        y = torch.empty(tuple(x.shape), dtype=y_dtype, device=x.device)
     if final_state is None and want_final:
         final_state = torch.empty((nseq, H, P, N), dtype=torch.float32, device=x.device)
     lib = load()
@@ -230,9 +244,12 @@ def chunked_scan(x, dt, A, B, C, D, chunk: int = 256, init_state=None, cu_seqlen
     return y, final_state
 
 
-def decode_step(state, x, dt, A, B, C, D, *, y=None):
-    """One cached decode step; ``state`` [b, H, P, N] fp32 is updated in place."""
+def decode_step(state, x, dt, A, B, C, D, *, y=None, y_dtype=None):
+    """One cached decode step; ``state`` [b, H, P, N] fp32 is updated in place.
+    ``y_dtype``: torch.float32 (default) or torch.bfloat16."""
     torch = _torch()
+    if y_dtype is None:
+        y_dtype = torch.float32 if y is None else y.dtype
     _need_cuda(state, x, dt, A, B, C, D)
     b, H, P = x.shape
     G, N = B.shape[-2], B.shape[-1]
@@ -242,14 +259,15 @@ def decode_step(state, x, dt, A, B, C, D, *, y=None):
     _expect(C, (b, G, N), x.dtype, "C")
     _expect(A, (H,), torch.float32, "A")
     _expect(D, (H,), torch.float32, "D")
-    _expect(y, (b, H, P), x.dtype, "y")
+    _expect(y, (b, H, P), y_dtype, "y")
     sh = _Shape()
     sh.batch, sh.seqlen = b, 1
     sh.nheads, sh.headdim = H, P
     sh.ngroups, sh.dstate = B.shape[-2], B.shape[-1]
     sh.dtype = _dtype_code(x)
+    sh.ydtype = _dtype_code_of(y_dtype)
     if y is None:
-        y = torch.empty_like(x)
+        y = torch.empty((b, H, P), dtype=y_dtype, device=x.device)
     st = load().ssd_decode_step(_ptr(state), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
                                 _ptr(y), ctypes.byref(sh), _stream_handle(x))
     _check(st, "ssd_decode_step")

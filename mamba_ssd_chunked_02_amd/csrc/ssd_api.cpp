@@ -44,6 +44,9 @@ struct Prepared {
 ssd_status check_head_dims(const ssd_shape* sh) {
     if (sh->dtype != SSD_F32 && sh->dtype != SSD_BF16)
         return fail(SSD_ERR_DTYPE, "dtype %d is neither SSD_F32 (0) nor SSD_BF16 (1)", sh->dtype);
+    if (sh->ydtype != SSD_F32 && sh->ydtype != SSD_BF16)
+        return fail(SSD_ERR_DTYPE, "ydtype %d is neither SSD_F32 (0) nor SSD_BF16 (1)", sh->ydtype);
+    if (sh->reserved != 0) return fail(SSD_ERR_SHAPE, "reserved field must be 0");
     if (sh->nheads < 1) return fail(SSD_ERR_SHAPE, "nheads must be >= 1 (got %d)", sh->nheads);
     if (sh->ngroups < 1 || sh->nheads % sh->ngroups != 0)
         return fail(SSD_ERR_SHAPE, "ngroups %d must be >= 1 and divide nheads %d", sh->ngroups,
@@ -224,6 +227,7 @@ ssd_status scan_impl(const void* x, const float* dt, const float* A, const void*
     a.final_state = final_state;
     a.ws = (char*)workspace;
     a.dtype = shape->dtype;
+    a.y_f32 = shape->ydtype == SSD_F32 ? 1 : 0;
     a.run_passing = pr.run_passing;
     pr.plan.seq_tab = (int32_t*)(a.ws + pr.lay.seq_tab);
     pr.plan.chunk_tab = (int32_t*)(a.ws + pr.lay.chunk_tab);
@@ -311,6 +315,7 @@ SSD_API ssd_status ssd_decode_step(float* state, const void* x, const float* dt,
     a.N = shape->dstate;
     a.G = shape->ngroups;
     a.dtype = shape->dtype;
+    a.y_f32 = shape->ydtype == SSD_F32 ? 1 : 0;
     const hipError_t err = ssd::launch_decode(a, (hipStream_t)stream);
     if (err != hipSuccess)
         return fail(SSD_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(err));

@@ -22,7 +22,7 @@ template <typename T, int TPR>
 __global__ __launch_bounds__(kDecThreads) void ssd_decode_kernel(
     int64_t rows, int H, int P, int N, int G, float* __restrict__ state, const T* __restrict__ x,
     const float* __restrict__ dt, const float* __restrict__ A, const T* __restrict__ B,
-    const T* __restrict__ C, const float* __restrict__ D, T* __restrict__ y) {
+    const T* __restrict__ C, const float* __restrict__ D, void* __restrict__ y, int y_f32) {
     constexpr int RPP = kDecThreads / TPR;  // rows per pass of the block
     const int lr = threadIdx.x / TPR, j = threadIdx.x % TPR;
     const int n = 4 * j;
@@ -66,7 +66,9 @@ __global__ __launch_bounds__(kDecThreads) void ssd_decode_kernel(
             if (n < N) __builtin_nontemporal_store(ns, (f32x4*)(state + r[i] * N + n));
             if (j == 0) {
                 const int h = (int)((r[i] / P) % H);
-                y[r[i]] = (T)(part + D[h] * xv[i]);
+                const float o = part + D[h] * xv[i];
+                if (y_f32) ((float*)y)[r[i]] = o;
+                else ((bf16_t*)y)[r[i]] = (bf16_t)o;
             }
         }
     }
@@ -79,7 +81,7 @@ hipError_t run(const DecodeArgs& a, hipStream_t stream) {
     const int64_t blocks = (rows + per_block - 1) / per_block;
     hipLaunchKernelGGL((ssd_decode_kernel<T, TPR>), dim3((unsigned)blocks), dim3(kDecThreads), 0, stream,
                        rows, a.H, a.P, a.N, a.G, a.state, (const T*)a.x, a.dt, a.A, (const T*)a.B,
-                       (const T*)a.C, a.D, (T*)a.y);
+                       (const T*)a.C, a.D, a.y, a.y_f32);
     return hipGetLastError();
 }
 

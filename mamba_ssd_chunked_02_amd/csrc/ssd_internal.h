@@ -61,7 +61,8 @@ struct ScanArgs {
     void* y;
     float* final_state;
     char* ws;
-    int32_t dtype;     // 0 f32, 1 bf16
+    int32_t dtype;     // 0 f32, 1 bf16 (x, B, C)
+    int32_t y_f32;     // 1: y is fp32, 0: y is bf16
     int32_t run_passing; // launch chunk_state + state_passing
 };
 
@@ -77,6 +78,7 @@ struct DecodeArgs {
     int64_t batch;
     int32_t H, P, N, G;
     int32_t dtype;
+    int32_t y_f32;
 };
 
 // LDS bytes the chunk-scan kernel needs (0 if the tile shape is not built).

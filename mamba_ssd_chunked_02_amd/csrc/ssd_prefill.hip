@@ -205,41 +205,59 @@ __global__ __launch_bounds__(64) void ssd_cb_kernel(Plan pl, const T* __restrict
 }
 
 // ------------------------------------------------------------------ x staging
-// Writes the chunk's x tile of head h transposed into LDS, rows p (PT of them,
-// zero past P) and k contiguous (pitch LP), scaled per token: X1[p][k] =
-// x[k][p] * s1[k] and, when TWO, X2[p][k] = x[k][p] * s2[k].  Tokens past
-// the chunk end are zero.  Each thread owns 8 tokens x 8 columns.
-template <typename T, int PT, bool TWO>
-__device__ inline void stage_xT(const T* __restrict__ x, const ChunkDesc& cd, int H, int P, int h,
-                                int Q, const float* s1, T* X1, const float* s2, T* X2, int LP) {
+// Operand precision.  x, B and C are exact in their dtype.  A product with a
+// per-token fp32 factor (x * w for the state update) and the fp32 state used
+// as an operand are not: for bf16 operands each is carried as a hi/lo pair of
+// bf16 values (hi = rn(v), lo = rn(v - hi)) and contracted with two MFMAs, so
+// the operand error is ~2^-16 relative instead of 2^-8.  fp32 operands need
+// no split.
+template <typename T>
+struct Split {
+    static constexpr bool on = !__is_same(T, float);
+};
+
+// Writes the chunk's x tile of head h transposed into LDS (rows p, PT of them,
+// zero past P; k contiguous, pitch LP; tokens past the chunk end are zero):
+//   RAW:    xr[p][k] = x[k][p]                     (exact)
+//   WITH_W: xh[p][k] + xl[p][k] = x[k][p] * w[k]   (hi/lo pair; xl unused for fp32)
+// Each thread owns 8 tokens x 8 columns per step.
+template <typename T, int PT, bool RAW, bool WITH_W>
+__device__ inline void stage_x(const T* __restrict__ x, const ChunkDesc& cd, int H, int P, int h,
+                               int Q, T* xr, const float* w, T* xh, T* xl, int LP) {
+    typedef typename Tr<T>::v8 v8;
     constexpr int NPB = PT / 8;
     const int nunits = (Q / 8) * NPB;
     for (int u = threadIdx.x; u < nunits; u += kThreads) {
         const int pb = u % NPB, kb = u / NPB;
         const int p0 = pb * 8, k0 = kb * 8;
-        f32x8 v[8];
+        v8 raw[8];
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
-            v[r] = f32x8{};
+            raw[r] = v8{};
             const int kk = k0 + r;
-            if (kk < cd.len && p0 < P) v[r] = Tr<T>::widen(Tr<T>::ld8(x + ((cd.row0 + kk) * H + h) * P + p0));
+            if (kk < cd.len && p0 < P) raw[r] = Tr<T>::ld8(x + ((cd.row0 + kk) * H + h) * P + p0);
         }
-        float a1[8], a2[8];
+        float ws[8];
+        if (WITH_W) {
 #pragma unroll
-        for (int r = 0; r < 8; ++r) {
-            a1[r] = s1[k0 + r];
-            if (TWO) a2[r] = s2[k0 + r];
+            for (int r = 0; r < 8; ++r) ws[r] = w[k0 + r];
         }
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            f32x8 o1, o2;
+            if (RAW) {
+                v8 o;
 #pragma unroll
-            for (int r = 0; r < 8; ++r) {
-                o1[r] = v[r][i] * a1[r];
-                if (TWO) o2[r] = v[r][i] * a2[r];
+                for (int r = 0; r < 8; ++r) o[r] = raw[r][i];
+                Tr<T>::st8(xr + (p0 + i) * LP + k0, o);
             }
-            Tr<T>::st8(X1 + (p0 + i) * LP + k0, Tr<T>::narrow(o1));
-            if (TWO) Tr<T>::st8(X2 + (p0 + i) * LP + k0, Tr<T>::narrow(o2));
+            if (WITH_W) {
+                f32x8 o;
+#pragma unroll
+                for (int r = 0; r < 8; ++r) o[r] = (float)raw[r][i] * ws[r];
+                const v8 hi = Tr<T>::narrow(o);
+                Tr<T>::st8(xh + (p0 + i) * LP + k0, hi);
+                if (Split<T>::on) Tr<T>::st8(xl + (p0 + i) * LP + k0, Tr<T>::narrow(o - Tr<T>::widen(hi)));
+            }
         }
     }
 }
@@ -248,6 +266,21 @@ __device__ inline void stage_xT(const T* __restrict__ x, const ChunkDesc& cd, in
 // wave w owns tiles w*TPW .. w*TPW+TPW-1 (index u -> nt = u / NPT, pt = u % NPT).
 // Accumulator register v of tile (nt, pt) holds S[p = 32pt + lane%32]
 // [n = 32nt + 8(v/4) + 4(lane/32) + v%4].
+
+// S^T(tile) <- dec * S^T + B^T(rows n) . xw(cols p) over the chunk's Q tokens,
+// xw given as the hi/lo pair xh/xl in LDS (pitch LP).
+template <typename T>
+__device__ inline void state_update_tile(f32x16& st, float dec, const T* __restrict__ btk, int n, int N,
+                                         int Q, const T* xh, const T* xl, int p, int LP, int half) {
+    typedef typename Tr<T>::v8 v8;
+    st *= dec;
+    for (int k0 = 0; k0 < Q; k0 += 16) {
+        v8 a = {};
+        if (n < N) a = Tr<T>::ld8(btk + (size_t)n * Q + k0 + 8 * half);
+        mma16(st, a, Tr<T>::ld8(xh + p * LP + k0 + 8 * half));
+        if (Split<T>::on) mma16(st, a, Tr<T>::ld8(xl + p * LP + k0 + 8 * half));
+    }
+}
 
 // ------------------------------------------------------------------ chunk_state
 // grid (segments, H).  For every segment that is not the last of its sequence,
@@ -262,12 +295,12 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_state_kernel(
     const int h = blockIdx.y;
     if (sd.seq < 0 || sd.last) return;
     constexpr int NPT = PT / 32, NNT = NT / 32, NTILE = NPT * NNT, TPW = (NTILE + 3) / 4;
-    typedef typename Tr<T>::v8 v8;
     const int Q = pl.Q, P = pl.P, N = pl.N, H = pl.H, G = pl.G;
     const int g = h / pl.hpg;
     const int LP = Q + 8;
-    T* xw = (T*)smem;
-    float* wl = (float*)(smem + (size_t)PT * LP * sizeof(T));
+    T* xh = (T*)smem;
+    T* xl = xh + PT * LP;
+    float* wl = (float*)(xl + (Split<T>::on ? PT * LP : 0));
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, half = lane >> 5, col = lane & 31;
     f32x16 st[TPW];
 #pragma unroll
@@ -280,24 +313,16 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_state_kernel(
         const float cl = csk[Q - 1];
         for (int q = threadIdx.x; q < Q; q += kThreads) wl[q] = __expf(cl - csk[q]) * dtk[q];
         __syncthreads();
-        stage_xT<T, PT, false>(x, cd, H, P, h, Q, wl, xw, nullptr, nullptr, LP);
+        stage_x<T, PT, false, true>(x, cd, H, P, h, Q, nullptr, wl, xh, xl, LP);
         __syncthreads();
         const float dec = __expf(cl);
         const T* btk = bt + ((size_t)kc * G + g) * N * Q;
 #pragma unroll
         for (int i = 0; i < TPW; ++i) {
             const int u = wave * TPW + i;
-            if (u < NTILE) {
-                const int nt = u / NPT, pt = u % NPT;
-                const int n = 32 * nt + col, p = 32 * pt + col;
-                st[i] *= dec;
-                for (int k0 = 0; k0 < Q; k0 += 16) {
-                    v8 a = {};
-                    if (n < N) a = Tr<T>::ld8(btk + (size_t)n * Q + k0 + 8 * half);
-                    const v8 b = Tr<T>::ld8(xw + p * LP + k0 + 8 * half);
-                    mma16(st[i], a, b);
-                }
-            }
+            if (u < NTILE)
+                state_update_tile<T>(st[i], dec, btk, 32 * (u / NPT) + col, N, Q, xh, xl,
+                                     32 * (u % NPT) + col, LP, half);
         }
         __syncthreads();
     }
@@ -322,8 +347,8 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_state_kernel(
 // ------------------------------------------------------------------ state_passing
 // grid (ceil(P*N/4/256), H, nseq).  Sequential over the segments of one
 // sequence, four (p, n) elements per thread, fp32:
-//   slot_j <- h (state entering segment j+1);  h <- exp(sum of cs_last over
-//   segment j) h + S_j.
+//   h <- exp(sum of cs_last over segment j) h + S_j;  slot_j <- h, the state
+//   entering segment j+1 (S_j is what slot_j held before).
 // A sequence without tokens gets final = initial state here.
 __global__ __launch_bounds__(kThreads) void ssd_state_passing_kernel(
     Plan pl, const float* __restrict__ cs, float* __restrict__ sbuf, const float* __restrict__ init,
@@ -348,39 +373,43 @@ __global__ __launch_bounds__(kThreads) void ssd_state_passing_kernel(
         const float dec = __expf(lsum);
         float* slot = sbuf + ((size_t)(si.w + j) * pl.H + h) * PN + e;
         const f32x4 own = *(const f32x4*)slot;
-        *(f32x4*)slot = st;
         st = dec * st + own;
+        *(f32x4*)slot = st;
     }
 }
 
 // ------------------------------------------------------------------ chunk_scan
 // grid (segments, H).  For each chunk of the segment, in order:
-//   Y^T[p][t]  = exp(cs_t) sum_n S[p][n] C[t][n]                  (state term)
-//              + sum_{k<=t} xd[k][p] cb[t][k] exp(cs_t - cs_k)     (causal intra-chunk term)
-//   y[t][p]    = Y^T[p][t] + D x[t][p]
-//   S^T       <- exp(cs_last) S^T + B^T xw                         (carry to the next chunk)
-// with xd = x dt and xw = x dt exp(cs_last - cs_k).  The state lives in fp32
-// accumulators; its MFMA operand copy (dtype T) sits in LDS as sl[p][n].
-// t-tiles are dealt to waves in snake order so the causal work balances.
+//   Y^T[p][t]  = exp(cs_t) sum_n S[p][n] C[t][n]                        (state term)
+//              + sum_{k<=t} x[k][p] cb[t][k] exp(cs_t - cs_k) dt_k        (causal intra-chunk term)
+//   y[t][p]    = Y^T[p][t] + D x[t][p]                                   (written in fp32 or bf16)
+//   S^T       <- exp(cs_last) S^T + B^T (x dt exp(cs_last - cs_k))       (carry to the next chunk)
+// The state lives in fp32 accumulators; its operand copy sits in LDS as a
+// hi/lo pair sh/sl[p][n].  The decay-weighted mask is built in registers from
+// cb, one bf16 rounding per element.  t-tiles are dealt to waves in snake
+// order so the causal work balances.
 template <typename T, int PT, int NT>
 __global__ __launch_bounds__(kThreads) void ssd_chunk_scan_kernel(
     Plan pl, const T* __restrict__ x, const float* __restrict__ cs, const float* __restrict__ dtc,
     const T* __restrict__ Cm, const float* __restrict__ cb, const T* __restrict__ bt,
     const float* __restrict__ D, const float* __restrict__ init, const float* __restrict__ sbuf,
-    T* __restrict__ y, float* __restrict__ fin) {
+    void* __restrict__ yv, int y_f32, float* __restrict__ fin) {
     extern __shared__ __align__(16) char smem[];
     const SegDesc sd = seg_desc(pl, blockIdx.x);
     const int h = blockIdx.y;
     if (sd.seq < 0) return;
+    constexpr bool SP = Split<T>::on;
     constexpr int NPT = PT / 32, NNT = NT / 32, NTILE = NPT * NNT, TPW = (NTILE + 3) / 4;
     typedef typename Tr<T>::v8 v8;
     const int Q = pl.Q, P = pl.P, N = pl.N, H = pl.H, G = pl.G;
     const int g = h / pl.hpg;
     const int LP = Q + 8, LS = NT + 8;
-    T* xd = (T*)smem;
-    T* xw = xd + PT * LP;
-    T* sl = xw + PT * LP;
-    float* csl = (float*)(sl + PT * LS);
+    T* xr = (T*)smem;
+    T* xh = xr + PT * LP;
+    T* xl = xh + PT * LP;
+    T* sh = xl + (SP ? PT * LP : 0);
+    T* sl = sh + PT * LS;
+    float* csl = (float*)(sl + (SP ? PT * LS : 0));
     float* dtl = csl + Q;
     float* wl = dtl + Q;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, half = lane >> 5, col = lane & 31;
@@ -423,8 +452,16 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_scan_kernel(
 #pragma unroll
                 for (int vg = 0; vg < 4; ++vg) {
                     const int n = 32 * nt + 8 * vg + 4 * half;
-                    Tr<T>::st4(sl + p * LS + n, f32x4{st[i][4 * vg], st[i][4 * vg + 1],
-                                                      st[i][4 * vg + 2], st[i][4 * vg + 3]});
+                    const f32x4 v = f32x4{st[i][4 * vg], st[i][4 * vg + 1], st[i][4 * vg + 2],
+                                          st[i][4 * vg + 3]};
+                    if (SP) {
+                        const bf16x4 hi = __builtin_convertvector(v, bf16x4);
+                        *(bf16x4*)((bf16_t*)sh + p * LS + n) = hi;
+                        *(bf16x4*)((bf16_t*)sl + p * LS + n) =
+                            __builtin_convertvector(v - __builtin_convertvector(hi, f32x4), bf16x4);
+                    } else {
+                        Tr<T>::st4(sh + p * LS + n, v);
+                    }
                 }
             }
         }
@@ -446,7 +483,8 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_scan_kernel(
             wl[q] = __expf(cl - a) * d;
         }
         __syncthreads();
-        stage_xT<T, PT, true>(x, cd, H, P, h, Q, dtl, xd, wl, xw, LP);
+        if (update) stage_x<T, PT, true, true>(x, cd, H, P, h, Q, xr, wl, xh, xl, LP);
+        else stage_x<T, PT, true, false>(x, cd, H, P, h, Q, xr, nullptr, nullptr, nullptr, LP);
         __syncthreads();
 
         const float* cbk = cb + ((size_t)kc * G + g) * Q * Q;
@@ -467,8 +505,9 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_scan_kernel(
                     if (tv && n < N) b = Tr<T>::ld8(crow + n);
 #pragma unroll
                     for (int pt = 0; pt < NPT; ++pt) {
-                        const v8 a = Tr<T>::ld8(sl + (32 * pt + col) * LS + n0 + 8 * half);
-                        mma16(ya[pt], a, b);
+                        const int off = (32 * pt + col) * LS + n0 + 8 * half;
+                        mma16(ya[pt], Tr<T>::ld8(sh + off), b);
+                        if (SP) mma16(ya[pt], Tr<T>::ld8(sl + off), b);
                     }
                 }
                 const float e = __expf(cst);
@@ -488,53 +527,44 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_scan_kernel(
                     for (int i = 0; i < 8; ++i) {
                         const int kk = kb + i;
                         const float gv = i < 4 ? g0[i] : g1[i - 4];
-                        const float e = (!diag || kk <= t) ? __expf(cst - csl[kk]) : 0.f;
-                        m[i] = (!diag || kk <= t) ? gv * e : 0.f;
+                        const bool keep = !diag || kk <= t;
+                        const float e = keep ? __expf(cst - csl[kk]) : 0.f;
+                        m[i] = keep ? gv * e * dtl[kk] : 0.f;
                     }
                     const v8 b = Tr<T>::narrow(m);
 #pragma unroll
-                    for (int pt = 0; pt < NPT; ++pt) {
-                        const v8 a = Tr<T>::ld8(xd + (32 * pt + col) * LP + kb);
-                        mma16(ya[pt], a, b);
-                    }
+                    for (int pt = 0; pt < NPT; ++pt) mma16(ya[pt], Tr<T>::ld8(xr + (32 * pt + col) * LP + kb), b);
                 }
             }
             if (tv) {
-                const T* xr = x + ((cd.row0 + t) * H + h) * P;
-                T* yr = y + ((cd.row0 + t) * H + h) * P;
+                const T* xrow = x + ((cd.row0 + t) * H + h) * P;
+                const size_t yoff = ((cd.row0 + t) * H + h) * P;
 #pragma unroll
                 for (int pt = 0; pt < NPT; ++pt) {
 #pragma unroll
                     for (int vg = 0; vg < 4; ++vg) {
                         const int p = 32 * pt + 8 * vg + 4 * half;
                         if (p < P) {
-                            const f32x4 xv = Tr<T>::ld4(xr + p);
+                            const f32x4 xv = Tr<T>::ld4(xrow + p);
                             const f32x4 o = f32x4{ya[pt][4 * vg], ya[pt][4 * vg + 1], ya[pt][4 * vg + 2],
                                                   ya[pt][4 * vg + 3]} + Dh * xv;
-                            Tr<T>::st4(yr + p, o);
+                            if (y_f32) *(f32x4*)((float*)yv + yoff + p) = o;
+                            else Tr<bf16_t>::st4((bf16_t*)yv + yoff + p, o);
                         }
                     }
                 }
             }
         }
         if (update) {
-            __syncthreads();  // all reads of the state operand sl are done
+            __syncthreads();  // all reads of the state operand sh/sl are done
             const float dec = __expf(cl);
             const T* btk = bt + ((size_t)kc * G + g) * N * Q;
 #pragma unroll
             for (int i = 0; i < TPW; ++i) {
                 const int u = wave * TPW + i;
-                if (u < NTILE) {
-                    const int nt = u / NPT, pt = u % NPT;
-                    const int n = 32 * nt + col, p = 32 * pt + col;
-                    st[i] *= dec;
-                    for (int k0 = 0; k0 < Q; k0 += 16) {
-                        v8 a = {};
-                        if (n < N) a = Tr<T>::ld8(btk + (size_t)n * Q + k0 + 8 * half);
-                        const v8 b = Tr<T>::ld8(xw + p * LP + k0 + 8 * half);
-                        mma16(st[i], a, b);
-                    }
-                }
+                if (u < NTILE)
+                    state_update_tile<T>(st[i], dec, btk, 32 * (u / NPT) + col, N, Q, xh, xl,
+                                         32 * (u % NPT) + col, LP, half);
             }
             state_to_lds();
             zero_state = false;
@@ -563,11 +593,13 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_scan_kernel(
 
 template <typename T, int PT, int NT>
 size_t scan_lds(int Q) {
-    return (size_t)2 * PT * (Q + 8) * sizeof(T) + (size_t)PT * (NT + 8) * sizeof(T) + 3 * Q * sizeof(float);
+    const size_t nx = Split<T>::on ? 3 : 2, ns = Split<T>::on ? 2 : 1;
+    return nx * PT * (Q + 8) * sizeof(T) + ns * PT * (NT + 8) * sizeof(T) + 3 * Q * sizeof(float);
 }
 template <typename T, int PT>
 size_t state_lds(int Q) {
-    return (size_t)PT * (Q + 8) * sizeof(T) + Q * sizeof(float);
+    const size_t nx = Split<T>::on ? 2 : 1;
+    return nx * PT * (Q + 8) * sizeof(T) + Q * sizeof(float);
 }
 
 template <typename F>
@@ -631,7 +663,7 @@ hipError_t run_prefill(const Plan& pl, const Layout& lay, const ScanArgs& a, hip
         auto* k4 = ssd_chunk_scan_kernel<T, PT, NT>;
         if ((err = allow_lds(k4, lds)) != hipSuccess) return err;
         hipLaunchKernelGGL(k4, dim3(pl.nseg_ub, pl.H), dim3(kThreads), lds, stream, pl, x, cs, dtc, C,
-                           cbm, bt, a.D, a.init, sbuf, (T*)a.y, a.final_state);
+                           cbm, bt, a.D, a.init, sbuf, a.y, a.y_f32, a.final_state);
         if ((err = hipGetLastError()) != hipSuccess) return err;
     }
     if ((err = mark(6)) != hipSuccess) return err;
@@ -658,7 +690,8 @@ size_t chunk_scan_lds_bytes(int dtype, int P, int N, int Q) {
     const int PT = P <= 32 ? 32 : P <= 64 ? 64 : 128;
     const int NT = N <= 32 ? 32 : N <= 64 ? 64 : N <= 128 ? 128 : 256;
     const size_t es = dtype == 1 ? 2 : 4;
-    return (size_t)2 * PT * (Q + 8) * es + (size_t)PT * (NT + 8) * es + 3 * Q * sizeof(float);
+    const size_t nx = dtype == 1 ? 3 : 2, ns = dtype == 1 ? 2 : 1;  // bf16 keeps hi/lo pairs
+    return nx * PT * (Q + 8) * es + ns * PT * (NT + 8) * es + 3 * Q * sizeof(float);
 }
 
 hipError_t launch_prefill(const Plan& plan, const Layout& lay, const ScanArgs& a, hipStream_t stream,

@@ -73,7 +73,8 @@ SMALL = [
     (1, 130, 2, 8, 8, 2, 64, "f32", 0.1),
     (2, 200, 3, 24, 40, 3, 32, "bf16", 0.1),
     (1, 513, 2, 64, 256, 1, 128, "bf16", 0.1),
-    (1, 96, 2, 128, 256, 1, 32, "bf16", 0.1),
+    (1, 96, 2, 64, 256, 1, 32, "bf16", 0.1),
+    (1, 160, 2, 128, 128, 2, 32, "bf16", 0.1),
 ]
 
 
@@ -233,7 +234,7 @@ def test_deterministic_and_independent_of_workspace_contents():
     g = to_gpu(inp)
     nbytes = ssd.workspace_size(g["x"], g["B"], 128, chunks_per_segment=2)
     ws = torch.full((nbytes // 4,), float("nan"), device="cuda").view(torch.uint8)
-    y_nan = torch.full_like(g["x"], float("nan"))
+    y_nan = torch.full(tuple(g["x"].shape), float("nan"), device="cuda")
     f_nan = torch.full((2, 4, 64, 128), float("nan"), device="cuda")
     y1, f1 = ssd.chunked_scan(g["x"], g["dt"], g["A"], g["B"], g["C"], g["D"], 128, init_state=g["init"],
                               y=y_nan, final_state=f_nan, workspace=ws, chunks_per_segment=2)
@@ -242,6 +243,28 @@ def test_deterministic_and_independent_of_workspace_contents():
     torch.cuda.synchronize()
     assert torch.isfinite(y1.float()).all() and torch.isfinite(f1).all()
     assert torch.equal(y1, y2) and torch.equal(f1, f2)
+
+
+def test_bf16_output_is_the_rounded_fp32_output():
+    """y in bf16 is exactly the fp32 y rounded to nearest even (same kernels,
+    different store), for the prefill and the decode step."""
+    wl = W.small_workload(batch=2, seqlen=500, H=4, P=64, N=128, G=2, chunk=128, dtype="bf16",
+                          init_var=0.1, decode_steps=1)
+    inp = W.generate(wl, 120)
+    g = to_gpu(inp)
+    y32, f32 = ssd.chunked_scan(g["x"], g["dt"], g["A"], g["B"], g["C"], g["D"], 128, init_state=g["init"])
+    y16, f16 = ssd.chunked_scan(g["x"], g["dt"], g["A"], g["B"], g["C"], g["D"], 128, init_state=g["init"],
+                                y_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert y16.dtype == torch.bfloat16
+    assert torch.equal(y16, y32.to(torch.bfloat16)) and torch.equal(f16, f32)
+    d = inp.decode[0]
+    args = (tdev(d["x"], "bf16"), tdev(d["dt"]), g["A"], tdev(d["B"], "bf16"), tdev(d["C"], "bf16"), g["D"])
+    s1, s2 = f32.clone(), f32.clone()
+    yd32 = ssd.decode_step(s1, *args)
+    yd16 = ssd.decode_step(s2, *args, y_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert torch.equal(yd16, yd32.to(torch.bfloat16)) and torch.equal(s1, s2)
 
 
 def test_empty_batch_is_a_no_op():
