@@ -177,16 +177,16 @@ def test_packed_equals_separate_dense_runs():
 
 # ------------------------------------------------------------------ cache semantics
 def test_prefill_then_decode_equals_longer_prefill():
-    wl = W.small_workload(batch=2, seqlen=600, H=4, P=64, N=128, G=1, chunk=256, dtype="f32",
+    wl = W.small_workload(batch=2, seqlen=600, H=4, P=64, N=128, G=1, chunk=128, dtype="f32",
                           init_var=0.1)
     inp = W.generate(wl, 90, A_range=(-0.3, -0.01))
     g = to_gpu(inp)
     L, k = 600, 5
-    y_full, f_full = ssd.chunked_scan(g["x"], g["dt"], g["A"], g["B"], g["C"], g["D"], 256,
+    y_full, f_full = ssd.chunked_scan(g["x"], g["dt"], g["A"], g["B"], g["C"], g["D"], 128,
                                       init_state=g["init"])
     sl = slice(0, L - k)
     _, state = ssd.chunked_scan(g["x"][:, sl].contiguous(), g["dt"][:, sl].contiguous(), g["A"],
-                                g["B"][:, sl].contiguous(), g["C"][:, sl].contiguous(), g["D"], 256,
+                                g["B"][:, sl].contiguous(), g["C"][:, sl].contiguous(), g["D"], 128,
                                 init_state=g["init"])
     for t in range(L - k, L):
         yd = ssd.decode_step(state, g["x"][:, t].contiguous(), g["dt"][:, t].contiguous(), g["A"],
