@@ -138,7 +138,7 @@ def main():
     x, dtt, A, Bm, Cm, D = (up(inp.x, True), up(inp.dt), up(inp.A), up(inp.B, True),
                             up(inp.C, True), up(inp.D))
     init = up(inp.init)
-    y = torch.empty_like(x)
+    y = torch.empty(tuple(x.shape), dtype=torch.float32, device=dev)  # fp32 y (the default)
     fin = torch.empty_like(init)
     nbytes = ssd.workspace_size(x, Bm, wl.chunk, chunks_per_segment=args.chunks_per_segment)
     ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
@@ -148,7 +148,7 @@ def main():
     d0 = dinp.decode[0]
     dx, ddt, dA, dB, dC, dD = (up(d0["x"], True), up(d0["dt"]), up(dinp.A), up(d0["B"], True),
                                up(d0["C"], True), up(dinp.D))
-    dy = torch.empty_like(dx)
+    dy = torch.empty(tuple(dx.shape), dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
 
     def prefill(stage_ms=None):

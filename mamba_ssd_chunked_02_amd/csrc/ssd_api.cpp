@@ -148,8 +148,8 @@ ssd_status prepare(const ssd_shape* sh, int32_t chunk, Prepared* out) {
     L.seg_tab = take(packed ? (size_t)pl.nseg_ub * 16 : 0);
     L.cs = take((size_t)pl.nchunk_ub * pl.H * chunk * 4);
     L.dtc = take((size_t)pl.nchunk_ub * pl.H * chunk * 4);
-    L.cb = take((size_t)pl.nchunk_ub * pl.G * chunk * chunk * 4);
-    L.bt = take((size_t)pl.nchunk_ub * pl.G * pl.N * chunk * es);
+    L.cb = take((size_t)pl.nchunk_ub * pl.G * chunk * chunk * es);
+    L.bt = take((size_t)pl.nchunk_ub * pl.G * ssd::padded_dstate(pl.N) * chunk * es);
     L.sbuf = take((size_t)pl.nslot_ub * pl.H * pl.P * pl.N * 4);
     L.total = std::max<size_t>(off, 256);
     return SSD_OK;

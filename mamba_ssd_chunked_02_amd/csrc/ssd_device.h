@@ -24,7 +24,10 @@ struct Tr;
 
 template <>
 struct Tr<bf16_t> {
+    typedef bf16_t elem;
     typedef bf16x8 v8;
+    typedef bf16x4 v4;
+    __device__ static inline v4 ld4raw(const bf16_t* p) { return *(const v4*)p; }
     __device__ static inline v8 ld8(const bf16_t* p) { return *(const v8*)p; }
     __device__ static inline void st8(bf16_t* p, v8 v) { *(v8*)p = v; }
     __device__ static inline f32x8 widen(v8 v) { return __builtin_convertvector(v, f32x8); }
@@ -39,7 +42,10 @@ struct Tr<bf16_t> {
 
 template <>
 struct Tr<float> {
+    typedef float elem;
     typedef f32x8 v8;
+    typedef f32x4 v4;
+    __device__ static inline v4 ld4raw(const float* p) { return *(const v4*)p; }
     __device__ static inline v8 ld8(const float* p) {
         f32x4 a = *(const f32x4*)p;
         f32x4 b = *(const f32x4*)(p + 4);

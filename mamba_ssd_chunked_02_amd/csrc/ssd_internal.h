@@ -44,8 +44,8 @@ struct Layout {
     size_t seq_tab, chunk_tab, seg_tab;  // int32 x4 entries
     size_t cs;      // f32 [nchunk_ub][H][Q]   decay exponent sums dA_cs
     size_t dtc;     // f32 [nchunk_ub][H][Q]   dt per chunk and head, 0 past the chunk end
-    size_t cb;      // f32 [nchunk_ub][G][Q][Q] C_t . B_k within each chunk
-    size_t bt;      // elem [nchunk_ub][G][N][Q] B transposed per chunk, 0 past the end
+    size_t cb;      // elem [nchunk_ub][G][Q][Q] C_t . B_k within each chunk
+    size_t bt;      // elem [nchunk_ub][G][NT][Q] B transposed per chunk, 0 past the end and N
     size_t sbuf;    // f32 [nslot_ub][H][P][N] segment states, then states passed on
     size_t total;
 };
@@ -80,6 +80,9 @@ struct DecodeArgs {
     int32_t dtype;
     int32_t y_f32;
 };
+
+// dstate padded to the 32-row tiles the kernels use.
+inline int padded_dstate(int N) { return N <= 32 ? 32 : N <= 64 ? 64 : N <= 128 ? 128 : 256; }
 
 // LDS bytes the chunk-scan kernel needs (0 if the tile shape is not built).
 size_t chunk_scan_lds_bytes(int dtype, int P, int N, int Q);

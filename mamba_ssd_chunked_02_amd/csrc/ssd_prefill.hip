@@ -161,12 +161,13 @@ __global__ __launch_bounds__(kThreads) void ssd_cumsum_kernel(Plan pl, const flo
 }
 
 // ------------------------------------------------------------------ C.B^T
-// grid (chunks, G, Q/32), one wave: row tile ti of cb = C B^T for column
-// tiles kj <= ti (the causal part the chunk scan reads), plus columns
-// [32 ti, 32 ti + 32) of B^T.  Rows/columns past the chunk end are zero.
+// grid (chunks, G, Q/32), one wave: row tile ti of cb = C B^T (stored in the
+// input dtype) for column tiles kj <= ti, the causal part the chunk scan
+// reads; plus columns [32 ti, 32 ti + 32) of B^T with rows padded with zeros
+// to ntp (a multiple of 32).  Rows/columns past the chunk end are zero.
 template <typename T>
-__global__ __launch_bounds__(64) void ssd_cb_kernel(Plan pl, const T* __restrict__ B,
-                                                    const T* __restrict__ C, float* __restrict__ cb,
+__global__ __launch_bounds__(64) void ssd_cb_kernel(Plan pl, int ntp, const T* __restrict__ B,
+                                                    const T* __restrict__ C, T* __restrict__ cb,
                                                     T* __restrict__ bt) {
     const int k = blockIdx.x, g = blockIdx.y, ti = blockIdx.z;
     const ChunkDesc cd = chunk_desc(pl, k);
@@ -176,172 +177,313 @@ __global__ __launch_bounds__(64) void ssd_cb_kernel(Plan pl, const T* __restrict
     typedef typename Tr<T>::v8 v8;
     const int t = 32 * ti + col;
     const bool tv = t < cd.len;
-    const T* crow = C + ((cd.row0 + t) * G + g) * N;
-    float* out = cb + ((size_t)k * G + g) * Q * Q;
+    const T* crow = C + ((cd.row0 + (tv ? t : 0)) * G + g) * N;
+    T* out = cb + ((size_t)k * G + g) * Q * Q;
     for (int kj = 0; kj <= ti; ++kj) {
         f32x16 acc = {};
         const int kk = 32 * kj + col;
         const bool kv = kk < cd.len;
-        const T* brow = B + ((cd.row0 + kk) * G + g) * N;
+        const T* brow = B + ((cd.row0 + (kv ? kk : 0)) * G + g) * N;
         for (int n0 = 0; n0 < N; n0 += 16) {
             const int n = n0 + 8 * half;
-            v8 a = {}, b = {};
-            if (tv && n < N) a = Tr<T>::ld8(crow + n);
-            if (kv && n < N) b = Tr<T>::ld8(brow + n);
-            mma16(acc, a, b);
+            const bool nv = n < N;
+            const v8 a0 = Tr<T>::ld8(crow + (nv ? n : 0));
+            const v8 b0 = Tr<T>::ld8(brow + (nv ? n : 0));
+            mma16(acc, (tv && nv) ? a0 : v8{}, (kv && nv) ? b0 : v8{});
         }
 #pragma unroll
-        for (int v = 0; v < 16; ++v) out[(size_t)(32 * ti + acc_row(v, lane)) * Q + 32 * kj + col] = acc[v];
+        for (int v = 0; v < 16; ++v) out[(size_t)(32 * ti + acc_row(v, lane)) * Q + 32 * kj + col] = (T)acc[v];
     }
-    T* btk = bt + ((size_t)k * G + g) * N * Q;
-    for (int idx = lane; idx < 32 * (N / 8); idx += 64) {
+    T* btk = bt + ((size_t)k * G + g) * ntp * Q;
+    for (int idx = lane; idx < 32 * (ntp / 8); idx += 64) {
         const int kk = idx & 31, ng = idx >> 5;
         const int kr = 32 * ti + kk;
-        v8 b = {};
-        if (kr < cd.len) b = Tr<T>::ld8(B + ((cd.row0 + kr) * G + g) * N + 8 * ng);
+        const bool ok = kr < cd.len && 8 * ng < N;
+        const v8 bv = Tr<T>::ld8(B + ((cd.row0 + (ok ? kr : 0)) * G + g) * N + (ok ? 8 * ng : 0));
+        const v8 b = ok ? bv : v8{};
 #pragma unroll
         for (int i = 0; i < 8; ++i) btk[(size_t)(8 * ng + i) * Q + kr] = b[i];
     }
 }
 
-// ------------------------------------------------------------------ x staging
-// Operand precision.  x, B and C are exact in their dtype.  A product with a
-// per-token fp32 factor (x * w for the state update) and the fp32 state used
-// as an operand are not: for bf16 operands each is carried as a hi/lo pair of
-// bf16 values (hi = rn(v), lo = rn(v - hi)) and contracted with two MFMAs, so
-// the operand error is ~2^-16 relative instead of 2^-8.  fp32 operands need
-// no split.
+// ------------------------------------------------------------------ shared pieces
+// Operand precision.  x, B, C are exact in their dtype.  Three products are
+// rounded to the operand dtype: C.B^T (once, by the cb kernel), x scaled by a
+// per-token fp32 weight, and the fp32 state used as an operand.  For bf16 the
+// last two are carried as hi/lo pairs (hi = rn(v), lo = rn(v - hi)) and
+// contracted with two MFMAs where the state's precision depends on them (the
+// state term of y and the state update), which keeps that error ~2^-16
+// relative; the intra-chunk term uses the hi part only.  fp32 operands are not
+// split.
 template <typename T>
 struct Split {
     static constexpr bool on = !__is_same(T, float);
 };
 
-// Writes the chunk's x tile of head h transposed into LDS (rows p, PT of them,
-// zero past P; k contiguous, pitch LP; tokens past the chunk end are zero):
-//   RAW:    xr[p][k] = x[k][p]                     (exact)
-//   WITH_W: xh[p][k] + xl[p][k] = x[k][p] * w[k]   (hi/lo pair; xl unused for fp32)
-// Each thread owns 8 tokens x 8 columns per step.
-template <typename T, int PT, bool RAW, bool WITH_W>
-__device__ inline void stage_x(const T* __restrict__ x, const ChunkDesc& cd, int H, int P, int h,
-                               int Q, T* xr, const float* w, T* xh, T* xl, int LP) {
+// Workgroup layout of the chunk-walking kernels: one wave per 32-wide tile of
+// the head dimension (NPT waves).  Wave pt owns columns p in [32pt, 32pt+32)
+// of the state S (P x N) and of y, for every n and every token, so the state
+// never leaves its registers: st[nt] is the 32x32 tile S^T[32nt.., 32pt..] in
+// accumulator layout, i.e. register v of lane l holds
+//   S[p = 32pt + l%32][n = 32nt + 8(v/4) + 4(l/32) + v%4].
+//
+// Decay bookkeeping.  The chunk is cut into 32-token blocks j with start
+// s_j = 32j - 1 and end e_j = 32j + 31 (cs_{-1} := 0).  Per chunk the
+// workgroup shares these fp32 tables in LDS:
+//   wb[k]   = exp(cs_{e(k)} - cs_k) dt_k          weight of token k to its block end (<= dt_k)
+//   gam[j]  = exp(cs_{e_j} - cs_{s_j})            decay across block j (<= 1)
+//   ul[t]   = exp(cs_t - cs_{s(t)})               decay from the block start to t (<= 1)
+//   ue[t]   = exp(cs_t - cs_{e(t)})               = ul[t] / gam[j] (>= 1)
+//   fast[j] = decay across block j below kFastBlockDecay (so ue stays finite)
+// Every factor exp(cs_t - cs_k) dt_k with k <= t then equals
+//   ul[t] * (prod of gam over the blocks strictly between k's block and t's) * wb[k] / ...
+// which both the output and the state update evaluate with a Horner scheme:
+// one 16-register multiply per block, no per-element exponentials, and all
+// factors <= 1 (an underflow only ever drops a term below 1e-38 of dt x).
+constexpr float kFastBlockDecay = 60.f;
+
+struct ChunkTables {
+    float* csl;  // [Q]
+    float* dtl;  // [Q]
+    float* wb;   // [Q]
+    float* ul;   // [Q]
+    float* ue;   // [Q]
+    float* gam;  // [8]
+    int* fast;   // [8]
+};
+
+__host__ __device__ inline size_t tables_bytes(int Q) {
+    return ((size_t)(5 * Q + 8) * sizeof(float) + 8 * sizeof(int) + 15) & ~(size_t)15;
+}
+
+__device__ inline ChunkTables carve_tables(char* base, int Q) {
+    ChunkTables tb;
+    tb.csl = (float*)base;
+    tb.dtl = tb.csl + Q;
+    tb.wb = tb.dtl + Q;
+    tb.ul = tb.wb + Q;
+    tb.ue = tb.ul + Q;
+    tb.gam = tb.ue + Q;
+    tb.fast = (int*)(tb.gam + 8);
+    return tb;
+}
+
+// Fill the tables for one chunk of one head.  The tables are private to one
+// wave (64 lanes fill them); LDS operations of one wave complete in order, so
+// its lanes may read them right after without a workgroup barrier.
+__device__ inline void build_tables(const ChunkTables& tb, const float* __restrict__ csk,
+                                    const float* __restrict__ dtk, int Q, int lane) {
+    for (int q = lane; q < Q; q += 64) {
+        const float a = csk[q], d = dtk[q];
+        const float ce = csk[q | 31];
+        const int s = (q & ~31) - 1;
+        const float cs0 = s >= 0 ? csk[s] : 0.f;
+        tb.csl[q] = a;
+        tb.dtl[q] = d;
+        tb.wb[q] = __expf(ce - a) * d;
+        tb.ul[q] = __expf(a - cs0);
+        tb.ue[q] = __expf(fminf(a - ce, kFastBlockDecay));
+    }
+    if (lane < Q / 32) {
+        const float cs0 = lane > 0 ? csk[32 * lane - 1] : 0.f;
+        const float ce = csk[32 * lane + 31];
+        tb.gam[lane] = __expf(ce - cs0);
+        tb.fast[lane] = (cs0 - ce) < kFastBlockDecay ? 1 : 0;
+    }
+}
+
+// Wave-private transposed copy of x * wb for the chunk's columns
+// [32pt, 32pt+32) of head h: xh[pl][k] + xl[pl][k] = x[row0+k][h][32pt+pl] wb[k]
+// (pitch LP; xl only when split), zero past the chunk end and past P.
+// One unit = 8 tokens x 8 columns per lane and step.
+template <typename T>
+__device__ inline void stage_xw(const T* __restrict__ x, const ChunkDesc& cd, int H, int P, int h, int Q,
+                                int pt, const float* wb, T* xh, T* xl, int LP, int lane) {
     typedef typename Tr<T>::v8 v8;
-    constexpr int NPB = PT / 8;
-    const int nunits = (Q / 8) * NPB;
-    for (int u = threadIdx.x; u < nunits; u += kThreads) {
-        const int pb = u % NPB, kb = u / NPB;
-        const int p0 = pb * 8, k0 = kb * 8;
-        v8 raw[8];
+    constexpr int kUnits = 2;  // Q <= 256: (Q/8) * 4 units over 64 lanes
+    const int nunits = (Q / 8) * 4;
+    v8 raw[kUnits][8];
+    // all loads first (addresses clamped in bounds, masked after), so the
+    // wave waits for memory once
+#pragma unroll
+    for (int s = 0; s < kUnits; ++s) {
+        const int u = lane + 64 * s;
+        const int pb = u & 3, kb = u >> 2;
+        const int p0 = min(32 * pt + 8 * pb, P - 8);
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
-            raw[r] = v8{};
-            const int kk = k0 + r;
-            if (kk < cd.len && p0 < P) raw[r] = Tr<T>::ld8(x + ((cd.row0 + kk) * H + h) * P + p0);
+            const int kk = min(8 * kb + r, cd.len - 1);
+            raw[s][r] = Tr<T>::ld8(x + ((cd.row0 + kk) * H + h) * P + p0);
         }
-        float ws[8];
-        if (WITH_W) {
+    }
 #pragma unroll
-            for (int r = 0; r < 8; ++r) ws[r] = w[k0 + r];
-        }
+    for (int s = 0; s < kUnits; ++s) {
+        const int u = lane + 64 * s;
+        if (u < nunits) {
+            const int pb = u & 3, kb = u >> 2;
+            const int k0 = 8 * kb;
+            const bool pok = 32 * pt + 8 * pb < P;
+            f32x8 f[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            if (RAW) {
-                v8 o;
-#pragma unroll
-                for (int r = 0; r < 8; ++r) o[r] = raw[r][i];
-                Tr<T>::st8(xr + (p0 + i) * LP + k0, o);
+            for (int r = 0; r < 8; ++r) {
+                const bool ok = pok && (k0 + r < cd.len);
+                f[r] = Tr<T>::widen(raw[s][r]) * (ok ? wb[k0 + r] : 0.f);
             }
-            if (WITH_W) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
                 f32x8 o;
 #pragma unroll
-                for (int r = 0; r < 8; ++r) o[r] = (float)raw[r][i] * ws[r];
+                for (int r = 0; r < 8; ++r) o[r] = f[r][i];
                 const v8 hi = Tr<T>::narrow(o);
-                Tr<T>::st8(xh + (p0 + i) * LP + k0, hi);
-                if (Split<T>::on) Tr<T>::st8(xl + (p0 + i) * LP + k0, Tr<T>::narrow(o - Tr<T>::widen(hi)));
+                Tr<T>::st8(xh + (8 * pb + i) * LP + k0, hi);
+                if (Split<T>::on) Tr<T>::st8(xl + (8 * pb + i) * LP + k0, Tr<T>::narrow(o - Tr<T>::widen(hi)));
             }
         }
     }
 }
 
-// State tiles: the (N x P) transposed state S^T is NT/32 x PT/32 tiles of 32x32;
-// wave w owns tiles w*TPW .. w*TPW+TPW-1 (index u -> nt = u / NPT, pt = u % NPT).
-// Accumulator register v of tile (nt, pt) holds S[p = 32pt + lane%32]
-// [n = 32nt + 8(v/4) + 4(lane/32) + v%4].
+template <typename T, int NNT>
+__device__ inline void load_bt_block(typename Tr<T>::v8 (&a)[2][NNT], const T* __restrict__ btk, int Q, int j,
+                                     int col, int half) {
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int nt = 0; nt < NNT; ++nt)
+            a[ks][nt] = Tr<T>::ld8(btk + (size_t)(32 * nt + col) * Q + 32 * j + 16 * ks + 8 * half);
+}
 
-// S^T(tile) <- dec * S^T + B^T(rows n) . xw(cols p) over the chunk's Q tokens,
-// xw given as the hi/lo pair xh/xl in LDS (pitch LP).
-template <typename T>
-__device__ inline void state_update_tile(f32x16& st, float dec, const T* __restrict__ btk, int n, int N,
-                                         int Q, const T* xh, const T* xl, int p, int LP, int half) {
+// One block of the Horner state update:  st <- gam_j st + B_j^T (x wb)_j.
+template <typename T, int NNT>
+__device__ inline void update_block(f32x16 (&st)[NNT], const typename Tr<T>::v8 (&a)[2][NNT], float gj,
+                                    const T* xhrow, const T* xlrow, int j, int half) {
     typedef typename Tr<T>::v8 v8;
-    st *= dec;
-    for (int k0 = 0; k0 < Q; k0 += 16) {
-        v8 a = {};
-        if (n < N) a = Tr<T>::ld8(btk + (size_t)n * Q + k0 + 8 * half);
-        mma16(st, a, Tr<T>::ld8(xh + p * LP + k0 + 8 * half));
-        if (Split<T>::on) mma16(st, a, Tr<T>::ld8(xl + p * LP + k0 + 8 * half));
+#pragma unroll
+    for (int nt = 0; nt < NNT; ++nt) st[nt] *= gj;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+        const int kb = 32 * j + 16 * ks + 8 * half;
+        const v8 bh = Tr<T>::ld8(xhrow + kb);
+#pragma unroll
+        for (int nt = 0; nt < NNT; ++nt) mma16(st[nt], a[ks][nt], bh);
+        if (Split<T>::on) {
+            const v8 bl = Tr<T>::ld8(xlrow + kb);
+#pragma unroll
+            for (int nt = 0; nt < NNT; ++nt) mma16(st[nt], a[ks][nt], bl);
+        }
     }
 }
 
-// ------------------------------------------------------------------ chunk_state
-// grid (segments, H).  For every segment that is not the last of its sequence,
-// the state that the segment alone produces from a zero state:
-//   S <- exp(cs_last) S + B^T diag(exp(cs_last - cs_k) dt_k) X   per chunk.
-template <typename T, int PT, int NT>
-__global__ __launch_bounds__(kThreads) void ssd_chunk_state_kernel(
-    Plan pl, const T* __restrict__ x, const float* __restrict__ cs, const float* __restrict__ dtc,
-    const T* __restrict__ bt, float* __restrict__ sbuf) {
-    extern __shared__ __align__(16) char smem[];
-    const SegDesc sd = seg_desc(pl, blockIdx.x);
-    const int h = blockIdx.y;
-    if (sd.seq < 0 || sd.last) return;
-    constexpr int NPT = PT / 32, NNT = NT / 32, NTILE = NPT * NNT, TPW = (NTILE + 3) / 4;
-    const int Q = pl.Q, P = pl.P, N = pl.N, H = pl.H, G = pl.G;
-    const int g = h / pl.hpg;
-    const int LP = Q + 8;
-    T* xh = (T*)smem;
-    T* xl = xh + PT * LP;
-    float* wl = (float*)(xl + (Split<T>::on ? PT * LP : 0));
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, half = lane >> 5, col = lane & 31;
-    f32x16 st[TPW];
+// Horner state update over the chunk's 32-token blocks:
+//   for each block j:  st <- gam[j] st + B_j^T (x wb)_j
+// which gives exp(cs_last) S + sum_k exp(cs_last - cs_k) dt_k x_k (outer) B_k.
+// B^T rows are padded with zeros to NT, so no bounds checks are needed.  The
+// next block's B^T fragments load while the current block computes.
+template <typename T, int NNT>
+__device__ inline void state_update(f32x16 (&st)[NNT], const T* __restrict__ btk, int Q, const T* xhrow,
+                                    const T* xlrow, const float* gam, int col, int half) {
+    typedef typename Tr<T>::v8 v8;
+    const int nti = Q / 32;
+    v8 a[2][NNT];
+    load_bt_block<T, NNT>(a, btk, Q, 0, col, half);
+    for (int j = 0; j < nti; ++j) {
+        const float gj = gam[j];
+        v8 cur[2][NNT];
 #pragma unroll
-    for (int i = 0; i < TPW; ++i) st[i] = f32x16{};
-    for (int c = 0; c < sd.nchunks; ++c) {
-        const int kc = sd.chunk0 + c;
-        const ChunkDesc cd = chunk_desc(pl, kc);
-        const float* csk = cs + ((size_t)kc * H + h) * Q;
-        const float* dtk = dtc + ((size_t)kc * H + h) * Q;
-        const float cl = csk[Q - 1];
-        for (int q = threadIdx.x; q < Q; q += kThreads) wl[q] = __expf(cl - csk[q]) * dtk[q];
-        __syncthreads();
-        stage_x<T, PT, false, true>(x, cd, H, P, h, Q, nullptr, wl, xh, xl, LP);
-        __syncthreads();
-        const float dec = __expf(cl);
-        const T* btk = bt + ((size_t)kc * G + g) * N * Q;
+        for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-        for (int i = 0; i < TPW; ++i) {
-            const int u = wave * TPW + i;
-            if (u < NTILE)
-                state_update_tile<T>(st[i], dec, btk, 32 * (u / NPT) + col, N, Q, xh, xl,
-                                     32 * (u % NPT) + col, LP, half);
-        }
-        __syncthreads();
+            for (int nt = 0; nt < NNT; ++nt) cur[ks][nt] = a[ks][nt];
+        if (j + 1 < nti) load_bt_block<T, NNT>(a, btk, Q, j + 1, col, half);
+        update_block<T, NNT>(st, cur, gj, xhrow, xlrow, j, half);
     }
-    float* out = sbuf + ((size_t)sd.slot_out * H + h) * P * N;
+}
+
+template <int NNT>
+__device__ inline void load_state(f32x16 (&st)[NNT], const float* src, int P, int N, int p, int half) {
 #pragma unroll
-    for (int i = 0; i < TPW; ++i) {
-        const int u = wave * TPW + i;
-        if (u < NTILE) {
-            const int nt = u / NPT, pt = u % NPT;
-            const int p = 32 * pt + col;
+    for (int nt = 0; nt < NNT; ++nt) {
+        st[nt] = f32x16{};
+        if (src && p < P) {
 #pragma unroll
             for (int vg = 0; vg < 4; ++vg) {
                 const int n = 32 * nt + 8 * vg + 4 * half;
-                if (p < P && n < N)
-                    *(f32x4*)(out + (size_t)p * N + n) =
-                        f32x4{st[i][4 * vg], st[i][4 * vg + 1], st[i][4 * vg + 2], st[i][4 * vg + 3]};
+                if (n < N) {
+                    const f32x4 v = *(const f32x4*)(src + (size_t)p * N + n);
+                    st[nt][4 * vg] = v[0];
+                    st[nt][4 * vg + 1] = v[1];
+                    st[nt][4 * vg + 2] = v[2];
+                    st[nt][4 * vg + 3] = v[3];
+                }
             }
         }
     }
+}
+
+template <int NNT>
+__device__ inline void store_state(const f32x16 (&st)[NNT], float* dst, int P, int N, int p, int half) {
+    if (p >= P) return;
+#pragma unroll
+    for (int nt = 0; nt < NNT; ++nt) {
+#pragma unroll
+        for (int vg = 0; vg < 4; ++vg) {
+            const int n = 32 * nt + 8 * vg + 4 * half;
+            if (n < N)
+                *(f32x4*)(dst + (size_t)p * N + n) =
+                    f32x4{st[nt][4 * vg], st[nt][4 * vg + 1], st[nt][4 * vg + 2], st[nt][4 * vg + 3]};
+        }
+    }
+}
+
+// Grid order: item i of (segment-major) work runs as workgroup L with
+// i = (L % 8) * per_xcd + L / 8.  Workgroups are dealt to the 8 XCDs round
+// robin, so each XCD walks a contiguous range of items: the heads of one
+// segment run together and share its chunks' C.B^T, C and B^T in that XCD's L2.
+__device__ inline int xcd_item(int per_xcd) { return (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3); }
+
+// LDS of one wave: its decay tables, then its x * wb tile (hi, and lo when split).
+template <typename T>
+__host__ __device__ inline size_t wave_lds_bytes(int Q) {
+    return tables_bytes(Q) + (size_t)(Split<T>::on ? 2 : 1) * 32 * (Q + 8) * sizeof(T);
+}
+template <typename T>
+__host__ __device__ inline size_t wave_kernel_lds_bytes(int NPT, int Q) {
+    return (size_t)NPT * wave_lds_bytes<T>(Q);
+}
+
+// ------------------------------------------------------------------ chunk_state
+// For every segment that is not the last of its sequence, the state that the
+// segment alone produces from a zero state (the Horner update above, chunk by
+// chunk).  The waves of a workgroup are independent.
+template <typename T, int NPT, int NT>
+__global__ __launch_bounds__(64 * NPT) void ssd_chunk_state_kernel(
+    Plan pl, int per_xcd, const T* __restrict__ x, const float* __restrict__ cs,
+    const float* __restrict__ dtc, const T* __restrict__ bt, float* __restrict__ sbuf) {
+    extern __shared__ __align__(16) char smem[];
+    constexpr int NNT = NT / 32;
+    const int item = xcd_item(per_xcd);
+    if (item >= pl.nseg_ub * pl.H) return;
+    const int h = item % pl.H;
+    const SegDesc sd = seg_desc(pl, item / pl.H);
+    if (sd.seq < 0 || sd.last) return;
+    const int Q = pl.Q, P = pl.P, N = pl.N, H = pl.H, G = pl.G;
+    const int g = h / pl.hpg;
+    const int LP = Q + 8;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, half = lane >> 5, col = lane & 31;
+    char* wl = smem + (size_t)wave * wave_lds_bytes<T>(Q);
+    const ChunkTables tb = carve_tables(wl, Q);
+    T* xh = (T*)(wl + tables_bytes(Q));
+    T* xl = xh + 32 * LP;
+    f32x16 st[NNT];
+#pragma unroll
+    for (int nt = 0; nt < NNT; ++nt) st[nt] = f32x16{};
+    for (int c = 0; c < sd.nchunks; ++c) {
+        const int kc = sd.chunk0 + c;
+        const ChunkDesc cd = chunk_desc(pl, kc);
+        build_tables(tb, cs + ((size_t)kc * H + h) * Q, dtc + ((size_t)kc * H + h) * Q, Q, lane);
+        stage_xw<T>(x, cd, H, P, h, Q, wave, tb.wb, xh, xl, LP, lane);
+        state_update<T, NNT>(st, bt + ((size_t)kc * G + g) * NT * Q, Q, xh + col * LP, xl + col * LP, tb.gam,
+                             col, half);
+    }
+    store_state<NNT>(st, sbuf + ((size_t)sd.slot_out * H + h) * P * N, P, N, 32 * wave + col, half);
 }
 
 // ------------------------------------------------------------------ state_passing
@@ -378,228 +520,213 @@ __global__ __launch_bounds__(kThreads) void ssd_state_passing_kernel(
     }
 }
 
+
+
+
+
 // ------------------------------------------------------------------ chunk_scan
-// grid (segments, H).  For each chunk of the segment, in order:
-//   Y^T[p][t]  = exp(cs_t) sum_n S[p][n] C[t][n]                        (state term)
-//              + sum_{k<=t} x[k][p] cb[t][k] exp(cs_t - cs_k) dt_k        (causal intra-chunk term)
-//   y[t][p]    = Y^T[p][t] + D x[t][p]                                   (written in fp32 or bf16)
-//   S^T       <- exp(cs_last) S^T + B^T (x dt exp(cs_last - cs_k))       (carry to the next chunk)
-// The state lives in fp32 accumulators; its operand copy sits in LDS as a
-// hi/lo pair sh/sl[p][n].  The decay-weighted mask is built in registers from
-// cb, one bf16 rounding per element.  t-tiles are dealt to waves in snake
-// order so the causal work balances.
-template <typename T, int PT, int NT>
-__global__ __launch_bounds__(kThreads) void ssd_chunk_scan_kernel(
-    Plan pl, const T* __restrict__ x, const float* __restrict__ cs, const float* __restrict__ dtc,
-    const T* __restrict__ Cm, const float* __restrict__ cb, const T* __restrict__ bt,
-    const float* __restrict__ D, const float* __restrict__ init, const float* __restrict__ sbuf,
-    void* __restrict__ yv, int y_f32, float* __restrict__ fin) {
+// For each chunk of the segment, in order (t, k tokens of the chunk):
+//   y[t][p] = exp(cs_t) sum_n C[t][n] S[p][n]                          (state term)
+//           + sum_{k<=t} (C_t . B_k) exp(cs_t - cs_k) dt_k x[k][p]      (causal intra-chunk term)
+//           + D x[t][p]
+//   S <- exp(cs_last) S + sum_k exp(cs_last - cs_k) dt_k x_k (outer) B_k  (carried to the next chunk)
+// Output tile (32-token block ti, this wave's p-tile), MFMA rows t, columns p:
+//   acc  = C_rows . S^T                 A = C (n in the state registers' order),
+//                                       B = state hi/lo pair from registers
+//   for blocks j < ti:  acc = gam[j] acc + cb[t, block j] . (x wb)_j
+//   diagonal block:     acc = gam[ti] acc + mask(cb[t, block ti]) . (x wb)_ti
+//   acc *= ue[t]                        (= exp(cs_t - cs_{e_ti}))
+// which leaves exp(cs_t) on the state term and exp(cs_t - cs_k) dt_k on every
+// intra-chunk pair.  A block with decay beyond kFastBlockDecay stops the
+// Horner scheme before its diagonal, scales by ul[t] and adds its diagonal
+// with exact per-element factors instead.  The operands of block ti+1 are
+// loaded while block ti computes.
+template <typename T, typename TY, int NPT, int NT>
+__global__ __launch_bounds__(64 * NPT) void ssd_chunk_scan_kernel(
+    Plan pl, int per_xcd, const T* __restrict__ x, const float* __restrict__ cs,
+    const float* __restrict__ dtc, const T* __restrict__ Cm, const T* __restrict__ cb,
+    const T* __restrict__ bt, const float* __restrict__ D, const float* __restrict__ init,
+    const float* __restrict__ sbuf, TY* __restrict__ y, float* __restrict__ fin) {
     extern __shared__ __align__(16) char smem[];
-    const SegDesc sd = seg_desc(pl, blockIdx.x);
-    const int h = blockIdx.y;
-    if (sd.seq < 0) return;
     constexpr bool SP = Split<T>::on;
-    constexpr int NPT = PT / 32, NNT = NT / 32, NTILE = NPT * NNT, TPW = (NTILE + 3) / 4;
+    constexpr int NNT = NT / 32;
     typedef typename Tr<T>::v8 v8;
+    const int item = xcd_item(per_xcd);
+    if (item >= pl.nseg_ub * pl.H) return;
+    const int h = item % pl.H;
+    const SegDesc sd = seg_desc(pl, item / pl.H);
+    if (sd.seq < 0) return;
     const int Q = pl.Q, P = pl.P, N = pl.N, H = pl.H, G = pl.G;
     const int g = h / pl.hpg;
-    const int LP = Q + 8, LS = NT + 8;
-    T* xr = (T*)smem;
-    T* xh = xr + PT * LP;
-    T* xl = xh + PT * LP;
-    T* sh = xl + (SP ? PT * LP : 0);
-    T* sl = sh + PT * LS;
-    float* csl = (float*)(sl + (SP ? PT * LS : 0));
-    float* dtl = csl + Q;
-    float* wl = dtl + Q;
+    const int LP = Q + 8;
+    const int nti = Q / 32;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, half = lane >> 5, col = lane & 31;
+    const int p = 32 * wave + col;  // this lane's column of S and y
+    char* wl = smem + (size_t)wave * wave_lds_bytes<T>(Q);
+    const ChunkTables tb = carve_tables(wl, Q);
+    T* xh = (T*)(wl + tables_bytes(Q));
+    T* xl = xh + 32 * LP;
+    const T* xhrow = xh + col * LP;
+    const T* xlrow = xl + col * LP;
     const bool need_final = sd.last && fin != nullptr;
     const float Dh = D[h];
+    const int HP = H * P;
 
-    // entering state: previous segment's passed state, else the initial state
     const float* src = nullptr;
     if (sd.slot_in >= 0) src = sbuf + ((size_t)sd.slot_in * H + h) * P * N;
     else if (init) src = init + ((size_t)sd.seq * H + h) * P * N;
     bool zero_state = (src == nullptr);
-    f32x16 st[TPW];
+    f32x16 st[NNT];
+    load_state<NNT>(st, src, P, N, p, half);
+    // state operand of the state term: fragment (nt, m) = st[nt][8m .. 8m+7];
+    // within a 16-wide step its element i of lane half hf is n = 16m + 8(i/4) + 4hf + i%4
+    v8 sh[NNT][2], sl[NNT][2];
+    auto split_state = [&]() {
 #pragma unroll
-    for (int i = 0; i < TPW; ++i) {
-        st[i] = f32x16{};
-        const int u = wave * TPW + i;
-        if (src && u < NTILE) {
-            const int nt = u / NPT, pt = u % NPT;
-            const int p = 32 * pt + col;
+        for (int nt = 0; nt < NNT; ++nt) {
 #pragma unroll
-            for (int vg = 0; vg < 4; ++vg) {
-                const int n = 32 * nt + 8 * vg + 4 * half;
-                if (p < P && n < N) {
-                    const f32x4 v = *(const f32x4*)(src + (size_t)p * N + n);
-                    st[i][4 * vg] = v[0];
-                    st[i][4 * vg + 1] = v[1];
-                    st[i][4 * vg + 2] = v[2];
-                    st[i][4 * vg + 3] = v[3];
-                }
-            }
-        }
-    }
-    auto state_to_lds = [&]() {
+            for (int m = 0; m < 2; ++m) {
+                f32x8 f;
 #pragma unroll
-        for (int i = 0; i < TPW; ++i) {
-            const int u = wave * TPW + i;
-            if (u < NTILE) {
-                const int nt = u / NPT, pt = u % NPT;
-                const int p = 32 * pt + col;
-#pragma unroll
-                for (int vg = 0; vg < 4; ++vg) {
-                    const int n = 32 * nt + 8 * vg + 4 * half;
-                    const f32x4 v = f32x4{st[i][4 * vg], st[i][4 * vg + 1], st[i][4 * vg + 2],
-                                          st[i][4 * vg + 3]};
-                    if (SP) {
-                        const bf16x4 hi = __builtin_convertvector(v, bf16x4);
-                        *(bf16x4*)((bf16_t*)sh + p * LS + n) = hi;
-                        *(bf16x4*)((bf16_t*)sl + p * LS + n) =
-                            __builtin_convertvector(v - __builtin_convertvector(hi, f32x4), bf16x4);
-                    } else {
-                        Tr<T>::st4(sh + p * LS + n, v);
-                    }
-                }
+                for (int j = 0; j < 8; ++j) f[j] = st[nt][8 * m + j];
+                sh[nt][m] = Tr<T>::narrow(f);
+                sl[nt][m] = SP ? Tr<T>::narrow(f - Tr<T>::widen(sh[nt][m])) : v8{};
             }
         }
     };
-    if (!zero_state) state_to_lds();
+    split_state();
 
-    const int nti = Q / 32;
     for (int c = 0; c < sd.nchunks; ++c) {
         const int kc = sd.chunk0 + c;
         const ChunkDesc cd = chunk_desc(pl, kc);
         const bool update = (c + 1 < sd.nchunks) || need_final;
-        const float* csk = cs + ((size_t)kc * H + h) * Q;
-        const float* dtk = dtc + ((size_t)kc * H + h) * Q;
-        const float cl = csk[Q - 1];
-        for (int q = threadIdx.x; q < Q; q += kThreads) {
-            const float a = csk[q], d = dtk[q];
-            csl[q] = a;
-            dtl[q] = d;
-            wl[q] = __expf(cl - a) * d;
-        }
-        __syncthreads();
-        if (update) stage_x<T, PT, true, true>(x, cd, H, P, h, Q, xr, wl, xh, xl, LP);
-        else stage_x<T, PT, true, false>(x, cd, H, P, h, Q, xr, nullptr, nullptr, nullptr, LP);
-        __syncthreads();
+        build_tables(tb, cs + ((size_t)kc * H + h) * Q, dtc + ((size_t)kc * H + h) * Q, Q, lane);
+        stage_xw<T>(x, cd, H, P, h, Q, wave, tb.wb, xh, xl, LP, lane);
 
-        const float* cbk = cb + ((size_t)kc * G + g) * Q * Q;
+        const T* cbk = cb + ((size_t)kc * G + g) * Q * Q;
+        const T* btk = bt + ((size_t)kc * G + g) * NT * Q;
+        // Operands of 32-token block ti for this lane's A row ta = 32 ti + col:
+        // C row ta in the state registers' n order, cb row ta, B^T block ti.
+        // Rows past the chunk end are clamped (their outputs are never stored).
+        v8 ca[NNT][2], ga[8][2], ba[2][NNT];
+        auto load_c = [&](int ti) {
+            if (zero_state) return;
+            const int ta = min(32 * ti + col, cd.len - 1);
+            const T* crow = Cm + ((cd.row0 + ta) * G + g) * N;
+#pragma unroll
+            for (int nt = 0; nt < NNT; ++nt)
+#pragma unroll
+                for (int m = 0; m < 2; ++m) {
+                    // padding columns n >= N meet zero state rows; clamp to stay in bounds
+                    const int n0 = 32 * nt + 16 * m + 4 * half;
+                    const typename Tr<T>::v4 c0 = Tr<T>::ld4raw(crow + min(n0, N - 4));
+                    const typename Tr<T>::v4 c1 = Tr<T>::ld4raw(crow + min(n0 + 8, N - 4));
+                    ca[nt][m] = __builtin_shufflevector(c0, c1, 0, 1, 2, 3, 4, 5, 6, 7);
+                }
+        };
+        auto load_g = [&](int ti) {
+            const T* grow = cbk + (size_t)(32 * ti + col) * Q;
+#pragma unroll
+            for (int kj = 0; kj < 8; ++kj)
+                if (kj <= ti) {
+                    ga[kj][0] = Tr<T>::ld8(grow + 32 * kj + 8 * half);
+                    ga[kj][1] = Tr<T>::ld8(grow + 32 * kj + 16 + 8 * half);
+                }
+        };
+        load_c(0);
+        if (update) load_bt_block<T, NNT>(ba, btk, Q, 0, col, half);
+        const T* xcol = x + (size_t)h * P + min(p, P - 1);
         for (int ti = 0; ti < nti; ++ti) {
-            const int owner = ((ti >> 2) & 1) ? 3 - (ti & 3) : (ti & 3);
-            if (owner != wave) continue;
-            f32x16 ya[NPT];
+            const int ta = 32 * ti + col;
+            // x at this lane's 16 output rows for the D x term (rows clamped)
+            float xd[16];
 #pragma unroll
-            for (int pt = 0; pt < NPT; ++pt) ya[pt] = f32x16{};
-            const int t = 32 * ti + col;
-            const bool tv = t < cd.len;
-            const float cst = csl[t];
+            for (int v = 0; v < 16; ++v) {
+                const int t = min(32 * ti + acc_row(v, lane), cd.len - 1);
+                xd[v] = (float)xcol[(size_t)(cd.row0 + t) * HP];
+            }
+            load_g(ti);  // covered by the state-term and update MFMAs below
+            f32x16 acc = {};
             if (!zero_state) {
-                const T* crow = Cm + ((cd.row0 + t) * G + g) * N;
-                for (int n0 = 0; n0 < NT; n0 += 16) {
-                    const int n = n0 + 8 * half;
-                    v8 b = {};
-                    if (tv && n < N) b = Tr<T>::ld8(crow + n);
 #pragma unroll
-                    for (int pt = 0; pt < NPT; ++pt) {
-                        const int off = (32 * pt + col) * LS + n0 + 8 * half;
-                        mma16(ya[pt], Tr<T>::ld8(sh + off), b);
-                        if (SP) mma16(ya[pt], Tr<T>::ld8(sl + off), b);
+                for (int nt = 0; nt < NNT; ++nt)
+#pragma unroll
+                    for (int m = 0; m < 2; ++m) {
+                        mma16(acc, ca[nt][m], sh[nt][m]);
+                        if (SP) mma16(acc, ca[nt][m], sl[nt][m]);
+                    }
+                if (ti + 1 < nti) load_c(ti + 1);
+            }
+            if (update) {
+                // the chunk-start state operand (sh/sl) stays untouched until the chunk ends
+                update_block<T, NNT>(st, ba, tb.gam[ti], xhrow, xlrow, ti, half);
+                if (ti + 1 < nti) load_bt_block<T, NNT>(ba, btk, Q, ti + 1, col, half);
+            }
+            const bool fast = tb.fast[ti] != 0;
+#pragma unroll
+            for (int kj = 0; kj < 8; ++kj) {
+                if (kj < ti || (kj == ti && fast)) {
+                    acc *= tb.gam[kj];
+#pragma unroll
+                    for (int ks = 0; ks < 2; ++ks) {
+                        v8 a = ga[kj][ks];
+                        if (kj == ti) {
+                            const int k0 = 32 * kj + 16 * ks + 8 * half;
+#pragma unroll
+                            for (int i = 0; i < 8; ++i) a[i] = (k0 + i <= ta) ? a[i] : (typename Tr<T>::elem)0;
+                        }
+                        mma16(acc, a, Tr<T>::ld8(xhrow + 32 * kj + 16 * ks + 8 * half));
                     }
                 }
-                const float e = __expf(cst);
-#pragma unroll
-                for (int pt = 0; pt < NPT; ++pt) ya[pt] *= e;
             }
-            const float* grow = cbk + (size_t)t * Q;
-            for (int kj = 0; kj <= ti; ++kj) {
-                const bool diag = (kj == ti);
+            const float* scale = fast ? tb.ue : tb.ul;
+#pragma unroll
+            for (int vg = 0; vg < 4; ++vg) {
+                const f32x4 u = *(const f32x4*)(scale + 32 * ti + 8 * vg + 4 * half);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[4 * vg + j] *= u[j];
+            }
+            if (!fast) {
+                // decay across this block beyond the fast range: exact factors, raw x
+                const float cst = tb.csl[ta];
+                const T* grow = cbk + (size_t)ta * Q;
 #pragma unroll
                 for (int ks = 0; ks < 2; ++ks) {
-                    const int kb = 32 * kj + 16 * ks + 8 * half;
-                    const f32x4 g0 = *(const f32x4*)(grow + kb);
-                    const f32x4 g1 = *(const f32x4*)(grow + kb + 4);
+                    const int k0 = 32 * ti + 16 * ks + 8 * half;
+                    const f32x8 gv = Tr<T>::widen(Tr<T>::ld8(grow + k0));
                     f32x8 m;
+                    v8 xb;
 #pragma unroll
                     for (int i = 0; i < 8; ++i) {
-                        const int kk = kb + i;
-                        const float gv = i < 4 ? g0[i] : g1[i - 4];
-                        const bool keep = !diag || kk <= t;
-                        const float e = keep ? __expf(cst - csl[kk]) : 0.f;
-                        m[i] = keep ? gv * e * dtl[kk] : 0.f;
+                        const int kk = k0 + i;
+                        const float e = __expf(fminf(cst - tb.csl[kk], 0.f)) * tb.dtl[kk];
+                        m[i] = kk <= ta ? gv[i] * e : 0.f;
+                        const int kr = min(kk, cd.len - 1);
+                        xb[i] = x[(cd.row0 + kr) * HP + h * P + min(p, P - 1)];
                     }
-                    const v8 b = Tr<T>::narrow(m);
-#pragma unroll
-                    for (int pt = 0; pt < NPT; ++pt) mma16(ya[pt], Tr<T>::ld8(xr + (32 * pt + col) * LP + kb), b);
+                    mma16(acc, Tr<T>::narrow(m), xb);
                 }
             }
-            if (tv) {
-                const T* xrow = x + ((cd.row0 + t) * H + h) * P;
-                const size_t yoff = ((cd.row0 + t) * H + h) * P;
+            // + D x; store rows t of this block, column p
+            if (p < P) {
+                TY* ycol = y + (size_t)(cd.row0 + 32 * ti) * HP + (size_t)h * P + p;
+                if (32 * ti + 32 <= cd.len) {
 #pragma unroll
-                for (int pt = 0; pt < NPT; ++pt) {
+                    for (int v = 0; v < 16; ++v) ycol[(size_t)acc_row(v, lane) * HP] = (TY)(acc[v] + Dh * xd[v]);
+                } else {
 #pragma unroll
-                    for (int vg = 0; vg < 4; ++vg) {
-                        const int p = 32 * pt + 8 * vg + 4 * half;
-                        if (p < P) {
-                            const f32x4 xv = Tr<T>::ld4(xrow + p);
-                            const f32x4 o = f32x4{ya[pt][4 * vg], ya[pt][4 * vg + 1], ya[pt][4 * vg + 2],
-                                                  ya[pt][4 * vg + 3]} + Dh * xv;
-                            if (y_f32) *(f32x4*)((float*)yv + yoff + p) = o;
-                            else Tr<bf16_t>::st4((bf16_t*)yv + yoff + p, o);
-                        }
-                    }
+                    for (int v = 0; v < 16; ++v)
+                        if (32 * ti + acc_row(v, lane) < cd.len)
+                            ycol[(size_t)acc_row(v, lane) * HP] = (TY)(acc[v] + Dh * xd[v]);
                 }
             }
         }
         if (update) {
-            __syncthreads();  // all reads of the state operand sh/sl are done
-            const float dec = __expf(cl);
-            const T* btk = bt + ((size_t)kc * G + g) * N * Q;
-#pragma unroll
-            for (int i = 0; i < TPW; ++i) {
-                const int u = wave * TPW + i;
-                if (u < NTILE)
-                    state_update_tile<T>(st[i], dec, btk, 32 * (u / NPT) + col, N, Q, xh, xl,
-                                         32 * (u % NPT) + col, LP, half);
-            }
-            state_to_lds();
+            split_state();
             zero_state = false;
         }
-        __syncthreads();
     }
-    if (need_final) {
-        float* out = fin + ((size_t)sd.seq * H + h) * P * N;
-#pragma unroll
-        for (int i = 0; i < TPW; ++i) {
-            const int u = wave * TPW + i;
-            if (u < NTILE) {
-                const int nt = u / NPT, pt = u % NPT;
-                const int p = 32 * pt + col;
-#pragma unroll
-                for (int vg = 0; vg < 4; ++vg) {
-                    const int n = 32 * nt + 8 * vg + 4 * half;
-                    if (p < P && n < N)
-                        *(f32x4*)(out + (size_t)p * N + n) =
-                            f32x4{st[i][4 * vg], st[i][4 * vg + 1], st[i][4 * vg + 2], st[i][4 * vg + 3]};
-                }
-            }
-        }
-    }
-}
-
-template <typename T, int PT, int NT>
-size_t scan_lds(int Q) {
-    const size_t nx = Split<T>::on ? 3 : 2, ns = Split<T>::on ? 2 : 1;
-    return nx * PT * (Q + 8) * sizeof(T) + ns * PT * (NT + 8) * sizeof(T) + 3 * Q * sizeof(float);
-}
-template <typename T, int PT>
-size_t state_lds(int Q) {
-    const size_t nx = Split<T>::on ? 2 : 1;
-    return nx * PT * (Q + 8) * sizeof(T) + Q * sizeof(float);
+    if (need_final) store_state<NNT>(st, fin + ((size_t)sd.seq * H + h) * P * N, P, N, p, half);
 }
 
 template <typename F>
@@ -608,7 +735,7 @@ hipError_t allow_lds(F* fn, size_t bytes) {
     return hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
 }
 
-template <typename T, int PT, int NT>
+template <typename T, int NPT, int NT>
 hipError_t run_prefill(const Plan& pl, const Layout& lay, const ScanArgs& a, hipStream_t stream,
                        hipEvent_t* marks) {
     char* ws = a.ws;
@@ -617,11 +744,13 @@ hipError_t run_prefill(const Plan& pl, const Layout& lay, const ScanArgs& a, hip
     const T* C = (const T*)a.C;
     float* cs = (float*)(ws + lay.cs);
     float* dtc = (float*)(ws + lay.dtc);
-    float* cbm = (float*)(ws + lay.cb);
+    T* cbm = (T*)(ws + lay.cb);
     T* bt = (T*)(ws + lay.bt);
     float* sbuf = (float*)(ws + lay.sbuf);
     hipError_t err;
     auto mark = [&](int i) -> hipError_t { return marks ? hipEventRecord(marks[i], stream) : hipSuccess; };
+    const int per_xcd = (int)(((int64_t)pl.nseg_ub * pl.H + 7) / 8);
+    const size_t lds = wave_kernel_lds_bytes<T>(NPT, pl.Q);
     if ((err = mark(0)) != hipSuccess) return err;
     if (!pl.dense && pl.nseq > 0) {
         hipLaunchKernelGGL(ssd_plan_kernel, dim3(1), dim3(kThreads), 0, stream, pl);
@@ -636,19 +765,16 @@ hipError_t run_prefill(const Plan& pl, const Layout& lay, const ScanArgs& a, hip
     if ((err = mark(2)) != hipSuccess) return err;
     if (pl.nchunk_ub > 0) {
         hipLaunchKernelGGL(ssd_cb_kernel<T>, dim3(pl.nchunk_ub, pl.G, pl.Q / 32), dim3(64), 0, stream,
-                           pl, B, C, cbm, bt);
+                           pl, NT, B, C, cbm, bt);
         if ((err = hipGetLastError()) != hipSuccess) return err;
     }
     if ((err = mark(3)) != hipSuccess) return err;
-    if (a.run_passing) {
-        if (pl.nseg_ub > 0 && pl.nslot_ub > 0) {
-            const size_t lds = state_lds<T, PT>(pl.Q);
-            auto* k2 = ssd_chunk_state_kernel<T, PT, NT>;
-            if ((err = allow_lds(k2, lds)) != hipSuccess) return err;
-            hipLaunchKernelGGL(k2, dim3(pl.nseg_ub, pl.H), dim3(kThreads), lds, stream, pl, x, cs, dtc,
-                               bt, sbuf);
-            if ((err = hipGetLastError()) != hipSuccess) return err;
-        }
+    if (a.run_passing && pl.nseg_ub > 0 && pl.nslot_ub > 0) {
+        auto* k2 = ssd_chunk_state_kernel<T, NPT, NT>;
+        if ((err = allow_lds(k2, lds)) != hipSuccess) return err;
+        hipLaunchKernelGGL(k2, dim3(8 * per_xcd), dim3(64 * NPT), lds, stream, pl, per_xcd, x, cs, dtc,
+                           bt, sbuf);
+        if ((err = hipGetLastError()) != hipSuccess) return err;
     }
     if ((err = mark(4)) != hipSuccess) return err;
     if (a.run_passing) {
@@ -659,11 +785,17 @@ hipError_t run_prefill(const Plan& pl, const Layout& lay, const ScanArgs& a, hip
     }
     if ((err = mark(5)) != hipSuccess) return err;
     if (pl.nseg_ub > 0) {
-        const size_t lds = scan_lds<T, PT, NT>(pl.Q);
-        auto* k4 = ssd_chunk_scan_kernel<T, PT, NT>;
-        if ((err = allow_lds(k4, lds)) != hipSuccess) return err;
-        hipLaunchKernelGGL(k4, dim3(pl.nseg_ub, pl.H), dim3(kThreads), lds, stream, pl, x, cs, dtc, C,
-                           cbm, bt, a.D, a.init, sbuf, a.y, a.y_f32, a.final_state);
+        if (a.y_f32) {
+            auto* k4 = ssd_chunk_scan_kernel<T, float, NPT, NT>;
+            if ((err = allow_lds(k4, lds)) != hipSuccess) return err;
+            hipLaunchKernelGGL(k4, dim3(8 * per_xcd), dim3(64 * NPT), lds, stream, pl, per_xcd, x, cs, dtc, C,
+                               cbm, bt, a.D, a.init, sbuf, (float*)a.y, a.final_state);
+        } else {
+            auto* k4 = ssd_chunk_scan_kernel<T, bf16_t, NPT, NT>;
+            if ((err = allow_lds(k4, lds)) != hipSuccess) return err;
+            hipLaunchKernelGGL(k4, dim3(8 * per_xcd), dim3(64 * NPT), lds, stream, pl, per_xcd, x, cs, dtc, C,
+                               cbm, bt, a.D, a.init, sbuf, (bf16_t*)a.y, a.final_state);
+        }
         if ((err = hipGetLastError()) != hipSuccess) return err;
     }
     if ((err = mark(6)) != hipSuccess) return err;
@@ -673,13 +805,14 @@ hipError_t run_prefill(const Plan& pl, const Layout& lay, const ScanArgs& a, hip
 template <typename T>
 hipError_t dispatch_nt(const Plan& pl, const Layout& lay, const ScanArgs& a, hipStream_t s,
                        hipEvent_t* marks) {
-    const int PT = pl.P <= 32 ? 32 : pl.P <= 64 ? 64 : 128;
-    const int NT = pl.N <= 32 ? 32 : pl.N <= 64 ? 64 : pl.N <= 128 ? 128 : 256;
-#define SSD_CASE(pt, nt) \
-    if (PT == pt && NT == nt) return run_prefill<T, pt, nt>(pl, lay, a, s, marks);
-    SSD_CASE(32, 32) SSD_CASE(32, 64) SSD_CASE(32, 128) SSD_CASE(32, 256)
-    SSD_CASE(64, 32) SSD_CASE(64, 64) SSD_CASE(64, 128) SSD_CASE(64, 256)
-    SSD_CASE(128, 32) SSD_CASE(128, 64) SSD_CASE(128, 128) SSD_CASE(128, 256)
+    const int NPT = (pl.P + 31) / 32;
+    const int NT = padded_dstate(pl.N);
+#define SSD_CASE(npt, nt) \
+    if (NPT == npt && NT == nt) return run_prefill<T, npt, nt>(pl, lay, a, s, marks);
+    SSD_CASE(1, 32) SSD_CASE(1, 64) SSD_CASE(1, 128) SSD_CASE(1, 256)
+    SSD_CASE(2, 32) SSD_CASE(2, 64) SSD_CASE(2, 128) SSD_CASE(2, 256)
+    SSD_CASE(3, 32) SSD_CASE(3, 64) SSD_CASE(3, 128) SSD_CASE(3, 256)
+    SSD_CASE(4, 32) SSD_CASE(4, 64) SSD_CASE(4, 128) SSD_CASE(4, 256)
 #undef SSD_CASE
     return hipErrorInvalidValue;
 }
@@ -687,11 +820,9 @@ hipError_t dispatch_nt(const Plan& pl, const Layout& lay, const ScanArgs& a, hip
 }  // namespace
 
 size_t chunk_scan_lds_bytes(int dtype, int P, int N, int Q) {
-    const int PT = P <= 32 ? 32 : P <= 64 ? 64 : 128;
-    const int NT = N <= 32 ? 32 : N <= 64 ? 64 : N <= 128 ? 128 : 256;
-    const size_t es = dtype == 1 ? 2 : 4;
-    const size_t nx = dtype == 1 ? 3 : 2, ns = dtype == 1 ? 2 : 1;  // bf16 keeps hi/lo pairs
-    return nx * PT * (Q + 8) * es + ns * PT * (NT + 8) * es + 3 * Q * sizeof(float);
+    (void)N;
+    const int npt = (P + 31) / 32;
+    return dtype == 1 ? wave_kernel_lds_bytes<bf16_t>(npt, Q) : wave_kernel_lds_bytes<float>(npt, Q);
 }
 
 hipError_t launch_prefill(const Plan& plan, const Layout& lay, const ScanArgs& a, hipStream_t stream,

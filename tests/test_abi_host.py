@@ -90,7 +90,6 @@ def test_workspace_size_valid(lib):
     (dict(chunks_per_segment=-1), 64, E_SHAPE),
     (dict(), 48, E_CHUNK),
     (dict(), 512, E_CHUNK),
-    (dict(headdim=128, dstate=256, dtype=0), 256, E_UNSUP),
 ])
 def test_shape_errors(lib, kw, chunk, code):
     st, _ = ws_size(lib, shape(**kw), chunk)
