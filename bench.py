@@ -45,23 +45,26 @@ def prefill_flops(wl, causal=False):
     return nch * (G * 2 * pairs * N + H * (2 * pairs * P + 4 * Q * N * P))
 
 
-def chunk_scan_work(wl, cps, es=2):
-    """Algorithmic FLOPs and HBM bytes of one chunk_scan launch (dense batch)."""
+def kernel_work(wl, es=2, ys=4):
+    """Algorithmic FLOPs and HBM bytes of each MFMA kernel launch (dense batch).
+
+    chunk_state: 2QNP per (chunk, head); reads x and B^T once, writes one fp32
+    P x N state per (chunk, head).
+    chunk_scan: 2QNP (state term) + 2Q^2P (dense intra-chunk product) per
+    (chunk, head); reads x, C, the causal half of C.B^T, the per-chunk decay
+    sums and one fp32 entering state per (chunk, head), writes y once."""
     Q, H, P, N, G, b, L = wl.chunk, wl.H, wl.P, wl.N, wl.G, wl.batch, wl.seqlen
-    cpseq = -(-L // Q)
-    spseq = -(-cpseq // cps)
-    updates = 0
-    for s in range(spseq):
-        n = min(cps, cpseq - s * cps)
-        updates += n if s == spseq - 1 else n - 1
-    nch = b * cpseq
-    flops = nch * H * (2 * Q * N * P + 2 * Q * Q * P) + b * updates * H * 2 * Q * N * P
-    nti = Q // 32
+    nch = b * (-(-L // Q))
     T = b * L
-    bytes_ = (2 * T * H * P * es + T * G * N * es + nch * G * nti * (nti + 1) // 2 * 1024 * 4
-              + nch * G * N * Q * es + 2 * nch * H * Q * 4 + b * spseq * H * P * N * 4
-              + b * H * P * N * 4)
-    return flops, bytes_
+    nti = Q // 32
+    state = nch * H * P * N * 4
+    ks = {"flops": nch * H * 2 * Q * N * P,
+          "bytes": T * H * P * es + nch * G * N * Q * es + state + 2 * nch * H * Q * 4}
+    kc = {"flops": nch * H * (2 * Q * N * P + 2 * Q * Q * P),
+          "bytes": (T * H * P * es + T * H * P * ys + T * G * N * es + state
+                    + nch * G * nti * (nti + 1) // 2 * 1024 * es + 2 * nch * H * Q * 4)}
+    kp = {"flops": 0, "bytes": 2 * state + nch * H * 4 + 2 * b * H * P * N * 4}
+    return {"chunk_state": ks, "chunk_scan": kc, "state_passing": kp}
 
 
 def decode_bytes(wd, es=2):
@@ -69,40 +72,75 @@ def decode_bytes(wd, es=2):
     return 2 * b * H * P * N * 4 + 2 * b * H * P * es + 2 * b * G * N * es + b * H * 4 + 2 * H * 4
 
 
-def cpu_baseline(inp, budget_s=12.0):
-    """The fp64 oracle on a bounded sample of the prefill workload: one
-    sequence, a few heads, all of its tokens; scaled to full-layer tokens/s."""
+def cpu_baseline(inp, max_seqs=None):
+    """The fp64 oracle (sequential recurrence, OpenMP over (sequence, head))
+    on the prefill workload's own inputs: all heads of the first `max_seqs`
+    sequences (all of them by default, ~30 core-seconds on 16 cores), scaled
+    to tokens/s of the whole layer."""
     import oracle
     wl = inp.wl
-    cores = len(os.sched_getaffinity(0))
+    nseq = wl.batch if max_seqs is None else min(max_seqs, wl.batch)
     threads = oracle.threads()
-    heads = max(1, min(wl.H, 2 * threads))
-    sl = np.arange(heads)
-    x = inp.x[:1, :, sl]
-    dt = inp.dt[:1, :, sl]
-    B = inp.B[:1]
-    C = inp.C[:1]
-    init = None if inp.init is None else inp.init[:1, sl]
+    init = None if inp.init is None else inp.init[:nseq]
     t0 = time.perf_counter()
-    oracle.scan(x, dt, inp.A[sl], B, C, inp.D[sl], init=init)
+    cpu0 = time.process_time()
+    oracle.scan(inp.x[:nseq], inp.dt[:nseq], inp.A, inp.B[:nseq], inp.C[:nseq], inp.D, init=init)
     t = time.perf_counter() - t0
-    # grow the sample toward the budget if the first pass was short
-    if t < budget_s / 4 and heads < wl.H:
-        heads = int(min(wl.H, max(heads + 1, heads * budget_s / 2 / max(t, 1e-3))))
-        sl = np.arange(heads)
-        x = inp.x[:1, :, sl]
-        dt = inp.dt[:1, :, sl]
-        init = None if inp.init is None else inp.init[:1, sl]
-        t0 = time.perf_counter()
-        oracle.scan(x, dt, inp.A[sl], B, C, inp.D[sl], init=init)
-        t = time.perf_counter() - t0
-    tokens_equiv = wl.seqlen * heads / wl.H
-    return {"value": tokens_equiv / t, "unit": "tokens/s", "cores": int(threads),
-            "host_cpus": int(cores), "kind": "oracle", "seconds": t,
-            "sample": "fp64 sequential oracle (C, OpenMP over (sequence, head)) on 1 of %d "
-                      "sequences x %d of %d heads x %d tokens of the prefill workload; value = "
-                      "full-layer tokens/s (tokens x heads/H / time)" % (wl.batch, heads, wl.H,
-                                                                         wl.seqlen)}
+    cpu_s = time.process_time() - cpu0
+    return {"value": nseq * wl.seqlen / t, "unit": "tokens/s", "cores": int(threads),
+            "host_cpus": len(os.sched_getaffinity(0)), "kind": "oracle", "seconds": round(t, 3),
+            "cpu_seconds": round(cpu_s, 1),
+            "sample": "fp64 sequential oracle (C, OpenMP over (sequence, head)) on %d of %d "
+                      "sequences x all %d heads x %d tokens of the prefill workload"
+                      % (nseq, wl.batch, wl.H, wl.seqlen)}
+
+
+def _source_digest():
+    """sha256 of the kernel sources, to tell whether counters are stale."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "mamba_ssd_chunked_02_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".h", ".cpp")):
+            h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def _traffic(path, kernel, alg_bytes):
+    """HBM bytes per launch of `kernel` from a committed counter summary:
+    lines `key: value` with fetch_kib, write_kib (per dispatch, rocprofv3
+    FETCH_SIZE / WRITE_SIZE), copy_fetch_factor and copy_write_factor (known
+    bytes of a plain copy / what the same counters read for it) and
+    source_digest.  None when the file is missing or the kernels changed."""
+    if not path or not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    try:
+        if kv.get("source_digest") != _source_digest():
+            return None
+        fetch = float(kv["fetch_kib"]) * 1024 * float(kv["copy_fetch_factor"])
+        write = float(kv["write_kib"]) * 1024 * float(kv["copy_write_factor"])
+    except (KeyError, ValueError):
+        return None
+    return {"bytes": round(fetch + write), "fetch_bytes": round(fetch), "write_bytes": round(write),
+            "over_algorithmic": round((fetch + write) / alg_bytes, 3), "source": os.path.relpath(path, ROOT)}
+
+
+def copy_calibration():
+    """A plain device-to-device copy of 1 GiB (read 1 GiB, write 1 GiB), run
+    under rocprofv3 --pmc to calibrate FETCH_SIZE / WRITE_SIZE."""
+    import torch
+    n = 1 << 28
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": n * 4, "copy_bytes_written": n * 4, "launches": 3}))
 
 
 def main():
@@ -110,14 +148,20 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--chunks-per-segment", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic_chunk_scan_2p7b.txt"),
+                    help="rocprofv3 FETCH_SIZE/WRITE_SIZE summary of the dominant kernel")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain device copy of known size (for counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (the scan shards "
               "over independent (sequence, head) pairs with no exchange; see the design notes). "
               "Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
 
     import torch
     import mamba_ssd_chunked_02_amd as ssd
@@ -140,7 +184,7 @@ def main():
     init = up(inp.init)
     y = torch.empty(tuple(x.shape), dtype=torch.float32, device=dev)  # fp32 y (the default)
     fin = torch.empty_like(init)
-    nbytes = ssd.workspace_size(x, Bm, wl.chunk, chunks_per_segment=args.chunks_per_segment)
+    nbytes = ssd.workspace_size(x, Bm, wl.chunk)
     ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     log("generating decode inputs:", wd.name)
     dinp = W.generate(wd, W.SEED_BASE + 2, decode_steps=1)
@@ -153,8 +197,7 @@ def main():
 
     def prefill(stage_ms=None):
         ssd.chunked_scan(x, dtt, A, Bm, Cm, D, wl.chunk, init_state=init, y=y, final_state=fin,
-                         workspace=ws, chunks_per_segment=args.chunks_per_segment,
-                         stage_ms=stage_ms)
+                         workspace=ws, stage_ms=stage_ms)
 
     def decode():
         ssd.decode_step(state, dx, ddt, dA, dB, dC, dD, y=dy)
@@ -195,24 +238,31 @@ def main():
     dense_tf = prefill_flops(wl) / (prefill_ms * 1e-3) / 1e12
     causal_tf = prefill_flops(wl, causal=True) / (prefill_ms * 1e-3) / 1e12
 
-    # chunk_scan (dominant prefill kernel) roofline
-    from ctypes import c_size_t  # noqa: F401  (kept for readers of the layout)
-    cps = args.chunks_per_segment or _auto_cps(wl)
-    ks_flops, ks_bytes = chunk_scan_work(wl, cps)
-    ks_ms = float(stage_mean[5])
-    ks_tflops = ks_flops / (ks_ms * 1e-3) / 1e12
-    ks_gbs = ks_bytes / (ks_ms * 1e-3) / 1e9
-    frac_mfma = ks_tflops / BF16_PEAK_TFLOPS
-    frac_hbm = ks_gbs / HBM_PEAK_GBS
-    if frac_hbm >= frac_mfma:
-        roof = {"bound": "hbm", "achieved": round(ks_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(frac_hbm, 4), "traffic": None}
-    else:
-        roof = {"bound": "mfma", "achieved": round(ks_tflops, 1), "peak": BF16_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(frac_mfma, 4), "traffic": None}
-    roof.update({"kernel": "ssd_chunk_scan_kernel<bf16,64,128>", "avg_ms": round(ks_ms, 4),
-                 "algorithmic_flops": ks_flops, "algorithmic_bytes": ks_bytes,
-                 "mfma_frac": round(frac_mfma, 4), "hbm_frac": round(frac_hbm, 4)})
+    # rooflines of the prefill kernels; the slowest one is the reported one
+    work = kernel_work(wl)
+    names = {"chunk_state": "ssd_chunk_state_kernel<bf16,NT=128,Q=256>",
+             "state_passing": "ssd_state_passing_kernel",
+             "chunk_scan": "ssd_chunk_scan_kernel<bf16,f32,NT=128,Q=256>"}
+    roofs = {}
+    for k, wk in work.items():
+        ms = float(stage_mean[ssd.STAGES.index(k)])
+        gbs = wk["bytes"] / (ms * 1e-3) / 1e9
+        tfl = wk["flops"] / (ms * 1e-3) / 1e12
+        fh, fm = gbs / HBM_PEAK_GBS, tfl / BF16_PEAK_TFLOPS
+        r = ({"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+              "frac": round(fh, 4)} if fh >= fm else
+             {"bound": "mfma", "achieved": round(tfl, 1), "peak": BF16_PEAK_TFLOPS,
+              "unit": "TFLOP/s", "frac": round(fm, 4)})
+        r.update({"traffic": None, "kernel": names[k], "avg_ms": round(ms, 4),
+                  "algorithmic_flops": wk["flops"], "algorithmic_bytes": wk["bytes"],
+                  "tflops": round(tfl, 2), "mfma_frac": round(fm, 4), "hbm_frac": round(fh, 4)})
+        roofs[k] = r
+    dominant = max(roofs, key=lambda k: roofs[k]["avg_ms"])
+    roof = dict(roofs[dominant])
+    if args.traffic:
+        roof["traffic"] = _traffic(args.traffic, names[dominant], roof["algorithmic_bytes"])
+    mfma_ms = float(stage_mean[ssd.STAGES.index("chunk_state")] + stage_mean[ssd.STAGES.index("chunk_scan")])
+    contraction_tf = (work["chunk_state"]["flops"] + work["chunk_scan"]["flops"]) / (mfma_ms * 1e-3) / 1e12
     dbytes = decode_bytes(wd)
     dgbs = dbytes / (decode_ms * 1e-3) / 1e9
     roof_dec = {"bound": "hbm", "achieved": round(dgbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -244,28 +294,22 @@ def main():
         "config": {"workload": "Mamba-2 2.7B-shaped SSD layer: prefill b8 L8192 H80 P64 N128 G1 "
                                "chunk256 (bf16 x/B/C, fp32 dt/A/D/state, init~N(0,0.1)) + one "
                                "decode step b256 H80 P64 N128 (fp32 state)",
-                   "global_batch": wl.batch, "seq_len": wl.seqlen, "parallelism": "none (1 GPU)",
-                   "chunks_per_segment": cps},
+                   "global_batch": wl.batch, "seq_len": wl.seqlen, "parallelism": "none (1 GPU)"},
         "tflops_dense": round(dense_tf, 2),
         "tflops_causal": round(causal_tf, 2),
         "stage_ms": {k: round(float(v), 4) for k, v in zip(ssd.STAGES, stage_mean)},
         "decode": {"ms_per_step": round(decode_ms, 4), "gbps": round(dgbs, 1),
                    "frac_of_hbm_peak": round(dgbs / HBM_PEAK_GBS, 4), "bytes_per_step": dbytes},
         "step_ms_prefill_plus_decode": round(prefill_ms + decode_ms, 4),
+        "tflops_contraction_kernels": round(contraction_tf, 2),
+        "frac_bf16_peak_contraction_kernels": round(contraction_tf / BF16_PEAK_TFLOPS, 4),
         "roofline": roof,
+        "roofline_kernels": roofs,
         "roofline_decode": roof_dec,
         "cpu_baseline": cpu,
         "wall_s_timed_region": round(wall, 3),
     }
     print(json.dumps(out), flush=True)
-
-
-def _auto_cps(wl):
-    """The library's automatic chunks-per-segment rule for a dense batch."""
-    cpseq = -(-wl.seqlen // wl.chunk)
-    pairs = max(1, wl.batch * wl.H)
-    want = max(1, min(-(-2048 // pairs), cpseq))
-    return -(-cpseq // want)
 
 
 if __name__ == "__main__":

@@ -68,9 +68,7 @@ typedef enum ssd_dtype { SSD_F32 = 0, SSD_BF16 = 1 } ssd_dtype;
  *     initial state through unchanged.
  *   headdim P in [8, 128] and dstate N in [8, 256], both multiples of 8;
  *   ngroups G >= 1 divides nheads H; head h reads B/C group h / (H/G).
- *   chunks_per_segment: scheduling knob of ssd_chunked_scan (how many
- *     consecutive chunks one workgroup walks while carrying the state);
- *     0 = let the library choose.  It never changes the result beyond rounding.
+ *   reserved: must be zero.
  */
 typedef struct ssd_shape {
     int64_t batch;
@@ -81,8 +79,7 @@ typedef struct ssd_shape {
     int32_t ngroups;
     int32_t dtype;               /* ssd_dtype of x, B, C */
     int32_t ydtype;              /* ssd_dtype of y (0 = SSD_F32, the default) */
-    int32_t chunks_per_segment;  /* 0 = automatic */
-    int32_t reserved;            /* must be 0 */
+    int32_t reserved[2];         /* must be 0 */
     const int32_t* cu_seqlens;      /* device int32 [batch+1], or NULL (dense) */
     const int32_t* cu_seqlens_host; /* optional host copy; validated when given */
 } ssd_shape;
@@ -109,7 +106,9 @@ ssd_status ssd_chunked_scan_workspace_size(const ssd_shape* shape, int32_t chunk
  *   final_state[nseq, H, P, N] fp32, or NULL (not written); may alias
  *              init_state (each element is read before it is written)
  *   workspace  device scratch of at least the queried size, owned by the
- *              caller, contents undefined on entry and exit
+ *              caller, contents undefined on entry and exit.  It holds the
+ *              per-chunk tables and one fp32 (P x N) state per (chunk, head),
+ *              about 4*P*N*H/chunk bytes per token.
  *   stream     hipStream_t (as void*) the kernels are queued on
  * Returns SSD_OK once the kernels are queued (asynchronous).
  */
@@ -131,7 +130,7 @@ ssd_status ssd_chunked_scan(const void* x, const float* dt, const float* A, cons
  *   A, D  [H]            fp32
  *   B, C  [batch, G, N]  dtype
  *   y     [batch, H, P]  ydtype   output; must not alias any input
- * shape->seqlen, shape->cu_seqlens and shape->chunks_per_segment are ignored.
+ * shape->seqlen and shape->cu_seqlens are ignored.
  */
 ssd_status ssd_decode_step(float* state, const void* x, const float* dt, const float* A,
                            const void* B, const void* C, const float* D, void* y,

@@ -42,7 +42,7 @@ class _Shape(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64), ("nheads", ctypes.c_int32),
                 ("headdim", ctypes.c_int32), ("dstate", ctypes.c_int32),
                 ("ngroups", ctypes.c_int32), ("dtype", ctypes.c_int32), ("ydtype", ctypes.c_int32),
-                ("chunks_per_segment", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("reserved", ctypes.c_int32 * 2),
                 ("cu_seqlens", ctypes.c_void_p),
                 ("cu_seqlens_host", ctypes.c_void_p)]
 
@@ -146,8 +146,8 @@ def _stream_handle(t) -> int:
     return torch.cuda.current_stream(t.device).cuda_stream
 
 
-def make_shape(x, B, cu_seqlens=None, cu_seqlens_host=None, chunks_per_segment: int = 0,
-               nseq: Optional[int] = None, y_dtype=None) -> Tuple[_Shape, object]:
+def make_shape(x, B, cu_seqlens=None, cu_seqlens_host=None, nseq: Optional[int] = None,
+               y_dtype=None) -> Tuple[_Shape, object]:
     """Build the C shape struct from tensors.  Returns (shape, keepalive)."""
     sh = _Shape()
     keep = None
@@ -167,12 +167,11 @@ def make_shape(x, B, cu_seqlens=None, cu_seqlens_host=None, chunks_per_segment: 
     sh.ngroups, sh.dstate = B.shape[-2], B.shape[-1]
     sh.dtype = _dtype_code(x)
     sh.ydtype = SSD_F32 if y_dtype is None else _dtype_code_of(y_dtype)
-    sh.chunks_per_segment = chunks_per_segment
     return sh, keep
 
 
-def workspace_size(x, B, chunk: int, cu_seqlens=None, chunks_per_segment: int = 0) -> int:
-    sh, _ = make_shape(x, B, cu_seqlens, None, chunks_per_segment)
+def workspace_size(x, B, chunk: int, cu_seqlens=None) -> int:
+    sh, _ = make_shape(x, B, cu_seqlens, None)
     n = ctypes.c_size_t(0)
     _check(load().ssd_chunked_scan_workspace_size(ctypes.byref(sh), int(chunk), ctypes.byref(n)),
            "ssd_chunked_scan_workspace_size")
@@ -184,7 +183,7 @@ STAGES = ("plan", "cumsum", "cb", "chunk_state", "state_passing", "chunk_scan")
 
 def chunked_scan(x, dt, A, B, C, D, chunk: int = 256, init_state=None, cu_seqlens=None, *,
                  y=None, final_state=None, want_final: bool = True, workspace=None,
-                 chunks_per_segment: int = 0, cu_seqlens_host: Optional[Sequence[int]] = None,
+                 cu_seqlens_host: Optional[Sequence[int]] = None,
                  stage_ms: Optional[list] = None, y_dtype=None):
     """Chunked prefill.  Returns (y, final_state or None).
 
@@ -207,7 +206,7 @@ def chunked_scan(x, dt, A, B, C, D, chunk: int = 256, init_state=None, cu_seqlen
         raise TypeError("cu_seqlens must be int32")
     if y_dtype is None:
         y_dtype = torch.float32 if y is None else y.dtype
-    sh, keep = make_shape(x, B, cu_seqlens, host_cu, chunks_per_segment, y_dtype=y_dtype)
+    sh, keep = make_shape(x, B, cu_seqlens, host_cu, y_dtype=y_dtype)
     nseq = sh.batch
     H, P, N = sh.nheads, sh.headdim, sh.dstate
     lead = tuple(x.shape[:-2])

@@ -1,6 +1,6 @@
 // Host side of the C ABI declared in include/ssd.h: argument validation (pure
-// host code, before any launch), the chunk/segment plan, the workspace carve
-// and the kernel queueing.  Nothing here allocates, frees or synchronizes.
+// host code, before any launch), the chunk plan, the workspace carve and the
+// kernel queueing.  Nothing here allocates, frees or synchronizes.
 #include <stdarg.h>
 #include <stdio.h>
 
@@ -33,12 +33,11 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 size_t up256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 constexpr size_t kMaxLds = 160 * 1024;  // LDS per CU on gfx950
-constexpr int kTargetWorkgroups = 2048;  // ~8 resident chunk-scan workgroups per CU
+constexpr int64_t kMaxGrid = ((int64_t)1 << 31) - 8;
 
 struct Prepared {
     ssd::Plan plan;
     ssd::Layout lay;
-    int run_passing;
 };
 
 ssd_status check_head_dims(const ssd_shape* sh) {
@@ -46,7 +45,8 @@ ssd_status check_head_dims(const ssd_shape* sh) {
         return fail(SSD_ERR_DTYPE, "dtype %d is neither SSD_F32 (0) nor SSD_BF16 (1)", sh->dtype);
     if (sh->ydtype != SSD_F32 && sh->ydtype != SSD_BF16)
         return fail(SSD_ERR_DTYPE, "ydtype %d is neither SSD_F32 (0) nor SSD_BF16 (1)", sh->ydtype);
-    if (sh->reserved != 0) return fail(SSD_ERR_SHAPE, "reserved field must be 0");
+    if (sh->reserved[0] != 0 || sh->reserved[1] != 0)
+        return fail(SSD_ERR_SHAPE, "reserved fields must be 0");
     if (sh->nheads < 1) return fail(SSD_ERR_SHAPE, "nheads must be >= 1 (got %d)", sh->nheads);
     if (sh->ngroups < 1 || sh->nheads % sh->ngroups != 0)
         return fail(SSD_ERR_SHAPE, "ngroups %d must be >= 1 and divide nheads %d", sh->ngroups,
@@ -66,7 +66,6 @@ ssd_status prepare(const ssd_shape* sh, int32_t chunk, Prepared* out) {
     if (chunk != 32 && chunk != 64 && chunk != 128 && chunk != 256)
         return fail(SSD_ERR_CHUNK, "chunk %d is not one of 32, 64, 128, 256", chunk);
     if (sh->seqlen < 0) return fail(SSD_ERR_SHAPE, "seqlen must be >= 0");
-    if (sh->chunks_per_segment < 0) return fail(SSD_ERR_SHAPE, "chunks_per_segment must be >= 0");
     const bool packed = sh->cu_seqlens != nullptr;
     const int64_t nseq = sh->batch;
     const int64_t T = packed ? sh->seqlen : sh->batch * sh->seqlen;
@@ -86,12 +85,11 @@ ssd_status prepare(const ssd_shape* sh, int32_t chunk, Prepared* out) {
     }
     if (!packed && sh->cu_seqlens_host)
         return fail(SSD_ERR_SHAPE, "cu_seqlens_host given without the device cu_seqlens");
-    const size_t lds = ssd::chunk_scan_lds_bytes(sh->dtype, sh->headdim, sh->dstate, chunk);
+    const size_t lds = ssd::prefill_lds_bytes(sh->dtype, sh->dstate, chunk);
     if (lds > kMaxLds)
         return fail(SSD_ERR_UNSUPPORTED,
-                    "headdim %d, dstate %d, chunk %d and dtype %d need %zu bytes of LDS (> %zu); "
-                    "use a smaller chunk",
-                    sh->headdim, sh->dstate, chunk, sh->dtype, lds, kMaxLds);
+                    "dstate %d, chunk %d and dtype %d need %zu bytes of LDS (> %zu); use a smaller chunk",
+                    sh->dstate, chunk, sh->dtype, lds, kMaxLds);
 
     ssd::Plan& pl = out->plan;
     pl = ssd::Plan{};
@@ -105,35 +103,22 @@ ssd_status prepare(const ssd_shape* sh, int32_t chunk, Prepared* out) {
     pl.dense = packed ? 0 : 1;
     pl.T = T;
     pl.cu = sh->cu_seqlens;
+    int64_t nchunks;
     if (!packed) {
         pl.L = sh->seqlen;
         pl.cpseq = (int32_t)((sh->seqlen + chunk - 1) / chunk);
-        int cps = sh->chunks_per_segment;
-        if (cps == 0) {
-            // enough segments per sequence to give ~kTargetWorkgroups chunk-scan workgroups
-            const int64_t pairs = std::max<int64_t>(1, nseq * sh->nheads);
-            int64_t want = (kTargetWorkgroups + pairs - 1) / pairs;
-            want = std::max<int64_t>(1, std::min<int64_t>(want, std::max(1, pl.cpseq)));
-            cps = (int)((std::max(1, pl.cpseq) + want - 1) / want);
-        }
-        pl.cps = std::max(1, std::min(cps, std::max(1, pl.cpseq)));
-        pl.spseq = pl.cpseq == 0 ? 0 : (pl.cpseq + pl.cps - 1) / pl.cps;
-        pl.nchunk_ub = (int32_t)(nseq * pl.cpseq);
-        pl.nseg_ub = (int32_t)(nseq * pl.spseq);
-        pl.nslot_ub = (int32_t)(nseq * std::max(0, pl.spseq - 1));
-        out->run_passing = (pl.spseq > 1 || (pl.cpseq == 0 && nseq > 0)) ? 1 : 0;
+        nchunks = nseq * pl.cpseq;
     } else {
         pl.L = 0;
-        const int64_t ub = nseq == 0 ? 0 : (T + nseq * (int64_t)(chunk - 1)) / chunk;
-        pl.nchunk_ub = (int32_t)ub;
-        int cps = sh->chunks_per_segment;
-        if (cps == 0) cps = (int)std::max<int64_t>(1, (ub * sh->nheads) / kTargetWorkgroups);
-        pl.cps = cps;
-        const int64_t sub = std::min<int64_t>(ub, (ub + nseq * (int64_t)(cps - 1)) / cps);
-        pl.nseg_ub = (int32_t)sub;
-        pl.nslot_ub = (int32_t)sub;
-        out->run_passing = nseq > 0 ? 1 : 0;
+        // every sequence wastes less than one chunk
+        nchunks = nseq == 0 ? 0 : (T + nseq * (int64_t)(chunk - 1)) / chunk;
     }
+    const int64_t npt = (sh->headdim + 31) / 32;
+    const int64_t nblk = ((int64_t)sh->headdim * sh->dstate / 4 + 255) / 256;
+    if (nchunks * sh->nheads * npt > kMaxGrid || nseq * sh->nheads * nblk > kMaxGrid ||
+        (sh->nheads + 3) / 4 > 65535 || sh->ngroups > 65535)
+        return fail(SSD_ERR_SHAPE, "problem too large for one launch grid");
+    pl.nchunk_ub = (int32_t)nchunks;
 
     ssd::Layout& L = out->lay;
     const size_t es = sh->dtype == SSD_BF16 ? 2 : 4;
@@ -145,12 +130,11 @@ ssd_status prepare(const ssd_shape* sh, int32_t chunk, Prepared* out) {
     };
     L.seq_tab = take(packed ? (size_t)nseq * 16 : 0);
     L.chunk_tab = take(packed ? (size_t)pl.nchunk_ub * 16 : 0);
-    L.seg_tab = take(packed ? (size_t)pl.nseg_ub * 16 : 0);
     L.cs = take((size_t)pl.nchunk_ub * pl.H * chunk * 4);
     L.dtc = take((size_t)pl.nchunk_ub * pl.H * chunk * 4);
     L.cb = take((size_t)pl.nchunk_ub * pl.G * chunk * chunk * es);
     L.bt = take((size_t)pl.nchunk_ub * pl.G * ssd::padded_dstate(pl.N) * chunk * es);
-    L.sbuf = take((size_t)pl.nslot_ub * pl.H * pl.P * pl.N * 4);
+    L.states = take((size_t)pl.nchunk_ub * pl.H * pl.P * pl.N * 4);
     L.total = std::max<size_t>(off, 256);
     return SSD_OK;
 }
@@ -228,10 +212,8 @@ ssd_status scan_impl(const void* x, const float* dt, const float* A, const void*
     a.ws = (char*)workspace;
     a.dtype = shape->dtype;
     a.y_f32 = shape->ydtype == SSD_F32 ? 1 : 0;
-    a.run_passing = pr.run_passing;
     pr.plan.seq_tab = (int32_t*)(a.ws + pr.lay.seq_tab);
     pr.plan.chunk_tab = (int32_t*)(a.ws + pr.lay.chunk_tab);
-    pr.plan.seg_tab = (int32_t*)(a.ws + pr.lay.seg_tab);
     if (pr.plan.nseq == 0 && !marks) return ok();
     const hipError_t err = ssd::launch_prefill(pr.plan, pr.lay, a, (hipStream_t)stream, marks);
     if (err != hipSuccess)

@@ -38,6 +38,9 @@ struct Tr<bf16_t> {
     __device__ static inline void st4(bf16_t* p, f32x4 v) {
         *(bf16x4*)p = __builtin_convertvector(v, bf16x4);
     }
+    __device__ static inline v4 narrow4(f32x4 v) { return __builtin_convertvector(v, bf16x4); }
+    __device__ static inline f32x4 widen4(v4 v) { return __builtin_convertvector(v, f32x4); }
+    __device__ static inline void st4raw(bf16_t* p, v4 v) { *(v4*)p = v; }
 };
 
 template <>
@@ -59,6 +62,9 @@ struct Tr<float> {
     __device__ static inline v8 narrow(f32x8 v) { return v; }
     __device__ static inline f32x4 ld4(const float* p) { return *(const f32x4*)p; }
     __device__ static inline void st4(float* p, f32x4 v) { *(f32x4*)p = v; }
+    __device__ static inline v4 narrow4(f32x4 v) { return v; }
+    __device__ static inline f32x4 widen4(v4 v) { return v; }
+    __device__ static inline void st4raw(float* p, v4 v) { *(v4*)p = v; }
 };
 
 // ---------------------------------------------------------------- MFMA
@@ -103,71 +109,35 @@ struct ChunkDesc {
     int32_t seq;   // -1: no such chunk
     int32_t len;
     int64_t row0;
-};
-
-struct SegDesc {
-    int32_t seq;      // -1: no such segment
-    int32_t chunk0;
-    int32_t nchunks;
-    int32_t idx;      // segment index inside its sequence
-    int32_t last;     // last segment of its sequence
-    int32_t slot_in;  // slot holding the entering state, -1: use the initial state
-    int32_t slot_out; // slot for this segment's own state, -1 when last
+    int32_t idx;   // chunk index inside its sequence
 };
 
 __device__ inline ChunkDesc chunk_desc(const Plan& pl, int k) {
     ChunkDesc d;
     if (pl.dense) {
-        if (k >= pl.nchunk_ub) { d.seq = -1; d.len = 0; d.row0 = 0; return d; }
+        if (k >= pl.nchunk_ub) { d.seq = -1; d.len = 0; d.row0 = 0; d.idx = 0; return d; }
         const int s = k / pl.cpseq;
         const int c = k - s * pl.cpseq;
         const int64_t t0 = (int64_t)c * pl.Q;
         d.seq = s;
         d.row0 = (int64_t)s * pl.L + t0;
         d.len = (int32_t)min((int64_t)pl.Q, pl.L - t0);
+        d.idx = c;
         return d;
     }
     const int4 e = ((const int4*)pl.chunk_tab)[k];
     d.seq = e.x;
     d.row0 = e.y;
     d.len = e.z;
-    return d;
-}
-
-__device__ inline SegDesc seg_desc(const Plan& pl, int j) {
-    SegDesc d;
-    if (pl.dense) {
-        if (j >= pl.nseg_ub) { d.seq = -1; return d; }
-        const int s = j / pl.spseq;
-        const int i = j - s * pl.spseq;
-        d.seq = s;
-        d.idx = i;
-        d.chunk0 = s * pl.cpseq + i * pl.cps;
-        d.nchunks = min(pl.cps, pl.cpseq - i * pl.cps);
-        d.last = (i == pl.spseq - 1);
-        const int slot0 = s * (pl.spseq - 1);
-        d.slot_in = i == 0 ? -1 : slot0 + i - 1;
-        d.slot_out = d.last ? -1 : slot0 + i;
-        return d;
-    }
-    const int4 e = ((const int4*)pl.seg_tab)[j];
-    d.seq = e.x;
-    if (d.seq < 0) return d;
-    d.chunk0 = e.y;
-    d.nchunks = e.z;
     d.idx = e.w;
-    const int4 q = ((const int4*)pl.seq_tab)[d.seq];
-    const int nseg = (q.y + pl.cps - 1) / pl.cps;
-    d.last = (d.idx == nseg - 1);
-    d.slot_in = d.idx == 0 ? -1 : q.w + d.idx - 1;
-    d.slot_out = d.last ? -1 : q.w + d.idx;
     return d;
 }
 
-// Sequence s: first chunk, chunk count and first slot.
-__device__ inline int4 seq_info(const Plan& pl, int s) {
-    if (pl.dense) return make_int4(s * pl.cpseq, pl.cpseq, s * pl.spseq, s * (pl.spseq - 1));
-    return ((const int4*)pl.seq_tab)[s];
+// Sequence s: first chunk and chunk count.
+__device__ inline int2 seq_chunks(const Plan& pl, int s) {
+    if (pl.dense) return make_int2(s * pl.cpseq, pl.cpseq);
+    const int4 q = ((const int4*)pl.seq_tab)[s];
+    return make_int2(q.x, q.y);
 }
 
 }  // namespace ssd

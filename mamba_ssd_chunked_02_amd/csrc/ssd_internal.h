@@ -13,40 +13,30 @@ namespace ssd {
 // on the host; for a packed batch the tables are filled on the device by the
 // plan kernel from the device copy of cu_seqlens.
 //
-// Terminology: a *chunk* is <= Q consecutive tokens of one sequence (chunks
-// restart at every sequence start).  A *segment* is <= cps consecutive chunks
-// of one sequence that one chunk-scan workgroup walks while carrying the state
-// in registers.  Every segment except the last of its sequence owns one
-// *slot* of the segment-state buffer: chunk_state writes the segment's own
-// state there and state_passing overwrites it with the state entering the
-// next segment.
+// A *chunk* is <= Q consecutive tokens of one sequence (chunks restart at
+// every sequence start).  Chunk-indexed launches cover nchunk_ub chunks; in a
+// packed batch the entries past the real chunk count are marked empty.
 struct Plan {
-    int32_t H, P, N, G, hpg, Q, cps;
+    int32_t H, P, N, G, hpg, Q;
     int32_t nseq;
     int32_t dense;     // 1: uniform batch, descriptors are arithmetic
-    int32_t pad0;
     int64_t L;         // dense: tokens per sequence
     int64_t T;         // total token rows
     int32_t nchunk_ub; // grid bound of chunk-indexed launches (exact when dense)
-    int32_t nseg_ub;   // grid bound of segment-indexed launches (exact when dense)
-    int32_t nslot_ub;  // slots in the segment-state buffer
     int32_t cpseq;     // dense: chunks per sequence
-    int32_t spseq;     // dense: segments per sequence
-    int32_t pad1;
     const int32_t* cu; // packed: device cu_seqlens [nseq+1]
-    int32_t* seq_tab;  // packed: per sequence {chunk0, nchunks, seg0, slot0}
-    int32_t* chunk_tab;// packed: per chunk {seq, row0, len, seg}
-    int32_t* seg_tab;  // packed: per segment {seq, chunk0, nchunks, index in sequence}
+    int32_t* seq_tab;  // packed: per sequence {chunk0, nchunks, 0, 0}
+    int32_t* chunk_tab;// packed: per chunk {seq, row0, len, index in sequence}
 };
 
 // Byte offsets of the workspace regions (all 256-byte aligned).
 struct Layout {
-    size_t seq_tab, chunk_tab, seg_tab;  // int32 x4 entries
-    size_t cs;      // f32 [nchunk_ub][H][Q]   decay exponent sums dA_cs
+    size_t seq_tab, chunk_tab;  // int32 x4 entries
+    size_t cs;      // f32 [nchunk_ub][H][Q]   inclusive sums of dt A within each chunk
     size_t dtc;     // f32 [nchunk_ub][H][Q]   dt per chunk and head, 0 past the chunk end
     size_t cb;      // elem [nchunk_ub][G][Q][Q] C_t . B_k within each chunk
     size_t bt;      // elem [nchunk_ub][G][NT][Q] B transposed per chunk, 0 past the end and N
-    size_t sbuf;    // f32 [nslot_ub][H][P][N] segment states, then states passed on
+    size_t states;  // f32 [nchunk_ub][H][P][N] chunk states, then the states entering each chunk
     size_t total;
 };
 
@@ -63,7 +53,6 @@ struct ScanArgs {
     char* ws;
     int32_t dtype;     // 0 f32, 1 bf16 (x, B, C)
     int32_t y_f32;     // 1: y is fp32, 0: y is bf16
-    int32_t run_passing; // launch chunk_state + state_passing
 };
 
 struct DecodeArgs {
@@ -84,8 +73,8 @@ struct DecodeArgs {
 // dstate padded to the 32-row tiles the kernels use.
 inline int padded_dstate(int N) { return N <= 32 ? 32 : N <= 64 ? 64 : N <= 128 ? 128 : 256; }
 
-// LDS bytes the chunk-scan kernel needs (0 if the tile shape is not built).
-size_t chunk_scan_lds_bytes(int dtype, int P, int N, int Q);
+// LDS bytes per workgroup of the largest prefill kernel for this shape.
+size_t prefill_lds_bytes(int dtype, int N, int Q);
 
 // Queue the prefill kernels.  Returns hipSuccess or the launch error.
 // When `marks` is non-NULL, an event is recorded before the first stage and

@@ -52,11 +52,12 @@ def test_only_the_abi_is_exported(lib):
 
 def shape(**kw):
     s = ssd._Shape()
-    d = dict(batch=1, seqlen=512, nheads=4, headdim=16, dstate=16, ngroups=1, dtype=0, ydtype=0,
-             chunks_per_segment=0, reserved=0)
+    d = dict(batch=1, seqlen=512, nheads=4, headdim=16, dstate=16, ngroups=1, dtype=0, ydtype=0)
+    res = kw.pop("reserved", (0, 0))
     d.update(kw)
     for k, v in d.items():
         setattr(s, k, v)
+    s.reserved[0], s.reserved[1] = res
     return s
 
 
@@ -78,7 +79,8 @@ def test_workspace_size_valid(lib):
 @pytest.mark.parametrize("kw,chunk,code", [
     (dict(dtype=7), 64, E_DTYPE),
     (dict(ydtype=2), 64, E_DTYPE),
-    (dict(reserved=1), 64, E_SHAPE),
+    (dict(reserved=(1, 0)), 64, E_SHAPE),
+    (dict(reserved=(0, 3)), 64, E_SHAPE),
     (dict(nheads=0), 64, E_SHAPE),
     (dict(nheads=6, ngroups=4), 64, E_SHAPE),
     (dict(headdim=12), 64, E_SHAPE),
@@ -87,7 +89,7 @@ def test_workspace_size_valid(lib):
     (dict(dstate=4), 64, E_SHAPE),
     (dict(batch=-1), 64, E_SHAPE),
     (dict(seqlen=-5), 64, E_SHAPE),
-    (dict(chunks_per_segment=-1), 64, E_SHAPE),
+    (dict(nheads=300000, ngroups=1), 64, E_SHAPE),
     (dict(), 48, E_CHUNK),
     (dict(), 512, E_CHUNK),
 ])

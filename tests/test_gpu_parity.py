@@ -20,20 +20,19 @@ def say(*a):
     sys.stdout.flush()
 
 
-def run_gpu(inp, chunk=None, cps=0, want_final=True):
+def run_gpu(inp, chunk=None, want_final=True):
     g = to_gpu(inp)
     chunk = chunk or inp.wl.chunk
     y, fin = ssd.chunked_scan(g["x"], g["dt"], g["A"], g["B"], g["C"], g["D"], chunk,
-                              init_state=g["init"], cu_seqlens=g.get("cu"),
-                              chunks_per_segment=cps, want_final=want_final)
+                              init_state=g["init"], cu_seqlens=g.get("cu"), want_final=want_final)
     torch.cuda.synchronize()
     return host(y), None if fin is None else host(fin)
 
 
-def check_scan(inp, chunk=None, cps=0, what=""):
+def check_scan(inp, chunk=None, what=""):
     dt = inp.wl.dtype
-    say("case:", inp.wl.name, "chunk", chunk, "cps", cps, what)
-    y, fin = run_gpu(inp, chunk, cps)
+    say("case:", inp.wl.name, "chunk", chunk, what)
+    y, fin = run_gpu(inp, chunk)
     yr, fr = oracle_scan(inp)
     ey = assert_close(y, yr, dt, "y " + what)
     ef = assert_close(fin, fr, dt, "final " + what)
@@ -93,8 +92,7 @@ def test_decay_variants(variant):
                           init_var=0.1)
     kw = dict(slow=dict(A_range=(-0.05, -0.001)), A0=dict(A_zero=True), x0=dict(x_zero=True))[variant]
     inp = W.generate(wl, 21, **kw)
-    for cps in (0, 1, 3):
-        check_scan(inp, cps=cps, what=variant)
+    check_scan(inp, what=variant)
 
 
 @pytest.mark.parametrize("chunk", [32, 64, 128, 256])
@@ -105,12 +103,15 @@ def test_chunk_sizes_agree(chunk):
     check_scan(inp, chunk=chunk)
 
 
-@pytest.mark.parametrize("cps", [1, 2, 3, 5, 100])
-def test_segment_lengths_agree(cps):
-    wl = W.small_workload(batch=2, seqlen=1100, H=3, P=64, N=128, G=1, chunk=64, dtype="bf16",
+@pytest.mark.parametrize("L", [64 * 7, 64 * 8, 64 * 9 + 5, 4100])
+def test_many_chunks_per_sequence(L):
+    """State passing walks the chunks in batches of eight: chunk counts below,
+    at and past a batch boundary, and a long sequence with slow decay so that
+    the passed state matters to the last chunk."""
+    wl = W.small_workload(batch=2, seqlen=L, H=3, P=64, N=128, G=1, chunk=64, dtype="bf16",
                           init_var=0.1)
-    inp = W.generate(wl, 41, A_range=(-0.1, -0.001))
-    check_scan(inp, cps=cps)
+    inp = W.generate(wl, 41 + L, A_range=(-0.02, -0.001))
+    check_scan(inp, what="L=%d" % L)
 
 
 def test_edge_lengths():
@@ -138,7 +139,7 @@ def test_final_state_may_alias_initial_state():
     g = to_gpu(inp)
     st = g["init"].clone()
     y, fin = ssd.chunked_scan(g["x"], g["dt"], g["A"], g["B"], g["C"], g["D"], 64, init_state=st,
-                              final_state=st, chunks_per_segment=2)
+                              final_state=st)
     torch.cuda.synchronize()
     yr, fr = oracle.scan(inp.x, inp.dt, inp.A, inp.B, inp.C, inp.D, init=inp.init)
     assert_close(host(st), fr, "f32", "aliased final")
@@ -146,16 +147,16 @@ def test_final_state_may_alias_initial_state():
 
 
 # ------------------------------------------------------------------ packed variable-length batches
-@pytest.mark.parametrize("lens,G,cps", [
-    ((100, 0, 513, 1, 256), 2, 0),
-    ((300, 700, 64, 65), 4, 1),
-    ((1024, 3000, 7), 8, 3),
-    ((0, 0), 1, 0),
+@pytest.mark.parametrize("lens,G", [
+    ((100, 0, 513, 1, 256), 2),
+    ((300, 700, 64, 65), 4),
+    ((1024, 3000, 7), 8),
+    ((0, 0), 1),
 ])
-def test_packed_batches(lens, G, cps):
+def test_packed_batches(lens, G):
     H = 8 if G in (1, 2, 4, 8) else G
     wl = W.small_workload(seqlens=lens, H=H, P=64, N=128, G=G, chunk=256, dtype="bf16", init_var=0.1)
-    check_scan(W.generate(wl, 70 + sum(lens)), cps=cps, what="lens=%s" % (lens,))
+    check_scan(W.generate(wl, 70 + sum(lens)), what="lens=%s" % (lens,))
 
 
 def test_packed_equals_separate_dense_runs():
@@ -232,14 +233,13 @@ def test_deterministic_and_independent_of_workspace_contents():
                           init_var=0.1)
     inp = W.generate(wl, 110)
     g = to_gpu(inp)
-    nbytes = ssd.workspace_size(g["x"], g["B"], 128, chunks_per_segment=2)
+    nbytes = ssd.workspace_size(g["x"], g["B"], 128)
     ws = torch.full((nbytes // 4,), float("nan"), device="cuda").view(torch.uint8)
     y_nan = torch.full(tuple(g["x"].shape), float("nan"), device="cuda")
     f_nan = torch.full((2, 4, 64, 128), float("nan"), device="cuda")
     y1, f1 = ssd.chunked_scan(g["x"], g["dt"], g["A"], g["B"], g["C"], g["D"], 128, init_state=g["init"],
-                              y=y_nan, final_state=f_nan, workspace=ws, chunks_per_segment=2)
-    y2, f2 = ssd.chunked_scan(g["x"], g["dt"], g["A"], g["B"], g["C"], g["D"], 128, init_state=g["init"],
-                              chunks_per_segment=2)
+                              y=y_nan, final_state=f_nan, workspace=ws)
+    y2, f2 = ssd.chunked_scan(g["x"], g["dt"], g["A"], g["B"], g["C"], g["D"], 128, init_state=g["init"])
     torch.cuda.synchronize()
     assert torch.isfinite(y1.float()).all() and torch.isfinite(f1).all()
     assert torch.equal(y1, y2) and torch.equal(f1, f2)
