@@ -34,11 +34,26 @@ size_t up256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 constexpr size_t kMaxLds = 160 * 1024;  // LDS per CU on gfx950
 constexpr int64_t kMaxGrid = ((int64_t)1 << 31) - 8;
+constexpr int64_t kTargetWorkgroups = 2048;  // ~8 per CU for chunk_state / chunk_scan
+constexpr int64_t kMaxHeadsPerWorkgroup = 16;
 
 struct Prepared {
     ssd::Plan plan;
     ssd::Layout lay;
 };
+
+// Heads of one group that a chunk_state / chunk_scan workgroup walks: the
+// group's per-chunk operands are loaded once per workgroup, so more heads per
+// workgroup means less L2 traffic, as long as ~2048 workgroups remain.
+int heads_per_workgroup(const ssd::Plan& pl) {
+    const int64_t npt = (pl.P + 31) / 32;
+    const int64_t units = (int64_t)pl.nchunk_ub * pl.H * npt;
+    int64_t hpw = units / kTargetWorkgroups;
+    hpw = std::max<int64_t>(1, std::min<int64_t>(hpw, std::min<int64_t>(kMaxHeadsPerWorkgroup, pl.hpg)));
+    // equal slices: the fewest slices of at most hpw heads, then spread evenly
+    const int64_t nslice = (pl.hpg + hpw - 1) / hpw;
+    return (int)((pl.hpg + nslice - 1) / nslice);
+}
 
 ssd_status check_head_dims(const ssd_shape* sh) {
     if (sh->dtype != SSD_F32 && sh->dtype != SSD_BF16)
@@ -118,6 +133,9 @@ ssd_status prepare(const ssd_shape* sh, int32_t chunk, Prepared* out) {
     if (nchunks * sh->nheads * npt > kMaxGrid || nseq * sh->nheads * nblk > kMaxGrid ||
         (sh->nheads + 3) / 4 > 65535 || sh->ngroups > 65535)
         return fail(SSD_ERR_SHAPE, "problem too large for one launch grid");
+    // one chunk of x or y is addressed with 32-bit byte offsets
+    if ((int64_t)chunk * sh->nheads * sh->headdim * 4 >= ((int64_t)1 << 31))
+        return fail(SSD_ERR_SHAPE, "nheads * headdim %lld too large", (long long)sh->nheads * sh->headdim);
     pl.nchunk_ub = (int32_t)nchunks;
 
     ssd::Layout& L = out->lay;
@@ -212,6 +230,7 @@ ssd_status scan_impl(const void* x, const float* dt, const float* A, const void*
     a.ws = (char*)workspace;
     a.dtype = shape->dtype;
     a.y_f32 = shape->ydtype == SSD_F32 ? 1 : 0;
+    a.hpw = heads_per_workgroup(pr.plan);
     pr.plan.seq_tab = (int32_t*)(a.ws + pr.lay.seq_tab);
     pr.plan.chunk_tab = (int32_t*)(a.ws + pr.lay.chunk_tab);
     if (pr.plan.nseq == 0 && !marks) return ok();

@@ -53,6 +53,7 @@ struct ScanArgs {
     char* ws;
     int32_t dtype;     // 0 f32, 1 bf16 (x, B, C)
     int32_t y_f32;     // 1: y is fp32, 0: y is bf16
+    int32_t hpw;       // heads per workgroup of chunk_state / chunk_scan (within one group)
 };
 
 struct DecodeArgs {

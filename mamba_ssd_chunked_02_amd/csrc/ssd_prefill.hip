@@ -134,8 +134,9 @@ __global__ __launch_bounds__(kThreads) void ssd_cumsum_kernel(Plan pl, const flo
 // ------------------------------------------------------------------ C.B^T
 // grid (chunks, G, Q/32), one wave: row tile ti of cb = C B^T (stored in the
 // input dtype) for column tiles kj <= ti, the causal part the chunk scan
-// reads; plus columns [32 ti, 32 ti + 32) of B^T with rows padded with zeros
-// to ntp (a multiple of 32).  Rows/columns past the chunk end are zero.
+// reads, with the diagonal tile's entries above the diagonal set to zero;
+// plus columns [32 ti, 32 ti + 32) of B^T with rows padded with zeros to ntp
+// (a multiple of 32).  Rows/columns past the chunk end are zero.
 template <typename T>
 __global__ __launch_bounds__(64) void ssd_cb_kernel(Plan pl, int ntp, const T* __restrict__ B,
                                                     const T* __restrict__ C, T* __restrict__ cb,
@@ -162,8 +163,12 @@ __global__ __launch_bounds__(64) void ssd_cb_kernel(Plan pl, int ntp, const T* _
             const v8 b0 = Tr<T>::ld8(brow + (nv ? n : 0));
             mma16(acc, (tv && nv) ? a0 : v8{}, (kv && nv) ? b0 : v8{});
         }
+        // the diagonal tile keeps only its causal part (column <= row)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) out[(size_t)(32 * ti + acc_row(v, lane)) * Q + 32 * kj + col] = (T)acc[v];
+        for (int v = 0; v < 16; ++v) {
+            const float val = (kj < ti || col <= acc_row(v, lane)) ? acc[v] : 0.f;
+            out[(size_t)(32 * ti + acc_row(v, lane)) * Q + 32 * kj + col] = (T)val;
+        }
     }
     T* btk = bt + ((size_t)k * G + g) * ntp * Q;
     for (int idx = lane; idx < 32 * (ntp / 8); idx += 64) {
@@ -199,103 +204,148 @@ __device__ inline int64_t xcd_item(int per_xcd) {
     return (int64_t)(blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
 }
 
-// Workgroup-cooperative transposed copy of x * w for the columns
-// [32pt, 32pt+32) of head h in one chunk:
+// Staging of x for one (chunk, head, 32-column tile): a unit is 4 tokens x 8
+// columns, loaded early into registers (XUnit), then scaled by per-token fp32
+// weights and written transposed to LDS:
 //   xh[pl][k] (+ xl[pl][k]) = x[row0+k][h][32pt+pl] * w[k]     (pitch LP)
 // zero past the chunk end and past P; xl (the rounding residue) only when LO.
-// One unit = 4 tokens x 8 columns; Q units, spread over the NTHR threads.
-template <typename T, bool LO, int Q, int NTHR>
-__device__ inline void stage_xw(const T* __restrict__ x, const ChunkDesc& cd, int H, int P, int h, int pt,
-                                const float* w, T* xh, T* xl, int LP, int tid) {
-    typedef typename Tr<T>::v8 v8;
+template <typename T>
+struct XUnit {
+    typename Tr<T>::v8 raw[4];
+    f32x4 cs4, dt4;  // cs and dt of the unit's tokens
+    float cref;      // cs the weights are taken relative to
+    int pb, k0;
+    bool pok;
+};
+
+template <typename T>
+__device__ inline void load_xunit(XUnit<T>& xu, const T* __restrict__ x, const ChunkDesc& cd, int H, int P,
+                                  int h, int pt, int u, const float* __restrict__ csk,
+                                  const float* __restrict__ dtk) {
+    xu.pb = u & 3;
+    xu.k0 = 4 * (u >> 2);
+    const int pc = 32 * pt + 8 * xu.pb;
+    xu.pok = pc < P;
+    const int p0 = xu.pok ? pc : 0;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int kk = min(xu.k0 + r, cd.len - 1);
+        xu.raw[r] = Tr<T>::ld8(x + ((cd.row0 + kk) * H + h) * P + p0);
+    }
+    xu.cs4 = *(const f32x4*)(csk + xu.k0);
+    xu.dt4 = *(const f32x4*)(dtk + xu.k0);
+}
+
+// w[k] = exp(cref - cs[k]) dt[k] (<= dt[k] for cref at or after k)
+template <typename T, bool LO>
+__device__ inline void store_xunit(const XUnit<T>& xu, const ChunkDesc& cd, T* xh, T* xl, int LP) {
     typedef typename Tr<T>::v4 v4;
+    f32x8 f[4];
 #pragma unroll
-    for (int u0 = 0; u0 < Q; u0 += NTHR) {
-        const int u = u0 + tid;
-        if (Q % NTHR != 0 && u >= Q) break;
-        const int pb = u & 3, k0 = 4 * (u >> 2);
-        const int pc = 32 * pt + 8 * pb;
-        const bool pok = pc < P;
-        const int p0 = pok ? pc : 0;
-        v8 raw[4];
+    for (int r = 0; r < 4; ++r) {
+        const float w = __expf(xu.cref - xu.cs4[r]) * xu.dt4[r];
+        f[r] = Tr<T>::widen(xu.raw[r]) * ((xu.pok && xu.k0 + r < cd.len) ? w : 0.f);
+    }
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int kk = min(k0 + r, cd.len - 1);
-            raw[r] = Tr<T>::ld8(x + ((cd.row0 + kk) * H + h) * P + p0);
-        }
-        const f32x4 wv = *(const f32x4*)(w + k0);
-        f32x8 f[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) f[r] = Tr<T>::widen(raw[r]) * ((pok && k0 + r < cd.len) ? wv[r] : 0.f);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const f32x4 o = {f[0][i], f[1][i], f[2][i], f[3][i]};
-            const v4 hi = Tr<T>::narrow4(o);
-            Tr<T>::st4raw(xh + (8 * pb + i) * LP + k0, hi);
-            if (LO) Tr<T>::st4raw(xl + (8 * pb + i) * LP + k0, Tr<T>::narrow4(o - Tr<T>::widen4(hi)));
-        }
+    for (int i = 0; i < 8; ++i) {
+        const f32x4 o = {f[0][i], f[1][i], f[2][i], f[3][i]};
+        const v4 hi = Tr<T>::narrow4(o);
+        Tr<T>::st4raw(xh + (8 * xu.pb + i) * LP + xu.k0, hi);
+        if (LO) Tr<T>::st4raw(xl + (8 * xu.pb + i) * LP + xu.k0, Tr<T>::narrow4(o - Tr<T>::widen4(hi)));
     }
 }
 
+// Work item of the MFMA kernels: (chunk k, group g, slice of hpw heads of the
+// group, tile pt of 32 columns of P).  The group's per-chunk operands (B^T,
+// C, C.B^T) are loaded once per workgroup and reused for every head of the
+// slice; the per-head inputs of the next head are loaded while the current
+// head computes.
+struct Item {
+    int k, g, pt, h0, nh;
+};
+
+__device__ inline bool decode_item(const Plan& pl, int per_xcd, int npt, int hpw, int nslice, Item& it) {
+    const int64_t item = xcd_item(per_xcd);
+    if (item >= (int64_t)pl.nchunk_ub * pl.G * nslice * npt) return false;
+    it.pt = (int)(item % npt);
+    int64_t r = item / npt;
+    const int slice = (int)(r % nslice);
+    r /= nslice;
+    it.g = (int)(r % pl.G);
+    it.k = (int)(r / pl.G);
+    it.h0 = it.g * pl.hpg + slice * hpw;
+    it.nh = min(hpw, pl.hpg - slice * hpw);
+    return it.nh > 0;
+}
+
 // ------------------------------------------------------------------ chunk_state
-// Workgroup per (chunk k, head h, tile pt of 32 columns of P):
+// Workgroup per item; for each head h of the slice:
 //   S_k[p][n] = sum_t exp(cs_last - cs_t) dt_t x[t][p] B[t][n]
 // for p in the tile and every n < N, as a (32 x Q) . (Q x NT) MFMA product:
 // A = (x w)^T from LDS (hi/lo pair when split), B = the B^T rows the cb
-// kernel wrote.  The weight w_t = exp(cs_last - cs_t) dt_t <= dt_t never
-// overflows.  Wave w computes the 32-wide n-tiles w, w + waves, ...
-__host__ __device__ constexpr int state_waves(int NT) { return NT / 32 < 4 ? NT / 32 : 4; }
-
+// kernel wrote, held in registers for the whole slice (one wave per 32-wide
+// n-tile).  The weight w_t = exp(cs_last - cs_t) dt_t <= dt_t never overflows.
 template <typename T>
 __host__ __device__ constexpr size_t chunk_state_lds_bytes(int Q) {
-    return (size_t)Q * sizeof(float) + (size_t)(Split<T>::on ? 2 : 1) * 32 * (Q + 8) * sizeof(T);
+    return (size_t)(Split<T>::on ? 2 : 1) * 32 * (Q + 8) * sizeof(T);
 }
 
 template <typename T, int NT, int NTI>
-__global__ __launch_bounds__(64 * state_waves(NT)) void ssd_chunk_state_kernel(
-    Plan pl, int per_xcd, int npt, const T* __restrict__ x, const float* __restrict__ cs,
+__global__ __launch_bounds__(2 * NT) void ssd_chunk_state_kernel(
+    Plan pl, int per_xcd, int npt, int hpw, int nslice, const T* __restrict__ x, const float* __restrict__ cs,
     const float* __restrict__ dtc, const T* __restrict__ bt, float* __restrict__ states) {
     extern __shared__ __align__(16) char smem[];
     constexpr bool SP = Split<T>::on;
-    constexpr int NNT = NT / 32, Q = 32 * NTI, LP = Q + 8;
-    constexpr int NW = state_waves(NT), NTHR = 64 * NW;
+    constexpr int Q = 32 * NTI, LP = Q + 8;
+    constexpr int NTHR = 2 * NT;  // one wave per n-tile
+    constexpr int UPT = (Q + NTHR - 1) / NTHR;
     typedef typename Tr<T>::v8 v8;
-    const int64_t item = xcd_item(per_xcd);
-    if (item >= (int64_t)pl.nchunk_ub * pl.H * npt) return;
-    const int pt = (int)(item % npt);
-    const int64_t kh = item / npt;
-    const int h = (int)(kh % pl.H), k = (int)(kh / pl.H);
-    const ChunkDesc cd = chunk_desc(pl, k);
+    Item it;
+    if (!decode_item(pl, per_xcd, npt, hpw, nslice, it)) return;
+    const ChunkDesc cd = chunk_desc(pl, it.k);
     if (cd.seq < 0) return;
-    const int P = pl.P, N = pl.N, H = pl.H, G = pl.G;
-    const int g = h / pl.hpg;
+    const int P = pl.P, N = pl.N, H = pl.H, G = pl.G, pt = it.pt, k = it.k;
     const int tid = threadIdx.x;
-    float* w = (float*)smem;
-    T* xh = (T*)(smem + Q * sizeof(float));
+    const int nt = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63, half = lane >> 5, col = lane & 31;
+    T* xh = (T*)smem;
     T* xl = xh + 32 * LP;
-    const float* csk = cs + ((size_t)k * H + h) * Q;
-    const float* dtk = dtc + ((size_t)k * H + h) * Q;
-    const float clast = csk[Q - 1];
-    for (int q = tid; q < Q; q += NTHR) w[q] = __expf(clast - csk[q]) * dtk[q];
-    __syncthreads();
-    stage_xw<T, SP, Q, NTHR>(x, cd, H, P, h, pt, w, xh, xl, LP, tid);
-    __syncthreads();
-    const int wave = tid >> 6, lane = tid & 63, half = lane >> 5, col = lane & 31;
-    const T* btk = bt + ((size_t)k * G + g) * NT * Q;
-    float* out = states + ((size_t)k * H + h) * P * N;
+    v8 bf[Q / 16];
+    const T* brow = bt + ((size_t)k * G + it.g) * NT * Q + (size_t)(32 * nt + col) * Q + 8 * half;
+#pragma unroll
+    for (int s = 0; s < Q / 16; ++s) bf[s] = Tr<T>::ld8(brow + 16 * s);
+    XUnit<T> xu[UPT];
+    float clast = 0.f;
+    auto prefetch = [&](int h) {
+        const float* csk = cs + ((size_t)k * H + h) * Q;
+        const float* dtk = dtc + ((size_t)k * H + h) * Q;
+#pragma unroll
+        for (int i = 0; i < UPT; ++i)
+            if (Q % NTHR == 0 || i * NTHR + tid < Q) load_xunit(xu[i], x, cd, H, P, h, pt, i * NTHR + tid, csk, dtk);
+        clast = csk[Q - 1];
+    };
+    prefetch(it.h0);
     const T* arow = xh + col * LP + 8 * half;
     const T* lrow = xl + col * LP + 8 * half;
-    for (int nt = wave; nt < NNT; nt += NW) {
+    const int n = 32 * nt + col;
+    for (int i = 0; i < it.nh; ++i) {
+        const int h = it.h0 + i;
+#pragma unroll
+        for (int u = 0; u < UPT; ++u)
+            if (Q % NTHR == 0 || u * NTHR + tid < Q) {
+                xu[u].cref = clast;
+                store_xunit<T, SP>(xu[u], cd, xh, xl, LP);
+            }
+        __syncthreads();
+        if (i + 1 < it.nh) prefetch(h + 1);
         f32x16 acc = {};
-        const T* brow = btk + (size_t)(32 * nt + col) * Q + 8 * half;
-#pragma unroll 8
+#pragma unroll
         for (int s = 0; s < Q / 16; ++s) {
-            const v8 b = Tr<T>::ld8(brow + 16 * s);
-            mma16(acc, Tr<T>::ld8(arow + 16 * s), b);
-            if (SP) mma16(acc, Tr<T>::ld8(lrow + 16 * s), b);
+            mma16(acc, Tr<T>::ld8(arow + 16 * s), bf[s]);
+            if (SP) mma16(acc, Tr<T>::ld8(lrow + 16 * s), bf[s]);
         }
-        // acc: row p = 32pt + acc_row(v), column n = 32nt + col
-        const int n = 32 * nt + col;
+        // acc: row p = 32pt + acc_row(v), column n
+        float* out = states + ((size_t)k * H + h) * P * N;
         if (n < N) {
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
@@ -303,6 +353,7 @@ __global__ __launch_bounds__(64 * state_waves(NT)) void ssd_chunk_state_kernel(
                 if (p < P) out[(size_t)p * N + n] = acc[v];
             }
         }
+        __syncthreads();  // the next head overwrites the LDS tile
     }
 }
 
@@ -407,55 +458,121 @@ __device__ inline ChunkTables carve_tables(char* base, int Q) {
     return tb;
 }
 
-template <int Q, int NTHR>
-__device__ inline void build_tables(const ChunkTables& tb, const float* __restrict__ csk,
-                                    const float* __restrict__ dtk, int tid) {
-    for (int q = tid; q < Q; q += NTHR) {
-        const float a = csk[q], d = dtk[q];
-        const float ce = csk[q | 31];
-        const int s = (q & ~31) - 1;
-        const float c0 = s >= 0 ? csk[s] : 0.f;
-        tb.cs[q] = a;
-        tb.dt[q] = d;
-        tb.wb[q] = __expf(ce - a) * d;
-        tb.ul[q] = __expf(a - c0);
-        tb.ue[q] = __expf(fminf(a - ce, kFastBlockDecay));
+// Table entries of token q, computed from values loaded early (TabIn).
+struct TabIn {
+    float a, d, ce, c0;  // cs_q, dt_q, cs at the end and before the start of q's block
+    float gc0, gce;      // block tid (tid < Q/32): cs before its start and at its end
+};
+
+template <int Q>
+__device__ inline void load_tab(TabIn& ti, const float* __restrict__ csk, const float* __restrict__ dtk,
+                                int tid) {
+    const int q = tid < Q ? tid : Q - 1;
+    ti.a = csk[q];
+    ti.d = dtk[q];
+    ti.ce = csk[q | 31];
+    const int s = (q & ~31) - 1;
+    ti.c0 = s >= 0 ? csk[s] : 0.f;
+    const int j = tid < Q / 32 ? tid : 0;
+    ti.gc0 = j > 0 ? csk[32 * j - 1] : 0.f;
+    ti.gce = csk[32 * j + 31];
+}
+
+template <int Q>
+__device__ inline void store_tab(const ChunkTables& tb, const TabIn& ti, int tid) {
+    if (tid < Q) {
+        tb.cs[tid] = ti.a;
+        tb.dt[tid] = ti.d;
+        tb.wb[tid] = __expf(ti.ce - ti.a) * ti.d;
+        tb.ul[tid] = __expf(ti.a - ti.c0);
+        tb.ue[tid] = __expf(fminf(ti.a - ti.ce, kFastBlockDecay));
     }
     if (tid < Q / 32) {
-        const float c0 = tid > 0 ? csk[32 * tid - 1] : 0.f;
-        const float ce = csk[32 * tid + 31];
-        tb.gam[tid] = __expf(ce - c0);
-        tb.fast[tid] = (c0 - ce) < kFastBlockDecay ? 1 : 0;
+        tb.gam[tid] = __expf(ti.gce - ti.gc0);
+        tb.fast[tid] = (ti.gc0 - ti.gce) < kFastBlockDecay ? 1 : 0;
     }
+}
+
+// Staging unit of the chunk scan: 2 tokens x 8 columns of x (one per thread
+// of the workgroup), scaled by wb and written transposed to the hi tile.
+template <typename T>
+struct XPair {
+    typename Tr<T>::v8 raw[2];
+    float c0, c1, d0, d1, ce;
+    int pb, k0;
+    bool pok;
+};
+
+template <typename T>
+__device__ inline void load_xpair(XPair<T>& xp, const T* __restrict__ x, const ChunkDesc& cd, int H, int P,
+                                  int h, int pt, int u, const float* __restrict__ csk,
+                                  const float* __restrict__ dtk) {
+    xp.pb = u & 3;
+    xp.k0 = 2 * (u >> 2);
+    const int pc = 32 * pt + 8 * xp.pb;
+    xp.pok = pc < P;
+    const int p0 = xp.pok ? pc : 0;
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+        const int kk = min(xp.k0 + r, cd.len - 1);
+        xp.raw[r] = Tr<T>::ld8(x + ((cd.row0 + kk) * H + h) * P + p0);
+    }
+    xp.c0 = csk[xp.k0];
+    xp.c1 = csk[xp.k0 + 1];
+    xp.d0 = dtk[xp.k0];
+    xp.d1 = dtk[xp.k0 + 1];
+    xp.ce = csk[xp.k0 | 31];
+}
+
+template <typename T>
+__device__ inline void store_xpair(const XPair<T>& xp, const ChunkDesc& cd, T* xh, int LP) {
+    const float w0 = (xp.pok && xp.k0 < cd.len) ? __expf(xp.ce - xp.c0) * xp.d0 : 0.f;
+    const float w1 = (xp.pok && xp.k0 + 1 < cd.len) ? __expf(xp.ce - xp.c1) * xp.d1 : 0.f;
+    const f32x8 f0 = Tr<T>::widen(xp.raw[0]) * w0;
+    const f32x8 f1 = Tr<T>::widen(xp.raw[1]) * w1;
+    typedef T t2 __attribute__((ext_vector_type(2)));
+#pragma unroll
+    for (int i = 0; i < 8; ++i) *(t2*)(xh + (8 * xp.pb + i) * LP + xp.k0) = t2{(T)f0[i], (T)f1[i]};
 }
 
 // hi/lo copy of the fp32 state rows p in [32pt, 32pt+32) as the B operand of
 // the state term: sh[pl][n] (+ sl[pl][n] when split), pitch NS, zero past P
-// and past N.
-template <typename T, int NT, int NTHR>
-__device__ inline void stage_state(const float* __restrict__ src, int P, int N, int pt, T* sh, T* sl,
-                                   int NS, int tid) {
-    typedef typename Tr<T>::v4 v4;
-    constexpr int NQ = NT / 4;
-    constexpr int U = 32 * NQ;
-    f32x4 v[(U + NTHR - 1) / NTHR];
+// and past N.  Loaded early (load_state_rows), written after (store_state_rows).
+template <int NT, int NTHR>
+struct StateRows {
+    static constexpr int NQ = NT / 4;
+    static constexpr int U = 32 * NQ;
+    static constexpr int PER = (U + NTHR - 1) / NTHR;
+    f32x4 v[PER];
+};
+
+template <int NT, int NTHR>
+__device__ inline void load_state_rows(StateRows<NT, NTHR>& sr, const float* __restrict__ src, int P, int N,
+                                       int pt, int tid) {
+    typedef StateRows<NT, NTHR> S;
 #pragma unroll
-    for (int i = 0; i * NTHR < U; ++i) {
+    for (int i = 0; i < S::PER; ++i) {
         const int u = i * NTHR + tid;
-        const int r = u / NQ, n = 4 * (u % NQ);
+        const int r = u / S::NQ, n = 4 * (u % S::NQ);
         const int p = 32 * pt + r;
-        const bool ok = (U % NTHR == 0 || u < U) && p < P && n < N;
+        const bool ok = (S::U % NTHR == 0 || u < S::U) && p < P && n < N;
         const f32x4 raw = *(const f32x4*)(src + (ok ? (size_t)p * N + n : 0));
-        v[i] = ok ? raw : f32x4{};
+        sr.v[i] = ok ? raw : f32x4{};
     }
+}
+
+template <typename T, int NT, int NTHR>
+__device__ inline void store_state_rows(const StateRows<NT, NTHR>& sr, T* sh, T* sl, int NS, int tid) {
+    typedef typename Tr<T>::v4 v4;
+    typedef StateRows<NT, NTHR> S;
 #pragma unroll
-    for (int i = 0; i * NTHR < U; ++i) {
+    for (int i = 0; i < S::PER; ++i) {
         const int u = i * NTHR + tid;
-        if (U % NTHR != 0 && u >= U) break;
-        const int r = u / NQ, n = 4 * (u % NQ);
-        const v4 hi = Tr<T>::narrow4(v[i]);
+        if (S::U % NTHR != 0 && u >= S::U) break;
+        const int r = u / S::NQ, n = 4 * (u % S::NQ);
+        const v4 hi = Tr<T>::narrow4(sr.v[i]);
         Tr<T>::st4raw(sh + r * NS + n, hi);
-        if (Split<T>::on) Tr<T>::st4raw(sl + r * NS + n, Tr<T>::narrow4(v[i] - Tr<T>::widen4(hi)));
+        if (Split<T>::on) Tr<T>::st4raw(sl + r * NS + n, Tr<T>::narrow4(sr.v[i] - Tr<T>::widen4(hi)));
     }
 }
 
@@ -465,78 +582,86 @@ __host__ __device__ constexpr size_t chunk_scan_lds_bytes(int NT, int Q) {
            (size_t)(Split<T>::on ? 2 : 1) * 32 * (NT + 8) * sizeof(T);
 }
 
-__host__ __device__ constexpr int scan_waves(int NTI) { return NTI < 4 ? NTI : 4; }
+// Raw buffer access (gfx9 descriptor: untyped 32-bit data format word).
+constexpr int kBufferWord3 = 0x00020000;
 
-template <typename T, typename TY>
-struct ScanCtx {
-    ChunkTables tb;
-    const T* xh;     // (x wb)^T hi, pitch Q + 8
-    const T* sh;     // entering state hi, pitch NT + 8
-    const T* sl;     // entering state lo
-    const T* cbk;    // C.B^T of the chunk, [Q][Q]
-    const T* Cm;     // C
-    const T* xcol;   // x at row 0, head h, column min(p, P-1)
-    TY* ycol;        // y at row 0, head h, column p
-    int64_t row0;
-    int len, G, g, N, HP, pvalid, has_state;
-    float Dh;
+__device__ inline __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kBufferWord3);
+}
+
+template <typename T>
+__device__ inline float buffer_load_elem(__amdgpu_buffer_rsrc_t r, int voff, int soff);
+template <>
+__device__ inline float buffer_load_elem<bf16_t>(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+    const unsigned short b = __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
+    return __builtin_bit_cast(float, (uint32_t)b << 16);
+}
+template <>
+__device__ inline float buffer_load_elem<float>(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
+}
+
+template <typename TY>
+__device__ inline void buffer_store_elem(TY v, __amdgpu_buffer_rsrc_t r, int voff, int soff);
+template <>
+__device__ inline void buffer_store_elem<float>(float v, __amdgpu_buffer_rsrc_t r, int voff, int soff) {
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, voff, soff, 0);
+}
+template <>
+__device__ inline void buffer_store_elem<bf16_t>(bf16_t v, __amdgpu_buffer_rsrc_t r, int voff, int soff) {
+    __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, v), r, voff, soff, 0);
+}
+
+// Per-wave operands of output block TI that do not depend on the head:
+// C.B^T rows of the block (A operand of the intra-chunk term) and C rows (A
+// operand of the state term).
+template <typename T, int NT, int TI>
+struct BlockOps {
+    typename Tr<T>::v8 ga[TI + 1][2];
+    typename Tr<T>::v8 ca[NT / 16];
 };
 
-// One 32-token output block TI of the workgroup's tile, for the calling wave.
+// One head's output block TI for the calling wave.  xrow/srow/lrow point to
+// this lane's row of the LDS tiles; xoff is the lane's byte offset of
+// (row 4*half, head h, column p) from the chunk's first row of x, yoff the same
+// for y.
 template <typename T, typename TY, int NT, int NTI, int TI>
-__device__ __forceinline__ void scan_block(const ScanCtx<T, TY>& c) {
+__device__ __forceinline__ void scan_block(const BlockOps<T, NT, TI>& o, const ChunkTables& tb, const T* xrow,
+                                           const T* srow, const T* lrow, bool has_state,
+                                           __amdgpu_buffer_rsrc_t rx, __amdgpu_buffer_rsrc_t ry, int xoff,
+                                           int yoff, int HP, int len, bool pvalid, float Dh) {
     constexpr bool SP = Split<T>::on;
-    constexpr int Q = 32 * NTI, LP = Q + 8, NS = NT + 8;
     typedef typename Tr<T>::v8 v8;
-    typedef typename Tr<T>::elem E;
     const int lane = threadIdx.x & 63, half = lane >> 5, col = lane & 31;
     const int ta = 32 * TI + col;  // this lane's A row
-    // global operands first: C.B^T rows of the block, then x for the D x term
-    v8 ga[TI + 1][2];
-    const T* grow = c.cbk + (size_t)ta * Q + 8 * half;
-#pragma unroll
-    for (int kj = 0; kj <= TI; ++kj)
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) ga[kj][ks] = Tr<T>::ld8(grow + 32 * kj + 16 * ks);
+    const bool full = 32 * TI + 32 <= len;
+    // x at this lane's 16 output rows (D x term); rows past the chunk end are
+    // clamped to its last row in a partial block
     float xd[16];
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
-        const int t = min(32 * TI + acc_row(v, lane), c.len - 1);
-        xd[v] = (float)c.xcol[(c.row0 + t) * c.HP];
+        const int r = 32 * TI + 8 * (v >> 2) + (v & 3);  // row of the lanes with half = 0
+        const int fix = full ? 0 : (min(r + 4 * half, len - 1) - (r + 4 * half)) * HP * (int)sizeof(T);
+        xd[v] = buffer_load_elem<T>(rx, xoff + fix, r * HP * (int)sizeof(T));
     }
     f32x16 acc = {};
-    if (c.has_state) {
-        const T* crow = c.Cm + ((c.row0 + min(ta, c.len - 1)) * c.G + c.g) * c.N;
-        const T* srow = c.sh + col * NS + 8 * half;
-        const T* lrow = c.sl + col * NS + 8 * half;
-        v8 ca[NT / 16];
-#pragma unroll
-        for (int s = 0; s < NT / 16; ++s) ca[s] = Tr<T>::ld8(crow + min(16 * s + 8 * half, c.N - 8));
+    if (has_state) {
 #pragma unroll
         for (int s = 0; s < NT / 16; ++s) {
-            mma16(acc, ca[s], Tr<T>::ld8(srow + 16 * s));
-            if (SP) mma16(acc, ca[s], Tr<T>::ld8(lrow + 16 * s));
+            mma16(acc, o.ca[s], Tr<T>::ld8(srow + 16 * s));
+            if (SP) mma16(acc, o.ca[s], Tr<T>::ld8(lrow + 16 * s));
         }
     }
-    const bool fast = c.tb.fast[TI] != 0;
-    const T* xrow = c.xh + col * LP + 8 * half;
+    const bool fast = tb.fast[TI] != 0;
 #pragma unroll
     for (int kj = 0; kj <= TI; ++kj) {
         if (kj < TI || fast) {
-            acc *= c.tb.gam[kj];
+            acc *= tb.gam[kj];
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                v8 a = ga[kj][ks];
-                if (kj == TI) {
-                    const int k0 = 32 * kj + 16 * ks + 8 * half;
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) a[i] = (k0 + i <= ta) ? a[i] : (E)0;
-                }
-                mma16(acc, a, Tr<T>::ld8(xrow + 32 * kj + 16 * ks));
-            }
+            for (int ks = 0; ks < 2; ++ks) mma16(acc, o.ga[kj][ks], Tr<T>::ld8(xrow + 32 * kj + 16 * ks));
         }
     }
-    const float* scale = fast ? c.tb.ue : c.tb.ul;
+    const float* scale = fast ? tb.ue : tb.ul;
 #pragma unroll
     for (int vg = 0; vg < 4; ++vg) {
         const f32x4 u = *(const f32x4*)(scale + 32 * TI + 8 * vg + 4 * half);
@@ -545,106 +670,144 @@ __device__ __forceinline__ void scan_block(const ScanCtx<T, TY>& c) {
     }
     if (!fast) {
         // decay across this block beyond the fast range: exact factors, raw x
-        const float cst = c.tb.cs[ta];
+        // (the C.B^T tile is already zero above its diagonal)
+        const float cst = tb.cs[ta];
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
             const int k0 = 32 * TI + 16 * ks + 8 * half;
-            const f32x8 gv = Tr<T>::widen(ga[TI][ks]);
+            const f32x8 gv = Tr<T>::widen(o.ga[TI][ks]);
             f32x8 m;
             v8 xb;
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 const int kk = k0 + i;
-                const float e = __expf(fminf(cst - c.tb.cs[kk], 0.f)) * c.tb.dt[kk];
-                m[i] = kk <= ta ? gv[i] * e : 0.f;
-                xb[i] = c.xcol[(c.row0 + min(kk, c.len - 1)) * c.HP];
+                m[i] = gv[i] * (__expf(fminf(cst - tb.cs[kk], 0.f)) * tb.dt[kk]);
+                const int kr = min(kk, len - 1);
+                xb[i] = (typename Tr<T>::elem)buffer_load_elem<T>(
+                    rx, xoff + (kr - 4 * half) * HP * (int)sizeof(T), 0);
             }
             mma16(acc, Tr<T>::narrow(m), xb);
         }
     }
     // + D x; rows t of this block, column p
-    if (c.pvalid) {
-        TY* yb = c.ycol + (c.row0 + 32 * TI) * c.HP;
-        if (32 * TI + 32 <= c.len) {
+    if (pvalid) {
+        if (full) {
 #pragma unroll
-            for (int v = 0; v < 16; ++v) yb[(int64_t)acc_row(v, lane) * c.HP] = (TY)(acc[v] + c.Dh * xd[v]);
+            for (int v = 0; v < 16; ++v) {
+                const int r = 32 * TI + 8 * (v >> 2) + (v & 3);
+                buffer_store_elem<TY>((TY)(acc[v] + Dh * xd[v]), ry, yoff, r * HP * (int)sizeof(TY));
+            }
         } else {
 #pragma unroll
-            for (int v = 0; v < 16; ++v)
-                if (32 * TI + acc_row(v, lane) < c.len)
-                    yb[(int64_t)acc_row(v, lane) * c.HP] = (TY)(acc[v] + c.Dh * xd[v]);
+            for (int v = 0; v < 16; ++v) {
+                const int r = 32 * TI + 8 * (v >> 2) + (v & 3);
+                if (r + 4 * half < len)
+                    buffer_store_elem<TY>((TY)(acc[v] + Dh * xd[v]), ry, yoff, r * HP * (int)sizeof(TY));
+            }
         }
     }
 }
 
+// Wave w of the workgroup computes output block blk(w) of every head of the
+// slice.  With 8 blocks the blocks are ordered so that waves w and w+4 (which
+// the hardware places on the same SIMD) hold causal work that sums to 9
+// block products.
+__host__ __device__ constexpr int scan_block_of_wave(int NTI, int w) {
+    return NTI == 8 ? (w < 4 ? w : 11 - w) : w;
+}
+
+template <typename T, typename TY, int NT, int NTI, int TI>
+__device__ __forceinline__ void scan_wave(const Plan& pl, const Item& it, const ChunkDesc& cd, char* smem,
+                                          const T* __restrict__ x, const float* __restrict__ cs,
+                                          const float* __restrict__ dtc, const T* __restrict__ Cm,
+                                          const T* __restrict__ cb, const float* __restrict__ D,
+                                          const float* __restrict__ states, bool has_state, TY* __restrict__ y) {
+    constexpr int Q = 32 * NTI, LP = Q + 8, NS = NT + 8;
+    constexpr int NTHR = 64 * NTI;
+    const int P = pl.P, N = pl.N, H = pl.H, G = pl.G, k = it.k, pt = it.pt;
+    const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5, col = lane & 31;
+    const ChunkTables tb = carve_tables(smem, Q);
+    T* xh = (T*)(smem + tables_bytes(Q));
+    T* sh = xh + 32 * LP;
+    T* sl = sh + 32 * NS;
+    // the group's operands of this wave's block, once for the whole slice
+    BlockOps<T, NT, TI> o;
+    {
+        const int ta = 32 * TI + col;
+        const T* grow = cb + ((size_t)k * G + it.g) * Q * Q + (size_t)ta * Q + 8 * half;
+#pragma unroll
+        for (int kj = 0; kj <= TI; ++kj)
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) o.ga[kj][ks] = Tr<T>::ld8(grow + 32 * kj + 16 * ks);
+        if (has_state) {
+            const T* crow = Cm + ((cd.row0 + min(ta, cd.len - 1)) * G + it.g) * N;
+#pragma unroll
+            for (int s = 0; s < NT / 16; ++s) o.ca[s] = Tr<T>::ld8(crow + min(16 * s + 8 * half, N - 8));
+        }
+    }
+    const int HP = H * P;
+    const int p = 32 * pt + col;
+    const __amdgpu_buffer_rsrc_t rx = buffer_rsrc(x + cd.row0 * HP, (uint32_t)(cd.len * HP * sizeof(T)));
+    const __amdgpu_buffer_rsrc_t ry = buffer_rsrc(y + cd.row0 * HP, (uint32_t)(cd.len * HP * sizeof(TY)));
+    // per-head inputs, loaded one head ahead
+    TabIn tin;
+    XPair<T> xp;
+    StateRows<NT, NTHR> sr;
+    auto prefetch = [&](int h) {
+        const float* csk = cs + ((size_t)k * H + h) * Q;
+        const float* dtk = dtc + ((size_t)k * H + h) * Q;
+        load_tab<Q>(tin, csk, dtk, tid);
+        load_xpair(xp, x, cd, H, P, h, pt, tid, csk, dtk);
+        if (has_state) load_state_rows<NT, NTHR>(sr, states + ((size_t)k * H + h) * P * N, P, N, pt, tid);
+    };
+    prefetch(it.h0);
+    const T* xrow = xh + col * LP + 8 * half;
+    const T* srow = sh + col * NS + 8 * half;
+    const T* lrow = sl + col * NS + 8 * half;
+    for (int i = 0; i < it.nh; ++i) {
+        const int h = it.h0 + i;
+        store_tab<Q>(tb, tin, tid);
+        store_xpair(xp, cd, xh, LP);
+        if (has_state) store_state_rows<T, NT, NTHR>(sr, sh, sl, NS, tid);
+        __syncthreads();
+        if (i + 1 < it.nh) prefetch(h + 1);
+        const int xoff = (4 * half * HP + h * P + min(p, P - 1)) * (int)sizeof(T);
+        const int yoff = (4 * half * HP + h * P + p) * (int)sizeof(TY);
+        scan_block<T, TY, NT, NTI, TI>(o, tb, xrow, srow, lrow, has_state, rx, ry, xoff, yoff, HP, cd.len, p < P,
+                                       D[h]);
+        __syncthreads();  // the next head overwrites the LDS tiles
+    }
+}
+
+// Workgroup per item (chunk, group, head slice, 32-column tile), one wave per
+// 32-token output block.  Per head: the decay tables, (x wb)^T and the
+// entering state's hi/lo pair are staged in LDS (loaded while the previous
+// head computed), then every wave computes its block.
 template <typename T, typename TY, int NT, int NTI>
-__global__ __launch_bounds__(64 * scan_waves(NTI)) void ssd_chunk_scan_kernel(
-    Plan pl, int per_xcd, int npt, const T* __restrict__ x, const float* __restrict__ cs,
+__global__ __launch_bounds__(64 * NTI) void ssd_chunk_scan_kernel(
+    Plan pl, int per_xcd, int npt, int hpw, int nslice, const T* __restrict__ x, const float* __restrict__ cs,
     const float* __restrict__ dtc, const T* __restrict__ Cm, const T* __restrict__ cb,
     const float* __restrict__ D, const float* __restrict__ init, const float* __restrict__ states,
     TY* __restrict__ y) {
     extern __shared__ __align__(16) char smem[];
-    constexpr int Q = 32 * NTI, LP = Q + 8, NS = NT + 8;
-    constexpr int NTHR = 64 * scan_waves(NTI);
-    const int64_t item = xcd_item(per_xcd);
-    if (item >= (int64_t)pl.nchunk_ub * pl.H * npt) return;
-    const int pt = (int)(item % npt);
-    const int64_t kh = item / npt;
-    const int h = (int)(kh % pl.H), k = (int)(kh / pl.H);
-    const ChunkDesc cd = chunk_desc(pl, k);
+    Item it;
+    if (!decode_item(pl, per_xcd, npt, hpw, nslice, it)) return;
+    const ChunkDesc cd = chunk_desc(pl, it.k);
     if (cd.seq < 0) return;
-    const int P = pl.P, N = pl.N, H = pl.H, G = pl.G;
-    const int tid = threadIdx.x;
-    ScanCtx<T, TY> c;
-    c.tb = carve_tables(smem, Q);
-    T* xh = (T*)(smem + tables_bytes(Q));
-    T* sh = xh + 32 * LP;
-    T* sl = sh + 32 * NS;
-    c.has_state = (cd.idx > 0 || init != nullptr) ? 1 : 0;
-    build_tables<Q, NTHR>(c.tb, cs + ((size_t)k * H + h) * Q, dtc + ((size_t)k * H + h) * Q, tid);
-    if (c.has_state)
-        stage_state<T, NT, NTHR>(states + ((size_t)k * H + h) * P * N, P, N, pt, sh, sl, NS, tid);
-    __syncthreads();
-    stage_xw<T, false, Q, NTHR>(x, cd, H, P, h, pt, c.tb.wb, xh, nullptr, LP, tid);
-    __syncthreads();
-    const int wave = tid >> 6, col = tid & 31;
-    const int p = 32 * pt + col;
-    c.xh = xh;
-    c.sh = sh;
-    c.sl = sl;
-    c.cbk = cb + ((size_t)k * G + (h / pl.hpg)) * Q * Q;
-    c.Cm = Cm;
-    c.HP = H * P;
-    c.xcol = x + (size_t)h * P + min(p, P - 1);
-    c.ycol = y + (size_t)h * P + p;
-    c.row0 = cd.row0;
-    c.len = cd.len;
-    c.G = G;
-    c.g = h / pl.hpg;
-    c.N = N;
-    c.pvalid = p < P;
-    c.Dh = D[h];
-    // causal work is balanced by pairing block w with block NTI-1-w
-    if constexpr (NTI == 8) {
-        switch (wave) {
-            case 0: scan_block<T, TY, NT, NTI, 0>(c); scan_block<T, TY, NT, NTI, 7>(c); break;
-            case 1: scan_block<T, TY, NT, NTI, 1>(c); scan_block<T, TY, NT, NTI, 6>(c); break;
-            case 2: scan_block<T, TY, NT, NTI, 2>(c); scan_block<T, TY, NT, NTI, 5>(c); break;
-            default: scan_block<T, TY, NT, NTI, 3>(c); scan_block<T, TY, NT, NTI, 4>(c); break;
-        }
-    } else if constexpr (NTI == 4) {
-        switch (wave) {
-            case 0: scan_block<T, TY, NT, NTI, 0>(c); break;
-            case 1: scan_block<T, TY, NT, NTI, 1>(c); break;
-            case 2: scan_block<T, TY, NT, NTI, 2>(c); break;
-            default: scan_block<T, TY, NT, NTI, 3>(c); break;
-        }
-    } else if constexpr (NTI == 2) {
-        if (wave == 0) scan_block<T, TY, NT, NTI, 0>(c);
-        else scan_block<T, TY, NT, NTI, 1>(c);
-    } else {
-        scan_block<T, TY, NT, NTI, 0>(c);
+    const bool has_state = cd.idx > 0 || init != nullptr;
+    // wave index as a scalar: each wave takes one branch below
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+#define SSD_WAVE(w)                                                                                   \
+    case w:                                                                                           \
+        if constexpr (w < NTI)                                                                        \
+            scan_wave<T, TY, NT, NTI, scan_block_of_wave(NTI, w)>(pl, it, cd, smem, x, cs, dtc, Cm, cb, D, \
+                                                                  states, has_state, y);              \
+        break;
+    switch (wave) {
+        SSD_WAVE(0) SSD_WAVE(1) SSD_WAVE(2) SSD_WAVE(3) SSD_WAVE(4) SSD_WAVE(5) SSD_WAVE(6) SSD_WAVE(7)
+        default: break;
     }
+#undef SSD_WAVE
 }
 
 // ------------------------------------------------------------------ launch
@@ -670,7 +833,8 @@ hipError_t run_prefill(const Plan& pl, const Layout& lay, const ScanArgs& a, hip
     hipError_t err;
     auto mark = [&](int i) -> hipError_t { return marks ? hipEventRecord(marks[i], stream) : hipSuccess; };
     const int npt = (pl.P + 31) / 32;
-    const int64_t nitems = (int64_t)pl.nchunk_ub * pl.H * npt;
+    const int nslice = (pl.hpg + a.hpw - 1) / a.hpw;
+    const int64_t nitems = (int64_t)pl.nchunk_ub * pl.G * nslice * npt;
     const int per_xcd = (int)((nitems + 7) / 8);
     if ((err = mark(0)) != hipSuccess) return err;
     if (!pl.dense && pl.nseq > 0) {
@@ -694,8 +858,8 @@ hipError_t run_prefill(const Plan& pl, const Layout& lay, const ScanArgs& a, hip
         auto* k2 = ssd_chunk_state_kernel<T, NT, NTI>;
         const size_t lds = chunk_state_lds_bytes<T>(Q);
         if ((err = allow_lds(k2, lds)) != hipSuccess) return err;
-        hipLaunchKernelGGL(k2, dim3(8 * per_xcd), dim3(64 * state_waves(NT)), lds, stream, pl, per_xcd, npt,
-                           x, cs, dtc, bt, states);
+        hipLaunchKernelGGL(k2, dim3(8 * per_xcd), dim3(2 * NT), lds, stream, pl, per_xcd, npt, a.hpw,
+                           nslice, x, cs, dtc, bt, states);
         if ((err = hipGetLastError()) != hipSuccess) return err;
     }
     if ((err = mark(4)) != hipSuccess) return err;
@@ -710,8 +874,8 @@ hipError_t run_prefill(const Plan& pl, const Layout& lay, const ScanArgs& a, hip
         auto* k4 = ssd_chunk_scan_kernel<T, TY, NT, NTI>;
         const size_t lds = chunk_scan_lds_bytes<T>(NT, Q);
         if ((err = allow_lds(k4, lds)) != hipSuccess) return err;
-        hipLaunchKernelGGL(k4, dim3(8 * per_xcd), dim3(64 * scan_waves(NTI)), lds, stream, pl, per_xcd, npt,
-                           x, cs, dtc, C, cbm, a.D, a.init, states, (TY*)a.y);
+        hipLaunchKernelGGL(k4, dim3(8 * per_xcd), dim3(64 * NTI), lds, stream, pl, per_xcd, npt, a.hpw,
+                           nslice, x, cs, dtc, C, cbm, a.D, a.init, states, (TY*)a.y);
         if ((err = hipGetLastError()) != hipSuccess) return err;
     }
     if ((err = mark(6)) != hipSuccess) return err;
