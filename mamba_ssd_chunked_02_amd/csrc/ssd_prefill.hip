@@ -218,12 +218,15 @@ struct XUnit {
     bool pok;
 };
 
-template <typename T>
+// Unit u covers column group pb and token group kb; 16 consecutive units share
+// pb, so a wave's transposed LDS writes fall on distinct banks.
+template <typename T, int Q>
 __device__ inline void load_xunit(XUnit<T>& xu, const T* __restrict__ x, const ChunkDesc& cd, int H, int P,
                                   int h, int pt, int u, const float* __restrict__ csk,
                                   const float* __restrict__ dtk) {
-    xu.pb = u & 3;
-    xu.k0 = 4 * (u >> 2);
+    constexpr int G16 = Q / 4 < 16 ? Q / 4 : 16;
+    xu.pb = (u / G16) & 3;
+    xu.k0 = 4 * (u % G16 + G16 * (u / (4 * G16)));
     const int pc = 32 * pt + 8 * xu.pb;
     xu.pok = pc < P;
     const int p0 = xu.pok ? pc : 0;
@@ -321,7 +324,8 @@ __global__ __launch_bounds__(2 * NT) void ssd_chunk_state_kernel(
         const float* dtk = dtc + ((size_t)k * H + h) * Q;
 #pragma unroll
         for (int i = 0; i < UPT; ++i)
-            if (Q % NTHR == 0 || i * NTHR + tid < Q) load_xunit(xu[i], x, cd, H, P, h, pt, i * NTHR + tid, csk, dtk);
+            if (Q % NTHR == 0 || i * NTHR + tid < Q)
+                load_xunit<T, Q>(xu[i], x, cd, H, P, h, pt, i * NTHR + tid, csk, dtk);
         clast = csk[Q - 1];
     };
     prefetch(it.h0);
@@ -494,7 +498,10 @@ __device__ inline void store_tab(const ChunkTables& tb, const TabIn& ti, int tid
 }
 
 // Staging unit of the chunk scan: 2 tokens x 8 columns of x (one per thread
-// of the workgroup), scaled by wb and written transposed to the hi tile.
+// of the workgroup), written as is to the row tile xr[t][p] (for the D x
+// term) and, scaled by wb, transposed to the hi tile.  16 consecutive units
+// share the column group, so a wave's transposed LDS writes fall on distinct
+// banks.
 template <typename T>
 struct XPair {
     typename Tr<T>::v8 raw[2];
@@ -507,8 +514,8 @@ template <typename T>
 __device__ inline void load_xpair(XPair<T>& xp, const T* __restrict__ x, const ChunkDesc& cd, int H, int P,
                                   int h, int pt, int u, const float* __restrict__ csk,
                                   const float* __restrict__ dtk) {
-    xp.pb = u & 3;
-    xp.k0 = 2 * (u >> 2);
+    xp.pb = (u >> 4) & 3;
+    xp.k0 = 2 * ((u & 15) + 16 * (u >> 6));
     const int pc = 32 * pt + 8 * xp.pb;
     xp.pok = pc < P;
     const int p0 = xp.pok ? pc : 0;
@@ -525,7 +532,9 @@ __device__ inline void load_xpair(XPair<T>& xp, const T* __restrict__ x, const C
 }
 
 template <typename T>
-__device__ inline void store_xpair(const XPair<T>& xp, const ChunkDesc& cd, T* xh, int LP) {
+__device__ inline void store_xpair(const XPair<T>& xp, const ChunkDesc& cd, T* xh, int LP, T* xr, int XRP) {
+    Tr<T>::st8(xr + xp.k0 * XRP + 8 * xp.pb, xp.raw[0]);
+    Tr<T>::st8(xr + (xp.k0 + 1) * XRP + 8 * xp.pb, xp.raw[1]);
     const float w0 = (xp.pok && xp.k0 < cd.len) ? __expf(xp.ce - xp.c0) * xp.d0 : 0.f;
     const float w1 = (xp.pok && xp.k0 + 1 < cd.len) ? __expf(xp.ce - xp.c1) * xp.d1 : 0.f;
     const f32x8 f0 = Tr<T>::widen(xp.raw[0]) * w0;
@@ -576,10 +585,21 @@ __device__ inline void store_state_rows(const StateRows<NT, NTHR>& sr, T* sh, T*
     }
 }
 
+// Row pitch (elements) of the raw x tile xr[t][p]: 32 columns plus 16 bytes.
+template <typename T>
+__host__ __device__ constexpr int xr_pitch() { return 32 + 16 / (int)sizeof(T); }
+
+// One staging buffer: tables | (x wb)^T hi [32][Q+8] | state hi, lo [32][NT+8] | x [Q][xr_pitch]
 template <typename T>
 __host__ __device__ constexpr size_t chunk_scan_lds_bytes(int NT, int Q) {
     return tables_bytes(Q) + (size_t)32 * (Q + 8) * sizeof(T) +
-           (size_t)(Split<T>::on ? 2 : 1) * 32 * (NT + 8) * sizeof(T);
+           (size_t)(Split<T>::on ? 2 : 1) * 32 * (NT + 8) * sizeof(T) + (size_t)Q * xr_pitch<T>() * sizeof(T);
+}
+
+// Two buffers (stage head i+1 while head i computes) when they fit in LDS.
+template <typename T>
+__host__ __device__ constexpr int chunk_scan_buffers(int NT, int Q) {
+    return 2 * chunk_scan_lds_bytes<T>(NT, Q) <= 160 * 1024 ? 2 : 1;
 }
 
 // Raw buffer access (gfx9 descriptor: untyped 32-bit data format word).
@@ -622,28 +642,25 @@ struct BlockOps {
 };
 
 // One head's output block TI for the calling wave.  xrow/srow/lrow point to
-// this lane's row of the LDS tiles; xoff is the lane's byte offset of
-// (row 4*half, head h, column p) from the chunk's first row of x, yoff the same
-// for y.
+// this lane's row of the LDS tiles, xcol to this lane's column of the raw x
+// tile (pitch XRP); yoff is the lane's byte offset of (row 4*half, head h,
+// column p) from the chunk's first row of y.  No global loads: the block
+// reads LDS and registers only, and its stores are the last memory operations.
 template <typename T, typename TY, int NT, int NTI, int TI>
 __device__ __forceinline__ void scan_block(const BlockOps<T, NT, TI>& o, const ChunkTables& tb, const T* xrow,
-                                           const T* srow, const T* lrow, bool has_state,
-                                           __amdgpu_buffer_rsrc_t rx, __amdgpu_buffer_rsrc_t ry, int xoff,
-                                           int yoff, int HP, int len, bool pvalid, float Dh) {
+                                           const T* srow, const T* lrow, const T* xcol, bool has_state,
+                                           __amdgpu_buffer_rsrc_t ry, int yoff, int HP, int len, bool pvalid,
+                                           float Dh) {
     constexpr bool SP = Split<T>::on;
+    constexpr int XRP = xr_pitch<T>();
     typedef typename Tr<T>::v8 v8;
     const int lane = threadIdx.x & 63, half = lane >> 5, col = lane & 31;
     const int ta = 32 * TI + col;  // this lane's A row
     const bool full = 32 * TI + 32 <= len;
-    // x at this lane's 16 output rows (D x term); rows past the chunk end are
-    // clamped to its last row in a partial block
+    // x at this lane's 16 output rows (D x term)
     float xd[16];
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-        const int r = 32 * TI + 8 * (v >> 2) + (v & 3);  // row of the lanes with half = 0
-        const int fix = full ? 0 : (min(r + 4 * half, len - 1) - (r + 4 * half)) * HP * (int)sizeof(T);
-        xd[v] = buffer_load_elem<T>(rx, xoff + fix, r * HP * (int)sizeof(T));
-    }
+    for (int v = 0; v < 16; ++v) xd[v] = (float)xcol[(32 * TI + acc_row(v, lane)) * XRP];
     f32x16 acc = {};
     if (has_state) {
 #pragma unroll
@@ -682,9 +699,7 @@ __device__ __forceinline__ void scan_block(const BlockOps<T, NT, TI>& o, const C
             for (int i = 0; i < 8; ++i) {
                 const int kk = k0 + i;
                 m[i] = gv[i] * (__expf(fminf(cst - tb.cs[kk], 0.f)) * tb.dt[kk]);
-                const int kr = min(kk, len - 1);
-                xb[i] = (typename Tr<T>::elem)buffer_load_elem<T>(
-                    rx, xoff + (kr - 4 * half) * HP * (int)sizeof(T), 0);
+                xb[i] = xcol[kk * XRP];
             }
             mma16(acc, Tr<T>::narrow(m), xb);
         }
@@ -726,10 +741,6 @@ __device__ __forceinline__ void scan_wave(const Plan& pl, const Item& it, const 
     constexpr int NTHR = 64 * NTI;
     const int P = pl.P, N = pl.N, H = pl.H, G = pl.G, k = it.k, pt = it.pt;
     const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5, col = lane & 31;
-    const ChunkTables tb = carve_tables(smem, Q);
-    T* xh = (T*)(smem + tables_bytes(Q));
-    T* sh = xh + 32 * LP;
-    T* sl = sh + 32 * NS;
     // the group's operands of this wave's block, once for the whole slice
     BlockOps<T, NT, TI> o;
     {
@@ -747,7 +758,6 @@ __device__ __forceinline__ void scan_wave(const Plan& pl, const Item& it, const 
     }
     const int HP = H * P;
     const int p = 32 * pt + col;
-    const __amdgpu_buffer_rsrc_t rx = buffer_rsrc(x + cd.row0 * HP, (uint32_t)(cd.len * HP * sizeof(T)));
     const __amdgpu_buffer_rsrc_t ry = buffer_rsrc(y + cd.row0 * HP, (uint32_t)(cd.len * HP * sizeof(TY)));
     // per-head inputs, loaded one head ahead
     TabIn tin;
@@ -760,22 +770,52 @@ __device__ __forceinline__ void scan_wave(const Plan& pl, const Item& it, const 
         load_xpair(xp, x, cd, H, P, h, pt, tid, csk, dtk);
         if (has_state) load_state_rows<NT, NTHR>(sr, states + ((size_t)k * H + h) * P * N, P, N, pt, tid);
     };
-    prefetch(it.h0);
-    const T* xrow = xh + col * LP + 8 * half;
-    const T* srow = sh + col * NS + 8 * half;
-    const T* lrow = sl + col * NS + 8 * half;
-    for (int i = 0; i < it.nh; ++i) {
-        const int h = it.h0 + i;
-        store_tab<Q>(tb, tin, tid);
-        store_xpair(xp, cd, xh, LP);
-        if (has_state) store_state_rows<T, NT, NTHR>(sr, sh, sl, NS, tid);
-        __syncthreads();
-        if (i + 1 < it.nh) prefetch(h + 1);
-        const int xoff = (4 * half * HP + h * P + min(p, P - 1)) * (int)sizeof(T);
+    constexpr size_t BUF = chunk_scan_lds_bytes<T>(NT, Q);
+    constexpr int XRP = xr_pitch<T>();
+    // buffer b: tables | xh | sh | sl | xr
+    auto tile = [&](int b, int which) -> T* {
+        char* base = smem + b * BUF;
+        T* xh = (T*)(base + tables_bytes(Q));
+        T* sh = xh + 32 * LP;
+        if (which == 0) return xh;
+        if (which == 1) return sh;
+        if (which == 2) return sh + 32 * NS;
+        return sh + (Split<T>::on ? 2 : 1) * 32 * NS;
+    };
+    auto stage = [&](int b) {
+        store_tab<Q>(carve_tables(smem + b * BUF, Q), tin, tid);
+        store_xpair(xp, cd, tile(b, 0), LP, tile(b, 3), XRP);
+        if (has_state) store_state_rows<T, NT, NTHR>(sr, tile(b, 1), tile(b, 2), NS, tid);
+    };
+    auto compute = [&](int b, int h) {
         const int yoff = (4 * half * HP + h * P + p) * (int)sizeof(TY);
-        scan_block<T, TY, NT, NTI, TI>(o, tb, xrow, srow, lrow, has_state, rx, ry, xoff, yoff, HP, cd.len, p < P,
-                                       D[h]);
-        __syncthreads();  // the next head overwrites the LDS tiles
+        scan_block<T, TY, NT, NTI, TI>(o, carve_tables(smem + b * BUF, Q), tile(b, 0) + col * LP + 8 * half,
+                                       tile(b, 1) + col * NS + 8 * half, tile(b, 2) + col * NS + 8 * half,
+                                       tile(b, 3) + col, has_state, ry, yoff, HP, cd.len, p < P, D[h]);
+    };
+    prefetch(it.h0);
+    if constexpr (chunk_scan_buffers<T>(NT, Q) == 2) {
+        // head i computes from buffer i%2 while head i+1 is staged into the
+        // other one: one workgroup barrier per head
+        stage(0);
+        __syncthreads();
+        if (it.nh > 1) prefetch(it.h0 + 1);
+        for (int i = 0; i < it.nh; ++i) {
+            const int h = it.h0 + i;
+            compute(i & 1, h);
+            if (i + 1 < it.nh) stage((i + 1) & 1);
+            if (i + 2 < it.nh) prefetch(h + 2);
+            __syncthreads();  // buffer i%2 is restaged at i+1; buffer (i+1)%2 is read at i+1
+        }
+    } else {
+        for (int i = 0; i < it.nh; ++i) {
+            const int h = it.h0 + i;
+            stage(0);
+            __syncthreads();
+            if (i + 1 < it.nh) prefetch(h + 1);
+            compute(0, h);
+            __syncthreads();  // the next head overwrites the LDS tiles
+        }
     }
 }
 
@@ -872,7 +912,7 @@ hipError_t run_prefill(const Plan& pl, const Layout& lay, const ScanArgs& a, hip
     if ((err = mark(5)) != hipSuccess) return err;
     if (nitems > 0) {
         auto* k4 = ssd_chunk_scan_kernel<T, TY, NT, NTI>;
-        const size_t lds = chunk_scan_lds_bytes<T>(NT, Q);
+        const size_t lds = chunk_scan_buffers<T>(NT, Q) * chunk_scan_lds_bytes<T>(NT, Q);
         if ((err = allow_lds(k4, lds)) != hipSuccess) return err;
         hipLaunchKernelGGL(k4, dim3(8 * per_xcd), dim3(64 * NTI), lds, stream, pl, per_xcd, npt, a.hpw,
                            nslice, x, cs, dtc, C, cbm, a.D, a.init, states, (TY*)a.y);
@@ -900,8 +940,11 @@ hipError_t dispatch(const Plan& pl, const Layout& lay, const ScanArgs& a, hipStr
 
 size_t prefill_lds_bytes(int dtype, int N, int Q) {
     const int NT = padded_dstate(N);
-    if (dtype == 1) return std::max(chunk_state_lds_bytes<bf16_t>(Q), chunk_scan_lds_bytes<bf16_t>(NT, Q));
-    return std::max(chunk_state_lds_bytes<float>(Q), chunk_scan_lds_bytes<float>(NT, Q));
+    if (dtype == 1)
+        return std::max(chunk_state_lds_bytes<bf16_t>(Q),
+                        chunk_scan_buffers<bf16_t>(NT, Q) * chunk_scan_lds_bytes<bf16_t>(NT, Q));
+    return std::max(chunk_state_lds_bytes<float>(Q),
+                    chunk_scan_buffers<float>(NT, Q) * chunk_scan_lds_bytes<float>(NT, Q));
 }
 
 hipError_t launch_prefill(const Plan& plan, const Layout& lay, const ScanArgs& a, hipStream_t stream,
