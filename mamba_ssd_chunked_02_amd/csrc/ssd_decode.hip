@@ -5,70 +5,79 @@
 //   S[p][:] <- exp(dt A) S[p][:] + (dt x[p]) B[:] ;  y[p] = S[p][:].C[:] + D x[p]
 //
 // The step is bound by HBM bandwidth: the fp32 state is read once and written
-// once (the read-D + write-D accounting of the SketchSSM page, Table 4).  Each
-// state row (b, h, p) of N floats is handled by TPR lanes with one 128-bit
-// non-temporal load and store per lane; the dot product with C is reduced
-// across those lanes with shuffles.  No MFMA: one multiply-add per element.
+// once (the read-D + write-D accounting of the SketchSSM page, Table 4).  One
+// wave streams one (sequence, head) block of P x N floats with 128-bit
+// non-temporal loads and stores, several in flight per lane; the dot product
+// with C is reduced across the row's lanes with DPP moves.  No MFMA: one
+// multiply-add per element.
 #include "ssd_device.h"
 
 namespace ssd {
 
 namespace {
 
-constexpr int kDecThreads = 256;
-constexpr int kRowsPerThread = 4;  // independent rows in flight per lane
+constexpr int kDecThreads = 256;  // four waves, one (sequence, head) state block each
+constexpr int kBatch = 8;         // 128-bit state loads in flight per lane
 
+// Sum over aligned groups of TPR lanes with DPP moves (no LDS): quad swaps,
+// half-row and row mirrors, then row broadcasts across 16-lane rows.  The
+// group's last lane always holds the group sum.
+template <int TPR>
+__device__ inline float group_sum(float v) {
+    if (TPR >= 2) v += dpp_take<0xB1, 0xf>(v);   // quad_perm [1,0,3,2]
+    if (TPR >= 4) v += dpp_take<0x4E, 0xf>(v);   // quad_perm [2,3,0,1]
+    if (TPR >= 8) v += dpp_take<0x141, 0xf>(v);  // row_half_mirror
+    if (TPR >= 16) v += dpp_take<0x140, 0xf>(v); // row_mirror
+    if (TPR >= 32) v += dpp_take<0x142, 0xa>(v); // row_bcast:15 into rows 1 and 3
+    if (TPR >= 64) v += dpp_take<0x143, 0xc>(v); // row_bcast:31 into rows 2 and 3
+    return v;
+}
+
+// Wave w of block L updates the state block (b, h) = 4L + w: P rows of N
+// floats, contiguous.  Lane l owns columns n = 4 (l % TPR) .. +3 of the rows
+// p = RPI i + l / TPR, so each wave instruction moves 64 x 16 contiguous bytes
+// and B, C, dt, A are loaded once per lane.
 template <typename T, int TPR>
 __global__ __launch_bounds__(kDecThreads) void ssd_decode_kernel(
-    int64_t rows, int H, int P, int N, int G, float* __restrict__ state, const T* __restrict__ x,
+    int64_t nbh, int H, int P, int N, int G, float* __restrict__ state, const T* __restrict__ x,
     const float* __restrict__ dt, const float* __restrict__ A, const T* __restrict__ B,
     const T* __restrict__ C, const float* __restrict__ D, void* __restrict__ y, int y_f32) {
-    constexpr int RPP = kDecThreads / TPR;  // rows per pass of the block
-    const int lr = threadIdx.x / TPR, j = threadIdx.x % TPR;
-    const int n = 4 * j;
-    const int hpg = H / G;
-    f32x4 s[kRowsPerThread], bv[kRowsPerThread], cv[kRowsPerThread];
-    float xv[kRowsPerThread], a[kRowsPerThread], u[kRowsPerThread];
-    int64_t r[kRowsPerThread];
-    // issue every load first so each lane keeps several 128-bit loads in flight
+    constexpr int RPI = 64 / TPR;  // rows per wave instruction
+    const int lane = threadIdx.x & 63;
+    const int64_t bh = (int64_t)blockIdx.x * (kDecThreads / 64) + (threadIdx.x >> 6);
+    if (bh >= nbh) return;
+    const int h = (int)(bh % H);
+    const int64_t b = bh / H;
+    const int g = h / (H / G);
+    const int j = lane % TPR, rsub = lane / TPR;
+    const bool nv = 4 * j < N;
+    const int n = nv ? 4 * j : N - 4;
+    const float d = dt[bh];
+    const float a = __expf(d * A[h]);
+    const float Dh = D[h];
+    const f32x4 bv = nv ? Tr<T>::ld4(B + (b * G + g) * N + n) : f32x4{};
+    const f32x4 cv = nv ? Tr<T>::ld4(C + (b * G + g) * N + n) : f32x4{};
+    float* sb = state + bh * P * N + n;
+    const T* xb = x + bh * P;
+    for (int p0 = 0; p0 < P; p0 += RPI * kBatch) {
+        f32x4 s[kBatch];
+        float xv[kBatch];
 #pragma unroll
-    for (int i = 0; i < kRowsPerThread; ++i) {
-        r[i] = ((int64_t)blockIdx.x * kRowsPerThread + i) * RPP + lr;
-        s[i] = f32x4{};
-        bv[i] = f32x4{};
-        cv[i] = f32x4{};
-        xv[i] = 0.f;
-        a[i] = 0.f;
-        u[i] = 0.f;
-        if (r[i] < rows) {
-            const int64_t bh = r[i] / P;
-            const int h = (int)(bh % H);
-            const int64_t b = bh / H;
-            const int g = h / hpg;
-            const float d = dt[bh];
-            xv[i] = (float)x[r[i]];
-            a[i] = __expf(d * A[h]);
-            u[i] = d * xv[i];
-            if (n < N) {
-                s[i] = __builtin_nontemporal_load((const f32x4*)(state + r[i] * N + n));
-                bv[i] = Tr<T>::ld4(B + (b * G + g) * N + n);
-                cv[i] = Tr<T>::ld4(C + (b * G + g) * N + n);
-            }
+        for (int u = 0; u < kBatch; ++u) {
+            const int p = min(p0 + u * RPI + rsub, P - 1);
+            s[u] = __builtin_nontemporal_load((const f32x4*)(sb + (int64_t)p * N));
+            xv[u] = (float)xb[p];
         }
-    }
 #pragma unroll
-    for (int i = 0; i < kRowsPerThread; ++i) {
-        const f32x4 ns = a[i] * s[i] + u[i] * bv[i];
-        float part = ns[0] * cv[i][0] + ns[1] * cv[i][1] + ns[2] * cv[i][2] + ns[3] * cv[i][3];
-#pragma unroll
-        for (int m = TPR / 2; m >= 1; m >>= 1) part += __shfl_xor(part, m, TPR);
-        if (r[i] < rows) {
-            if (n < N) __builtin_nontemporal_store(ns, (f32x4*)(state + r[i] * N + n));
-            if (j == 0) {
-                const int h = (int)((r[i] / P) % H);
-                const float o = part + D[h] * xv[i];
-                if (y_f32) ((float*)y)[r[i]] = o;
-                else ((bf16_t*)y)[r[i]] = (bf16_t)o;
+        for (int u = 0; u < kBatch; ++u) {
+            const int p = p0 + u * RPI + rsub;
+            const f32x4 ns = a * s[u] + (d * xv[u]) * bv;
+            if (p < P && nv) __builtin_nontemporal_store(ns, (f32x4*)(sb + (int64_t)p * N));
+            const float tot = group_sum<TPR>(ns[0] * cv[0] + ns[1] * cv[1] + ns[2] * cv[2] + ns[3] * cv[3]);
+            if (j == TPR - 1 && p < P) {
+                const float o = tot + Dh * xv[u];
+                if (y_f32) ((float*)y)[bh * P + p] = o;
+                else ((bf16_t*)y)[bh * P + p] = (bf16_t)o;
             }
         }
     }
@@ -76,11 +85,10 @@ __global__ __launch_bounds__(kDecThreads) void ssd_decode_kernel(
 
 template <typename T, int TPR>
 hipError_t run(const DecodeArgs& a, hipStream_t stream) {
-    const int64_t rows = a.batch * a.H * a.P;
-    constexpr int per_block = (kDecThreads / TPR) * kRowsPerThread;
-    const int64_t blocks = (rows + per_block - 1) / per_block;
+    const int64_t nbh = a.batch * a.H;
+    const int64_t blocks = (nbh + kDecThreads / 64 - 1) / (kDecThreads / 64);
     hipLaunchKernelGGL((ssd_decode_kernel<T, TPR>), dim3((unsigned)blocks), dim3(kDecThreads), 0, stream,
-                       rows, a.H, a.P, a.N, a.G, a.state, (const T*)a.x, a.dt, a.A, (const T*)a.B,
+                       nbh, a.H, a.P, a.N, a.G, a.state, (const T*)a.x, a.dt, a.A, (const T*)a.B,
                        (const T*)a.C, a.D, a.y, a.y_f32);
     return hipGetLastError();
 }
