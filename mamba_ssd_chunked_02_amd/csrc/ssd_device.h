@@ -133,6 +133,21 @@ __device__ inline ChunkDesc chunk_desc(const Plan& pl, int k) {
     return d;
 }
 
+// The descriptor of a workgroup's chunk is the same for every lane; saying so
+// lets the compiler keep it in scalar registers (buffer descriptors built from
+// it then need no per-lane handling).
+__device__ inline ChunkDesc uniform_desc(ChunkDesc d) {
+    ChunkDesc u;
+    u.seq = __builtin_amdgcn_readfirstlane(d.seq);
+    u.len = __builtin_amdgcn_readfirstlane(d.len);
+    u.idx = __builtin_amdgcn_readfirstlane(d.idx);
+    const uint64_t r = (uint64_t)d.row0;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)r);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(r >> 32));
+    u.row0 = (int64_t)(((uint64_t)hi << 32) | lo);
+    return u;
+}
+
 // Sequence s: first chunk and chunk count.
 __device__ inline int2 seq_chunks(const Plan& pl, int s) {
     if (pl.dense) return make_int2(s * pl.cpseq, pl.cpseq);

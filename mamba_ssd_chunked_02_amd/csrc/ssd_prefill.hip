@@ -305,7 +305,7 @@ __global__ __launch_bounds__(2 * NT) void ssd_chunk_state_kernel(
     typedef typename Tr<T>::v8 v8;
     Item it;
     if (!decode_item(pl, per_xcd, npt, hpw, nslice, it)) return;
-    const ChunkDesc cd = chunk_desc(pl, it.k);
+    const ChunkDesc cd = uniform_desc(chunk_desc(pl, it.k));
     if (cd.seq < 0) return;
     const int P = pl.P, N = pl.N, H = pl.H, G = pl.G, pt = it.pt, k = it.k;
     const int tid = threadIdx.x;
@@ -661,22 +661,34 @@ __device__ __forceinline__ void scan_block(const BlockOps<T, NT, TI>& o, const C
     float xd[16];
 #pragma unroll
     for (int v = 0; v < 16; ++v) xd[v] = (float)xcol[(32 * TI + acc_row(v, lane)) * XRP];
-    f32x16 acc = {};
+    // two independent accumulation chains, so their MFMAs and the Horner
+    // scaling overlap: the state term (hi and lo) and the intra-chunk Horner
+    // scheme, joined with the state term's decay exp(cs) at the scheme's end
+    f32x16 sacc = {};
     if (has_state) {
 #pragma unroll
         for (int s = 0; s < NT / 16; ++s) {
-            mma16(acc, o.ca[s], Tr<T>::ld8(srow + 16 * s));
-            if (SP) mma16(acc, o.ca[s], Tr<T>::ld8(lrow + 16 * s));
+            mma16(sacc, o.ca[s], Tr<T>::ld8(srow + 16 * s));
+            if (SP) mma16(sacc, o.ca[s], Tr<T>::ld8(lrow + 16 * s));
         }
     }
     const bool fast = tb.fast[TI] != 0;
+    f32x16 acc = {};
 #pragma unroll
     for (int kj = 0; kj <= TI; ++kj) {
         if (kj < TI || fast) {
-            acc *= tb.gam[kj];
+            if (kj > 0) acc *= tb.gam[kj];
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) mma16(acc, o.ga[kj][ks], Tr<T>::ld8(xrow + 32 * kj + 16 * ks));
         }
+    }
+    if (has_state) {
+        // decay of the state term up to where the scheme stopped: the end of
+        // block TI (fast) or the end of block TI-1
+        const int e = fast ? 32 * TI + 31 : 32 * TI - 1;
+        const float dec = e >= 0 ? __expf(tb.cs[e]) : 1.f;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[v] += dec * sacc[v];
     }
     const float* scale = fast ? tb.ue : tb.ul;
 #pragma unroll
@@ -832,7 +844,7 @@ __global__ __launch_bounds__(64 * NTI) void ssd_chunk_scan_kernel(
     extern __shared__ __align__(16) char smem[];
     Item it;
     if (!decode_item(pl, per_xcd, npt, hpw, nslice, it)) return;
-    const ChunkDesc cd = chunk_desc(pl, it.k);
+    const ChunkDesc cd = uniform_desc(chunk_desc(pl, it.k));
     if (cd.seq < 0) return;
     const bool has_state = cd.idx > 0 || init != nullptr;
     // wave index as a scalar: each wave takes one branch below
