@@ -555,6 +555,9 @@ struct StateRows {
     f32x4 v[PER];
 };
 
+// The loads only move data (addresses outside the tile are clamped in bounds);
+// the zeroing happens when the rows are written to LDS, so no instruction
+// between the load and its consumer needs the loaded value.
 template <int NT, int NTHR>
 __device__ inline void load_state_rows(StateRows<NT, NTHR>& sr, const float* __restrict__ src, int P, int N,
                                        int pt, int tid) {
@@ -565,13 +568,13 @@ __device__ inline void load_state_rows(StateRows<NT, NTHR>& sr, const float* __r
         const int r = u / S::NQ, n = 4 * (u % S::NQ);
         const int p = 32 * pt + r;
         const bool ok = (S::U % NTHR == 0 || u < S::U) && p < P && n < N;
-        const f32x4 raw = *(const f32x4*)(src + (ok ? (size_t)p * N + n : 0));
-        sr.v[i] = ok ? raw : f32x4{};
+        sr.v[i] = *(const f32x4*)(src + (ok ? (size_t)p * N + n : 0));
     }
 }
 
 template <typename T, int NT, int NTHR>
-__device__ inline void store_state_rows(const StateRows<NT, NTHR>& sr, T* sh, T* sl, int NS, int tid) {
+__device__ inline void store_state_rows(const StateRows<NT, NTHR>& sr, T* sh, T* sl, int NS, int P, int N, int pt,
+                                        int tid) {
     typedef typename Tr<T>::v4 v4;
     typedef StateRows<NT, NTHR> S;
 #pragma unroll
@@ -579,9 +582,11 @@ __device__ inline void store_state_rows(const StateRows<NT, NTHR>& sr, T* sh, T*
         const int u = i * NTHR + tid;
         if (S::U % NTHR != 0 && u >= S::U) break;
         const int r = u / S::NQ, n = 4 * (u % S::NQ);
-        const v4 hi = Tr<T>::narrow4(sr.v[i]);
+        const bool ok = 32 * pt + r < P && n < N;
+        const f32x4 v = ok ? sr.v[i] : f32x4{};
+        const v4 hi = Tr<T>::narrow4(v);
         Tr<T>::st4raw(sh + r * NS + n, hi);
-        if (Split<T>::on) Tr<T>::st4raw(sl + r * NS + n, Tr<T>::narrow4(sr.v[i] - Tr<T>::widen4(hi)));
+        if (Split<T>::on) Tr<T>::st4raw(sl + r * NS + n, Tr<T>::narrow4(v - Tr<T>::widen4(hi)));
     }
 }
 
@@ -596,10 +601,16 @@ __host__ __device__ constexpr size_t chunk_scan_lds_bytes(int NT, int Q) {
            (size_t)(Split<T>::on ? 2 : 1) * 32 * (NT + 8) * sizeof(T) + (size_t)Q * xr_pitch<T>() * sizeof(T);
 }
 
-// Two buffers (stage head i+1 while head i computes) when they fit in LDS.
+// Two staging buffers (stage head i+1 while head i computes) when they fit
+// in LDS next to the per-wave output tiles.
 template <typename T>
 __host__ __device__ constexpr int chunk_scan_buffers(int NT, int Q) {
-    return 2 * chunk_scan_lds_bytes<T>(NT, Q) <= 160 * 1024 ? 2 : 1;
+    return 2 * chunk_scan_lds_bytes<T>(NT, Q) + (Q / 32) * 32 * 36 * 4 <= 160 * 1024 ? 2 : 1;
+}
+
+template <typename T>
+__host__ __device__ constexpr size_t chunk_scan_total_lds(int NT, int Q) {
+    return chunk_scan_buffers<T>(NT, Q) * chunk_scan_lds_bytes<T>(NT, Q) + (size_t)(Q / 32) * 32 * 36 * 4;
 }
 
 // Raw buffer access (gfx9 descriptor: untyped 32-bit data format word).
@@ -609,28 +620,26 @@ __device__ inline __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t 
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kBufferWord3);
 }
 
-template <typename T>
-__device__ inline float buffer_load_elem(__amdgpu_buffer_rsrc_t r, int voff, int soff);
+// Four consecutive outputs through a raw buffer descriptor (byte offset voff).
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+template <typename TY>
+__device__ inline void buffer_store4(f32x4 v, __amdgpu_buffer_rsrc_t r, int voff);
 template <>
-__device__ inline float buffer_load_elem<bf16_t>(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
-    const unsigned short b = __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
-    return __builtin_bit_cast(float, (uint32_t)b << 16);
+__device__ inline void buffer_store4<float>(f32x4 v, __amdgpu_buffer_rsrc_t r, int voff) {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, voff, 0, 0);
 }
 template <>
-__device__ inline float buffer_load_elem<float>(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
+__device__ inline void buffer_store4<bf16_t>(f32x4 v, __amdgpu_buffer_rsrc_t r, int voff) {
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, Tr<bf16_t>::narrow4(v)), r, voff, 0, 0);
 }
 
-template <typename TY>
-__device__ inline void buffer_store_elem(TY v, __amdgpu_buffer_rsrc_t r, int voff, int soff);
-template <>
-__device__ inline void buffer_store_elem<float>(float v, __amdgpu_buffer_rsrc_t r, int voff, int soff) {
-    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, voff, soff, 0);
-}
-template <>
-__device__ inline void buffer_store_elem<bf16_t>(bf16_t v, __amdgpu_buffer_rsrc_t r, int voff, int soff) {
-    __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, v), r, voff, soff, 0);
-}
+// A raw buffer offset past any descriptor's range (accesses there are dropped).
+constexpr int kOutOfRange = 0x7ffffff0;
+
+// Per-wave LDS tile for the output transpose: 32 tokens x 32 columns fp32.
+constexpr int kEpPitch = 36;
+constexpr int kEpBytes = 32 * kEpPitch * 4;
 
 // Per-wave operands of output block TI that do not depend on the head:
 // C.B^T rows of the block (A operand of the intra-chunk term) and C rows (A
@@ -643,24 +652,20 @@ struct BlockOps {
 
 // One head's output block TI for the calling wave.  xrow/srow/lrow point to
 // this lane's row of the LDS tiles, xcol to this lane's column of the raw x
-// tile (pitch XRP); yoff is the lane's byte offset of (row 4*half, head h,
-// column p) from the chunk's first row of y.  No global loads: the block
-// reads LDS and registers only, and its stores are the last memory operations.
+// tile xr (pitch XRP), ep to the wave's output tile.  yoff is the byte offset
+// of (row 32 TI, head h, column 32 pt) from the chunk's first row of y; pcols
+// the tile's columns inside P.  No global loads: the block reads LDS and
+// registers only; its outputs leave through the LDS tile as 16-byte rows.
 template <typename T, typename TY, int NT, int NTI, int TI>
 __device__ __forceinline__ void scan_block(const BlockOps<T, NT, TI>& o, const ChunkTables& tb, const T* xrow,
-                                           const T* srow, const T* lrow, const T* xcol, bool has_state,
-                                           __amdgpu_buffer_rsrc_t ry, int yoff, int HP, int len, bool pvalid,
-                                           float Dh) {
+                                           const T* srow, const T* lrow, const T* xcol, float* ep,
+                                           bool has_state, __amdgpu_buffer_rsrc_t ry, int yoff, int HP, int len,
+                                           int pcols, float Dh) {
     constexpr bool SP = Split<T>::on;
     constexpr int XRP = xr_pitch<T>();
     typedef typename Tr<T>::v8 v8;
     const int lane = threadIdx.x & 63, half = lane >> 5, col = lane & 31;
     const int ta = 32 * TI + col;  // this lane's A row
-    const bool full = 32 * TI + 32 <= len;
-    // x at this lane's 16 output rows (D x term)
-    float xd[16];
-#pragma unroll
-    for (int v = 0; v < 16; ++v) xd[v] = (float)xcol[(32 * TI + acc_row(v, lane)) * XRP];
     // two independent accumulation chains, so their MFMAs and the Horner
     // scaling overlap: the state term (hi and lo) and the intra-chunk Horner
     // scheme, joined with the state term's decay exp(cs) at the scheme's end
@@ -716,22 +721,22 @@ __device__ __forceinline__ void scan_block(const BlockOps<T, NT, TI>& o, const C
             mma16(acc, Tr<T>::narrow(m), xb);
         }
     }
-    // + D x; rows t of this block, column p
-    if (pvalid) {
-        if (full) {
+    // transpose through the wave's LDS tile: lane (column p) writes its 16
+    // rows, then each lane reads 4 consecutive columns of one row; LDS
+    // operations of one wave complete in order, so no barrier is needed
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int r = 32 * TI + 8 * (v >> 2) + (v & 3);
-                buffer_store_elem<TY>((TY)(acc[v] + Dh * xd[v]), ry, yoff, r * HP * (int)sizeof(TY));
-            }
-        } else {
+    for (int v = 0; v < 16; ++v) ep[acc_row(v, lane) * kEpPitch + col] = acc[v];
+    const T* xr0 = xcol - col;  // raw x tile, row 0, column 0
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int r = 32 * TI + 8 * (v >> 2) + (v & 3);
-                if (r + 4 * half < len)
-                    buffer_store_elem<TY>((TY)(acc[v] + Dh * xd[v]), ry, yoff, r * HP * (int)sizeof(TY));
-            }
-        }
+    for (int it = 0; it < 4; ++it) {
+        const int tr = (lane >> 3) + 8 * it, c4 = 4 * (lane & 7);
+        const f32x4 xv = Tr<T>::ld4(xr0 + (32 * TI + tr) * XRP + c4);
+        const f32x4 r = *(const f32x4*)(ep + tr * kEpPitch + c4) + Dh * xv;
+        // every lane stores: an output outside the chunk or past P gets an
+        // offset beyond the descriptor's range, which the hardware drops;
+        // no branch, so the wait counters stay exact for the next loads
+        const bool ok = 32 * TI + tr < len && c4 < pcols;
+        buffer_store4<TY>(r, ry, ok ? yoff + (tr * HP + c4) * (int)sizeof(TY) : kOutOfRange);
     }
 }
 
@@ -780,7 +785,7 @@ __device__ __forceinline__ void scan_wave(const Plan& pl, const Item& it, const 
         const float* dtk = dtc + ((size_t)k * H + h) * Q;
         load_tab<Q>(tin, csk, dtk, tid);
         load_xpair(xp, x, cd, H, P, h, pt, tid, csk, dtk);
-        if (has_state) load_state_rows<NT, NTHR>(sr, states + ((size_t)k * H + h) * P * N, P, N, pt, tid);
+        load_state_rows<NT, NTHR>(sr, states + ((size_t)k * H + h) * P * N, P, N, pt, tid);
     };
     constexpr size_t BUF = chunk_scan_lds_bytes<T>(NT, Q);
     constexpr int XRP = xr_pitch<T>();
@@ -797,34 +802,44 @@ __device__ __forceinline__ void scan_wave(const Plan& pl, const Item& it, const 
     auto stage = [&](int b) {
         store_tab<Q>(carve_tables(smem + b * BUF, Q), tin, tid);
         store_xpair(xp, cd, tile(b, 0), LP, tile(b, 3), XRP);
-        if (has_state) store_state_rows<T, NT, NTHR>(sr, tile(b, 1), tile(b, 2), NS, tid);
+        if (has_state) store_state_rows<T, NT, NTHR>(sr, tile(b, 1), tile(b, 2), NS, P, N, pt, tid);
     };
+    float* ep = (float*)(smem + chunk_scan_buffers<T>(NT, Q) * BUF) + (tid >> 6) * (kEpBytes / 4);
+    const int pcols = P - 32 * pt;
     auto compute = [&](int b, int h) {
-        const int yoff = (4 * half * HP + h * P + p) * (int)sizeof(TY);
+        const int yoff = (32 * TI * HP + h * P + 32 * pt) * (int)sizeof(TY);
         scan_block<T, TY, NT, NTI, TI>(o, carve_tables(smem + b * BUF, Q), tile(b, 0) + col * LP + 8 * half,
                                        tile(b, 1) + col * NS + 8 * half, tile(b, 2) + col * NS + 8 * half,
-                                       tile(b, 3) + col, has_state, ry, yoff, HP, cd.len, p < P, D[h]);
+                                       tile(b, 3) + col, ep, has_state, ry, yoff, HP, cd.len, pcols, D[h]);
     };
     prefetch(it.h0);
     if constexpr (chunk_scan_buffers<T>(NT, Q) == 2) {
         // head i computes from buffer i%2 while head i+1 is staged into the
         // other one: one workgroup barrier per head
+        // the loads of every iteration are issued unconditionally (past the
+        // slice's last head they repeat it), so the compiler's wait counts
+        // never have to cover a path without them
+        const int hl = it.h0 + it.nh - 1;
         stage(0);
         __syncthreads();
-        if (it.nh > 1) prefetch(it.h0 + 1);
+        // the block operands loaded before the loop are complete here; saying
+        // so keeps their loads out of the loop's wait counts
+        __builtin_amdgcn_s_waitcnt(0);
+        prefetch(min(it.h0 + 1, hl));
         for (int i = 0; i < it.nh; ++i) {
             const int h = it.h0 + i;
             compute(i & 1, h);
-            if (i + 1 < it.nh) stage((i + 1) & 1);
-            if (i + 2 < it.nh) prefetch(h + 2);
+            stage((i + 1) & 1);
+            prefetch(min(h + 2, hl));
             __syncthreads();  // buffer i%2 is restaged at i+1; buffer (i+1)%2 is read at i+1
         }
     } else {
+        const int hl = it.h0 + it.nh - 1;
         for (int i = 0; i < it.nh; ++i) {
             const int h = it.h0 + i;
             stage(0);
             __syncthreads();
-            if (i + 1 < it.nh) prefetch(h + 1);
+            prefetch(min(h + 1, hl));
             compute(0, h);
             __syncthreads();  // the next head overwrites the LDS tiles
         }
@@ -924,7 +939,7 @@ hipError_t run_prefill(const Plan& pl, const Layout& lay, const ScanArgs& a, hip
     if ((err = mark(5)) != hipSuccess) return err;
     if (nitems > 0) {
         auto* k4 = ssd_chunk_scan_kernel<T, TY, NT, NTI>;
-        const size_t lds = chunk_scan_buffers<T>(NT, Q) * chunk_scan_lds_bytes<T>(NT, Q);
+        const size_t lds = chunk_scan_total_lds<T>(NT, Q);
         if ((err = allow_lds(k4, lds)) != hipSuccess) return err;
         hipLaunchKernelGGL(k4, dim3(8 * per_xcd), dim3(64 * NTI), lds, stream, pl, per_xcd, npt, a.hpw,
                            nslice, x, cs, dtc, C, cbm, a.D, a.init, states, (TY*)a.y);
@@ -952,11 +967,8 @@ hipError_t dispatch(const Plan& pl, const Layout& lay, const ScanArgs& a, hipStr
 
 size_t prefill_lds_bytes(int dtype, int N, int Q) {
     const int NT = padded_dstate(N);
-    if (dtype == 1)
-        return std::max(chunk_state_lds_bytes<bf16_t>(Q),
-                        chunk_scan_buffers<bf16_t>(NT, Q) * chunk_scan_lds_bytes<bf16_t>(NT, Q));
-    return std::max(chunk_state_lds_bytes<float>(Q),
-                    chunk_scan_buffers<float>(NT, Q) * chunk_scan_lds_bytes<float>(NT, Q));
+    if (dtype == 1) return std::max(chunk_state_lds_bytes<bf16_t>(Q), chunk_scan_total_lds<bf16_t>(NT, Q));
+    return std::max(chunk_state_lds_bytes<float>(Q), chunk_scan_total_lds<float>(NT, Q));
 }
 
 hipError_t launch_prefill(const Plan& plan, const Layout& lay, const ScanArgs& a, hipStream_t stream,
