@@ -204,6 +204,35 @@ __device__ inline int64_t xcd_item(int per_xcd) {
     return (int64_t)(blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
 }
 
+// Raw buffer access (gfx9 descriptor: untyped 32-bit data format word).
+constexpr int kBufferWord3 = 0x00020000;
+
+__device__ inline __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kBufferWord3);
+}
+
+// A raw buffer offset past any descriptor's range (accesses there are dropped).
+constexpr int kOutOfRange = 0x7ffffff0;
+
+// Four consecutive outputs through a raw buffer descriptor (byte offset voff).
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+template <typename TY>
+__device__ inline void buffer_store4(f32x4 v, __amdgpu_buffer_rsrc_t r, int voff);
+template <>
+__device__ inline void buffer_store4<float>(f32x4 v, __amdgpu_buffer_rsrc_t r, int voff) {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, voff, 0, 0);
+}
+template <>
+__device__ inline void buffer_store4<bf16_t>(f32x4 v, __amdgpu_buffer_rsrc_t r, int voff) {
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, Tr<bf16_t>::narrow4(v)), r, voff, 0, 0);
+}
+
+
+// Per-wave LDS tile for the output transpose: 32 tokens x 32 columns fp32.
+constexpr int kEpPitch = 36;
+constexpr int kEpBytes = 32 * kEpPitch * 4;
+
 // Staging of x for one (chunk, head, 32-column tile): a unit is 4 tokens x 8
 // columns, loaded early into registers (XUnit), then scaled by per-token fp32
 // weights and written transposed to LDS:
@@ -289,8 +318,14 @@ __device__ inline bool decode_item(const Plan& pl, int per_xcd, int npt, int hpw
 // kernel wrote, held in registers for the whole slice (one wave per 32-wide
 // n-tile).  The weight w_t = exp(cs_last - cs_t) dt_t <= dt_t never overflows.
 template <typename T>
-__host__ __device__ constexpr size_t chunk_state_lds_bytes(int Q) {
+__host__ __device__ constexpr size_t chunk_state_stage_bytes(int Q) {
     return (size_t)(Split<T>::on ? 2 : 1) * 32 * (Q + 8) * sizeof(T);
+}
+
+// staging tile, then one 32 x 32 fp32 output tile per wave (NT/32 waves)
+template <typename T>
+__host__ __device__ constexpr size_t chunk_state_lds_bytes(int NT, int Q) {
+    return chunk_state_stage_bytes<T>(Q) + (size_t)(NT / 32) * 32 * 36 * 4;
 }
 
 template <typename T, int NT, int NTI>
@@ -313,6 +348,7 @@ __global__ __launch_bounds__(2 * NT) void ssd_chunk_state_kernel(
     const int lane = tid & 63, half = lane >> 5, col = lane & 31;
     T* xh = (T*)smem;
     T* xl = xh + 32 * LP;
+    float* ep = (float*)(smem + chunk_state_stage_bytes<T>(Q)) + nt * (kEpBytes / 4);
     v8 bf[Q / 16];
     const T* brow = bt + ((size_t)k * G + it.g) * NT * Q + (size_t)(32 * nt + col) * Q + 8 * half;
 #pragma unroll
@@ -329,9 +365,13 @@ __global__ __launch_bounds__(2 * NT) void ssd_chunk_state_kernel(
         clast = csk[Q - 1];
     };
     prefetch(it.h0);
+    // the B^T fragments and the first head's inputs are needed at once; past
+    // this point the loop's own loads are the only ones in flight
+    __builtin_amdgcn_s_waitcnt(0);
     const T* arow = xh + col * LP + 8 * half;
     const T* lrow = xl + col * LP + 8 * half;
     const int n = 32 * nt + col;
+    const int hl = it.h0 + it.nh - 1;
     for (int i = 0; i < it.nh; ++i) {
         const int h = it.h0 + i;
 #pragma unroll
@@ -341,21 +381,28 @@ __global__ __launch_bounds__(2 * NT) void ssd_chunk_state_kernel(
                 store_xunit<T, SP>(xu[u], cd, xh, xl, LP);
             }
         __syncthreads();
-        if (i + 1 < it.nh) prefetch(h + 1);
+        // unconditional (the last head repeats itself), so the wait counts
+        // never cover a path without these loads
+        prefetch(min(h + 1, hl));
         f32x16 acc = {};
 #pragma unroll
         for (int s = 0; s < Q / 16; ++s) {
             mma16(acc, Tr<T>::ld8(arow + 16 * s), bf[s]);
             if (SP) mma16(acc, Tr<T>::ld8(lrow + 16 * s), bf[s]);
         }
-        // acc: row p = 32pt + acc_row(v), column n
-        float* out = states + ((size_t)k * H + h) * P * N;
-        if (n < N) {
+        // acc: row p = 32pt + acc_row(v), column n.  Out through the wave's
+        // LDS tile as 16-byte rows; every lane stores, rows past P and
+        // columns past N go beyond the descriptor's range and are dropped
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int p = 32 * pt + acc_row(v, lane);
-                if (p < P) out[(size_t)p * N + n] = acc[v];
-            }
+        for (int v = 0; v < 16; ++v) ep[acc_row(v, lane) * kEpPitch + col] = acc[v];
+        const __amdgpu_buffer_rsrc_t rs =
+            buffer_rsrc(states + ((size_t)k * H + h) * P * N, (uint32_t)(P * N * sizeof(float)));
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+            const int pr = (lane >> 3) + 8 * i4, c4 = 4 * (lane & 7);
+            const f32x4 r = *(const f32x4*)(ep + pr * kEpPitch + c4);
+            const bool ok = 32 * pt + pr < P && 32 * nt + c4 < N;
+            buffer_store4<float>(r, rs, ok ? ((32 * pt + pr) * N + 32 * nt + c4) * 4 : kOutOfRange);
         }
         __syncthreads();  // the next head overwrites the LDS tile
     }
@@ -613,33 +660,7 @@ __host__ __device__ constexpr size_t chunk_scan_total_lds(int NT, int Q) {
     return chunk_scan_buffers<T>(NT, Q) * chunk_scan_lds_bytes<T>(NT, Q) + (size_t)(Q / 32) * 32 * 36 * 4;
 }
 
-// Raw buffer access (gfx9 descriptor: untyped 32-bit data format word).
-constexpr int kBufferWord3 = 0x00020000;
 
-__device__ inline __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kBufferWord3);
-}
-
-// Four consecutive outputs through a raw buffer descriptor (byte offset voff).
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-template <typename TY>
-__device__ inline void buffer_store4(f32x4 v, __amdgpu_buffer_rsrc_t r, int voff);
-template <>
-__device__ inline void buffer_store4<float>(f32x4 v, __amdgpu_buffer_rsrc_t r, int voff) {
-    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, voff, 0, 0);
-}
-template <>
-__device__ inline void buffer_store4<bf16_t>(f32x4 v, __amdgpu_buffer_rsrc_t r, int voff) {
-    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, Tr<bf16_t>::narrow4(v)), r, voff, 0, 0);
-}
-
-// A raw buffer offset past any descriptor's range (accesses there are dropped).
-constexpr int kOutOfRange = 0x7ffffff0;
-
-// Per-wave LDS tile for the output transpose: 32 tokens x 32 columns fp32.
-constexpr int kEpPitch = 36;
-constexpr int kEpBytes = 32 * kEpPitch * 4;
 
 // Per-wave operands of output block TI that do not depend on the head:
 // C.B^T rows of the block (A operand of the intra-chunk term) and C rows (A
@@ -923,7 +944,7 @@ hipError_t run_prefill(const Plan& pl, const Layout& lay, const ScanArgs& a, hip
     if ((err = mark(3)) != hipSuccess) return err;
     if (nitems > 0) {
         auto* k2 = ssd_chunk_state_kernel<T, NT, NTI>;
-        const size_t lds = chunk_state_lds_bytes<T>(Q);
+        const size_t lds = chunk_state_lds_bytes<T>(NT, Q);
         if ((err = allow_lds(k2, lds)) != hipSuccess) return err;
         hipLaunchKernelGGL(k2, dim3(8 * per_xcd), dim3(2 * NT), lds, stream, pl, per_xcd, npt, a.hpw,
                            nslice, x, cs, dtc, bt, states);
@@ -967,8 +988,8 @@ hipError_t dispatch(const Plan& pl, const Layout& lay, const ScanArgs& a, hipStr
 
 size_t prefill_lds_bytes(int dtype, int N, int Q) {
     const int NT = padded_dstate(N);
-    if (dtype == 1) return std::max(chunk_state_lds_bytes<bf16_t>(Q), chunk_scan_total_lds<bf16_t>(NT, Q));
-    return std::max(chunk_state_lds_bytes<float>(Q), chunk_scan_total_lds<float>(NT, Q));
+    if (dtype == 1) return std::max(chunk_state_lds_bytes<bf16_t>(NT, Q), chunk_scan_total_lds<bf16_t>(NT, Q));
+    return std::max(chunk_state_lds_bytes<float>(NT, Q), chunk_scan_total_lds<float>(NT, Q));
 }
 
 hipError_t launch_prefill(const Plan& plan, const Layout& lay, const ScanArgs& a, hipStream_t stream,
