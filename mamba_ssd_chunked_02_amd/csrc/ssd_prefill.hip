@@ -699,14 +699,27 @@ __device__ __forceinline__ void scan_block(const BlockOps<T, NT, TI>& o, const C
         }
     }
     const bool fast = tb.fast[TI] != 0;
-    f32x16 acc = {};
+    // the Horner scheme as two interleaved chains (even and odd blocks), each
+    // stepping two blocks at a time with the product of their decays; the
+    // chain that does not end at the last included block K takes gam[K]
+    f32x16 ce = {}, co = {};
 #pragma unroll
     for (int kj = 0; kj <= TI; ++kj) {
         if (kj < TI || fast) {
-            if (kj > 0) acc *= tb.gam[kj];
+            f32x16& ch = (kj & 1) ? co : ce;
+            if (kj >= 2) ch *= tb.gam[kj - 1] * tb.gam[kj];
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks) mma16(acc, o.ga[kj][ks], Tr<T>::ld8(xrow + 32 * kj + 16 * ks));
+            for (int ks = 0; ks < 2; ++ks) mma16(ch, o.ga[kj][ks], Tr<T>::ld8(xrow + 32 * kj + 16 * ks));
         }
+    }
+    const int K = fast ? TI : TI - 1;  // last block in the scheme
+    f32x16 acc;
+    if (K < 1) {
+        acc = ce;  // at most block 0 (K = -1: no block, ce is zero)
+    } else {
+        const float gk = tb.gam[K];
+        if (K & 1) acc = co + gk * ce;
+        else acc = ce + gk * co;
     }
     if (has_state) {
         // decay of the state term up to where the scheme stopped: the end of
