@@ -270,6 +270,23 @@ def main():
                 "kernel": "ssd_decode_kernel<bf16,32>", "avg_ms": round(decode_ms, 4),
                 "algorithmic_bytes": dbytes}
 
+    # context for the HBM fractions: a plain device copy of the decode state's
+    # size (read + write), the practical streaming rate of this device
+    src = torch.empty_like(state)
+    dst = torch.empty_like(state)
+    for _ in range(3):
+        dst.copy_(src)
+    c0 = torch.cuda.Event(enable_timing=True)
+    c1 = torch.cuda.Event(enable_timing=True)
+    c0.record(stream)
+    for _ in range(10):
+        dst.copy_(src)
+    c1.record(stream)
+    c1.synchronize()
+    copy_ms = c0.elapsed_time(c1) / 10
+    copy_gbs = 2 * state.numel() * 4 / (copy_ms * 1e-3) / 1e9
+    del src, dst
+
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a sample")
@@ -306,6 +323,9 @@ def main():
         "roofline": roof,
         "roofline_kernels": roofs,
         "roofline_decode": roof_dec,
+        "copy_reference": {"bytes": 2 * state.numel() * 4, "ms": round(copy_ms, 4), "gbps": round(copy_gbs, 1),
+                           "frac_of_hbm_peak": round(copy_gbs / HBM_PEAK_GBS, 4),
+                           "what": "torch device-to-device copy of a buffer the size of the decode state"},
         "cpu_baseline": cpu,
         "wall_s_timed_region": round(wall, 3),
     }

@@ -33,16 +33,31 @@ __device__ inline float group_sum(float v) {
     return v;
 }
 
+// Raw buffer descriptor (gfx9 untyped data word) and an offset beyond any
+// descriptor's range: stores there are dropped by the hardware.
+constexpr int kBufferWord3 = 0x00020000;
+constexpr int kOutOfRange = 0x7ffffff0;
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ inline __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kBufferWord3);
+}
+
 // Wave w of block L updates the state block (b, h) = 4L + w: P rows of N
 // floats, contiguous.  Lane l owns columns n = 4 (l % TPR) .. +3 of the rows
 // p = RPI i + l / TPR, so each wave instruction moves 64 x 16 contiguous bytes
-// and B, C, dt, A are loaded once per lane.
+// and B, C, dt, A are loaded once per lane.  Rows go in batches of kBatch
+// instructions; the next batch is loaded before the current one is stored,
+// and every lane issues every store (rows past P, columns past N and the
+// lanes that do not own a y element get an out-of-range offset), so the wait
+// for a batch never includes the previous batch's stores.
 template <typename T, int TPR>
 __global__ __launch_bounds__(kDecThreads) void ssd_decode_kernel(
     int64_t nbh, int H, int P, int N, int G, float* __restrict__ state, const T* __restrict__ x,
     const float* __restrict__ dt, const float* __restrict__ A, const T* __restrict__ B,
     const T* __restrict__ C, const float* __restrict__ D, void* __restrict__ y, int y_f32) {
     constexpr int RPI = 64 / TPR;  // rows per wave instruction
+    constexpr int RPB = RPI * kBatch;  // rows per batch
     const int lane = threadIdx.x & 63;
     const int64_t bh = (int64_t)blockIdx.x * (kDecThreads / 64) + (threadIdx.x >> 6);
     if (bh >= nbh) return;
@@ -57,28 +72,44 @@ __global__ __launch_bounds__(kDecThreads) void ssd_decode_kernel(
     const float Dh = D[h];
     const f32x4 bv = nv ? Tr<T>::ld4(B + (b * G + g) * N + n) : f32x4{};
     const f32x4 cv = nv ? Tr<T>::ld4(C + (b * G + g) * N + n) : f32x4{};
-    float* sb = state + bh * P * N + n;
+    float* sb = state + bh * P * N;
     const T* xb = x + bh * P;
-    for (int p0 = 0; p0 < P; p0 += RPI * kBatch) {
-        f32x4 s[kBatch];
-        float xv[kBatch];
+    const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(sb, (uint32_t)(P * N * sizeof(float)));
+    const __amdgpu_buffer_rsrc_t ry =
+        buffer_rsrc((char*)y + bh * P * (y_f32 ? 4 : 2), (uint32_t)(P * (y_f32 ? 4 : 2)));
+    f32x4 s[kBatch], sn[kBatch];
+    float xv[kBatch], xn[kBatch];
+    auto load = [&](int p0, f32x4 (&dst)[kBatch], float (&xd)[kBatch]) {
 #pragma unroll
         for (int u = 0; u < kBatch; ++u) {
             const int p = min(p0 + u * RPI + rsub, P - 1);
-            s[u] = __builtin_nontemporal_load((const f32x4*)(sb + (int64_t)p * N));
-            xv[u] = (float)xb[p];
+            dst[u] = __builtin_nontemporal_load((const f32x4*)(sb + (int64_t)p * N + n));
+            xd[u] = (float)xb[p];
         }
+    };
+    load(0, s, xv);
+    for (int p0 = 0; p0 < P; p0 += RPB) {
+        load(min(p0 + RPB, P - 1), sn, xn);  // next batch (repeats the last rows at the end)
 #pragma unroll
         for (int u = 0; u < kBatch; ++u) {
             const int p = p0 + u * RPI + rsub;
             const f32x4 ns = a * s[u] + (d * xv[u]) * bv;
-            if (p < P && nv) __builtin_nontemporal_store(ns, (f32x4*)(sb + (int64_t)p * N));
             const float tot = group_sum<TPR>(ns[0] * cv[0] + ns[1] * cv[1] + ns[2] * cv[2] + ns[3] * cv[3]);
-            if (j == TPR - 1 && p < P) {
-                const float o = tot + Dh * xv[u];
-                if (y_f32) ((float*)y)[bh * P + p] = o;
-                else ((bf16_t*)y)[bh * P + p] = (bf16_t)o;
-            }
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, ns), rs,
+                                                   (p < P && nv) ? (p * N + n) * 4 : kOutOfRange, 0, 0);
+            const float o = tot + Dh * xv[u];
+            const bool yo = j == TPR - 1 && p < P;
+            if (y_f32)
+                __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, o), ry, yo ? p * 4 : kOutOfRange,
+                                                      0, 0);
+            else
+                __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, (bf16_t)o), ry,
+                                                      yo ? p * 2 : kOutOfRange, 0, 0);
+        }
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            s[u] = sn[u];
+            xv[u] = xn[u];
         }
     }
 }
