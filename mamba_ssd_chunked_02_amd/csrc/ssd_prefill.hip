@@ -329,7 +329,7 @@ __host__ __device__ constexpr size_t chunk_state_lds_bytes(int NT, int Q) {
 }
 
 template <typename T, int NT, int NTI>
-__global__ __launch_bounds__(2 * NT) void ssd_chunk_state_kernel(
+__global__ __launch_bounds__(2 * NT, (Split<T>::on && NT >= 128) ? 3 : 1) void ssd_chunk_state_kernel(
     Plan pl, int per_xcd, int npt, int hpw, int nslice, const T* __restrict__ x, const float* __restrict__ cs,
     const float* __restrict__ dtc, const T* __restrict__ bt, float* __restrict__ states) {
     extern __shared__ __align__(16) char smem[];
