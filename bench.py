@@ -45,11 +45,14 @@ def prefill_flops(wl, causal=False):
     return nch * (G * 2 * pairs * N + H * (2 * pairs * P + 4 * Q * N * P))
 
 
-def kernel_work(wl, es=2, ys=4):
+def kernel_work(wl, es=2, ys=4, fused=True):
     """Algorithmic FLOPs and HBM bytes of each MFMA kernel launch (dense batch).
 
     chunk_state: 2QNP per (chunk, head); reads x and B^T once, writes one fp32
-    P x N state per (chunk, head).
+    P x N state per (chunk, head).  With `fused` (one walk per (sequence,
+    head, column tile) that also passes the states between chunks) those
+    written states are the entering ones, and it also reads the initial and
+    writes the final state; there is no separate state_passing launch.
     chunk_scan: 2QNP (state term) + 2Q^2P (dense intra-chunk product) per
     (chunk, head); reads x, C, the causal half of C.B^T, the per-chunk decay
     sums and one fp32 entering state per (chunk, head), writes y once."""
@@ -64,6 +67,9 @@ def kernel_work(wl, es=2, ys=4):
           "bytes": (T * H * P * es + T * H * P * ys + T * G * N * es + state
                     + nch * G * nti * (nti + 1) // 2 * 1024 * es + 2 * nch * H * Q * 4)}
     kp = {"flops": 0, "bytes": 2 * state + nch * H * 4 + 2 * b * H * P * N * 4}
+    if fused:
+        ks["bytes"] += 2 * b * H * P * N * 4
+        return {"chunk_state": ks, "chunk_scan": kc}
     return {"chunk_state": ks, "chunk_scan": kc, "state_passing": kp}
 
 
@@ -239,8 +245,12 @@ def main():
     causal_tf = prefill_flops(wl, causal=True) / (prefill_ms * 1e-3) / 1e12
 
     # rooflines of the prefill kernels; the slowest one is the reported one
-    work = kernel_work(wl)
-    names = {"chunk_state": "ssd_chunk_state_kernel<bf16,NT=128,Q=256>",
+    # the library folds state passing into chunk_state when it has enough
+    # (sequence, head, tile) walks; the passing stage then reads 0
+    fused = float(stage_mean[ssd.STAGES.index("state_passing")]) == 0.0
+    work = kernel_work(wl, fused=fused)
+    names = {"chunk_state": ("ssd_chunk_state_passing_kernel<bf16,NT=128,Q=256>" if fused else
+                             "ssd_chunk_state_kernel<bf16,NT=128,Q=256>"),
              "state_passing": "ssd_state_passing_kernel",
              "chunk_scan": "ssd_chunk_scan_kernel<bf16,f32,NT=128,Q=256>"}
     roofs = {}

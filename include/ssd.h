@@ -142,7 +142,9 @@ ssd_status ssd_decode_step(float* state, const void* x, const float* dt, const f
  * then waits for the last event and writes each stage's elapsed time in
  * milliseconds to stage_ms[SSD_PREFILL_STAGES], in the order plan, cumsum,
  * cb, chunk_state, state_passing, chunk_scan (0 for a stage that did not
- * run).  Unlike ssd_chunked_scan it blocks the calling thread until the
+ * run: with enough (sequence, head, 32-column tile) walks, 256 or more, the
+ * state passing runs inside the chunk_state stage and state_passing reads
+ * 0).  Unlike ssd_chunked_scan it blocks the calling thread until the
  * kernels finish.  Same arguments and errors as ssd_chunked_scan, plus
  * SSD_ERR_NULL when stage_ms is NULL.
  */

@@ -36,6 +36,7 @@ constexpr size_t kMaxLds = 160 * 1024;  // LDS per CU on gfx950
 constexpr int64_t kMaxGrid = ((int64_t)1 << 31) - 8;
 constexpr int64_t kTargetWorkgroups = 2048;  // ~8 per CU for chunk_state / chunk_scan
 constexpr int64_t kMaxHeadsPerWorkgroup = 16;
+constexpr int64_t kFusedMinWalks = 256;  // one per CU
 
 struct Prepared {
     ssd::Plan plan;
@@ -53,6 +54,15 @@ int heads_per_workgroup(const ssd::Plan& pl) {
     // equal slices: the fewest slices of at most hpw heads, then spread evenly
     const int64_t nslice = (pl.hpg + hpw - 1) / hpw;
     return (int)((pl.hpg + nslice - 1) / nslice);
+}
+
+// Chunk states and the passing between chunks in one launch when there are
+// enough (sequence, head, column tile) walks to fill the chip: each walk is
+// sequential over its sequence's chunks, so with few of them the separate
+// kernels, parallel over chunks, finish first.
+bool fuse_state_passing(const ssd::Plan& pl) {
+    const int64_t npt = (pl.P + 31) / 32;
+    return (int64_t)pl.nseq * pl.H * npt >= kFusedMinWalks;
 }
 
 ssd_status check_head_dims(const ssd_shape* sh) {
@@ -131,6 +141,7 @@ ssd_status prepare(const ssd_shape* sh, int32_t chunk, Prepared* out) {
     const int64_t npt = (sh->headdim + 31) / 32;
     const int64_t nblk = ((int64_t)sh->headdim * sh->dstate / 4 + 255) / 256;
     if (nchunks * sh->nheads * npt > kMaxGrid || nseq * sh->nheads * nblk > kMaxGrid ||
+        nseq * sh->nheads * npt > kMaxGrid ||
         (sh->nheads + 3) / 4 > 65535 || sh->ngroups > 65535)
         return fail(SSD_ERR_SHAPE, "problem too large for one launch grid");
     // one chunk of x or y is addressed with 32-bit byte offsets
@@ -192,7 +203,8 @@ namespace {
 ssd_status scan_impl(const void* x, const float* dt, const float* A, const void* B, const void* C,
                      const float* D, int32_t chunk, const float* init_state, void* y,
                      float* final_state, const ssd_shape* shape, void* workspace,
-                     size_t workspace_bytes, void* stream, hipEvent_t* marks) {
+                     size_t workspace_bytes, void* stream, hipEvent_t* marks,
+                     int* fused_out = nullptr) {
     Prepared pr;
     ssd_status st = prepare(shape, chunk, &pr);
     if (st != SSD_OK) return st;
@@ -231,6 +243,8 @@ ssd_status scan_impl(const void* x, const float* dt, const float* A, const void*
     a.dtype = shape->dtype;
     a.y_f32 = shape->ydtype == SSD_F32 ? 1 : 0;
     a.hpw = heads_per_workgroup(pr.plan);
+    a.fused = fuse_state_passing(pr.plan) ? 1 : 0;
+    if (fused_out) *fused_out = a.fused;
     pr.plan.seq_tab = (int32_t*)(a.ws + pr.lay.seq_tab);
     pr.plan.chunk_tab = (int32_t*)(a.ws + pr.lay.chunk_tab);
     if (pr.plan.nseq == 0 && !marks) return ok();
@@ -268,11 +282,13 @@ SSD_API ssd_status ssd_chunked_scan_profiled(const void* x, const float* dt, con
         st = fail(SSD_ERR_HIP, "hipEventCreate failed: %s", hipGetErrorString(err));
         --made;
     } else {
+        int fused = 0;
         st = scan_impl(x, dt, A, B, C, D, chunk, init_state, y, final_state, shape, workspace,
-                       workspace_bytes, stream, ev);
+                       workspace_bytes, stream, ev, &fused);
         if (st == SSD_OK) err = hipEventSynchronize(ev[kMarks - 1]);
         for (int i = 0; st == SSD_OK && err == hipSuccess && i < SSD_PREFILL_STAGES; ++i)
             err = hipEventElapsedTime(&stage_ms[i], ev[i], ev[i + 1]);
+        if (st == SSD_OK && err == hipSuccess && fused) stage_ms[4] = 0.f;  // folded into chunk_state
         if (st == SSD_OK && err != hipSuccess)
             st = fail(SSD_ERR_HIP, "event timing failed: %s", hipGetErrorString(err));
     }

@@ -155,4 +155,27 @@ __device__ inline int2 seq_chunks(const Plan& pl, int s) {
     return make_int2(q.x, q.y);
 }
 
+// Sequence s: first chunk, chunk count, first token row and token count.
+struct SeqExtent {
+    int32_t chunk0, nchunks, len;
+    int64_t row0;
+};
+
+__device__ inline SeqExtent seq_extent(const Plan& pl, int s) {
+    SeqExtent e;
+    if (pl.dense) {
+        e.chunk0 = s * pl.cpseq;
+        e.nchunks = pl.cpseq;
+        e.len = (int32_t)pl.L;
+        e.row0 = (int64_t)s * pl.L;
+        return e;
+    }
+    const int4 q = ((const int4*)pl.seq_tab)[s];
+    e.chunk0 = q.x;
+    e.nchunks = q.y;
+    e.row0 = q.z;
+    e.len = q.w;
+    return e;
+}
+
 }  // namespace ssd

@@ -25,7 +25,7 @@ struct Plan {
     int32_t nchunk_ub; // grid bound of chunk-indexed launches (exact when dense)
     int32_t cpseq;     // dense: chunks per sequence
     const int32_t* cu; // packed: device cu_seqlens [nseq+1]
-    int32_t* seq_tab;  // packed: per sequence {chunk0, nchunks, 0, 0}
+    int32_t* seq_tab;  // packed: per sequence {chunk0, nchunks, first row, tokens}
     int32_t* chunk_tab;// packed: per chunk {seq, row0, len, index in sequence}
 };
 
@@ -35,7 +35,7 @@ struct Layout {
     size_t cs;      // f32 [nchunk_ub][H][Q]   inclusive sums of dt A within each chunk
     size_t dtc;     // f32 [nchunk_ub][H][Q]   dt per chunk and head, 0 past the chunk end
     size_t cb;      // elem [nchunk_ub][G][Q][Q] C_t . B_k within each chunk
-    size_t bt;      // elem [nchunk_ub][G][NT][Q] B transposed per chunk, 0 past the end and N
+    size_t bt;      // elem [nchunk_ub][G][NT * Q] B transposed per chunk in MFMA fragment order, 0 past the end and N
     size_t states;  // f32 [nchunk_ub][H][P][N] chunk states, then the states entering each chunk
     size_t total;
 };
@@ -54,6 +54,7 @@ struct ScanArgs {
     int32_t dtype;     // 0 f32, 1 bf16 (x, B, C)
     int32_t y_f32;     // 1: y is fp32, 0: y is bf16
     int32_t hpw;       // heads per workgroup of chunk_state / chunk_scan (within one group)
+    int32_t fused;     // 1: chunk states and state passing in one launch per (sequence, head, tile)
 };
 
 struct DecodeArgs {
@@ -80,7 +81,8 @@ size_t prefill_lds_bytes(int dtype, int N, int Q);
 // Queue the prefill kernels.  Returns hipSuccess or the launch error.
 // When `marks` is non-NULL, an event is recorded before the first stage and
 // after each of the six stages (plan, cumsum, cb, chunk_state, state_passing,
-// chunk_scan), seven events in all.
+// chunk_scan), seven events in all.  With a.fused the chunk_state stage
+// includes the state passing and the state_passing stage is empty.
 hipError_t launch_prefill(const Plan& plan, const Layout& lay, const ScanArgs& a,
                           hipStream_t stream, hipEvent_t* marks = nullptr);
 

@@ -45,10 +45,12 @@ __global__ __launch_bounds__(kThreads) void ssd_plan_kernel(Plan pl) {
     __syncthreads();
     for (int base = 0; base < pl.nseq; base += kThreads) {
         const int s = base + tid;
-        int nc = 0;
+        int nc = 0, len = 0, row0 = 0;
         if (s < pl.nseq) {
             const int a = pl.cu[s], b = pl.cu[s + 1];
-            const int len = (a >= 0 && b >= a && (int64_t)b <= pl.T) ? b - a : 0;
+            const bool valid = a >= 0 && b >= a && (int64_t)b <= pl.T;
+            len = valid ? b - a : 0;
+            row0 = valid ? a : 0;
             nc = (len + pl.Q - 1) / pl.Q;
         }
         s_a[tid] = nc;
@@ -59,7 +61,7 @@ __global__ __launch_bounds__(kThreads) void ssd_plan_kernel(Plan pl) {
             s_a[tid] += va;
             __syncthreads();
         }
-        if (s < pl.nseq) ((int4*)pl.seq_tab)[s] = make_int4(s_carry + s_a[tid] - nc, nc, 0, 0);
+        if (s < pl.nseq) ((int4*)pl.seq_tab)[s] = make_int4(s_carry + s_a[tid] - nc, nc, row0, len);
         __syncthreads();
         if (tid == kThreads - 1) s_carry += s_a[tid];
         __syncthreads();
@@ -132,15 +134,27 @@ __global__ __launch_bounds__(kThreads) void ssd_cumsum_kernel(Plan pl, const flo
 }
 
 // ------------------------------------------------------------------ C.B^T
+// B^T of a chunk is kept in the order the chunk_state MFMAs consume it: for
+// n-tile nt (32 values of n), k-step s (16 tokens) and lane l = 32 half + col
+// the eight tokens 16 s + 8 half + j (j < 8) of row n = 32 nt + col are
+// consecutive, so each wave-wide 16-byte-per-lane load reads one contiguous
+// fragment.  Element (n, t) of chunk k, group g sits at
+//   bt[(k G + g) ntp Q + ((nt (Q/16) + s) 64 + l) 8 + j].
+__host__ __device__ constexpr int bt_frag(int Q, int nt, int s, int lane) {
+    return ((nt * (Q / 16) + s) * 64 + lane) * 8;
+}
+
 // grid (chunks, G, Q/32), one wave: row tile ti of cb = C B^T (stored in the
 // input dtype) for column tiles kj <= ti, the causal part the chunk scan
 // reads, with the diagonal tile's entries above the diagonal set to zero;
-// plus columns [32 ti, 32 ti + 32) of B^T with rows padded with zeros to ntp
-// (a multiple of 32).  Rows/columns past the chunk end are zero.
+// plus tokens [32 ti, 32 ti + 32) of B^T with rows n padded with zeros to
+// ntp (a multiple of 32).  Rows/columns past the chunk end are zero.
 template <typename T>
 __global__ __launch_bounds__(64) void ssd_cb_kernel(Plan pl, int ntp, const T* __restrict__ B,
                                                     const T* __restrict__ C, T* __restrict__ cb,
                                                     T* __restrict__ bt) {
+    // the block's 32 tokens of B (rows) x ntp (columns), pitch ntp + 8
+    __shared__ __align__(16) T bs[32 * (256 + 8)];
     const int k = blockIdx.x, g = blockIdx.y, ti = blockIdx.z;
     const ChunkDesc cd = chunk_desc(pl, k);
     if (cd.seq < 0) return;
@@ -170,15 +184,24 @@ __global__ __launch_bounds__(64) void ssd_cb_kernel(Plan pl, int ntp, const T* _
             out[(size_t)(32 * ti + acc_row(v, lane)) * Q + 32 * kj + col] = (T)val;
         }
     }
-    T* btk = bt + ((size_t)k * G + g) * ntp * Q;
+    const int bp = ntp + 8;
     for (int idx = lane; idx < 32 * (ntp / 8); idx += 64) {
         const int kk = idx & 31, ng = idx >> 5;
         const int kr = 32 * ti + kk;
         const bool ok = kr < cd.len && 8 * ng < N;
         const v8 bv = Tr<T>::ld8(B + ((cd.row0 + (ok ? kr : 0)) * G + g) * N + (ok ? 8 * ng : 0));
-        const v8 b = ok ? bv : v8{};
+        Tr<T>::st8(bs + kk * bp + 8 * ng, ok ? bv : v8{});
+    }
+    __syncthreads();
+    // fragments (nt, s = 2 ti + sl, lane): 64 lanes write 64 consecutive ones
+    T* btk = bt + ((size_t)k * G + g) * ntp * Q;
+    for (int f = 0; f < 2 * (ntp / 32); ++f) {
+        const int nt = f >> 1, sl = f & 1;
+        const int n = 32 * nt + col, t0 = 16 * sl + 8 * half;
+        v8 b;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) btk[(size_t)(8 * ng + i) * Q + kr] = b[i];
+        for (int j = 0; j < 8; ++j) b[j] = bs[(t0 + j) * bp + n];
+        Tr<T>::st8(btk + bt_frag(Q, nt, 2 * ti + sl, lane), b);
     }
 }
 
@@ -228,6 +251,25 @@ __device__ inline void buffer_store4<bf16_t>(f32x4 v, __amdgpu_buffer_rsrc_t r, 
     __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, Tr<bf16_t>::narrow4(v)), r, voff, 0, 0);
 }
 
+// Eight consecutive elements through a raw buffer descriptor (byte offset voff).
+template <typename T>
+__device__ inline typename Tr<T>::v8 buffer_ld8(__amdgpu_buffer_rsrc_t r, int voff);
+template <>
+__device__ inline bf16x8 buffer_ld8<bf16_t>(__amdgpu_buffer_rsrc_t r, int voff) {
+    return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0));
+}
+template <>
+__device__ inline f32x8 buffer_ld8<float>(__amdgpu_buffer_rsrc_t r, int voff) {
+    const f32x4 a = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0));
+    const f32x4 b = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff + 16, 0, 0));
+    return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// The x rows of one chunk as a buffer: uniform base, 32-bit lane offsets.
+template <typename T>
+__device__ inline __amdgpu_buffer_rsrc_t chunk_x_rsrc(const T* x, const ChunkDesc& cd, int H, int P) {
+    return buffer_rsrc(x + (size_t)cd.row0 * H * P, (uint32_t)((size_t)cd.len * H * P * sizeof(T)));
+}
 
 // Per-wave LDS tile for the output transpose: 32 tokens x 32 columns fp32.
 constexpr int kEpPitch = 36;
@@ -250,7 +292,7 @@ struct XUnit {
 // Unit u covers column group pb and token group kb; 16 consecutive units share
 // pb, so a wave's transposed LDS writes fall on distinct banks.
 template <typename T, int Q>
-__device__ inline void load_xunit(XUnit<T>& xu, const T* __restrict__ x, const ChunkDesc& cd, int H, int P,
+__device__ inline void load_xunit(XUnit<T>& xu, __amdgpu_buffer_rsrc_t rx, const ChunkDesc& cd, int H, int P,
                                   int h, int pt, int u, const float* __restrict__ csk,
                                   const float* __restrict__ dtk) {
     constexpr int G16 = Q / 4 < 16 ? Q / 4 : 16;
@@ -262,7 +304,7 @@ __device__ inline void load_xunit(XUnit<T>& xu, const T* __restrict__ x, const C
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
         const int kk = min(xu.k0 + r, cd.len - 1);
-        xu.raw[r] = Tr<T>::ld8(x + ((cd.row0 + kk) * H + h) * P + p0);
+        xu.raw[r] = buffer_ld8<T>(rx, ((kk * H + h) * P + p0) * (int)sizeof(T));
     }
     xu.cs4 = *(const f32x4*)(csk + xu.k0);
     xu.dt4 = *(const f32x4*)(dtk + xu.k0);
@@ -350,18 +392,19 @@ __global__ __launch_bounds__(2 * NT, (Split<T>::on && NT >= 128) ? 3 : 1) void s
     T* xl = xh + 32 * LP;
     float* ep = (float*)(smem + chunk_state_stage_bytes<T>(Q)) + nt * (kEpBytes / 4);
     v8 bf[Q / 16];
-    const T* brow = bt + ((size_t)k * G + it.g) * NT * Q + (size_t)(32 * nt + col) * Q + 8 * half;
+    const T* bfr = bt + ((size_t)k * G + it.g) * NT * Q + bt_frag(Q, nt, 0, lane);
 #pragma unroll
-    for (int s = 0; s < Q / 16; ++s) bf[s] = Tr<T>::ld8(brow + 16 * s);
+    for (int s = 0; s < Q / 16; ++s) bf[s] = Tr<T>::ld8(bfr + 512 * s);
     XUnit<T> xu[UPT];
     float clast = 0.f;
+    const __amdgpu_buffer_rsrc_t rx = chunk_x_rsrc(x, cd, H, P);
     auto prefetch = [&](int h) {
         const float* csk = cs + ((size_t)k * H + h) * Q;
         const float* dtk = dtc + ((size_t)k * H + h) * Q;
 #pragma unroll
         for (int i = 0; i < UPT; ++i)
             if (Q % NTHR == 0 || i * NTHR + tid < Q)
-                load_xunit<T, Q>(xu[i], x, cd, H, P, h, pt, i * NTHR + tid, csk, dtk);
+                load_xunit<T, Q>(xu[i], rx, cd, H, P, h, pt, i * NTHR + tid, csk, dtk);
         clast = csk[Q - 1];
     };
     prefetch(it.h0);
@@ -406,6 +449,146 @@ __global__ __launch_bounds__(2 * NT, (Split<T>::on && NT >= 128) ? 3 : 1) void s
         }
         __syncthreads();  // the next head overwrites the LDS tile
     }
+}
+
+// ------------------------------------------------------------------ chunk_state with state passing
+// Workgroup per (sequence s, head h, tile pt of 32 columns of P); it walks the
+// sequence's chunks in order and keeps the running state in the MFMA
+// accumulators (row p = 32pt + acc_row(v), column n as in chunk_state):
+//   acc <- initial state (or 0)
+//   per chunk k:  slot_k <- acc;   acc <- exp(cs_last,k) acc + S_k
+// with S_k the chunk_state contraction accumulated straight onto the decayed
+// state, and acc written as the final state at the end.  The slots then hold
+// the states entering each chunk, as state_passing leaves them, without the
+// S_k round trip through memory.  The next chunk's x, cs, dt and B^T are
+// loaded while the current one computes.
+template <typename T, int NT, int NTI>
+__global__ __launch_bounds__(2 * NT, (Split<T>::on && NT >= 128) ? 3 : 1) void ssd_chunk_state_passing_kernel(
+    Plan pl, int per_xcd, int npt, const T* __restrict__ x, const float* __restrict__ cs,
+    const float* __restrict__ dtc, const T* __restrict__ bt, float* __restrict__ states,
+    const float* __restrict__ init, float* __restrict__ fin) {
+    extern __shared__ __align__(16) char smem[];
+    constexpr bool SP = Split<T>::on;
+    constexpr int Q = 32 * NTI, LP = Q + 8;
+    constexpr int NTHR = 2 * NT;  // one wave per n-tile
+    constexpr int UPT = (Q + NTHR - 1) / NTHR;
+    typedef typename Tr<T>::v8 v8;
+    const int64_t item = xcd_item(per_xcd);
+    if (item >= (int64_t)pl.nseq * pl.H * npt) return;
+    const int pt = (int)(item % npt);
+    const int h = (int)((item / npt) % pl.H);
+    const int s = (int)(item / npt / pl.H);
+    const int P = pl.P, N = pl.N, H = pl.H, G = pl.G, g = h / pl.hpg;
+    const int tid = threadIdx.x;
+    const int nt = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63, half = lane >> 5, col = lane & 31;
+    T* xh = (T*)smem;
+    T* xl = xh + 32 * LP;
+    float* ep = (float*)(smem + chunk_state_stage_bytes<T>(Q)) + nt * (kEpBytes / 4);
+    const size_t hoff = ((size_t)s * H + h) * P * N;
+    const uint32_t hbytes = (uint32_t)(P * N * sizeof(float));
+    // 16-byte rows of the wave's 32 x 32 tile: row pr, columns c4 .. c4+3
+    const int c4 = 4 * (lane & 7);
+    auto row_off = [&](int i4) {
+        const int pr = (lane >> 3) + 8 * i4;
+        const bool ok = 32 * pt + pr < P && 32 * nt + c4 < N;
+        return ok ? ((32 * pt + pr) * N + 32 * nt + c4) * 4 : kOutOfRange;
+    };
+    auto put_state = [&](const f32x16& acc, float* dst) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) ep[acc_row(v, lane) * kEpPitch + col] = acc[v];
+        const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(dst, hbytes);
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+            const f32x4 r = *(const f32x4*)(ep + ((lane >> 3) + 8 * i4) * kEpPitch + c4);
+            buffer_store4<float>(r, rs, row_off(i4));
+        }
+    };
+    f32x16 acc = {};
+    if (init) {
+        // the initial state into the accumulator layout through the LDS tile
+        const __amdgpu_buffer_rsrc_t ri = buffer_rsrc(init + hoff, hbytes);
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+            const u32x4 r = __builtin_amdgcn_raw_buffer_load_b128(ri, row_off(i4), 0, 0);
+            *(f32x4*)(ep + ((lane >> 3) + 8 * i4) * kEpPitch + c4) = __builtin_bit_cast(f32x4, r);
+        }
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[v] = ep[acc_row(v, lane) * kEpPitch + col];
+    }
+    const SeqExtent se = seq_extent(pl, s);
+    const int nck = __builtin_amdgcn_readfirstlane(se.nchunks);
+    if (nck > 0) {
+        const int k0 = __builtin_amdgcn_readfirstlane(se.chunk0);
+        const int slen = __builtin_amdgcn_readfirstlane(se.len);
+        const int64_t srow = (int64_t)__builtin_amdgcn_readfirstlane((int)se.row0);
+        auto desc = [&](int c) {
+            ChunkDesc d;
+            d.seq = s;
+            d.idx = c;
+            d.row0 = srow + (int64_t)c * Q;
+            d.len = min(Q, slen - c * Q);
+            return d;
+        };
+        // B^T fragments of the chunk: uniform base, one lane offset for every chunk
+        const int boff = bt_frag(Q, nt, 0, lane) * (int)sizeof(T);
+        v8 bf[Q / 16];
+        auto load_b = [&](int k) {
+            const __amdgpu_buffer_rsrc_t rb =
+                buffer_rsrc(bt + ((size_t)k * G + g) * NT * Q, (uint32_t)(NT * Q * sizeof(T)));
+#pragma unroll
+            for (int i = 0; i < Q / 16; ++i) bf[i] = buffer_ld8<T>(rb, boff + 512 * i * (int)sizeof(T));
+        };
+        XUnit<T> xu[UPT];
+        float clast = 0.f;
+        auto prefetch = [&](int c) {
+            const int k = k0 + c;
+            const ChunkDesc d = desc(c);
+            const __amdgpu_buffer_rsrc_t rx = chunk_x_rsrc(x, d, H, P);
+            const float* csk = cs + ((size_t)k * H + h) * Q;
+            const float* dtk = dtc + ((size_t)k * H + h) * Q;
+#pragma unroll
+            for (int i = 0; i < UPT; ++i)
+                if (Q % NTHR == 0 || i * NTHR + tid < Q)
+                    load_xunit<T, Q>(xu[i], rx, d, H, P, h, pt, i * NTHR + tid, csk, dtk);
+            clast = csk[Q - 1];
+        };
+        load_b(k0);
+        prefetch(0);
+        // everything above is needed at once; past this point the loop's own
+        // loads and stores are the only ones in flight
+        __builtin_amdgcn_s_waitcnt(0);
+        const T* arow = xh + col * LP + 8 * half;
+        const T* lrow = xl + col * LP + 8 * half;
+        for (int c = 0; c < nck; ++c) {
+            const int k = k0 + c;
+            const ChunkDesc cd = desc(c);
+            const float ck = clast;
+#pragma unroll
+            for (int u = 0; u < UPT; ++u)
+                if (Q % NTHR == 0 || u * NTHR + tid < Q) {
+                    xu[u].cref = ck;
+                    store_xunit<T, SP>(xu[u], cd, xh, xl, LP);
+                }
+            __syncthreads();
+            // unconditional (the last chunk repeats itself), so the wait
+            // counts never cover a path without these loads
+            const int cn = min(c + 1, nck - 1);
+            prefetch(cn);
+            put_state(acc, states + ((size_t)k * H + h) * P * N);
+            const float dec = __expf(ck);
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[v] *= dec;
+#pragma unroll
+            for (int i = 0; i < Q / 16; ++i) {
+                mma16(acc, Tr<T>::ld8(arow + 16 * i), bf[i]);
+                if (SP) mma16(acc, Tr<T>::ld8(lrow + 16 * i), bf[i]);
+            }
+            load_b(k0 + cn);
+            __syncthreads();  // the next chunk overwrites the staging tile
+        }
+    }
+    if (fin) put_state(acc, fin + hoff);
 }
 
 // ------------------------------------------------------------------ state_passing
@@ -955,20 +1138,35 @@ hipError_t run_prefill(const Plan& pl, const Layout& lay, const ScanArgs& a, hip
         if ((err = hipGetLastError()) != hipSuccess) return err;
     }
     if ((err = mark(3)) != hipSuccess) return err;
-    if (nitems > 0) {
-        auto* k2 = ssd_chunk_state_kernel<T, NT, NTI>;
-        const size_t lds = chunk_state_lds_bytes<T>(NT, Q);
-        if ((err = allow_lds(k2, lds)) != hipSuccess) return err;
-        hipLaunchKernelGGL(k2, dim3(8 * per_xcd), dim3(2 * NT), lds, stream, pl, per_xcd, npt, a.hpw,
-                           nslice, x, cs, dtc, bt, states);
-        if ((err = hipGetLastError()) != hipSuccess) return err;
-    }
-    if ((err = mark(4)) != hipSuccess) return err;
-    if (pl.nseq > 0) {
-        const int nblk = (pl.P * pl.N / 4 + kThreads - 1) / kThreads;
-        hipLaunchKernelGGL(ssd_state_passing_kernel, dim3((unsigned)((int64_t)pl.nseq * pl.H * nblk)),
-                           dim3(kThreads), 0, stream, pl, nblk, cs, states, a.init, a.final_state);
-        if ((err = hipGetLastError()) != hipSuccess) return err;
+    if (a.fused) {
+        // one launch walks every sequence: chunk states and the passing between them
+        const int64_t nfused = (int64_t)pl.nseq * pl.H * npt;
+        const int fper_xcd = (int)((nfused + 7) / 8);
+        if (nfused > 0) {
+            auto* k2 = ssd_chunk_state_passing_kernel<T, NT, NTI>;
+            const size_t lds = chunk_state_lds_bytes<T>(NT, Q);
+            if ((err = allow_lds(k2, lds)) != hipSuccess) return err;
+            hipLaunchKernelGGL(k2, dim3(8 * fper_xcd), dim3(2 * NT), lds, stream, pl, fper_xcd, npt, x, cs,
+                               dtc, bt, states, a.init, a.final_state);
+            if ((err = hipGetLastError()) != hipSuccess) return err;
+        }
+        if ((err = mark(4)) != hipSuccess) return err;
+    } else {
+        if (nitems > 0) {
+            auto* k2 = ssd_chunk_state_kernel<T, NT, NTI>;
+            const size_t lds = chunk_state_lds_bytes<T>(NT, Q);
+            if ((err = allow_lds(k2, lds)) != hipSuccess) return err;
+            hipLaunchKernelGGL(k2, dim3(8 * per_xcd), dim3(2 * NT), lds, stream, pl, per_xcd, npt, a.hpw,
+                               nslice, x, cs, dtc, bt, states);
+            if ((err = hipGetLastError()) != hipSuccess) return err;
+        }
+        if ((err = mark(4)) != hipSuccess) return err;
+        if (pl.nseq > 0) {
+            const int nblk = (pl.P * pl.N / 4 + kThreads - 1) / kThreads;
+            hipLaunchKernelGGL(ssd_state_passing_kernel, dim3((unsigned)((int64_t)pl.nseq * pl.H * nblk)),
+                               dim3(kThreads), 0, stream, pl, nblk, cs, states, a.init, a.final_state);
+            if ((err = hipGetLastError()) != hipSuccess) return err;
+        }
     }
     if ((err = mark(5)) != hipSuccess) return err;
     if (nitems > 0) {

@@ -176,6 +176,64 @@ def test_packed_equals_separate_dense_runs():
         assert_close(fin[s], host(fs)[0], "f32", "seq %d final" % s)
 
 
+# ------------------------------------------------------------------ one walk per (sequence, head, tile)
+# With at least 256 (sequence, head, 32-column tile) walks the chunk states
+# and the passing between chunks run as one kernel that walks each
+# sequence's chunks in order; these shapes take that path.
+FUSED = [
+    # (batch, L, H, P, N, G, chunk, dtype, init)
+    (4, 300, 32, 64, 128, 2, 64, "bf16", 0.1),
+    (8, 130, 32, 32, 64, 4, 32, "f32", 0.1),
+    (2, 513, 128, 40, 40, 8, 128, "bf16", 0.1),
+    (16, 100, 16, 64, 256, 1, 64, "bf16", 0.0),
+    (64, 70, 4, 8, 8, 2, 32, "f32", 0.1),
+    (2, 1000, 64, 64, 128, 1, 256, "bf16", 0.1),
+    (4, 257, 32, 128, 32, 4, 128, "f32", 0.1),
+]
+
+
+@pytest.mark.parametrize("case", FUSED, ids=lambda c: "b%d-L%d-H%d-P%d-N%d-G%d-Q%d-%s" % c[:8])
+def test_fused_state_walk_shapes(case):
+    b, L, H, P, N, G, Q, dt, iv = case
+    wl = W.small_workload(batch=b, seqlen=L, H=H, P=P, N=N, G=G, chunk=Q, dtype=dt, init_var=iv)
+    check_scan(W.generate(wl, 13 + L), what=str(case))
+
+
+def test_fused_state_walk_slow_decay_long_sequences():
+    wl = W.small_workload(batch=4, seqlen=2300, H=32, P=64, N=128, G=1, chunk=128, dtype="bf16",
+                          init_var=0.1)
+    check_scan(W.generate(wl, 23, A_range=(-0.02, -0.001)), what="slow decay")
+
+
+def test_fused_state_walk_packed_with_empty_sequences():
+    lens = (100, 0, 513, 1, 256, 0, 700, 64, 65, 300, 0, 7, 1024, 33, 0, 250)
+    wl = W.small_workload(seqlens=lens, H=8, P=64, N=128, G=2, chunk=256, dtype="bf16", init_var=0.1)
+    check_scan(W.generate(wl, 71), what="packed, %d sequences" % len(lens))
+
+
+def test_fused_walk_equals_separate_runs():
+    """A packed batch of 40 sequences takes the one-kernel walk; each sequence
+    alone (16 walks) takes the chunk-parallel kernels.  Both must agree."""
+    rng = np.random.default_rng(5)
+    lens = tuple(int(v) for v in rng.integers(0, 600, size=40))
+    wl = W.small_workload(seqlens=lens, H=8, P=64, N=64, G=2, chunk=64, dtype="f32", init_var=0.1)
+    inp = W.generate(wl, 81)
+    y, fin = run_gpu(inp)
+    cu = inp.cu_seqlens
+    for s in range(0, len(lens), 7):
+        a, b = cu[s], cu[s + 1]
+        if b == a:
+            assert_close(fin[s], inp.init[s], "f32", "empty seq %d final" % s)
+            continue
+        g = dict(x=tdev(inp.x[None, a:b]), dt=tdev(inp.dt[None, a:b]), B=tdev(inp.B[None, a:b]),
+                 C=tdev(inp.C[None, a:b]))
+        ys, fs = ssd.chunked_scan(g["x"], g["dt"], tdev(inp.A), g["B"], g["C"], tdev(inp.D), 64,
+                                  init_state=tdev(inp.init[s:s + 1]))
+        torch.cuda.synchronize()
+        assert_close(y[a:b], host(ys)[0], "f32", "seq %d y" % s)
+        assert_close(fin[s], host(fs)[0], "f32", "seq %d final" % s)
+
+
 # ------------------------------------------------------------------ cache semantics
 def test_prefill_then_decode_equals_longer_prefill():
     wl = W.small_workload(batch=2, seqlen=600, H=4, P=64, N=128, G=1, chunk=128, dtype="f32",
