@@ -161,6 +161,7 @@ ssd_status prepare(const ssd_shape* sh, int32_t chunk, Prepared* out) {
     L.chunk_tab = take(packed ? (size_t)pl.nchunk_ub * 16 : 0);
     L.cs = take((size_t)pl.nchunk_ub * pl.H * chunk * 4);
     L.dtc = take((size_t)pl.nchunk_ub * pl.H * chunk * 4);
+    L.wst = take((size_t)pl.nchunk_ub * pl.H * chunk * 4);
     L.cb = take((size_t)pl.nchunk_ub * pl.G * chunk * chunk * es);
     L.bt = take((size_t)pl.nchunk_ub * pl.G * ssd::padded_dstate(pl.N) * chunk * es);
     L.states = take((size_t)pl.nchunk_ub * pl.H * pl.P * pl.N * 4);

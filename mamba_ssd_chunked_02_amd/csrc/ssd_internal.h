@@ -34,6 +34,7 @@ struct Layout {
     size_t seq_tab, chunk_tab;  // int32 x4 entries
     size_t cs;      // f32 [nchunk_ub][H][Q]   inclusive sums of dt A within each chunk
     size_t dtc;     // f32 [nchunk_ub][H][Q]   dt per chunk and head, 0 past the chunk end
+    size_t wst;     // f32 [nchunk_ub][H][Q]   exp(cs_last - cs) dt, each token's weight in the chunk state
     size_t cb;      // elem [nchunk_ub][G][Q][Q] C_t . B_k within each chunk
     size_t bt;      // elem [nchunk_ub][G][NT * Q] B transposed per chunk in MFMA fragment order, 0 past the end and N
     size_t states;  // f32 [nchunk_ub][H][P][N] chunk states, then the states entering each chunk

@@ -97,11 +97,14 @@ __global__ __launch_bounds__(kThreads) void ssd_plan_kernel(Plan pl) {
 // ------------------------------------------------------------------ cumsum
 // grid (chunks, ceil(H/4)); wave w of the block handles head 4*blockIdx.y + w.
 // cs[q] = sum_{s<=q} dt_s A_h inside the chunk; positions past the chunk end
-// repeat the last value (dt = 0 there), dtc holds dt with zeros past the end.
+// repeat the last value (dt = 0 there), dtc holds dt with zeros past the end,
+// and wst[q] = exp(cs[Q-1] - cs[q]) dt[q] is each token's weight in the chunk
+// state (<= dt, 0 past the end).
 __global__ __launch_bounds__(kThreads) void ssd_cumsum_kernel(Plan pl, const float* __restrict__ dt,
                                                                const float* __restrict__ A,
                                                                float* __restrict__ cs,
-                                                               float* __restrict__ dtc) {
+                                                               float* __restrict__ dtc,
+                                                               float* __restrict__ wst) {
     const int k = blockIdx.x;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int h = blockIdx.y * 4 + wave;
@@ -122,14 +125,24 @@ __global__ __launch_bounds__(kThreads) void ssd_cumsum_kernel(Plan pl, const flo
     float run = wave_inclusive_scan(own) - own;  // exclusive prefix of lane totals
     float* csr = cs + ((size_t)k * H + h) * Q;
     float* dtr = dtc + ((size_t)k * H + h) * Q;
+    float* wsr = wst + ((size_t)k * H + h) * Q;
+    float c[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int q = lane * ppl + i;
+        run += d[i] * a;
+        c[i] = run;
         if (i < ppl && q < Q) {
-            run += d[i] * a;
             csr[q] = run;
             dtr[q] = d[i];
         }
+    }
+    // cs[Q-1], from the lane that wrote it
+    const float last = __shfl(run, (Q - 1) / ppl);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int q = lane * ppl + i;
+        if (i < ppl && q < Q) wsr[q] = __expf(last - c[i]) * d[i];
     }
 }
 
@@ -277,14 +290,14 @@ constexpr int kEpBytes = 32 * kEpPitch * 4;
 
 // Staging of x for one (chunk, head, 32-column tile): a unit is 4 tokens x 8
 // columns, loaded early into registers (XUnit), then scaled by per-token fp32
-// weights and written transposed to LDS:
+// weights (the cumsum kernel's wst, 0 past the chunk end) and written
+// transposed to LDS:
 //   xh[pl][k] (+ xl[pl][k]) = x[row0+k][h][32pt+pl] * w[k]     (pitch LP)
-// zero past the chunk end and past P; xl (the rounding residue) only when LO.
+// zero past P; xl (the rounding residue) only when LO.
 template <typename T>
 struct XUnit {
     typename Tr<T>::v8 raw[4];
-    f32x4 cs4, dt4;  // cs and dt of the unit's tokens
-    float cref;      // cs the weights are taken relative to
+    f32x4 w4;  // weights of the unit's tokens
     int pb, k0;
     bool pok;
 };
@@ -293,8 +306,7 @@ struct XUnit {
 // pb, so a wave's transposed LDS writes fall on distinct banks.
 template <typename T, int Q>
 __device__ inline void load_xunit(XUnit<T>& xu, __amdgpu_buffer_rsrc_t rx, const ChunkDesc& cd, int H, int P,
-                                  int h, int pt, int u, const float* __restrict__ csk,
-                                  const float* __restrict__ dtk) {
+                                  int h, int pt, int u, const float* __restrict__ wsk) {
     constexpr int G16 = Q / 4 < 16 ? Q / 4 : 16;
     xu.pb = (u / G16) & 3;
     xu.k0 = 4 * (u % G16 + G16 * (u / (4 * G16)));
@@ -306,27 +318,25 @@ __device__ inline void load_xunit(XUnit<T>& xu, __amdgpu_buffer_rsrc_t rx, const
         const int kk = min(xu.k0 + r, cd.len - 1);
         xu.raw[r] = buffer_ld8<T>(rx, ((kk * H + h) * P + p0) * (int)sizeof(T));
     }
-    xu.cs4 = *(const f32x4*)(csk + xu.k0);
-    xu.dt4 = *(const f32x4*)(dtk + xu.k0);
+    xu.w4 = *(const f32x4*)(wsk + xu.k0);
 }
 
-// w[k] = exp(cref - cs[k]) dt[k] (<= dt[k] for cref at or after k)
+// Column i of a 4-token x 8-column unit, weighted, into the transposed tiles.
 template <typename T, bool LO>
-__device__ inline void store_xunit(const XUnit<T>& xu, const ChunkDesc& cd, T* xh, T* xl, int LP) {
+__device__ inline void stage_column(const typename Tr<T>::v8 (&raw)[4], f32x4 w, int i, T* xh, T* xl, int off) {
     typedef typename Tr<T>::v4 v4;
-    f32x8 f[4];
+    const f32x4 o = {(float)raw[0][i] * w[0], (float)raw[1][i] * w[1], (float)raw[2][i] * w[2],
+                     (float)raw[3][i] * w[3]};
+    const v4 hi = Tr<T>::narrow4(o);
+    Tr<T>::st4raw(xh + off, hi);
+    if (LO) Tr<T>::st4raw(xl + off, Tr<T>::narrow4(o - Tr<T>::widen4(hi)));
+}
+
+template <typename T, bool LO>
+__device__ inline void store_xunit(const XUnit<T>& xu, T* xh, T* xl, int LP) {
+    const f32x4 w = xu.pok ? xu.w4 : f32x4{};
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const float w = __expf(xu.cref - xu.cs4[r]) * xu.dt4[r];
-        f[r] = Tr<T>::widen(xu.raw[r]) * ((xu.pok && xu.k0 + r < cd.len) ? w : 0.f);
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const f32x4 o = {f[0][i], f[1][i], f[2][i], f[3][i]};
-        const v4 hi = Tr<T>::narrow4(o);
-        Tr<T>::st4raw(xh + (8 * xu.pb + i) * LP + xu.k0, hi);
-        if (LO) Tr<T>::st4raw(xl + (8 * xu.pb + i) * LP + xu.k0, Tr<T>::narrow4(o - Tr<T>::widen4(hi)));
-    }
+    for (int i = 0; i < 8; ++i) stage_column<T, LO>(xu.raw, w, i, xh, xl, (8 * xu.pb + i) * LP + xu.k0);
 }
 
 // Work item of the MFMA kernels: (chunk k, group g, slice of hpw heads of the
@@ -372,8 +382,8 @@ __host__ __device__ constexpr size_t chunk_state_lds_bytes(int NT, int Q) {
 
 template <typename T, int NT, int NTI>
 __global__ __launch_bounds__(2 * NT, (Split<T>::on && NT >= 128) ? 3 : 1) void ssd_chunk_state_kernel(
-    Plan pl, int per_xcd, int npt, int hpw, int nslice, const T* __restrict__ x, const float* __restrict__ cs,
-    const float* __restrict__ dtc, const T* __restrict__ bt, float* __restrict__ states) {
+    Plan pl, int per_xcd, int npt, int hpw, int nslice, const T* __restrict__ x, const float* __restrict__ wst,
+    const T* __restrict__ bt, float* __restrict__ states) {
     extern __shared__ __align__(16) char smem[];
     constexpr bool SP = Split<T>::on;
     constexpr int Q = 32 * NTI, LP = Q + 8;
@@ -396,16 +406,13 @@ __global__ __launch_bounds__(2 * NT, (Split<T>::on && NT >= 128) ? 3 : 1) void s
 #pragma unroll
     for (int s = 0; s < Q / 16; ++s) bf[s] = Tr<T>::ld8(bfr + 512 * s);
     XUnit<T> xu[UPT];
-    float clast = 0.f;
     const __amdgpu_buffer_rsrc_t rx = chunk_x_rsrc(x, cd, H, P);
     auto prefetch = [&](int h) {
-        const float* csk = cs + ((size_t)k * H + h) * Q;
-        const float* dtk = dtc + ((size_t)k * H + h) * Q;
+        const float* wsk = wst + ((size_t)k * H + h) * Q;
 #pragma unroll
         for (int i = 0; i < UPT; ++i)
             if (Q % NTHR == 0 || i * NTHR + tid < Q)
-                load_xunit<T, Q>(xu[i], rx, cd, H, P, h, pt, i * NTHR + tid, csk, dtk);
-        clast = csk[Q - 1];
+                load_xunit<T, Q>(xu[i], rx, cd, H, P, h, pt, i * NTHR + tid, wsk);
     };
     prefetch(it.h0);
     // the B^T fragments and the first head's inputs are needed at once; past
@@ -419,10 +426,7 @@ __global__ __launch_bounds__(2 * NT, (Split<T>::on && NT >= 128) ? 3 : 1) void s
         const int h = it.h0 + i;
 #pragma unroll
         for (int u = 0; u < UPT; ++u)
-            if (Q % NTHR == 0 || u * NTHR + tid < Q) {
-                xu[u].cref = clast;
-                store_xunit<T, SP>(xu[u], cd, xh, xl, LP);
-            }
+            if (Q % NTHR == 0 || u * NTHR + tid < Q) store_xunit<T, SP>(xu[u], xh, xl, LP);
         __syncthreads();
         // unconditional (the last head repeats itself), so the wait counts
         // never cover a path without these loads
@@ -460,12 +464,13 @@ __global__ __launch_bounds__(2 * NT, (Split<T>::on && NT >= 128) ? 3 : 1) void s
 // with S_k the chunk_state contraction accumulated straight onto the decayed
 // state, and acc written as the final state at the end.  The slots then hold
 // the states entering each chunk, as state_passing leaves them, without the
-// S_k round trip through memory.  The next chunk's x, cs, dt and B^T are
-// loaded while the current one computes.
+// S_k round trip through memory.  Each wave holds its n-tile's B^T fragments
+// of the chunk in registers; the next chunk's x, weights and B^T are loaded
+// while the current one computes.
 template <typename T, int NT, int NTI>
 __global__ __launch_bounds__(2 * NT, (Split<T>::on && NT >= 128) ? 3 : 1) void ssd_chunk_state_passing_kernel(
     Plan pl, int per_xcd, int npt, const T* __restrict__ x, const float* __restrict__ cs,
-    const float* __restrict__ dtc, const T* __restrict__ bt, float* __restrict__ states,
+    const float* __restrict__ wst, const T* __restrict__ bt, float* __restrict__ states,
     const float* __restrict__ init, float* __restrict__ fin) {
     extern __shared__ __align__(16) char smem[];
     constexpr bool SP = Split<T>::on;
@@ -545,13 +550,12 @@ __global__ __launch_bounds__(2 * NT, (Split<T>::on && NT >= 128) ? 3 : 1) void s
             const int k = k0 + c;
             const ChunkDesc d = desc(c);
             const __amdgpu_buffer_rsrc_t rx = chunk_x_rsrc(x, d, H, P);
-            const float* csk = cs + ((size_t)k * H + h) * Q;
-            const float* dtk = dtc + ((size_t)k * H + h) * Q;
+            const float* wsk = wst + ((size_t)k * H + h) * Q;
 #pragma unroll
             for (int i = 0; i < UPT; ++i)
                 if (Q % NTHR == 0 || i * NTHR + tid < Q)
-                    load_xunit<T, Q>(xu[i], rx, d, H, P, h, pt, i * NTHR + tid, csk, dtk);
-            clast = csk[Q - 1];
+                    load_xunit<T, Q>(xu[i], rx, d, H, P, h, pt, i * NTHR + tid, wsk);
+            clast = cs[((size_t)k * H + h) * Q + Q - 1];
         };
         load_b(k0);
         prefetch(0);
@@ -562,21 +566,16 @@ __global__ __launch_bounds__(2 * NT, (Split<T>::on && NT >= 128) ? 3 : 1) void s
         const T* lrow = xl + col * LP + 8 * half;
         for (int c = 0; c < nck; ++c) {
             const int k = k0 + c;
-            const ChunkDesc cd = desc(c);
-            const float ck = clast;
+            const float dec = __expf(clast);
 #pragma unroll
             for (int u = 0; u < UPT; ++u)
-                if (Q % NTHR == 0 || u * NTHR + tid < Q) {
-                    xu[u].cref = ck;
-                    store_xunit<T, SP>(xu[u], cd, xh, xl, LP);
-                }
+                if (Q % NTHR == 0 || u * NTHR + tid < Q) store_xunit<T, SP>(xu[u], xh, xl, LP);
             __syncthreads();
             // unconditional (the last chunk repeats itself), so the wait
             // counts never cover a path without these loads
             const int cn = min(c + 1, nck - 1);
             prefetch(cn);
             put_state(acc, states + ((size_t)k * H + h) * P * N);
-            const float dec = __expf(ck);
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[v] *= dec;
 #pragma unroll
@@ -1111,6 +1110,7 @@ hipError_t run_prefill(const Plan& pl, const Layout& lay, const ScanArgs& a, hip
     const T* C = (const T*)a.C;
     float* cs = (float*)(ws + lay.cs);
     float* dtc = (float*)(ws + lay.dtc);
+    float* wst = (float*)(ws + lay.wst);
     T* cbm = (T*)(ws + lay.cb);
     T* bt = (T*)(ws + lay.bt);
     float* states = (float*)(ws + lay.states);
@@ -1128,7 +1128,7 @@ hipError_t run_prefill(const Plan& pl, const Layout& lay, const ScanArgs& a, hip
     if ((err = mark(1)) != hipSuccess) return err;
     if (pl.nchunk_ub > 0) {
         hipLaunchKernelGGL(ssd_cumsum_kernel, dim3(pl.nchunk_ub, (pl.H + 3) / 4), dim3(kThreads), 0,
-                           stream, pl, a.dt, a.A, cs, dtc);
+                           stream, pl, a.dt, a.A, cs, dtc, wst);
         if ((err = hipGetLastError()) != hipSuccess) return err;
     }
     if ((err = mark(2)) != hipSuccess) return err;
@@ -1147,7 +1147,7 @@ hipError_t run_prefill(const Plan& pl, const Layout& lay, const ScanArgs& a, hip
             const size_t lds = chunk_state_lds_bytes<T>(NT, Q);
             if ((err = allow_lds(k2, lds)) != hipSuccess) return err;
             hipLaunchKernelGGL(k2, dim3(8 * fper_xcd), dim3(2 * NT), lds, stream, pl, fper_xcd, npt, x, cs,
-                               dtc, bt, states, a.init, a.final_state);
+                               wst, bt, states, a.init, a.final_state);
             if ((err = hipGetLastError()) != hipSuccess) return err;
         }
         if ((err = mark(4)) != hipSuccess) return err;
@@ -1157,7 +1157,7 @@ hipError_t run_prefill(const Plan& pl, const Layout& lay, const ScanArgs& a, hip
             const size_t lds = chunk_state_lds_bytes<T>(NT, Q);
             if ((err = allow_lds(k2, lds)) != hipSuccess) return err;
             hipLaunchKernelGGL(k2, dim3(8 * per_xcd), dim3(2 * NT), lds, stream, pl, per_xcd, npt, a.hpw,
-                               nslice, x, cs, dtc, bt, states);
+                               nslice, x, wst, bt, states);
             if ((err = hipGetLastError()) != hipSuccess) return err;
         }
         if ((err = mark(4)) != hipSuccess) return err;
