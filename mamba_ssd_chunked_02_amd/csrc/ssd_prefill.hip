@@ -964,6 +964,12 @@ __host__ __device__ constexpr int scan_block_of_wave(int NTI, int w) {
     return NTI == 8 ? (w < 4 ? w : 11 - w) : w;
 }
 
+// With 8 blocks, the four waves of blocks 0-3 (the least causal work) stage
+// every head's LDS inputs on their own, so the waves of blocks 4-7, which set
+// the pace, only compute; with fewer blocks every wave stages a share.
+__host__ __device__ constexpr bool scan_stager(int NTI, int TI) { return NTI != 8 || TI < 4; }
+__host__ __device__ constexpr int scan_stage_threads(int NTI) { return NTI == 8 ? 256 : 64 * NTI; }
+
 template <typename T, typename TY, int NT, int NTI, int TI>
 __device__ __forceinline__ void scan_wave(const Plan& pl, const Item& it, const ChunkDesc& cd, char* smem,
                                           const T* __restrict__ x, const float* __restrict__ cs,
@@ -971,7 +977,9 @@ __device__ __forceinline__ void scan_wave(const Plan& pl, const Item& it, const 
                                           const T* __restrict__ cb, const float* __restrict__ D,
                                           const float* __restrict__ states, bool has_state, TY* __restrict__ y) {
     constexpr int Q = 32 * NTI, LP = Q + 8, NS = NT + 8;
-    constexpr int NTHR = 64 * NTI;
+    constexpr bool STAGER = scan_stager(NTI, TI);
+    constexpr int NTHR = scan_stage_threads(NTI);  // threads that stage
+    constexpr int XPT = 64 * NTI / NTHR;           // x units per staging thread
     const int P = pl.P, N = pl.N, H = pl.H, G = pl.G, k = it.k, pt = it.pt;
     const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5, col = lane & 31;
     // the group's operands of this wave's block, once for the whole slice
@@ -992,15 +1000,16 @@ __device__ __forceinline__ void scan_wave(const Plan& pl, const Item& it, const 
     const int HP = H * P;
     const int p = 32 * pt + col;
     const __amdgpu_buffer_rsrc_t ry = buffer_rsrc(y + cd.row0 * HP, (uint32_t)(cd.len * HP * sizeof(TY)));
-    // per-head inputs, loaded one head ahead
+    // per-head inputs, loaded one head ahead by the staging waves
     TabIn tin;
-    XPair<T> xp;
+    XPair<T> xp[XPT];
     StateRows<NT, NTHR> sr;
     auto prefetch = [&](int h) {
         const float* csk = cs + ((size_t)k * H + h) * Q;
         const float* dtk = dtc + ((size_t)k * H + h) * Q;
         load_tab<Q>(tin, csk, dtk, tid);
-        load_xpair(xp, x, cd, H, P, h, pt, tid, csk, dtk);
+#pragma unroll
+        for (int r = 0; r < XPT; ++r) load_xpair(xp[r], x, cd, H, P, h, pt, tid + r * NTHR, csk, dtk);
         load_state_rows<NT, NTHR>(sr, states + ((size_t)k * H + h) * P * N, P, N, pt, tid);
     };
     constexpr size_t BUF = chunk_scan_lds_bytes<T>(NT, Q);
@@ -1017,7 +1026,8 @@ __device__ __forceinline__ void scan_wave(const Plan& pl, const Item& it, const 
     };
     auto stage = [&](int b) {
         store_tab<Q>(carve_tables(smem + b * BUF, Q), tin, tid);
-        store_xpair(xp, cd, tile(b, 0), LP, tile(b, 3), XRP);
+#pragma unroll
+        for (int r = 0; r < XPT; ++r) store_xpair(xp[r], cd, tile(b, 0), LP, tile(b, 3), XRP);
         if (has_state) store_state_rows<T, NT, NTHR>(sr, tile(b, 1), tile(b, 2), NS, P, N, pt, tid);
     };
     float* ep = (float*)(smem + chunk_scan_buffers<T>(NT, Q) * BUF) + (tid >> 6) * (kEpBytes / 4);
@@ -1028,7 +1038,7 @@ __device__ __forceinline__ void scan_wave(const Plan& pl, const Item& it, const 
                                        tile(b, 1) + col * NS + 8 * half, tile(b, 2) + col * NS + 8 * half,
                                        tile(b, 3) + col, ep, has_state, ry, yoff, HP, cd.len, pcols, D[h]);
     };
-    prefetch(it.h0);
+    if (STAGER) prefetch(it.h0);
     if constexpr (chunk_scan_buffers<T>(NT, Q) == 2) {
         // head i computes from buffer i%2 while head i+1 is staged into the
         // other one: one workgroup barrier per head
@@ -1036,26 +1046,28 @@ __device__ __forceinline__ void scan_wave(const Plan& pl, const Item& it, const 
         // slice's last head they repeat it), so the compiler's wait counts
         // never have to cover a path without them
         const int hl = it.h0 + it.nh - 1;
-        stage(0);
+        if (STAGER) stage(0);
         __syncthreads();
         // the block operands loaded before the loop are complete here; saying
         // so keeps their loads out of the loop's wait counts
         __builtin_amdgcn_s_waitcnt(0);
-        prefetch(min(it.h0 + 1, hl));
+        if (STAGER) prefetch(min(it.h0 + 1, hl));
         for (int i = 0; i < it.nh; ++i) {
             const int h = it.h0 + i;
             compute(i & 1, h);
-            stage((i + 1) & 1);
-            prefetch(min(h + 2, hl));
+            if (STAGER) {
+                stage((i + 1) & 1);
+                prefetch(min(h + 2, hl));
+            }
             __syncthreads();  // buffer i%2 is restaged at i+1; buffer (i+1)%2 is read at i+1
         }
     } else {
         const int hl = it.h0 + it.nh - 1;
         for (int i = 0; i < it.nh; ++i) {
             const int h = it.h0 + i;
-            stage(0);
+            if (STAGER) stage(0);
             __syncthreads();
-            prefetch(min(h + 1, hl));
+            if (STAGER) prefetch(min(h + 1, hl));
             compute(0, h);
             __syncthreads();  // the next head overwrites the LDS tiles
         }
