@@ -95,56 +95,77 @@ __global__ __launch_bounds__(kThreads) void ssd_plan_kernel(Plan pl) {
 }
 
 // ------------------------------------------------------------------ cumsum
-// grid (chunks, ceil(H/4)); wave w of the block handles head 4*blockIdx.y + w.
-// cs[q] = sum_{s<=q} dt_s A_h inside the chunk; positions past the chunk end
-// repeat the last value (dt = 0 there), dtc holds dt with zeros past the end,
-// and wst[q] = exp(cs[Q-1] - cs[q]) dt[q] is each token's weight in the chunk
-// state (<= dt, 0 past the end).
+// grid (chunks, ceil(H/16)): the workgroup reads the chunk's dt for 16 heads
+// as contiguous 64-byte row pieces into LDS, then wave w scans heads
+// w, w+4, w+8, w+12 of the block.  Per (chunk, head):
+//   cs[q]  = sum_{s<=q} dt_s A_h inside the chunk; positions past the chunk
+//            end repeat the last value (dt = 0 there)
+//   dtc[q] = dt with zeros past the end
+//   wst[q] = exp(cs[Q-1] - cs[q]) dt[q], each token's weight in the chunk
+//            state (<= dt, 0 past the end)
+constexpr int kCumHeads = 16;
+
 __global__ __launch_bounds__(kThreads) void ssd_cumsum_kernel(Plan pl, const float* __restrict__ dt,
                                                                const float* __restrict__ A,
                                                                float* __restrict__ cs,
                                                                float* __restrict__ dtc,
                                                                float* __restrict__ wst) {
+    constexpr int SP = 256 + 4;  // LDS row pitch (floats): one row per head
+    __shared__ __align__(16) float sdt[kCumHeads * SP];
     const int k = blockIdx.x;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int h = blockIdx.y * 4 + wave;
-    const ChunkDesc cd = chunk_desc(pl, k);
-    if (cd.seq < 0 || h >= pl.H) return;
-    const int Q = pl.Q, H = pl.H;
-    const float a = A[h];
-    const int ppl = Q >= 64 ? Q / 64 : 1;  // consecutive positions per lane
-    float d[4];
-    float own = 0.f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        d[i] = 0.f;
-        const int q = lane * ppl + i;
-        if (i < ppl && q < cd.len) d[i] = dt[(cd.row0 + q) * H + h];
-        own += d[i] * a;
-    }
-    float run = wave_inclusive_scan(own) - own;  // exclusive prefix of lane totals
-    float* csr = cs + ((size_t)k * H + h) * Q;
-    float* dtr = dtc + ((size_t)k * H + h) * Q;
-    float* wsr = wst + ((size_t)k * H + h) * Q;
-    float c[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int q = lane * ppl + i;
-        run += d[i] * a;
-        c[i] = run;
-        if (i < ppl && q < Q) {
-            csr[q] = run;
-            dtr[q] = d[i];
+    const ChunkDesc cd = uniform_desc(chunk_desc(pl, k));
+    if (cd.seq < 0) return;
+    const int Q = pl.Q, H = pl.H, h0 = blockIdx.y * kCumHeads;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    // thread (token q = tid/16 + 16i, head h0 + tid%16)
+    {
+        const int hh = tid % kCumHeads;
+        const bool hok = h0 + hh < H;
+        for (int q = tid / kCumHeads; q < Q; q += kThreads / kCumHeads) {
+            const bool ok = hok && q < cd.len;
+            sdt[hh * SP + q] = ok ? dt[(cd.row0 + q) * H + h0 + hh] : 0.f;
         }
     }
-    // cs[Q-1], from the lane that wrote it
-    const float last = __shfl(run, (Q - 1) / ppl);
+    __syncthreads();
+    const int ppl = Q >= 64 ? Q / 64 : 1;  // consecutive positions per lane
+    for (int hh = wave; hh < kCumHeads; hh += kThreads / 64) {
+        const int h = h0 + hh;
+        if (h >= H) break;
+        const float a = A[h];
+        float d[4];
+        float own = 0.f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int q = lane * ppl + i;
-        if (i < ppl && q < Q) wsr[q] = __expf(last - c[i]) * d[i];
+        for (int i = 0; i < 4; ++i) {
+            const int q = lane * ppl + i;
+            d[i] = (i < ppl && q < Q) ? sdt[hh * SP + q] : 0.f;
+            own += d[i] * a;
+        }
+        float run = wave_inclusive_scan(own) - own;  // exclusive prefix of lane totals
+        float c[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            run += d[i] * a;
+            c[i] = run;
+        }
+        // cs[Q-1], from the lane that holds it
+        const float last = __shfl(run, (Q - 1) / ppl);
+        float* csr = cs + ((size_t)k * H + h) * Q;
+        float* dtr = dtc + ((size_t)k * H + h) * Q;
+        float* wsr = wst + ((size_t)k * H + h) * Q;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int q = lane * ppl + i;
+            if (i < ppl && q < Q) {
+                csr[q] = c[i];
+                dtr[q] = d[i];
+                wsr[q] = __expf(last - c[i]) * d[i];
+            }
+        }
     }
 }
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // ------------------------------------------------------------------ C.B^T
 // B^T of a chunk is kept in the order the chunk_state MFMAs consume it: for
@@ -157,64 +178,83 @@ __host__ __device__ constexpr int bt_frag(int Q, int nt, int s, int lane) {
     return ((nt * (Q / 16) + s) * 64 + lane) * 8;
 }
 
-// grid (chunks, G, Q/32), one wave: row tile ti of cb = C B^T (stored in the
-// input dtype) for column tiles kj <= ti, the causal part the chunk scan
-// reads, with the diagonal tile's entries above the diagonal set to zero;
-// plus tokens [32 ti, 32 ti + 32) of B^T with rows n padded with zeros to
-// ntp (a multiple of 32).  Rows/columns past the chunk end are zero.
+// grid (chunks, G, NTI (NTI + 1) / 2), one wave per causal 32 x 32 tile
+// (ti, kj <= ti) of cb = C B^T, stored in the input dtype, the part the chunk
+// scan reads; the diagonal tile's entries above the diagonal are zero, rows
+// and columns past the chunk end are zero.  The diagonal tile's wave also
+// writes tokens [32 ti, 32 ti + 32) of B^T in fragment order, rows n padded
+// with zeros to NT.  Outputs leave through LDS as 16-byte rows.
 template <typename T>
-__global__ __launch_bounds__(64) void ssd_cb_kernel(Plan pl, int ntp, const T* __restrict__ B,
-                                                    const T* __restrict__ C, T* __restrict__ cb,
-                                                    T* __restrict__ bt) {
-    // the block's 32 tokens of B (rows) x ntp (columns), pitch ntp + 8
-    __shared__ __align__(16) T bs[32 * (256 + 8)];
-    const int k = blockIdx.x, g = blockIdx.y, ti = blockIdx.z;
-    const ChunkDesc cd = chunk_desc(pl, k);
+__host__ __device__ constexpr size_t cb_lds_bytes(int NT) {
+    return (size_t)32 * (NT + 16 / sizeof(T)) * sizeof(T);
+}
+
+template <typename T, int NT>
+__global__ __launch_bounds__(64) void ssd_cb_kernel(Plan pl, const T* __restrict__ B, const T* __restrict__ C,
+                                                    T* __restrict__ cb, T* __restrict__ bt) {
+    extern __shared__ __align__(16) char smem[];
+    T* ls = (T*)smem;
+    constexpr int EPC = 16 / sizeof(T);  // elements per 16 bytes
+    const int k = blockIdx.x, g = blockIdx.y;
+    int kj = blockIdx.z, ti = 0;
+    while (kj > ti) {  // blockIdx.z = ti (ti + 1) / 2 + kj
+        kj -= ti + 1;
+        ++ti;
+    }
+    const ChunkDesc cd = uniform_desc(chunk_desc(pl, k));
     if (cd.seq < 0) return;
     const int Q = pl.Q, N = pl.N, G = pl.G;
     const int lane = threadIdx.x, half = lane >> 5, col = lane & 31;
     typedef typename Tr<T>::v8 v8;
-    const int t = 32 * ti + col;
-    const bool tv = t < cd.len;
+    const int t = 32 * ti + col, kk = 32 * kj + col;
+    const bool tv = t < cd.len, kv = kk < cd.len;
     const T* crow = C + ((cd.row0 + (tv ? t : 0)) * G + g) * N;
-    T* out = cb + ((size_t)k * G + g) * Q * Q;
-    for (int kj = 0; kj <= ti; ++kj) {
-        f32x16 acc = {};
-        const int kk = 32 * kj + col;
-        const bool kv = kk < cd.len;
-        const T* brow = B + ((cd.row0 + (kv ? kk : 0)) * G + g) * N;
-        for (int n0 = 0; n0 < N; n0 += 16) {
-            const int n = n0 + 8 * half;
-            const bool nv = n < N;
-            const v8 a0 = Tr<T>::ld8(crow + (nv ? n : 0));
-            const v8 b0 = Tr<T>::ld8(brow + (nv ? n : 0));
-            mma16(acc, (tv && nv) ? a0 : v8{}, (kv && nv) ? b0 : v8{});
-        }
-        // the diagonal tile keeps only its causal part (column <= row)
+    const T* brow = B + ((cd.row0 + (kv ? kk : 0)) * G + g) * N;
+    v8 a[NT / 16], b[NT / 16];
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            const float val = (kj < ti || col <= acc_row(v, lane)) ? acc[v] : 0.f;
-            out[(size_t)(32 * ti + acc_row(v, lane)) * Q + 32 * kj + col] = (T)val;
-        }
+    for (int s = 0; s < NT / 16; ++s) {
+        const int n = 16 * s + 8 * half;
+        a[s] = Tr<T>::ld8(crow + (n < N ? n : 0));
+        b[s] = Tr<T>::ld8(brow + (n < N ? n : 0));
     }
-    const int bp = ntp + 8;
-    for (int idx = lane; idx < 32 * (ntp / 8); idx += 64) {
-        const int kk = idx & 31, ng = idx >> 5;
-        const int kr = 32 * ti + kk;
-        const bool ok = kr < cd.len && 8 * ng < N;
-        const v8 bv = Tr<T>::ld8(B + ((cd.row0 + (ok ? kr : 0)) * G + g) * N + (ok ? 8 * ng : 0));
-        Tr<T>::st8(bs + kk * bp + 8 * ng, ok ? bv : v8{});
+#pragma unroll
+    for (int s = 0; s < NT / 16; ++s) {
+        const bool nv = 16 * s + 8 * half < N;
+        if (!(tv && nv)) a[s] = v8{};
+        if (!(kv && nv)) b[s] = v8{};
     }
-    __syncthreads();
-    // fragments (nt, s = 2 ti + sl, lane): 64 lanes write 64 consecutive ones
-    T* btk = bt + ((size_t)k * G + g) * ntp * Q;
-    for (int f = 0; f < 2 * (ntp / 32); ++f) {
+    f32x16 acc = {};
+#pragma unroll
+    for (int s = 0; s < NT / 16; ++s) mma16(acc, a[s], b[s]);
+    // the tile through LDS (pitch 32 + EPC), then 16-byte rows; LDS
+    // operations of one wave complete in order
+    constexpr int TP = 32 + EPC;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+        const int r = acc_row(v, lane);
+        ls[r * TP + col] = (T)((kj < ti || col <= r) ? acc[v] : 0.f);
+    }
+    T* out = cb + ((size_t)k * G + g) * Q * Q + (size_t)(32 * ti) * Q + 32 * kj;
+#pragma unroll
+    for (int i = 0; i < 32 * 32 / EPC / 64; ++i) {
+        const int c = i * 64 + lane, r = c / (32 / EPC), c0 = (c % (32 / EPC)) * EPC;
+        *(u32x4*)(out + (size_t)r * Q + c0) = *(const u32x4*)(ls + r * TP + c0);
+    }
+    if (kj != ti) return;
+    // B^T fragments of this block's tokens: this wave's B operand rows, into
+    // LDS as [token][n] (pitch NT + EPC), read back transposed
+    constexpr int BP = NT + EPC;
+#pragma unroll
+    for (int s = 0; s < NT / 16; ++s) Tr<T>::st8(ls + col * BP + 16 * s + 8 * half, b[s]);
+    T* btk = bt + ((size_t)k * G + g) * NT * Q;
+#pragma unroll
+    for (int f = 0; f < 2 * (NT / 32); ++f) {
         const int nt = f >> 1, sl = f & 1;
         const int n = 32 * nt + col, t0 = 16 * sl + 8 * half;
-        v8 b;
+        v8 bv;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) b[j] = bs[(t0 + j) * bp + n];
-        Tr<T>::st8(btk + bt_frag(Q, nt, 2 * ti + sl, lane), b);
+        for (int j = 0; j < 8; ++j) bv[j] = ls[(t0 + j) * BP + n];
+        Tr<T>::st8(btk + bt_frag(Q, nt, 2 * ti + sl, lane), bv);
     }
 }
 
@@ -251,8 +291,6 @@ __device__ inline __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t 
 constexpr int kOutOfRange = 0x7ffffff0;
 
 // Four consecutive outputs through a raw buffer descriptor (byte offset voff).
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 template <typename TY>
 __device__ inline void buffer_store4(f32x4 v, __amdgpu_buffer_rsrc_t r, int voff);
 template <>
@@ -420,7 +458,6 @@ __global__ __launch_bounds__(2 * NT, (Split<T>::on && NT >= 128) ? 3 : 1) void s
     __builtin_amdgcn_s_waitcnt(0);
     const T* arow = xh + col * LP + 8 * half;
     const T* lrow = xl + col * LP + 8 * half;
-    const int n = 32 * nt + col;
     const int hl = it.h0 + it.nh - 1;
     for (int i = 0; i < it.nh; ++i) {
         const int h = it.h0 + i;
@@ -1139,14 +1176,15 @@ hipError_t run_prefill(const Plan& pl, const Layout& lay, const ScanArgs& a, hip
     }
     if ((err = mark(1)) != hipSuccess) return err;
     if (pl.nchunk_ub > 0) {
-        hipLaunchKernelGGL(ssd_cumsum_kernel, dim3(pl.nchunk_ub, (pl.H + 3) / 4), dim3(kThreads), 0,
+        hipLaunchKernelGGL(ssd_cumsum_kernel, dim3(pl.nchunk_ub, (pl.H + kCumHeads - 1) / kCumHeads), dim3(kThreads), 0,
                            stream, pl, a.dt, a.A, cs, dtc, wst);
         if ((err = hipGetLastError()) != hipSuccess) return err;
     }
     if ((err = mark(2)) != hipSuccess) return err;
     if (pl.nchunk_ub > 0) {
-        hipLaunchKernelGGL(ssd_cb_kernel<T>, dim3(pl.nchunk_ub, pl.G, NTI), dim3(64), 0, stream, pl, NT, B,
-                           C, cbm, bt);
+        auto* k1 = ssd_cb_kernel<T, NT>;
+        hipLaunchKernelGGL(k1, dim3(pl.nchunk_ub, pl.G, NTI * (NTI + 1) / 2), dim3(64), cb_lds_bytes<T>(NT),
+                           stream, pl, B, C, cbm, bt);
         if ((err = hipGetLastError()) != hipSuccess) return err;
     }
     if ((err = mark(3)) != hipSuccess) return err;
