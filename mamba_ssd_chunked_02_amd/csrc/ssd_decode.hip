@@ -37,6 +37,7 @@ __device__ inline float group_sum(float v) {
 // descriptor's range: stores there are dropped by the hardware.
 constexpr int kBufferWord3 = 0x00020000;
 constexpr int kOutOfRange = 0x7ffffff0;
+constexpr int kNonTemporal = 2;  // cache-policy bit of gfx9.4+ buffer instructions: streaming store
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ inline __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
@@ -96,15 +97,15 @@ __global__ __launch_bounds__(kDecThreads) void ssd_decode_kernel(
             const f32x4 ns = a * s[u] + (d * xv[u]) * bv;
             const float tot = group_sum<TPR>(ns[0] * cv[0] + ns[1] * cv[1] + ns[2] * cv[2] + ns[3] * cv[3]);
             __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, ns), rs,
-                                                   (p < P && nv) ? (p * N + n) * 4 : kOutOfRange, 0, 0);
+                                                   (p < P && nv) ? (p * N + n) * 4 : kOutOfRange, 0, kNonTemporal);
             const float o = tot + Dh * xv[u];
             const bool yo = j == TPR - 1 && p < P;
             if (y_f32)
                 __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, o), ry, yo ? p * 4 : kOutOfRange,
-                                                      0, 0);
+                                                      0, kNonTemporal);
             else
                 __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, (bf16_t)o), ry,
-                                                      yo ? p * 2 : kOutOfRange, 0, 0);
+                                                      yo ? p * 2 : kOutOfRange, 0, kNonTemporal);
         }
 #pragma unroll
         for (int u = 0; u < kBatch; ++u) {

@@ -291,15 +291,20 @@ __device__ inline __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t 
 constexpr int kOutOfRange = 0x7ffffff0;
 
 // Four consecutive outputs through a raw buffer descriptor (byte offset voff).
+// These stores carry the non-temporal hint: y and the per-chunk states are
+// written once and not read again by the same kernel, so they should not
+// displace its inputs from the caches.
+constexpr int kNonTemporal = 2;  // cache-policy bit of gfx9.4+ buffer instructions
 template <typename TY>
 __device__ inline void buffer_store4(f32x4 v, __amdgpu_buffer_rsrc_t r, int voff);
 template <>
 __device__ inline void buffer_store4<float>(f32x4 v, __amdgpu_buffer_rsrc_t r, int voff) {
-    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, voff, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, voff, 0, kNonTemporal);
 }
 template <>
 __device__ inline void buffer_store4<bf16_t>(f32x4 v, __amdgpu_buffer_rsrc_t r, int voff) {
-    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, Tr<bf16_t>::narrow4(v)), r, voff, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, Tr<bf16_t>::narrow4(v)), r, voff, 0,
+                                          kNonTemporal);
 }
 
 // Eight consecutive elements through a raw buffer descriptor (byte offset voff).
