@@ -235,6 +235,19 @@ def main():
     wall = time.perf_counter() - t_wall0
     log("timed region %.3f s" % wall)
 
+    # the decode kernel in steady state: back-to-back steps on the same state,
+    # as a serving loop runs them (in the step above it follows a prefill)
+    for _ in range(20):
+        decode()
+    c0 = torch.cuda.Event(enable_timing=True)
+    c1 = torch.cuda.Event(enable_timing=True)
+    c0.record(stream)
+    for _ in range(100):
+        decode()
+    c1.record(stream)
+    c1.synchronize()
+    decode_steady_ms = c0.elapsed_time(c1) / 100
+
     stages = np.array(stages)              # [steps, 6] ms
     stage_mean = stages.mean(axis=0)
     prefill_ms = float(stages.sum(axis=1).mean())
@@ -326,7 +339,10 @@ def main():
         "tflops_causal": round(causal_tf, 2),
         "stage_ms": {k: round(float(v), 4) for k, v in zip(ssd.STAGES, stage_mean)},
         "decode": {"ms_per_step": round(decode_ms, 4), "gbps": round(dgbs, 1),
-                   "frac_of_hbm_peak": round(dgbs / HBM_PEAK_GBS, 4), "bytes_per_step": dbytes},
+                   "frac_of_hbm_peak": round(dgbs / HBM_PEAK_GBS, 4), "bytes_per_step": dbytes,
+                   "steady_ms_per_step": round(decode_steady_ms, 4),
+                   "steady_gbps": round(dbytes / (decode_steady_ms * 1e-3) / 1e9, 1),
+                   "steady": "100 back-to-back steps after the timed region"},
         "step_ms_prefill_plus_decode": round(prefill_ms + decode_ms, 4),
         "tflops_contraction_kernels": round(contraction_tf, 2),
         "frac_bf16_peak_contraction_kernels": round(contraction_tf / BF16_PEAK_TFLOPS, 4),
