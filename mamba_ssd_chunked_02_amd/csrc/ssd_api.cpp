@@ -34,8 +34,12 @@ size_t up256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 constexpr size_t kMaxLds = 160 * 1024;  // LDS per CU on gfx950
 constexpr int64_t kMaxGrid = ((int64_t)1 << 31) - 8;
-constexpr int64_t kTargetWorkgroups = 2048;  // ~8 per CU for chunk_state / chunk_scan
-constexpr int64_t kMaxHeadsPerWorkgroup = 16;
+// chunk-parallel chunk_state: ~8 workgroups per CU (three fit at once), at most 16 heads each
+constexpr int64_t kStateWorkgroups = 2048;
+constexpr int64_t kStateMaxHeads = 16;
+// chunk_scan: one 8-wave workgroup fits per CU; two per CU, each walking as
+// many heads as that allows, amortize the per-workgroup block operands best
+constexpr int64_t kScanWorkgroups = 512;
 constexpr int64_t kFusedMinWalks = 256;  // one per CU
 
 struct Prepared {
@@ -45,12 +49,13 @@ struct Prepared {
 
 // Heads of one group that a chunk_state / chunk_scan workgroup walks: the
 // group's per-chunk operands are loaded once per workgroup, so more heads per
-// workgroup means less L2 traffic, as long as ~2048 workgroups remain.
-int heads_per_workgroup(const ssd::Plan& pl) {
+// workgroup means less L2 traffic and prologue, as long as about `target`
+// workgroups remain.
+int heads_per_workgroup(const ssd::Plan& pl, int64_t target, int64_t max_heads) {
     const int64_t npt = (pl.P + 31) / 32;
     const int64_t units = (int64_t)pl.nchunk_ub * pl.H * npt;
-    int64_t hpw = units / kTargetWorkgroups;
-    hpw = std::max<int64_t>(1, std::min<int64_t>(hpw, std::min<int64_t>(kMaxHeadsPerWorkgroup, pl.hpg)));
+    int64_t hpw = units / target;
+    hpw = std::max<int64_t>(1, std::min<int64_t>(hpw, std::min<int64_t>(max_heads, pl.hpg)));
     // equal slices: the fewest slices of at most hpw heads, then spread evenly
     const int64_t nslice = (pl.hpg + hpw - 1) / hpw;
     return (int)((pl.hpg + nslice - 1) / nslice);
@@ -243,7 +248,8 @@ ssd_status scan_impl(const void* x, const float* dt, const float* A, const void*
     a.ws = (char*)workspace;
     a.dtype = shape->dtype;
     a.y_f32 = shape->ydtype == SSD_F32 ? 1 : 0;
-    a.hpw = heads_per_workgroup(pr.plan);
+    a.hpw = heads_per_workgroup(pr.plan, kScanWorkgroups, pr.plan.hpg);
+    a.hpw_state = heads_per_workgroup(pr.plan, kStateWorkgroups, kStateMaxHeads);
     a.fused = fuse_state_passing(pr.plan) ? 1 : 0;
     if (fused_out) *fused_out = a.fused;
     pr.plan.seq_tab = (int32_t*)(a.ws + pr.lay.seq_tab);

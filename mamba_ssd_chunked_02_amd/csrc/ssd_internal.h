@@ -54,7 +54,8 @@ struct ScanArgs {
     char* ws;
     int32_t dtype;     // 0 f32, 1 bf16 (x, B, C)
     int32_t y_f32;     // 1: y is fp32, 0: y is bf16
-    int32_t hpw;       // heads per workgroup of chunk_state / chunk_scan (within one group)
+    int32_t hpw;       // heads per workgroup of chunk_scan (within one group)
+    int32_t hpw_state; // heads per workgroup of the chunk-parallel chunk_state
     int32_t fused;     // 1: chunk states and state passing in one launch per (sequence, head, tile)
 };
 

@@ -1171,6 +1171,7 @@ hipError_t run_prefill(const Plan& pl, const Layout& lay, const ScanArgs& a, hip
     hipError_t err;
     auto mark = [&](int i) -> hipError_t { return marks ? hipEventRecord(marks[i], stream) : hipSuccess; };
     const int npt = (pl.P + 31) / 32;
+    // chunk_scan items: (chunk, group, slice of a.hpw heads, column tile)
     const int nslice = (pl.hpg + a.hpw - 1) / a.hpw;
     const int64_t nitems = (int64_t)pl.nchunk_ub * pl.G * nslice * npt;
     const int per_xcd = (int)((nitems + 7) / 8);
@@ -1207,12 +1208,16 @@ hipError_t run_prefill(const Plan& pl, const Layout& lay, const ScanArgs& a, hip
         }
         if ((err = mark(4)) != hipSuccess) return err;
     } else {
-        if (nitems > 0) {
+        // chunk_state items: the same, with slices of a.hpw_state heads
+        const int nslice_s = (pl.hpg + a.hpw_state - 1) / a.hpw_state;
+        const int64_t nitems_s = (int64_t)pl.nchunk_ub * pl.G * nslice_s * npt;
+        const int per_xcd_s = (int)((nitems_s + 7) / 8);
+        if (nitems_s > 0) {
             auto* k2 = ssd_chunk_state_kernel<T, NT, NTI>;
             const size_t lds = chunk_state_lds_bytes<T>(NT, Q);
             if ((err = allow_lds(k2, lds)) != hipSuccess) return err;
-            hipLaunchKernelGGL(k2, dim3(8 * per_xcd), dim3(2 * NT), lds, stream, pl, per_xcd, npt, a.hpw,
-                               nslice, x, wst, bt, states);
+            hipLaunchKernelGGL(k2, dim3(8 * per_xcd_s), dim3(2 * NT), lds, stream, pl, per_xcd_s, npt,
+                               a.hpw_state, nslice_s, x, wst, bt, states);
             if ((err = hipGetLastError()) != hipSuccess) return err;
         }
         if ((err = mark(4)) != hipSuccess) return err;
