@@ -13,15 +13,23 @@
 //
 // Kernels (queued in this order on one stream):
 //   plan           packed batches only: chunk and sequence tables
-//   cumsum         cs and dt per (chunk, head), wave64 DPP prefix scan
-//   cb             C.B^T per (chunk, group) on MFMA, and B^T per chunk
-//   chunk_state    S_c per (chunk, head, 32-column tile of P), MFMA
+//   cumsum         cs, dt and the chunk-state weights per (chunk, head),
+//                  wave64 DPP prefix scan
+//   cb             C.B^T per (chunk, group) on MFMA, and B^T per chunk in
+//                  MFMA fragment order
+// then either (enough (sequence, head, tile) walks to fill the chip)
+//   chunk_state_passing  per (sequence, head, 32-column tile of P): walks the
+//                  sequence's chunks, accumulating each S_c by MFMA onto the
+//                  decayed running state; writes every h_c and the final state
+// or
+//   chunk_state    S_c per (chunk, head slice, 32-column tile of P), MFMA
 //   state_passing  sequential over the chunks of a sequence, parallel over
 //                  (head, P, N); replaces S_c by h_c, writes final states
-//   chunk_scan     y per (chunk, head, 32-column tile of P), MFMA
+// and
+//   chunk_scan     y per (chunk, head slice, 32-column tile of P), MFMA
 // chunk_state and chunk_scan have no dependence between chunks, so every
-// (chunk, head, tile) is an independent workgroup.  The contractions run on
-// 32x32 MFMA tiles (bf16 inputs: 32x32x16 bf16; fp32 inputs: 32x32x2 f32),
+// (chunk, head slice, tile) is an independent workgroup.  The contractions run
+// on 32x32 MFMA tiles (bf16 inputs: 32x32x16 bf16; fp32 inputs: 32x32x2 f32),
 // fp32 accumulation everywhere.
 #include <algorithm>
 
@@ -684,7 +692,7 @@ __global__ __launch_bounds__(kThreads) void ssd_state_passing_kernel(Plan pl, in
 //           + sum_{s<=t} (C_t . B_s) exp(cs_t - cs_s) dt_s x[s][p]   (causal intra-chunk term)
 //           + D x[t][p]
 // for the chunk's tokens t and the tile's columns p, with h_k the state
-// entering the chunk (written by state_passing).
+// entering the chunk (written by the state walk or by state_passing).
 //
 // Decay bookkeeping.  The chunk is cut into 32-token blocks j with start
 // s_j = 32j - 1 and end e_j = 32j + 31 (cs_{-1} := 0).  The workgroup shares
