@@ -238,6 +238,32 @@ def main():
     wall = time.perf_counter() - t_wall0
     log("timed region %.3f s" % wall)
 
+    # the same prefill with the dt activation fused (the raw input is the
+    # inverse softplus of the workload's dt, so the kernels see the same dt)
+    raw = up(np.log(np.expm1(inp.dt.astype(np.float64))).astype(np.float32))
+
+    def back_to_back(act):
+        def one():
+            if act:
+                ssd.chunked_scan(x, raw, A, Bm, Cm, D, wl.chunk, init_state=init, y=y, final_state=fin,
+                                 workspace=ws, dt_softplus=True)
+            else:
+                prefill()
+        for _ in range(3):
+            one()
+        a0 = torch.cuda.Event(enable_timing=True)
+        a1 = torch.cuda.Event(enable_timing=True)
+        a0.record(stream)
+        for _ in range(args.steps):
+            one()
+        a1.record(stream)
+        a1.synchronize()
+        return a0.elapsed_time(a1) / args.steps
+
+    plain_b2b_ms = back_to_back(False)
+    act_ms = back_to_back(True)
+    del raw
+
     # per-kernel durations: the same prefill through the measuring entry point
     # (HIP events before and after every stage on the same stream)
     stages = []
@@ -358,6 +384,11 @@ def main():
                    "steady_gbps": round(dbytes / (decode_steady_ms * 1e-3) / 1e9, 1),
                    "steady": "100 back-to-back steps after the timed region"},
         "step_ms_prefill_plus_decode": round(prefill_ms + decode_ms, 4),
+        "prefill_dt_activation": {"ms_per_step": round(act_ms, 4), "tokens_per_s": round(tokens / (act_ms * 1e-3), 1),
+                                  "plain_ms_per_step": round(plain_b2b_ms, 4),
+                                  "what": "same prefill through ssd_chunked_scan_dt_act (softplus fused into "
+                                          "the cumsum kernel) and through ssd_chunked_scan, back-to-back "
+                                          "calls each"},
         "tflops_contraction_kernels": round(contraction_tf, 2),
         "frac_bf16_peak_contraction_kernels": round(contraction_tf / BF16_PEAK_TFLOPS, 4),
         "roofline": roof,

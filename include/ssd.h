@@ -52,7 +52,8 @@ typedef enum ssd_status {
     SSD_ERR_WORKSPACE = -6,   /* workspace NULL or smaller than the query says */
     SSD_ERR_HIP = -7,         /* the HIP runtime reported an error at launch */
     SSD_ERR_UNSUPPORTED = -8, /* valid but outside what the kernels implement */
-    SSD_ERR_SEQLENS = -9      /* host copy of cu_seqlens is not a valid offset list */
+    SSD_ERR_SEQLENS = -9,     /* host copy of cu_seqlens is not a valid offset list */
+    SSD_ERR_VALUE = -10       /* a scalar argument is out of its range */
 } ssd_status;
 
 typedef enum ssd_dtype { SSD_F32 = 0, SSD_BF16 = 1 } ssd_dtype;
@@ -135,6 +136,41 @@ ssd_status ssd_chunked_scan(const void* x, const float* dt, const float* A, cons
 ssd_status ssd_decode_step(float* state, const void* x, const float* dt, const float* A,
                            const void* B, const void* C, const float* D, void* y,
                            const ssd_shape* shape, void* stream);
+
+/*
+ * Fused dt activation.  The step size comes from a softplus of the projected
+ * input plus a per-head bias ("Engineering hybrid state-space models",
+ * section 3, architecture figure of the Mamba-2 block).  The *_dt_act entry
+ * points take that raw dt and use, for every (token, head),
+ *
+ *     dt = min(max(softplus(dt_raw[., h] + dt_bias[h]), dt_min), dt_max)
+ *     softplus(v) = log(1 + exp(v)), taken as v itself for v > 20,
+ *
+ * evaluated in fp32 where dt enters the kernels (the cumsum stage of the
+ * prefill, the decode step).  Everything else is exactly ssd_chunked_scan /
+ * ssd_decode_step; the `dt` argument holds dt_raw.
+ *
+ *   dt_bias  [H] fp32 device pointer, 16-byte aligned, or NULL for no bias
+ *   dt_min   lower clamp: finite and >= 0
+ *   dt_max   upper clamp: >= dt_min (INFINITY: no upper clamp)
+ * Errors as the plain entry points, plus SSD_ERR_NULL for a NULL `act` and
+ * SSD_ERR_VALUE for a clamp range outside the above (NaN included).
+ */
+typedef struct ssd_dt_activation {
+    const float* dt_bias;
+    float dt_min;
+    float dt_max;
+} ssd_dt_activation;
+
+ssd_status ssd_chunked_scan_dt_act(const void* x, const float* dt_raw, const float* A, const void* B,
+                                   const void* C, const float* D, int32_t chunk,
+                                   const float* init_state, void* y, float* final_state,
+                                   const ssd_dt_activation* act, const ssd_shape* shape,
+                                   void* workspace, size_t workspace_bytes, void* stream);
+
+ssd_status ssd_decode_step_dt_act(float* state, const void* x, const float* dt_raw, const float* A,
+                                  const void* B, const void* C, const float* D, void* y,
+                                  const ssd_dt_activation* act, const ssd_shape* shape, void* stream);
 
 /*
  * Measurement helper, for benchmarks only: does what ssd_chunked_scan does,

@@ -47,6 +47,10 @@ class _Shape(ctypes.Structure):
                 ("cu_seqlens_host", ctypes.c_void_p)]
 
 
+class _DtAct(ctypes.Structure):
+    _fields_ = [("dt_bias", ctypes.c_void_p), ("dt_min", ctypes.c_float), ("dt_max", ctypes.c_float)]
+
+
 def library_path() -> str:
     return os.path.join(_PKG, _LIB_NAME)
 
@@ -73,6 +77,12 @@ def load():
         lib.ssd_chunked_scan_profiled.restype = ctypes.c_int32
         lib.ssd_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, sp, vp]
         lib.ssd_decode_step.restype = ctypes.c_int32
+        ap = ctypes.POINTER(_DtAct)
+        lib.ssd_chunked_scan_dt_act.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_int32, vp, vp, vp, ap, sp,
+                                                vp, ctypes.c_size_t, vp]
+        lib.ssd_chunked_scan_dt_act.restype = ctypes.c_int32
+        lib.ssd_decode_step_dt_act.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, ap, sp, vp]
+        lib.ssd_decode_step_dt_act.restype = ctypes.c_int32
         lib.ssd_status_string.argtypes = [ctypes.c_int32]
         lib.ssd_status_string.restype = ctypes.c_char_p
         lib.ssd_last_error_detail.argtypes = []
@@ -181,11 +191,33 @@ def workspace_size(x, B, chunk: int, cu_seqlens=None) -> int:
 STAGES = ("plan", "cumsum", "cb", "chunk_state", "state_passing", "chunk_scan")
 
 
+def _dt_act(dt_softplus, dt_bias, dt_limit, H):
+    """ssd_dt_activation for the *_dt_act entry points, or None."""
+    if not dt_softplus:
+        if dt_bias is not None or dt_limit is not None:
+            raise ValueError("dt_bias / dt_limit need dt_softplus=True")
+        return None
+    torch = _torch()
+    if dt_bias is not None:
+        _need_cuda(dt_bias)
+        _expect(dt_bias, (H,), torch.float32, "dt_bias")
+    lo, hi = (0.0, float("inf")) if dt_limit is None else dt_limit
+    act = _DtAct()
+    act.dt_bias = _ptr(dt_bias)
+    act.dt_min, act.dt_max = float(lo), float(hi)
+    return act
+
+
 def chunked_scan(x, dt, A, B, C, D, chunk: int = 256, init_state=None, cu_seqlens=None, *,
                  y=None, final_state=None, want_final: bool = True, workspace=None,
                  cu_seqlens_host: Optional[Sequence[int]] = None,
-                 stage_ms: Optional[list] = None, y_dtype=None):
+                 stage_ms: Optional[list] = None, y_dtype=None,
+                 dt_softplus: bool = False, dt_bias=None, dt_limit=None):
     """Chunked prefill.  Returns (y, final_state or None).
+
+    ``dt_softplus``: ``dt`` holds raw step sizes and the kernels use
+    ``clamp(softplus(dt + dt_bias[h]), *dt_limit)`` (``dt_bias`` [H] fp32 or
+    None, ``dt_limit`` (lo, hi), default (0, inf)).
 
     ``cu_seqlens`` (packed batch) may be a GPU int32 tensor or a host sequence;
     a host sequence is copied to the GPU and also validated on the host.
@@ -230,6 +262,16 @@ def chunked_scan(x, dt, A, B, C, D, chunk: int = 256, init_state=None, cu_seqlen
            "ssd_chunked_scan_workspace_size")
     if workspace is None or workspace.numel() < nbytes.value:
         workspace = torch.empty(int(nbytes.value), dtype=torch.uint8, device=x.device)
+    act = _dt_act(dt_softplus, dt_bias, dt_limit, H)
+    if act is not None:
+        if stage_ms is not None:
+            raise ValueError("stage_ms is not available with dt_softplus")
+        _check(lib.ssd_chunked_scan_dt_act(_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), int(chunk),
+                                           _ptr(init_state), _ptr(y), _ptr(final_state), ctypes.byref(act),
+                                           ctypes.byref(sh), _ptr(workspace), int(workspace.numel()),
+                                           _stream_handle(x)), "ssd_chunked_scan_dt_act")
+        del keep
+        return y, final_state
     args = (_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), int(chunk), _ptr(init_state),
             _ptr(y), _ptr(final_state), ctypes.byref(sh), _ptr(workspace), int(workspace.numel()),
             _stream_handle(x))
@@ -243,9 +285,11 @@ def chunked_scan(x, dt, A, B, C, D, chunk: int = 256, init_state=None, cu_seqlen
     return y, final_state
 
 
-def decode_step(state, x, dt, A, B, C, D, *, y=None, y_dtype=None):
+def decode_step(state, x, dt, A, B, C, D, *, y=None, y_dtype=None, dt_softplus: bool = False,
+                dt_bias=None, dt_limit=None):
     """One cached decode step; ``state`` [b, H, P, N] fp32 is updated in place.
-    ``y_dtype``: torch.float32 (default) or torch.bfloat16."""
+    ``y_dtype``: torch.float32 (default) or torch.bfloat16.  ``dt_softplus``,
+    ``dt_bias``, ``dt_limit``: as for chunked_scan."""
     torch = _torch()
     if y_dtype is None:
         y_dtype = torch.float32 if y is None else y.dtype
@@ -267,6 +311,12 @@ def decode_step(state, x, dt, A, B, C, D, *, y=None, y_dtype=None):
     sh.ydtype = _dtype_code_of(y_dtype)
     if y is None:
         y = torch.empty((b, H, P), dtype=y_dtype, device=x.device)
+    act = _dt_act(dt_softplus, dt_bias, dt_limit, H)
+    if act is not None:
+        st = load().ssd_decode_step_dt_act(_ptr(state), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+                                           _ptr(y), ctypes.byref(act), ctypes.byref(sh), _stream_handle(x))
+        _check(st, "ssd_decode_step_dt_act")
+        return y
     st = load().ssd_decode_step(_ptr(state), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
                                 _ptr(y), ctypes.byref(sh), _stream_handle(x))
     _check(st, "ssd_decode_step")

@@ -188,6 +188,7 @@ SSD_API const char* ssd_status_string(int32_t status) {
         case SSD_ERR_HIP: return "HIP runtime error";
         case SSD_ERR_UNSUPPORTED: return "valid but unsupported configuration";
         case SSD_ERR_SEQLENS: return "cu_seqlens is not a valid offset list";
+        case SSD_ERR_VALUE: return "a scalar argument is out of range";
         default: return "unknown status";
     }
 }
@@ -210,7 +211,7 @@ ssd_status scan_impl(const void* x, const float* dt, const float* A, const void*
                      const float* D, int32_t chunk, const float* init_state, void* y,
                      float* final_state, const ssd_shape* shape, void* workspace,
                      size_t workspace_bytes, void* stream, hipEvent_t* marks,
-                     int* fused_out = nullptr) {
+                     int* fused_out = nullptr, const ssd::DtAct* act = nullptr) {
     Prepared pr;
     ssd_status st = prepare(shape, chunk, &pr);
     if (st != SSD_OK) return st;
@@ -251,6 +252,7 @@ ssd_status scan_impl(const void* x, const float* dt, const float* A, const void*
     a.hpw = heads_per_workgroup(pr.plan, kScanWorkgroups, pr.plan.hpg);
     a.hpw_state = heads_per_workgroup(pr.plan, kStateWorkgroups, kStateMaxHeads);
     a.fused = fuse_state_passing(pr.plan) ? 1 : 0;
+    a.act = act ? *act : ssd::DtAct{nullptr, 0.f, 0.f, 0};
     if (fused_out) *fused_out = a.fused;
     pr.plan.seq_tab = (int32_t*)(a.ws + pr.lay.seq_tab);
     pr.plan.chunk_tab = (int32_t*)(a.ws + pr.lay.chunk_tab);
@@ -303,9 +305,58 @@ SSD_API ssd_status ssd_chunked_scan_profiled(const void* x, const float* dt, con
     return st;
 }
 
+namespace {
+
+// Validated copy of an activation argument.
+ssd_status dt_act_of(const ssd_dt_activation* act, ssd::DtAct* out) {
+    if (!act) return fail(SSD_ERR_NULL, "act is NULL");
+    if (act->dt_bias && !aligned16(act->dt_bias)) return fail(SSD_ERR_ALIGN, "dt_bias is not 16-byte aligned");
+    const float lo = act->dt_min, hi = act->dt_max;
+    if (!(lo >= 0.f) || lo > 3.0e38f) return fail(SSD_ERR_VALUE, "dt_min %g must be finite and >= 0", (double)lo);
+    if (!(hi >= lo)) return fail(SSD_ERR_VALUE, "dt_max %g must be >= dt_min %g", (double)hi, (double)lo);
+    *out = ssd::DtAct{act->dt_bias, lo, hi, 1};
+    return SSD_OK;
+}
+
+ssd_status decode_impl(float* state, const void* x, const float* dt, const float* A, const void* B,
+                       const void* C, const float* D, void* y, const ssd_shape* shape, void* stream,
+                       const ssd::DtAct* act);
+
+}  // namespace
+
+SSD_API ssd_status ssd_chunked_scan_dt_act(const void* x, const float* dt_raw, const float* A,
+                                           const void* B, const void* C, const float* D, int32_t chunk,
+                                           const float* init_state, void* y, float* final_state,
+                                           const ssd_dt_activation* act, const ssd_shape* shape,
+                                           void* workspace, size_t workspace_bytes, void* stream) {
+    ssd::DtAct a;
+    const ssd_status st = dt_act_of(act, &a);
+    if (st != SSD_OK) return st;
+    return scan_impl(x, dt_raw, A, B, C, D, chunk, init_state, y, final_state, shape, workspace,
+                     workspace_bytes, stream, nullptr, nullptr, &a);
+}
+
+SSD_API ssd_status ssd_decode_step_dt_act(float* state, const void* x, const float* dt_raw, const float* A,
+                                          const void* B, const void* C, const float* D, void* y,
+                                          const ssd_dt_activation* act, const ssd_shape* shape,
+                                          void* stream) {
+    ssd::DtAct a;
+    const ssd_status st = dt_act_of(act, &a);
+    if (st != SSD_OK) return st;
+    return decode_impl(state, x, dt_raw, A, B, C, D, y, shape, stream, &a);
+}
+
 SSD_API ssd_status ssd_decode_step(float* state, const void* x, const float* dt, const float* A,
                                    const void* B, const void* C, const float* D, void* y,
                                    const ssd_shape* shape, void* stream) {
+    return decode_impl(state, x, dt, A, B, C, D, y, shape, stream, nullptr);
+}
+
+namespace {
+
+ssd_status decode_impl(float* state, const void* x, const float* dt, const float* A, const void* B,
+                       const void* C, const float* D, void* y, const ssd_shape* shape, void* stream,
+                       const ssd::DtAct* act) {
     if (!shape) return fail(SSD_ERR_NULL, "shape is NULL");
     ssd_status st = check_head_dims(shape);
     if (st != SSD_OK) return st;
@@ -340,8 +391,11 @@ SSD_API ssd_status ssd_decode_step(float* state, const void* x, const float* dt,
     a.G = shape->ngroups;
     a.dtype = shape->dtype;
     a.y_f32 = shape->ydtype == SSD_F32 ? 1 : 0;
+    a.act = act ? *act : ssd::DtAct{nullptr, 0.f, 0.f, 0};
     const hipError_t err = ssd::launch_decode(a, (hipStream_t)stream);
     if (err != hipSuccess)
         return fail(SSD_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(err));
     return ok();
 }
+
+}  // namespace

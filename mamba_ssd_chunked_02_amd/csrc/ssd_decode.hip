@@ -56,7 +56,7 @@ template <typename T, int TPR>
 __global__ __launch_bounds__(kDecThreads) void ssd_decode_kernel(
     int64_t nbh, int H, int P, int N, int G, float* __restrict__ state, const T* __restrict__ x,
     const float* __restrict__ dt, const float* __restrict__ A, const T* __restrict__ B,
-    const T* __restrict__ C, const float* __restrict__ D, void* __restrict__ y, int y_f32) {
+    const T* __restrict__ C, const float* __restrict__ D, void* __restrict__ y, int y_f32, DtAct act) {
     constexpr int RPI = 64 / TPR;  // rows per wave instruction
     constexpr int RPB = RPI * kBatch;  // rows per batch
     const int lane = threadIdx.x & 63;
@@ -68,7 +68,7 @@ __global__ __launch_bounds__(kDecThreads) void ssd_decode_kernel(
     const int j = lane % TPR, rsub = lane / TPR;
     const bool nv = 4 * j < N;
     const int n = nv ? 4 * j : N - 4;
-    const float d = dt[bh];
+    const float d = dt_activate(act, dt[bh], h);
     const float a = __expf(d * A[h]);
     const float Dh = D[h];
     const f32x4 bv = nv ? Tr<T>::ld4(B + (b * G + g) * N + n) : f32x4{};
@@ -121,7 +121,7 @@ hipError_t run(const DecodeArgs& a, hipStream_t stream) {
     const int64_t blocks = (nbh + kDecThreads / 64 - 1) / (kDecThreads / 64);
     hipLaunchKernelGGL((ssd_decode_kernel<T, TPR>), dim3((unsigned)blocks), dim3(kDecThreads), 0, stream,
                        nbh, a.H, a.P, a.N, a.G, a.state, (const T*)a.x, a.dt, a.A, (const T*)a.B,
-                       (const T*)a.C, a.D, a.y, a.y_f32);
+                       (const T*)a.C, a.D, a.y, a.y_f32, a.act);
     return hipGetLastError();
 }
 

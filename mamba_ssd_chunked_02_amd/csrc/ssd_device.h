@@ -104,6 +104,16 @@ __device__ inline float wave_inclusive_scan(float v) {
     return v;
 }
 
+// ---------------------------------------------------------------- dt activation
+// softplus(raw + bias[h]) clamped to [lo, hi] when a.on (raw as given
+// otherwise); softplus(v) = log(1 + exp(v)), v itself above 20.
+__device__ inline float dt_activate(const DtAct& a, float raw, int h) {
+    if (!a.on) return raw;
+    const float v = raw + (a.bias ? a.bias[h] : 0.f);
+    const float sp = v > 20.f ? v : log1pf(expf(v));
+    return fminf(fmaxf(sp, a.lo), a.hi);
+}
+
 // ---------------------------------------------------------------- descriptors
 struct ChunkDesc {
     int32_t seq;   // -1: no such chunk

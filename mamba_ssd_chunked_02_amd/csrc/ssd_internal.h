@@ -41,6 +41,14 @@ struct Layout {
     size_t total;
 };
 
+// dt activation applied where dt enters the kernels (on = 0: dt used as given):
+// dt = min(max(softplus(raw + bias[h]), lo), hi).
+struct DtAct {
+    const float* bias;  // [H] or NULL
+    float lo, hi;
+    int32_t on;
+};
+
 struct ScanArgs {
     const void* x;
     const float* dt;
@@ -57,6 +65,7 @@ struct ScanArgs {
     int32_t hpw;       // heads per workgroup of chunk_scan (within one group)
     int32_t hpw_state; // heads per workgroup of the chunk-parallel chunk_state
     int32_t fused;     // 1: chunk states and state passing in one launch per (sequence, head, tile)
+    DtAct act;
 };
 
 struct DecodeArgs {
@@ -72,6 +81,7 @@ struct DecodeArgs {
     int32_t H, P, N, G;
     int32_t dtype;
     int32_t y_f32;
+    DtAct act;
 };
 
 // dstate padded to the 32-row tiles the kernels use.

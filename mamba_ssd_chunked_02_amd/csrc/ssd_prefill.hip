@@ -104,8 +104,9 @@ __global__ __launch_bounds__(kThreads) void ssd_plan_kernel(Plan pl) {
 
 // ------------------------------------------------------------------ cumsum
 // grid (chunks, ceil(H/16)): the workgroup reads the chunk's dt for 16 heads
-// as contiguous 64-byte row pieces into LDS, then wave w scans heads
-// w, w+4, w+8, w+12 of the block.  Per (chunk, head):
+// as contiguous 64-byte row pieces into LDS (through the dt activation when
+// one is given), then wave w scans heads w, w+4, w+8, w+12 of the block.  Per
+// (chunk, head):
 //   cs[q]  = sum_{s<=q} dt_s A_h inside the chunk; positions past the chunk
 //            end repeat the last value (dt = 0 there)
 //   dtc[q] = dt with zeros past the end
@@ -117,7 +118,7 @@ __global__ __launch_bounds__(kThreads) void ssd_cumsum_kernel(Plan pl, const flo
                                                                const float* __restrict__ A,
                                                                float* __restrict__ cs,
                                                                float* __restrict__ dtc,
-                                                               float* __restrict__ wst) {
+                                                               float* __restrict__ wst, DtAct act) {
     constexpr int SP = 256 + 4;  // LDS row pitch (floats): one row per head
     __shared__ __align__(16) float sdt[kCumHeads * SP];
     const int k = blockIdx.x;
@@ -131,7 +132,7 @@ __global__ __launch_bounds__(kThreads) void ssd_cumsum_kernel(Plan pl, const flo
         const bool hok = h0 + hh < H;
         for (int q = tid / kCumHeads; q < Q; q += kThreads / kCumHeads) {
             const bool ok = hok && q < cd.len;
-            sdt[hh * SP + q] = ok ? dt[(cd.row0 + q) * H + h0 + hh] : 0.f;
+            sdt[hh * SP + q] = ok ? dt_activate(act, dt[(cd.row0 + q) * H + h0 + hh], h0 + hh) : 0.f;
         }
     }
     __syncthreads();
@@ -1191,7 +1192,7 @@ hipError_t run_prefill(const Plan& pl, const Layout& lay, const ScanArgs& a, hip
     if ((err = mark(1)) != hipSuccess) return err;
     if (pl.nchunk_ub > 0) {
         hipLaunchKernelGGL(ssd_cumsum_kernel, dim3(pl.nchunk_ub, (pl.H + kCumHeads - 1) / kCumHeads), dim3(kThreads), 0,
-                           stream, pl, a.dt, a.A, cs, dtc, wst);
+                           stream, pl, a.dt, a.A, cs, dtc, wst, a.act);
         if ((err = hipGetLastError()) != hipSuccess) return err;
     }
     if ((err = mark(2)) != hipSuccess) return err;

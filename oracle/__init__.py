@@ -13,6 +13,10 @@ Contents
     (innvotechnologies blog), section 2, with Abar = exp(dt*A) and the input
     term dt*B*x, plus the D skip term of the continuous SSM (lesty.tech Mamba
     explainer, section 2).
+``dt_activation``
+    The step-size activation that precedes the scan in the Mamba-2 block
+    (blog, section 3, architecture figure: Delta = Softplus(Linear(x) +
+    bias)), with an optional clamp range, in fp64.
 ``quadratic``
     Brute-force quadratic (attention-like) form of the same map, the duality
     statement of the blog's section 2 (Y = (M o CB^T) X with M a 1-semiseparable
@@ -121,6 +125,20 @@ def scan(x, dt, A, B, C, D, init=None, cu_seqlens=None, nthreads: int = 0
     if rc != 0:
         raise ValueError("oracle scan rejected its arguments")
     return y, final
+
+
+def dt_activation(dt_raw, dt_bias=None, dt_limit=(0.0, float("inf"))) -> np.ndarray:
+    """dt = clamp(softplus(dt_raw + dt_bias), *dt_limit) in fp64.
+
+    softplus(v) = log(1 + exp(v)), evaluated as logaddexp(0, v) so that it
+    neither overflows for large v nor loses the tail for very negative v.
+    ``dt_bias`` [H] broadcasts over the last axis of ``dt_raw`` [..., H].
+    """
+    v = _f64(dt_raw)
+    if dt_bias is not None:
+        v = v + _f64(dt_bias)
+    lo, hi = dt_limit
+    return np.minimum(np.maximum(np.logaddexp(0.0, v), lo), hi)
 
 
 def decode(state, x, dt, A, B, C, D, nthreads: int = 0) -> Tuple[np.ndarray, np.ndarray]:

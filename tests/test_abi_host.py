@@ -13,6 +13,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "ssd.h")
 
 OK, E_NULL, E_SHAPE, E_DTYPE, E_ALIGN, E_CHUNK, E_WS, E_HIP, E_UNSUP, E_SEQ = 0, -1, -2, -3, -4, -5, -6, -7, -8, -9
+E_VALUE = -10
 FAKE = 0x7F0000000000  # 16-byte aligned, never dereferenced: validation fails first
 
 
@@ -32,7 +33,8 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ["ssd_chunked_scan", "ssd_decode_step", "ssd_chunked_scan_workspace_size",
-              "ssd_status_string", "ssd_last_error_detail"]:
+              "ssd_status_string", "ssd_last_error_detail", "ssd_chunked_scan_dt_act",
+              "ssd_decode_step_dt_act"]:
         assert n in names
 
 
@@ -161,7 +163,7 @@ def test_decode_errors(lib):
 
 
 def test_status_strings(lib):
-    for code in [OK, E_NULL, E_SHAPE, E_DTYPE, E_ALIGN, E_CHUNK, E_WS, E_HIP, E_UNSUP, E_SEQ]:
+    for code in [OK, E_NULL, E_SHAPE, E_DTYPE, E_ALIGN, E_CHUNK, E_WS, E_HIP, E_UNSUP, E_SEQ, E_VALUE]:
         s = lib.ssd_status_string(code).decode()
         assert s and s != "unknown status"
     assert lib.ssd_status_string(123).decode() == "unknown status"
@@ -172,3 +174,36 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(ssd, "_PKG", str(tmp_path))
     with pytest.raises(RuntimeError, match="not built"):
         ssd.load()
+
+
+def test_dt_activation_argument_errors(lib):
+    """The *_dt_act entry points validate the activation first: NULL act, a
+    misaligned bias, and clamp ranges that are negative, NaN, infinite at the
+    bottom or inverted; then the usual argument checks apply."""
+    sh = shape(batch=2)
+    inf, nan = float("inf"), float("nan")
+
+    def act(bias=None, lo=0.0, hi=inf):
+        a = ssd._DtAct()
+        a.dt_bias, a.dt_min, a.dt_max = bias, lo, hi
+        return a
+
+    def scan_act(a, s=sh):
+        return lib.ssd_chunked_scan_dt_act(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 64, None, FAKE + 4096, None,
+                                           None if a is None else ctypes.byref(a), ctypes.byref(s),
+                                           FAKE + 8192, 1, None)
+
+    def dec_act(a, s=sh):
+        return lib.ssd_decode_step_dt_act(FAKE, FAKE + 16, FAKE + 32, FAKE + 48, FAKE + 64, FAKE + 80,
+                                          FAKE + 96, FAKE + 112, None if a is None else ctypes.byref(a),
+                                          ctypes.byref(s), None)
+
+    for call in (scan_act, dec_act):
+        assert call(None) == E_NULL
+        assert call(act(bias=FAKE + 4)) == E_ALIGN
+        for lo, hi in [(-0.1, 1.0), (nan, 1.0), (0.0, nan), (inf, inf), (0.5, 0.1)]:
+            assert call(act(lo=lo, hi=hi)) == E_VALUE, (lo, hi)
+            assert lib.ssd_last_error_detail().decode()
+        # a valid activation reaches the usual checks (a bad dtype here)
+        assert call(act(lo=0.001, hi=0.1), shape(batch=2, dtype=7)) == E_DTYPE
+    assert scan_act(act()) == E_WS  # workspace_bytes 1 is too small

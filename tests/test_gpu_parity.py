@@ -234,6 +234,85 @@ def test_fused_walk_equals_separate_runs():
         assert_close(fin[s], host(fs)[0], "f32", "seq %d final" % s)
 
 
+# ------------------------------------------------------------------ fused dt activation
+# Raw step sizes (softplus argument) with a per-head bias; the kernels apply
+# clamp(softplus(raw + bias), lo, hi) where dt enters (cumsum, decode) and the
+# oracle runs on the same activation computed in fp64.
+ACT = [
+    # (batch, L, H, P, N, G, chunk, dtype): chunk-parallel state kernels, the walk, fp32
+    (2, 300, 4, 64, 128, 2, 128, "bf16"),
+    (4, 300, 32, 64, 128, 2, 128, "bf16"),
+    (1, 200, 4, 16, 16, 1, 64, "f32"),
+]
+
+
+def raw_dt(shape, H, seed):
+    rng = np.random.default_rng(seed)
+    raw = rng.normal(-4.0, 1.0, size=shape).astype(np.float32)
+    bias = rng.normal(0.0, 0.5, size=H).astype(np.float32)
+    return raw, bias
+
+
+@pytest.mark.parametrize("limit", [None, (0.001, 0.1)], ids=["nolimit", "limit"])
+@pytest.mark.parametrize("case", ACT, ids=lambda c: "b%d-L%d-H%d-P%d-N%d-G%d-Q%d-%s" % c[:8])
+def test_dt_activation_prefill(case, limit):
+    b, L, H, P, N, G, Q, dt = case
+    wl = W.small_workload(batch=b, seqlen=L, H=H, P=P, N=N, G=G, chunk=Q, dtype=dt, init_var=0.1)
+    inp = W.generate(wl, 17 + H)
+    raw, bias = raw_dt(inp.dt.shape, H, H + L)
+    say("case: dt activation", case, limit)
+    g = to_gpu(inp)
+    y, fin = ssd.chunked_scan(g["x"], tdev(raw), g["A"], g["B"], g["C"], g["D"], Q, init_state=g["init"],
+                              dt_softplus=True, dt_bias=tdev(bias), dt_limit=limit)
+    torch.cuda.synchronize()
+    dta = oracle.dt_activation(raw, bias, limit or (0.0, float("inf")))
+    yr, fr = oracle.scan(inp.x, dta, inp.A, inp.B, inp.C, inp.D, init=inp.init)
+    assert_close(host(y), yr, dt, "y")
+    assert_close(host(fin), fr, dt, "final")
+
+
+def test_dt_activation_decode_and_packed():
+    """Packed prefill and then decode steps, both with the activation and no bias."""
+    lens = (100, 0, 257, 64)
+    wl = W.small_workload(seqlens=lens, H=8, P=64, N=64, G=2, chunk=64, dtype="f32", init_var=0.1,
+                          decode_steps=3, decode_batch=len(lens))
+    inp = W.generate(wl, 19)
+    raw, _ = raw_dt(inp.dt.shape, 8, 5)
+    g = to_gpu(inp)
+    y, fin = ssd.chunked_scan(g["x"], tdev(raw), g["A"], g["B"], g["C"], g["D"], 64, init_state=g["init"],
+                              cu_seqlens=g["cu"], dt_softplus=True)
+    torch.cuda.synchronize()
+    yr, fr = oracle.scan(inp.x, oracle.dt_activation(raw), inp.A, inp.B, inp.C, inp.D, init=inp.init,
+                         cu_seqlens=inp.cu_seqlens)
+    assert_close(host(y), yr, "f32", "y")
+    assert_close(host(fin), fr, "f32", "final")
+    state, ref = fin, fr
+    for k, d in enumerate(inp.decode):
+        rd, _ = raw_dt(d["dt"].shape, 8, 100 + k)
+        yd = ssd.decode_step(state, tdev(d["x"]), tdev(rd), g["A"], tdev(d["B"]), tdev(d["C"]), g["D"],
+                             dt_softplus=True, dt_limit=(0.0, 0.2))
+        yref, ref = oracle.decode(ref, d["x"], oracle.dt_activation(rd, None, (0.0, 0.2)), inp.A, d["B"],
+                                  d["C"], inp.D)
+        assert_close(host(yd), yref, "f32", "decode y %d" % k)
+        assert_close(host(state), ref, "f32", "decode state %d" % k)
+
+
+def test_dt_activation_equals_activated_input():
+    """The fused activation and the plain entry point on dt activated on the
+    host (fp32) agree to fp32 rounding of dt."""
+    wl = W.small_workload(batch=2, seqlen=333, H=4, P=32, N=64, G=1, chunk=64, dtype="f32", init_var=0.1)
+    inp = W.generate(wl, 23)
+    raw, bias = raw_dt(inp.dt.shape, 4, 9)
+    g = to_gpu(inp)
+    y1, f1 = ssd.chunked_scan(g["x"], tdev(raw), g["A"], g["B"], g["C"], g["D"], 64, init_state=g["init"],
+                              dt_softplus=True, dt_bias=tdev(bias))
+    pre = oracle.dt_activation(raw, bias).astype(np.float32)
+    y2, f2 = ssd.chunked_scan(g["x"], tdev(pre), g["A"], g["B"], g["C"], g["D"], 64, init_state=g["init"])
+    torch.cuda.synchronize()
+    assert_close(host(y1), host(y2).astype(np.float64), "f32", "y")
+    assert_close(host(f1), host(f2).astype(np.float64), "f32", "final")
+
+
 # ------------------------------------------------------------------ cache semantics
 def test_prefill_then_decode_equals_longer_prefill():
     wl = W.small_workload(batch=2, seqlen=600, H=4, P=64, N=128, G=1, chunk=128, dtype="f32",

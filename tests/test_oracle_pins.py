@@ -274,3 +274,35 @@ def test_chunked_packed_restart_at_sequence_start():
     # chunks never straddle a sequence boundary
     for c in inter:
         assert cu[c["seq"]] <= c["start"] and c["start"] + c["len"] <= cu[c["seq"] + 1]
+
+
+# ------------------------------------------------------------------ dt activation
+def test_dt_activation_closed_forms():
+    """softplus(0) = ln 2; softplus(v) - softplus(-v) = v; softplus(v) ~ exp(v)
+    far below 0 and ~ v far above; positive and increasing everywhere."""
+    assert oracle.dt_activation(np.array([0.0]))[0] == pytest.approx(np.log(2.0), rel=1e-15)
+    v = np.linspace(-30.0, 30.0, 601)
+    sp = oracle.dt_activation(v)
+    sm = oracle.dt_activation(-v)
+    np.testing.assert_allclose(sp - sm, v, rtol=0, atol=1e-12)
+    assert np.all(sp > 0) and np.all(np.diff(sp) > 0)
+    far = np.array([-40.0, -60.0, -700.0])
+    np.testing.assert_allclose(oracle.dt_activation(far), np.exp(far), rtol=1e-15)
+    big = np.array([40.0, 300.0, 1e6])
+    np.testing.assert_allclose(oracle.dt_activation(big), big, rtol=1e-15)
+
+
+def test_dt_activation_bias_per_head_and_clamp():
+    rng = np.random.default_rng(3)
+    raw = rng.normal(-4.0, 1.0, size=(5, 7, 3))
+    bias = np.array([0.0, 2.0, -1.5])
+    out = oracle.dt_activation(raw, bias)
+    for h in range(3):
+        np.testing.assert_array_equal(out[..., h], oracle.dt_activation(raw[..., h] + bias[h]))
+    lo, hi = 0.01, 0.05
+    cl = oracle.dt_activation(raw, bias, (lo, hi))
+    free = oracle.dt_activation(raw, bias)
+    assert cl.min() >= lo and cl.max() <= hi
+    inside = (free >= lo) & (free <= hi)
+    np.testing.assert_array_equal(cl[inside], free[inside])
+    assert np.all(cl[free < lo] == lo) and np.all(cl[free > hi] == hi)
