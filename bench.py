@@ -101,6 +101,59 @@ def cpu_baseline(inp, max_seqs=None):
                       % (nseq, wl.batch, wl.H, wl.seqlen)}
 
 
+def decode_vs_recompute(torch, ssd, context=4096, steps=64, reps=20):
+    """Per-token cost of cached decode against recomputing the whole prefix, at
+    batch 1 and `context` tokens, on the 130M-like (H=24) and 2.7B-like (H=80)
+    layer shapes (P=64, N=128, bf16 x/B/C, fp32 state): the prefill of
+    `context` tokens is what one token costs without a cache; the decode step
+    is what it costs with one, launched eagerly or as a graph-captured loop of
+    `steps` steps."""
+    from mamba_ssd_chunked_02_amd.decode_loop import DecodeLoop
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device="cpu").manual_seed(11)
+    out = {}
+    for name, H in (("130m_layer", 24), ("2p7b_layer", 80)):
+        P, N = 64, 128
+        x = torch.randn(1, context, H, P, generator=g).to(torch.bfloat16).to(dev)
+        dt = (torch.rand(1, context, H, generator=g) * 0.099 + 0.001).to(dev)
+        A = (-torch.exp(torch.rand(H, generator=g) * np.log(16.0))).to(dev)
+        B = (torch.randn(1, context, 1, N, generator=g) / N ** 0.5).to(torch.bfloat16).to(dev)
+        C = (torch.randn(1, context, 1, N, generator=g) / N ** 0.5).to(torch.bfloat16).to(dev)
+        D = torch.randn(H, generator=g).to(dev)
+        y = torch.empty(tuple(x.shape), device=dev)
+        fin = torch.empty(1, H, P, N, device=dev)
+        ws = torch.empty(ssd.workspace_size(x, B, 256), dtype=torch.uint8, device=dev)
+        loop = DecodeLoop(steps, 1, H, P, N, 1, A, D, dtype=torch.bfloat16)
+        loop.x.normal_()
+        loop.dt.uniform_(0.001, 0.1)
+        loop.B.normal_(0, N ** -0.5)
+        loop.C.normal_(0, N ** -0.5)
+
+        def timed(fn, n):
+            for _ in range(3):
+                fn()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(n):
+                fn()
+            e1.record()
+            e1.synchronize()
+            return e0.elapsed_time(e1) / n
+
+        pre = timed(lambda: ssd.chunked_scan(x, dt, A, B, C, D, 256, y=y, final_state=fin, workspace=ws),
+                    reps)
+        graph = timed(loop.replay, reps) / steps
+        eager = timed(loop.run_eager, reps) / steps
+        out[name] = {"recompute_ms_per_token": round(pre, 4), "cached_graph_ms_per_token": round(graph, 5),
+                     "cached_eager_ms_per_token": round(eager, 5),
+                     "speedup_graph": round(pre / graph, 1), "speedup_eager": round(pre / eager, 1)}
+        del x, dt, B, C, y, ws, loop
+    out["what"] = ("batch 1, %d-token context: prefill of the whole context (no cache) vs one cached "
+                   "decode step (graph-captured loop of %d steps, or eager launches)" % (context, steps))
+    return out
+
+
 def _source_digest():
     """sha256 of the kernel sources, to tell whether counters are stale."""
     import hashlib
@@ -347,6 +400,9 @@ def main():
     copy_gbs = 2 * state.numel() * 4 / (copy_ms * 1e-3) / 1e9
     del src, dst
 
+    log("cached decode vs full-prefix recompute")
+    dvr = decode_vs_recompute(torch, ssd)
+
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a sample")
@@ -384,6 +440,7 @@ def main():
                    "steady_gbps": round(dbytes / (decode_steady_ms * 1e-3) / 1e9, 1),
                    "steady": "100 back-to-back steps after the timed region"},
         "step_ms_prefill_plus_decode": round(prefill_ms + decode_ms, 4),
+        "decode_vs_recompute": dvr,
         "prefill_dt_activation": {"ms_per_step": round(act_ms, 4), "tokens_per_s": round(tokens / (act_ms * 1e-3), 1),
                                   "plain_ms_per_step": round(plain_b2b_ms, 4),
                                   "what": "same prefill through ssd_chunked_scan_dt_act (softplus fused into "

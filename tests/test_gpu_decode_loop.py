@@ -1,0 +1,91 @@
+"""Graph-captured decode loop: every replay equals the same steps launched
+eagerly (bitwise: same kernels on the same inputs), with eager work and
+synchronizations between the replays; and the loop agrees with the oracle."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from mamba_ssd_chunked_02_amd import workloads as W
+from mamba_ssd_chunked_02_amd.decode_loop import DecodeLoop
+from parity import assert_close, host, tdev
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def fill(loop, inp, dtype):
+    for k, d in enumerate(inp.decode):
+        loop.x[k].copy_(tdev(d["x"], dtype))
+        loop.dt[k].copy_(tdev(d["dt"]))
+        loop.B[k].copy_(tdev(d["B"], dtype))
+        loop.C[k].copy_(tdev(d["C"], dtype))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_replays_equal_eager_steps(dtype):
+    steps = 6
+    wl = W.small_workload(batch=4, seqlen=0, H=6, P=64, N=128, G=2, dtype=dtype, init_var=0.1,
+                          decode_steps=steps, decode_batch=4)
+    inp = W.generate(wl, 31)
+    say("case: decode loop", dtype)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    A, D = tdev(inp.A), tdev(inp.D)
+    loop = DecodeLoop(steps, 4, 6, 64, 128, 2, A, D, dtype=tdt)
+    fill(loop, inp, dtype)
+    s0 = tdev(inp.init)
+    # eager reference
+    loop.state.copy_(s0)
+    loop.run_eager()
+    torch.cuda.synchronize()
+    y_ref, s_ref = loop.y.clone(), loop.state.clone()
+    for rep in range(4):
+        loop.state.copy_(s0)
+        loop.y.zero_()
+        junk = torch.randn(1 << 20, device="cuda").sum()  # unrelated eager work between replays
+        torch.cuda.synchronize()
+        loop.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(loop.y, y_ref), "replay %d y" % rep
+        assert torch.equal(loop.state, s_ref), "replay %d state" % rep
+        del junk
+    # and the loop is the recurrence: compare with the oracle
+    ref = inp.init.astype(np.float64)
+    for k, d in enumerate(inp.decode):
+        yk, ref = oracle.decode(ref, d["x"], d["dt"], inp.A, d["B"], d["C"], inp.D)
+        assert_close(host(y_ref[k]), yk, dtype, "y step %d" % k)
+    assert_close(host(s_ref), ref, dtype, "state")
+
+
+def test_consecutive_replays_advance_the_state():
+    """Two replays of a k-step loop equal 2k eager steps when the second
+    replay's inputs are refilled between them."""
+    steps = 4
+    wl = W.small_workload(batch=2, seqlen=0, H=4, P=32, N=64, G=1, dtype="f32", init_var=0.1,
+                          decode_steps=2 * steps, decode_batch=2)
+    inp = W.generate(wl, 37)
+    A, D = tdev(inp.A), tdev(inp.D)
+    loop = DecodeLoop(steps, 2, 4, 32, 64, 1, A, D, dtype=torch.float32)
+    loop.state.copy_(tdev(inp.init))
+    ys = []
+    for half in range(2):
+        for k in range(steps):
+            d = inp.decode[half * steps + k]
+            loop.x[k].copy_(tdev(d["x"]))
+            loop.dt[k].copy_(tdev(d["dt"]))
+            loop.B[k].copy_(tdev(d["B"]))
+            loop.C[k].copy_(tdev(d["C"]))
+        loop.replay()
+        torch.cuda.synchronize()
+        ys.append(host(loop.y))
+    ref = inp.init.astype(np.float64)
+    for j, d in enumerate(inp.decode):
+        yk, ref = oracle.decode(ref, d["x"], d["dt"], inp.A, d["B"], d["C"], inp.D)
+        assert_close(ys[j // steps][j % steps], yk, "f32", "y token %d" % j)
+    assert_close(host(loop.state), ref, "f32", "state")
