@@ -154,6 +154,70 @@ def decode_vs_recompute(torch, ssd, context=4096, steps=64, reps=20):
     return out
 
 
+def decode_window(torch, ssd, wd, window=16, reps=20):
+    """Exact windowed decode against the ordinary decode step on the decode
+    batch (b256 H80 P64 N128, bf16 x/B/C, fp32 state): a window of `window`
+    tokens through ssd_decode_window_step (slot t = 0..window-1, the state
+    written back at the last slot only) against `window` ordinary steps.  The
+    window form reads the state every token and writes it once per window."""
+    dev = torch.device("cuda:0")
+    b, H, P, N, G = wd.nseq, wd.H, wd.P, wd.N, wd.G
+    g = torch.Generator(device="cpu").manual_seed(13)
+    state = (torch.randn(b, H, P, N, generator=g) * 0.3).to(dev)
+    x = torch.randn(b, window, H, P, generator=g).to(torch.bfloat16).to(dev)
+    dt = (torch.rand(b, window, H, generator=g) * 0.099 + 0.001).to(dev)
+    A = (-torch.exp(torch.rand(H, generator=g) * np.log(16.0))).to(dev)
+    B = (torch.randn(b, window, G, N, generator=g) / N ** 0.5).to(torch.bfloat16).to(dev)
+    C = (torch.randn(b, window, G, N, generator=g) / N ** 0.5).to(torch.bfloat16).to(dev)
+    D = torch.randn(H, generator=g).to(dev)
+    y = torch.empty(b, H, P, device=dev)
+    # per-token views for the ordinary step
+    xs = [x[:, t].contiguous() for t in range(window)]
+    dts = [dt[:, t].contiguous() for t in range(window)]
+    Bs = [B[:, t].contiguous() for t in range(window)]
+    Cs = [C[:, t].contiguous() for t in range(window)]
+
+    def win():
+        for t in range(window):
+            ssd.decode_window_step(state, x, dt, A, B, C, D, t, t == window - 1, y=y)
+
+    def plain():
+        for t in range(window):
+            ssd.decode_step(state, xs[t], dts[t], A, Bs[t], Cs[t], D, y=y)
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        e1.synchronize()
+        return e0.elapsed_time(e1) / (reps * window)
+
+    w_ms = timed(win)
+    p_ms = timed(plain)
+    # the two kernel variants on their own: a read-only step (slot 7) and a flush
+    read_ms = timed(lambda: ssd.decode_window_step(state, x, dt, A, B, C, D, 7, False, y=y))
+    flush_ms = timed(lambda: ssd.decode_window_step(state, x, dt, A, B, C, D, window - 1, True, y=y))
+    sb = b * H * P * N * 4
+    es = 2
+    # per token: the state read, the state written once per window, the window
+    # slots 0..t of x, B, C and dt read (mean over t), y written
+    slots = (window + 1) / 2
+    wbytes = sb + sb / window + slots * (b * H * P * es + 2 * b * G * N * es + b * H * 4) + b * H * P * 4 + 2 * H * 4
+    pbytes = decode_bytes(wd)
+    return {"window": window, "ms_per_token": round(w_ms, 4), "plain_ms_per_token": round(p_ms, 4),
+            "speedup": round(p_ms / w_ms, 3), "bytes_per_token": int(wbytes), "plain_bytes_per_token": pbytes,
+            "gbps": round(wbytes / (w_ms * 1e-3) / 1e9, 1),
+            "read_only_step_ms": round(read_ms * window, 4), "flush_step_ms": round(flush_ms * window, 4),
+            "read_only_step_gbps": round(sb / (read_ms * window * 1e-3) / 1e9, 1),
+            "what": "ssd_decode_window_step over a %d-token window (state written once per window) vs "
+                    "%d ssd_decode_step calls, b%d H%d P%d N%d, eager back-to-back" % (window, window, b, H, P, N)}
+
+
 def _source_digest():
     """sha256 of the kernel sources, to tell whether counters are stale."""
     import hashlib
@@ -402,6 +466,8 @@ def main():
 
     log("cached decode vs full-prefix recompute")
     dvr = decode_vs_recompute(torch, ssd)
+    log("windowed exact decode vs ordinary decode")
+    dwin = decode_window(torch, ssd, wd)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -441,6 +507,7 @@ def main():
                    "steady": "100 back-to-back steps after the timed region"},
         "step_ms_prefill_plus_decode": round(prefill_ms + decode_ms, 4),
         "decode_vs_recompute": dvr,
+        "decode_window": dwin,
         "prefill_dt_activation": {"ms_per_step": round(act_ms, 4), "tokens_per_s": round(tokens / (act_ms * 1e-3), 1),
                                   "plain_ms_per_step": round(plain_b2b_ms, 4),
                                   "what": "same prefill through ssd_chunked_scan_dt_act (softplus fused into "

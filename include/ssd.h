@@ -173,6 +173,38 @@ ssd_status ssd_decode_step_dt_act(float* state, const void* x, const float* dt_r
                                   const ssd_dt_activation* act, const ssd_shape* shape, void* stream);
 
 /*
+ * Exact windowed decode step ("SketchSSM: Write to the Full State, Read from
+ * a Compact Sketch", Fig. 3(a), Fig. 4 and Table 4: ReplaySSM reads the full
+ * state at every step and writes it once per window of W tokens, D + D/W
+ * state traffic per step instead of 2D).
+ *
+ * The caller keeps the state S0 as of the last flush and the tokens since
+ * then in window slots 0..t; slot t holds the current token.  The call writes
+ * the current token's output
+ *     y_t = exp(cs_t) S0 C_t + sum_{s<=t} exp(cs_t - cs_s) dt_s (B_s . C_t) x_s + D x_t,
+ *     cs_s = A sum_{u<=s} dt_u,
+ * which equals what t+1 ssd_decode_step calls from S0 would give, and, when
+ * `flush` is 1, replaces S0 by the state after token t (the caller then
+ * starts a new window at slot 0).  With flush = 0 the state is only read.
+ *
+ *   state  [batch, H, P, N] fp32   S0 (rewritten only when flush = 1)
+ *   x      [batch, W, H, P] dtype  window slots; slots > t are not read
+ *   dt     [batch, W, H]    fp32   (raw when act is given)
+ *   A, D   [H]              fp32
+ *   B, C   [batch, W, G, N] dtype
+ *   y      [batch, H, P]    ydtype output of token t; must not alias an input
+ *   window W in [1, 16]; t in [0, W); flush 0 or 1
+ *   act    NULL, or the dt activation of ssd_decode_step_dt_act
+ * shape->seqlen and shape->cu_seqlens are ignored.  Errors as ssd_decode_step,
+ * plus SSD_ERR_VALUE for window, t or flush out of range (and the activation
+ * errors).
+ */
+ssd_status ssd_decode_window_step(float* state, const void* x, const float* dt, const float* A,
+                                  const void* B, const void* C, const float* D, void* y, int32_t window,
+                                  int32_t t, int32_t flush, const ssd_dt_activation* act,
+                                  const ssd_shape* shape, void* stream);
+
+/*
  * Measurement helper, for benchmarks only: does what ssd_chunked_scan does,
  * with a HIP event recorded on `stream` before and after every kernel stage,
  * then waits for the last event and writes each stage's elapsed time in

@@ -83,6 +83,9 @@ def load():
         lib.ssd_chunked_scan_dt_act.restype = ctypes.c_int32
         lib.ssd_decode_step_dt_act.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, ap, sp, vp]
         lib.ssd_decode_step_dt_act.restype = ctypes.c_int32
+        lib.ssd_decode_window_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int32, ctypes.c_int32,
+                                               ctypes.c_int32, ap, sp, vp]
+        lib.ssd_decode_window_step.restype = ctypes.c_int32
         lib.ssd_status_string.argtypes = [ctypes.c_int32]
         lib.ssd_status_string.restype = ctypes.c_char_p
         lib.ssd_last_error_detail.argtypes = []
@@ -320,4 +323,42 @@ def decode_step(state, x, dt, A, B, C, D, *, y=None, y_dtype=None, dt_softplus: 
     st = load().ssd_decode_step(_ptr(state), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
                                 _ptr(y), ctypes.byref(sh), _stream_handle(x))
     _check(st, "ssd_decode_step")
+    return y
+
+
+def decode_window_step(state, x, dt, A, B, C, D, t: int, flush: bool, *, y=None, y_dtype=None,
+                       dt_softplus: bool = False, dt_bias=None, dt_limit=None):
+    """Exact windowed decode step: output of the token in window slot ``t``.
+
+    ``state`` [b, H, P, N] fp32 is the state at the window start (rewritten to
+    the state after token ``t`` when ``flush``); ``x`` [b, W, H, P], ``dt``
+    [b, W, H], ``B``/``C`` [b, W, G, N] hold the window's tokens in slots
+    0..t.  W = x.shape[1] <= 16.  Returns y [b, H, P]."""
+    torch = _torch()
+    if y_dtype is None:
+        y_dtype = torch.float32 if y is None else y.dtype
+    _need_cuda(state, x, dt, A, B, C, D)
+    b, W, H, P = x.shape
+    G, N = B.shape[-2], B.shape[-1]
+    _expect(state, (b, H, P, N), torch.float32, "state")
+    _expect(dt, (b, W, H), torch.float32, "dt")
+    _expect(B, (b, W, G, N), x.dtype, "B")
+    _expect(C, (b, W, G, N), x.dtype, "C")
+    _expect(A, (H,), torch.float32, "A")
+    _expect(D, (H,), torch.float32, "D")
+    _expect(y, (b, H, P), y_dtype, "y")
+    sh = _Shape()
+    sh.batch, sh.seqlen = b, 1
+    sh.nheads, sh.headdim = H, P
+    sh.ngroups, sh.dstate = G, N
+    sh.dtype = _dtype_code(x)
+    sh.ydtype = _dtype_code_of(y_dtype)
+    if y is None:
+        y = torch.empty((b, H, P), dtype=y_dtype, device=x.device)
+    act = _dt_act(dt_softplus, dt_bias, dt_limit, H)
+    st = load().ssd_decode_window_step(_ptr(state), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+                                       _ptr(y), int(W), int(t), 1 if flush else 0,
+                                       None if act is None else ctypes.byref(act), ctypes.byref(sh),
+                                       _stream_handle(x))
+    _check(st, "ssd_decode_window_step")
     return y

@@ -354,9 +354,9 @@ SSD_API ssd_status ssd_decode_step(float* state, const void* x, const float* dt,
 
 namespace {
 
-ssd_status decode_impl(float* state, const void* x, const float* dt, const float* A, const void* B,
-                       const void* C, const float* D, void* y, const ssd_shape* shape, void* stream,
-                       const ssd::DtAct* act) {
+// Argument checks shared by the decode entry points (one token per sequence).
+ssd_status check_decode(const float* state, const void* x, const float* dt, const float* A, const void* B,
+                        const void* C, const float* D, const void* y, const ssd_shape* shape) {
     if (!shape) return fail(SSD_ERR_NULL, "shape is NULL");
     ssd_status st = check_head_dims(shape);
     if (st != SSD_OK) return st;
@@ -375,6 +375,14 @@ ssd_status decode_impl(float* state, const void* x, const float* dt, const float
         return fail(SSD_ERR_SHAPE, "y aliases an input");
     if (shape->batch * (int64_t)shape->nheads * shape->headdim > ((int64_t)1 << 40))
         return fail(SSD_ERR_SHAPE, "tensor too large");
+    return SSD_OK;
+}
+
+ssd_status decode_impl(float* state, const void* x, const float* dt, const float* A, const void* B,
+                       const void* C, const float* D, void* y, const ssd_shape* shape, void* stream,
+                       const ssd::DtAct* act) {
+    const ssd_status st = check_decode(state, x, dt, A, B, C, D, y, shape);
+    if (st != SSD_OK) return st;
     ssd::DecodeArgs a;
     a.state = state;
     a.x = x;
@@ -398,4 +406,50 @@ ssd_status decode_impl(float* state, const void* x, const float* dt, const float
     return ok();
 }
 
+constexpr int32_t kMaxWindow = 16;
+
 }  // namespace
+
+SSD_API ssd_status ssd_decode_window_step(float* state, const void* x, const float* dt, const float* A,
+                                          const void* B, const void* C, const float* D, void* y,
+                                          int32_t window, int32_t t, int32_t flush,
+                                          const ssd_dt_activation* act, const ssd_shape* shape,
+                                          void* stream) {
+    ssd::DtAct da{nullptr, 0.f, 0.f, 0};
+    if (act) {
+        const ssd_status sa = dt_act_of(act, &da);
+        if (sa != SSD_OK) return sa;
+    }
+    if (window < 1 || window > kMaxWindow)
+        return fail(SSD_ERR_VALUE, "window %d must be in [1, %d]", window, kMaxWindow);
+    if (t < 0 || t >= window) return fail(SSD_ERR_VALUE, "t %d must be in [0, window %d)", t, window);
+    if (flush != 0 && flush != 1) return fail(SSD_ERR_VALUE, "flush must be 0 or 1 (got %d)", flush);
+    const ssd_status st = check_decode(state, x, dt, A, B, C, D, y, shape);
+    if (st != SSD_OK) return st;
+    if (shape->batch * (int64_t)window * shape->nheads * shape->headdim > ((int64_t)1 << 40))
+        return fail(SSD_ERR_SHAPE, "tensor too large");
+    ssd::WindowArgs a;
+    a.state = state;
+    a.x = x;
+    a.dt = dt;
+    a.A = A;
+    a.B = B;
+    a.C = C;
+    a.D = D;
+    a.y = y;
+    a.batch = shape->batch;
+    a.H = shape->nheads;
+    a.P = shape->headdim;
+    a.N = shape->dstate;
+    a.G = shape->ngroups;
+    a.W = window;
+    a.t = t;
+    a.flush = flush;
+    a.dtype = shape->dtype;
+    a.y_f32 = shape->ydtype == SSD_F32 ? 1 : 0;
+    a.act = da;
+    const hipError_t err = ssd::launch_decode_window(a, (hipStream_t)stream);
+    if (err != hipSuccess)
+        return fail(SSD_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(err));
+    return ok();
+}

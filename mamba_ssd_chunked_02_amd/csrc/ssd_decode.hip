@@ -137,7 +137,190 @@ hipError_t dispatch(const DecodeArgs& a, hipStream_t stream) {
     return hipErrorInvalidValue;
 }
 
+// ------------------------------------------------------------------ windowed decode
+// Exact windowed update ("SketchSSM: Write to the Full State...", Fig. 3(a),
+// Fig. 4 and Table 4: the full state S0 is read every step and written once
+// per window of W tokens).  The window holds the tokens since the last flush
+// (slots 0..t, the current token in slot t).  With cs_s = sum_{u<=s} dt_u A,
+//   y_t = exp(cs_t) (S0 C_t) + sum_{s<=t} exp(cs_t - cs_s) dt_s (B_s . C_t) x_s + D x_t
+// and on a flush step
+//   S0 <- exp(cs_t) S0 + sum_{s<=t} exp(cs_t - cs_s) dt_s x_s (outer) B_s.
+// Same traversal as the decode step: one wave per (sequence, head), lanes
+// own 4 columns of a row.  Per-token scalars of the window (decay sums,
+// weights, B_s . C_t) are wave-uniform; the window's x rows sit in LDS.
+constexpr int kWinMax = 16;
+constexpr int kWinPitch = kWinMax + 4;  // floats per x row of the window in LDS (16-byte aligned rows)
+
+// Every step streams the state block once for y (and, with FLUSH, writes the
+// new state in the same pass).  The prologue reduces the window to per-lane
+// constants: C_t, the decay exp(cs_t), y's intra-window part per row (LDS) and,
+// with FLUSH, u_s = exp(cs_t - cs_s) dt_s B_s and the window's x rows
+// (LDS, one row of W values per p).  Rows are streamed as in the decode step:
+// batches of kBatch 128-bit loads, the next batch in flight while the current
+// one is used.
+template <typename T, int TPR, bool FLUSH>
+__global__ __launch_bounds__(kDecThreads, FLUSH ? 2 : (sizeof(T) == 2 ? 4 : 3)) void ssd_decode_window_kernel(
+    int64_t nbh, int H, int P, int N, int G, int W, int t, float* __restrict__ state,
+    const T* __restrict__ xw, const float* __restrict__ dtw, const float* __restrict__ A,
+    const T* __restrict__ Bw, const T* __restrict__ Cw, const float* __restrict__ D, void* __restrict__ y,
+    int y_f32, DtAct act) {
+    constexpr int RPI = 64 / TPR;      // rows per wave instruction
+    constexpr int RPB = RPI * kBatch;  // rows per batch
+    // x of the window, transposed: row p holds x_s[p] for s = 0..15 (zero past t).
+    // The flush step reads a row with 128-bit loads (16-byte aligned pitch);
+    // the other step only reads it once per lane, with an odd pitch that keeps
+    // the transposing writes free of bank conflicts.
+    constexpr int XPITCH = FLUSH ? kWinPitch : kWinMax + 1;
+    __shared__ __align__(16) float yis[kDecThreads / 64][128];
+    __shared__ __align__(16) float xts[kDecThreads / 64][128][XPITCH];
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int64_t bh = (int64_t)blockIdx.x * (kDecThreads / 64) + wave;
+    if (bh >= nbh) return;
+    const int h = (int)(bh % H);
+    const int64_t b = bh / H;
+    const int g = h / (H / G);
+    const int j = lane % TPR, rsub = lane / TPR;
+    const bool nv = 4 * j < N;
+    const int n = nv ? 4 * j : N - 4;
+    float* yi = yis[wave];
+    float* sb = state + bh * P * N;
+    const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(sb, (uint32_t)(P * N * sizeof(float)));
+    const __amdgpu_buffer_rsrc_t ry =
+        buffer_rsrc((char*)y + bh * P * (y_f32 ? 4 : 2), (uint32_t)(P * (y_f32 ? 4 : 2)));
+    f32x4 s0[kBatch], sn[kBatch];
+    auto load = [&](int p0, f32x4 (&dst)[kBatch]) {
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            const int p = min(p0 + u * RPI + rsub, P - 1);
+            dst[u] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (p * N + n) * 4, 0, 0));
+        }
+    };
+    // the first state rows go out first: their latency covers the window set-up
+    load(0, s0);
+    // Window inputs: every slot is loaded (slots past t repeat slot t and are
+    // masked afterwards), so the loads issue back to back with no branch.
+    // lane s (< 16) takes window slot s's dt
+    const float rawl = dtw[(b * W + min(lane & (kWinMax - 1), t)) * H + h];
+    typename Tr<T>::v4 bq[kWinMax];
+#pragma unroll
+    for (int s = 0; s < kWinMax; ++s) bq[s] = Tr<T>::ld4raw(Bw + ((b * W + min(s, t)) * G + g) * N + n);
+    const typename Tr<T>::v4 cq = Tr<T>::ld4raw(Cw + ((b * W + t) * G + g) * N + n);
+    // x of the window: P/8 chunks of 8 values per slot, at most 4 per lane
+    const int cpr = P >> 3, nch = kWinMax * cpr;
+    typename Tr<T>::v8 xq[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int c = min(lane + 64 * i, nch - 1);
+        const int sl = c / cpr, q = c - sl * cpr;
+        xq[i] = Tr<T>::ld8(xw + ((b * W + min(sl, t)) * H + h) * P + 8 * q);
+    }
+    const f32x4 ct = nv ? Tr<T>::widen4(cq) : f32x4{};
+    // window scalars, one slot per lane: dt, decay sums cs_s (a prefix scan
+    // over the lanes), weights w_s = exp(cs_t - cs_s) dt_s; zero past t
+    const float dl = lane <= t ? dt_activate(act, rawl, h) : 0.f;
+    const float csl = wave_inclusive_scan(dl * A[h]);
+    const float cst = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, csl), t));
+    const float wl = lane <= t ? __expf(cst - csl) * dl : 0.f;
+    float k[kWinMax];
+    f32x4 us[FLUSH ? kWinMax : 1];
+#pragma unroll
+    for (int s = 0; s < kWinMax; ++s) {
+        const f32x4 bv = nv ? Tr<T>::widen4(bq[s]) : f32x4{};
+        const float w = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wl), s));
+        const float dot = group_sum<TPR>(bv[0] * ct[0] + bv[1] * ct[1] + bv[2] * ct[2] + bv[3] * ct[3]);
+        // the group's last lane holds the dot product; it is the same for every row
+        k[s] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, dot), TPR - 1)) * w;
+        if constexpr (FLUSH) us[s] = w * bv;
+    }
+    const float Dh = D[h];
+    float(*xt)[XPITCH] = xts[wave];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int c = lane + 64 * i;
+        if (c < nch) {
+            const int sl = c / cpr, q = c - sl * cpr;
+            const f32x8 v = Tr<T>::widen(xq[i]);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) xt[8 * q + e][sl] = sl <= t ? v[e] : 0.f;
+        }
+    }
+    __builtin_amdgcn_wave_barrier();
+    // per row p: y's window part sum_s k_s x_s[p] + D x_t[p]
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+        const int p = lane + 64 * m;
+        if (p < P) {
+            float acc = 0.f;
+#pragma unroll
+            for (int s = 0; s < kWinMax; ++s) acc += k[s] * xt[p][s];
+            yi[p] = acc + Dh * xt[p][t];
+        }
+    }
+    // rows written by one lane are read by others below (same wave, in-order LDS)
+    __builtin_amdgcn_wave_barrier();
+    const float et = __expf(cst);
+    for (int p0 = 0; p0 < P; p0 += RPB) {
+        load(min(p0 + RPB, P - 1), sn);  // next batch (repeats the last rows at the end)
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            const int p = p0 + u * RPI + rsub;
+            const int pc = min(p, P - 1);
+            const float tot = group_sum<TPR>(s0[u][0] * ct[0] + s0[u][1] * ct[1] + s0[u][2] * ct[2] + s0[u][3] * ct[3]);
+            const float o = et * tot + yi[pc];
+            const bool yo = j == TPR - 1 && p < P;
+            if (y_f32)
+                __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, o), ry, yo ? p * 4 : kOutOfRange,
+                                                      0, kNonTemporal);
+            else
+                __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, (bf16_t)o), ry,
+                                                      yo ? p * 2 : kOutOfRange, 0, kNonTemporal);
+            if constexpr (FLUSH) {
+                const f32x4* xr = (const f32x4*)xt[pc];
+                f32x4 ns = et * s0[u];
+#pragma unroll
+                for (int q = 0; q < kWinMax / 4; ++q) {
+                    const f32x4 xq = xr[q];
+                    ns += xq[0] * us[4 * q] + xq[1] * us[4 * q + 1] + xq[2] * us[4 * q + 2] + xq[3] * us[4 * q + 3];
+                }
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, ns), rs,
+                                                       (p < P && nv) ? (p * N + n) * 4 : kOutOfRange, 0,
+                                                       kNonTemporal);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) s0[u] = sn[u];
+    }
+}
+
+template <typename T, int TPR>
+hipError_t run_window(const WindowArgs& a, hipStream_t stream) {
+    const int64_t nbh = a.batch * a.H;
+    const int64_t blocks = (nbh + kDecThreads / 64 - 1) / (kDecThreads / 64);
+    auto* k = a.flush ? ssd_decode_window_kernel<T, TPR, true> : ssd_decode_window_kernel<T, TPR, false>;
+    hipLaunchKernelGGL(k, dim3((unsigned)blocks), dim3(kDecThreads), 0, stream, nbh, a.H, a.P, a.N, a.G, a.W, a.t,
+                       a.state, (const T*)a.x, a.dt, a.A, (const T*)a.B, (const T*)a.C, a.D, a.y, a.y_f32, a.act);
+    return hipGetLastError();
+}
+
+template <typename T>
+hipError_t dispatch_window(const WindowArgs& a, hipStream_t stream) {
+    const int need = (a.N + 3) / 4;
+    if (need <= 2) return run_window<T, 2>(a, stream);
+    if (need <= 4) return run_window<T, 4>(a, stream);
+    if (need <= 8) return run_window<T, 8>(a, stream);
+    if (need <= 16) return run_window<T, 16>(a, stream);
+    if (need <= 32) return run_window<T, 32>(a, stream);
+    if (need <= 64) return run_window<T, 64>(a, stream);
+    return hipErrorInvalidValue;
+}
+
 }  // namespace
+
+hipError_t launch_decode_window(const WindowArgs& a, hipStream_t stream) {
+    if (a.batch * a.H * a.P == 0) return hipSuccess;
+    if (a.dtype == 1) return dispatch_window<bf16_t>(a, stream);
+    return dispatch_window<float>(a, stream);
+}
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
     if (a.batch * a.H * a.P == 0) return hipSuccess;

@@ -84,6 +84,23 @@ struct DecodeArgs {
     DtAct act;
 };
 
+struct WindowArgs {
+    float* state;      // S0, [batch, H, P, N]; rewritten on a flush step
+    const void* x;     // [batch, W, H, P]
+    const float* dt;   // [batch, W, H]
+    const float* A;
+    const void* B;     // [batch, W, G, N]
+    const void* C;     // [batch, W, G, N]
+    const float* D;
+    void* y;           // [batch, H, P]
+    int64_t batch;
+    int32_t H, P, N, G;
+    int32_t W, t, flush;
+    int32_t dtype;
+    int32_t y_f32;
+    DtAct act;
+};
+
 // dstate padded to the 32-row tiles the kernels use.
 inline int padded_dstate(int N) { return N <= 32 ? 32 : N <= 64 ? 64 : N <= 128 ? 128 : 256; }
 
@@ -100,5 +117,8 @@ hipError_t launch_prefill(const Plan& plan, const Layout& lay, const ScanArgs& a
 
 // Queue the decode kernel.
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+
+// Queue the windowed decode kernel (window <= 16).
+hipError_t launch_decode_window(const WindowArgs& a, hipStream_t stream);
 
 }  // namespace ssd

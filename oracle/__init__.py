@@ -17,6 +17,11 @@ Contents
     The step-size activation that precedes the scan in the Mamba-2 block
     (blog, section 3, architecture figure: Delta = Softplus(Linear(x) +
     bias)), with an optional clamp range, in fp64.
+``decode_window``
+    The windowed form of the decode step (SketchSSM page, Fig. 3(a), Fig. 4,
+    Table 4: read the state of the window start every step, write it once per
+    window): output of window token t, and the state after it, from the
+    window-start state and the window's tokens.
 ``quadratic``
     Brute-force quadratic (attention-like) form of the same map, the duality
     statement of the blog's section 2 (Y = (M o CB^T) X with M a 1-semiseparable
@@ -162,3 +167,34 @@ def decode(state, x, dt, A, B, C, D, nthreads: int = 0) -> Tuple[np.ndarray, np.
     if rc != 0:
         raise ValueError("oracle decode rejected its arguments")
     return y, st
+
+
+def decode_window(state0, xw, dtw, A, Bw, Cw, D, t: int) -> Tuple[np.ndarray, np.ndarray]:
+    """Windowed decode in fp64: (y_t [b,H,P], state after token t [b,H,P,N]).
+
+    state0 [b,H,P,N] is the state at the window start; xw [b,W,H,P], dtw
+    [b,W,H], Bw/Cw [b,W,G,N] hold the window's tokens, of which slots 0..t
+    are used.  With cs_s = A sum_{u<=s} dt_u over the window,
+      y_t   = exp(cs_t) S0 C_t + sum_{s<=t} exp(cs_t - cs_s) dt_s (B_s . C_t) x_s + D x_t
+      S_t   = exp(cs_t) S0 + sum_{s<=t} exp(cs_t - cs_s) dt_s x_s (outer) B_s
+    (the window treated as one chunk of the regrouping).
+    """
+    S0 = _f64(state0)
+    x = _f64(xw)[:, : t + 1]
+    dt = _f64(dtw)[:, : t + 1]
+    A = _f64(A)
+    D = _f64(D)
+    b, H, P, N = S0.shape
+    G = Bw.shape[-2]
+    grp = np.arange(H) // (H // G)
+    Bh = _f64(Bw)[:, : t + 1][:, :, grp]       # [b, s, H, N]
+    Ch = _f64(Cw)[:, t][:, grp]                # [b, H, N]
+    cs = np.cumsum(dt * A, axis=1)             # [b, s, H]
+    dec = np.exp(cs[:, -1:, :] - cs)           # exp(cs_t - cs_s)
+    w = dec * dt                               # [b, s, H]
+    kern = w * np.einsum("bshn,bhn->bsh", Bh, Ch)
+    et = np.exp(cs[:, -1])                     # [b, H]
+    y = (et[:, :, None] * np.einsum("bhpn,bhn->bhp", S0, Ch)
+         + np.einsum("bsh,bshp->bhp", kern, x) + D[None, :, None] * x[:, -1])
+    St = et[:, :, None, None] * S0 + np.einsum("bsh,bshp,bshn->bhpn", w, x, Bh)
+    return y, St

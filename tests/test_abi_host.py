@@ -207,3 +207,24 @@ def test_dt_activation_argument_errors(lib):
         # a valid activation reaches the usual checks (a bad dtype here)
         assert call(act(lo=0.001, hi=0.1), shape(batch=2, dtype=7)) == E_DTYPE
     assert scan_act(act()) == E_WS  # workspace_bytes 1 is too small
+
+
+def test_window_step_errors(lib):
+    sh = shape(batch=2)
+
+    def win(window=16, t=0, flush=0, act=None, **kw):
+        p = dict(state=FAKE, x=FAKE + 16, dt=FAKE + 32, A=FAKE + 48, B=FAKE + 64, C=FAKE + 80,
+                 D=FAKE + 96, y=FAKE + 112)
+        p.update(kw)
+        return lib.ssd_decode_window_step(p["state"], p["x"], p["dt"], p["A"], p["B"], p["C"], p["D"],
+                                          p["y"], window, t, flush, act, ctypes.byref(sh), None)
+
+    for window, t, flush in [(0, 0, 0), (17, 0, 0), (16, 16, 0), (4, -1, 0), (4, 0, 2)]:
+        assert win(window, t, flush) == E_VALUE, (window, t, flush)
+    for name in ["state", "x", "dt", "A", "B", "C", "D", "y"]:
+        assert win(**{name: None}) == E_NULL, name
+        assert win(**{name: FAKE + 8}) == E_ALIGN, name
+    assert win(y=FAKE + 16) == E_SHAPE  # y aliases x
+    a = ssd._DtAct()
+    a.dt_bias, a.dt_min, a.dt_max = None, -1.0, 1.0
+    assert win(act=ctypes.byref(a)) == E_VALUE

@@ -306,3 +306,25 @@ def test_dt_activation_bias_per_head_and_clamp():
     inside = (free >= lo) & (free <= hi)
     np.testing.assert_array_equal(cl[inside], free[inside])
     assert np.all(cl[free < lo] == lo) and np.all(cl[free > hi] == hi)
+
+
+# ------------------------------------------------------------------ windowed decode
+@pytest.mark.parametrize("W,G", [(1, 1), (5, 2), (16, 3)])
+def test_decode_window_equals_sequential_steps(W, G):
+    """The windowed form of every window position equals that many sequential
+    decode steps of the C oracle from the window-start state."""
+    rng = np.random.default_rng(40 + W)
+    b, H, P, N = 2, 6, 5, 7
+    S0 = rng.normal(size=(b, H, P, N))
+    xw = rng.normal(size=(b, W, H, P))
+    dtw = rng.uniform(0.001, 0.3, size=(b, W, H))
+    A = -rng.uniform(0.1, 3.0, size=H)
+    Bw = rng.normal(size=(b, W, G, N))
+    Cw = rng.normal(size=(b, W, G, N))
+    D = rng.normal(size=H)
+    st = S0.copy()
+    for t in range(W):
+        y_seq, st = oracle.decode(st, xw[:, t], dtw[:, t], A, Bw[:, t], Cw[:, t], D)
+        y_win, s_win = oracle.decode_window(S0, xw, dtw, A, Bw, Cw, D, t)
+        np.testing.assert_allclose(y_win, y_seq, rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(s_win, st, rtol=1e-12, atol=1e-12)
