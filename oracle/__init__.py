@@ -22,6 +22,10 @@ Contents
     Table 4: read the state of the window start every step, write it once per
     window): output of window token t, and the state after it, from the
     window-start state and the window's tokens.
+``conv.causal_conv1d`` / ``conv.causal_conv1d_batch`` / ``conv.conv1d_step``
+    The causal depthwise conv1d (width K, optional SiLU) that precedes the
+    scan in the Mamba-2 block, with its conv state of K-1 past inputs per
+    channel (blog, sections 3 and 4), in fp64: the sum over taps written out.
 ``quadratic``
     Brute-force quadratic (attention-like) form of the same map, the duality
     statement of the blog's section 2 (Y = (M o CB^T) X with M a 1-semiseparable

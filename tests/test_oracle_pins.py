@@ -14,6 +14,10 @@ against things other than itself:
     separate runs, head permutation, prefill + decode == longer prefill.
 The fp64 chunked regrouping (oracle.chunked) is pinned against the
 sequential oracle for many chunk sizes, including ragged tails.
+The conv1d oracle (oracle.conv) is pinned against numpy.convolve and
+scipy.signal.lfilter per channel, its impulse response (tap order, no channel
+mixing), SiLU closed forms and scipy.special.expit, and the continuation of
+its state across segments of 0, 1 and more tokens.
 """
 import json
 import os
@@ -328,3 +332,104 @@ def test_decode_window_equals_sequential_steps(W, G):
         y_win, s_win = oracle.decode_window(S0, xw, dtw, A, Bw, Cw, D, t)
         np.testing.assert_allclose(y_win, y_seq, rtol=1e-12, atol=1e-12)
         np.testing.assert_allclose(s_win, st, rtol=1e-12, atol=1e-12)
+
+
+# ------------------------------------------------------------------ conv1d (row f-4)
+from oracle import conv as oconv  # noqa: E402
+import scipy.special  # noqa: E402
+
+
+def test_silu_closed_forms_and_library_sigmoid():
+    v = np.array([-800.0, -30.0, -2.5, -1e-9, 0.0, 1e-9, 0.7, 3.0, 40.0, 800.0])
+    s = oconv.silu(v)
+    assert s[4] == 0.0
+    # silu(v) - silu(-v) = v (odd part of v * sigmoid(v))
+    assert np.allclose(oconv.silu(v) - oconv.silu(-v), v, rtol=1e-15, atol=1e-300)
+    # against the library logistic function
+    assert np.allclose(s, v * scipy.special.expit(v), rtol=1e-14, atol=0)
+    # tails: silu(v) -> v above, -> 0 below; derivative 1/2 at 0
+    assert s[-1] == 800.0 and abs(s[0]) < 1e-300
+    assert abs(oconv.silu(1e-9) / 1e-9 - 0.5) < 1e-9
+    # silu(ln 2-ish) exact: silu(log(3)) = log(3) * 3/4
+    assert abs(oconv.silu(np.log(3.0)) - np.log(3.0) * 0.75) < 1e-15
+
+
+@pytest.mark.parametrize("K", [2, 3, 4])
+def test_conv1d_equals_library_convolution_per_channel(K):
+    rng = np.random.default_rng(100 + K)
+    L, C = 37, 24
+    x = rng.normal(size=(L, C))
+    w = rng.uniform(-1, 1, size=(C, K))
+    bias = rng.normal(size=C)
+    st = rng.normal(size=(K - 1, C))
+    y, fin = oconv.causal_conv1d(x, w, bias, st, activation=False)
+    xp = np.concatenate([st, x])
+    for c in range(C):
+        # numpy's convolution flips the kernel; the reversed taps give the
+        # correlation with tap K-1 on the newest sample
+        ref = np.convolve(xp[:, c], w[c, ::-1], mode="valid") + bias[c]
+        assert np.allclose(y[:, c], ref, rtol=1e-13, atol=1e-13)
+        # the same FIR filter through scipy, zero state: first K-1 outputs see zeros
+        ref0 = scipy.signal.lfilter(w[c, ::-1], [1.0], x[:, c]) + bias[c]
+        y0, _ = oconv.causal_conv1d(x[:, c:c + 1], w[c:c + 1], bias[c:c + 1], None, activation=False)
+        assert np.allclose(y0[:, 0], ref0, rtol=1e-13, atol=1e-13)
+    ya, _ = oconv.causal_conv1d(x, w, bias, st, activation=True)
+    assert np.allclose(ya, y * scipy.special.expit(y), rtol=1e-13, atol=1e-15)
+
+
+def test_conv1d_impulse_response_orients_the_taps():
+    K, C, L, t0 = 4, 3, 10, 2
+    w = np.arange(1.0, 1.0 + C * K).reshape(C, K)
+    x = np.zeros((L, C))
+    x[t0, 1] = 1.0
+    y, _ = oconv.causal_conv1d(x, w, None, None, activation=False)
+    # the impulse reaches outputs t0 .. t0+K-1 with the taps newest first
+    assert np.array_equal(y[t0:t0 + K, 1], w[1, ::-1])
+    assert not y[:t0].any() and not y[t0 + K:].any()
+    assert not y[:, 0].any() and not y[:, 2].any()  # depthwise: no channel mixing
+
+
+def test_conv1d_state_continuation_and_short_segments():
+    rng = np.random.default_rng(7)
+    K, C = 4, 16
+    w = rng.uniform(-1, 1, size=(C, K))
+    bias = rng.normal(size=C)
+    x = rng.normal(size=(12, C))
+    st0 = rng.normal(size=(K - 1, C))
+    y_all, fin_all = oconv.causal_conv1d(x, w, bias, st0)
+    # split into segments of 1, 2, 0, 5, 4 tokens, each continuing from the last state
+    st = st0
+    ys = []
+    for a, b in [(0, 1), (1, 3), (3, 3), (3, 8), (8, 12)]:
+        yseg, st = oconv.causal_conv1d(x[a:b], w, bias, st)
+        ys.append(yseg)
+    assert np.allclose(np.concatenate(ys), y_all, rtol=1e-14, atol=1e-14)
+    assert np.array_equal(st, fin_all)
+    assert np.array_equal(fin_all, x[-(K - 1):])
+    # a sequence shorter than K-1 keeps the tail of its incoming state
+    _, fin1 = oconv.causal_conv1d(x[:1], w, bias, st0)
+    assert np.array_equal(fin1, np.concatenate([st0[1:], x[:1]]))
+    _, fin0 = oconv.causal_conv1d(x[:0], w, bias, st0)
+    assert np.array_equal(fin0, st0)
+
+
+def test_conv1d_steps_equal_prefill_and_packed_batch():
+    rng = np.random.default_rng(8)
+    K, C = 4, 8
+    w = rng.uniform(-1, 1, size=(C, K))
+    bias = rng.normal(size=C)
+    lens = [5, 0, 1, 9]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    x = rng.normal(size=(cu[-1], C))
+    st0 = rng.normal(size=(len(lens), K - 1, C))
+    y, fin = oconv.causal_conv1d_batch(x, w, bias, st0, cu_seqlens=cu)
+    for i, n in enumerate(lens):
+        ys, fs = oconv.causal_conv1d(x[cu[i]:cu[i + 1]], w, bias, st0[i])
+        assert np.array_equal(y[cu[i]:cu[i + 1]], ys) and np.array_equal(fin[i], fs)
+    # token-by-token decode steps reproduce the prefill of one sequence
+    xs = x[cu[3]:cu[4]]
+    st = st0[3:4]
+    for t in range(lens[3]):
+        yt, st = oconv.conv1d_step(st, xs[t:t + 1], w, bias)
+        assert np.allclose(yt[0], y[cu[3] + t], rtol=1e-14, atol=1e-14)
+    assert np.array_equal(st[0], fin[3])
