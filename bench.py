@@ -218,6 +218,56 @@ def decode_window(torch, ssd, wd, window=16, reps=20):
                     "%d ssd_decode_step calls, b%d H%d P%d N%d, eager back-to-back" % (window, window, b, H, P, N)}
 
 
+def conv1d_measure(torch, ssd, wl, wd, reps=20):
+    """Causal conv1d + SiLU on the xBC channels of the 2.7B-shaped layer
+    (C = H*P + 2*G*N = 5376, width 4, bf16 in and out), written straight into
+    the scan's x, B and C buffers: the prefill batch (b8 L8192) and one decode
+    step of the decode batch (b256).  Algorithmic bytes: x read once and the
+    output written once (plus weights, bias and conv states)."""
+    dev = torch.device("cuda:0")
+    H, P, G, N, K = wl.H, wl.P, wl.G, wl.N, 4
+    parts = [H * P, G * N, G * N]
+    C = sum(parts)
+    b, L = wl.batch, wl.seqlen
+    g = torch.Generator(device="cpu").manual_seed(17)
+    x = torch.randn(b, L, C, generator=g).to(torch.bfloat16).to(dev)
+    w = ((torch.rand(C, K, generator=g) * 2 - 1) * 0.5).to(dev)
+    bias = ((torch.rand(C, generator=g) * 2 - 1) * 0.5).to(dev)
+    st = torch.randn(b, K - 1, C, generator=g).to(torch.bfloat16).to(dev)
+    fin = torch.empty_like(st)
+    outs = [torch.empty(b, L, c, dtype=torch.bfloat16, device=dev) for c in parts]
+
+    def timed(fn, n):
+        for _ in range(3):
+            fn()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            fn()
+        e1.record()
+        e1.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    pre = timed(lambda: ssd.causal_conv1d(x, w, bias, conv_state=st, final_conv_state=fin, split=parts,
+                                          outs=outs), reps)
+    pbytes = 2 * b * L * C * 2 + C * (K + 1) * 4 + 2 * b * (K - 1) * C * 2
+    del x, outs
+    bd = wd.nseq
+    xd = torch.randn(bd, C, generator=g).to(torch.bfloat16).to(dev)
+    sd = torch.randn(bd, K - 1, C, generator=g).to(torch.bfloat16).to(dev)
+    od = [torch.empty(bd, c, dtype=torch.bfloat16, device=dev) for c in parts]
+    step = timed(lambda: ssd.conv1d_step(sd, xd, w, bias, split=parts, outs=od), 100)
+    sbytes = bd * C * 2 * 2 + 2 * bd * (K - 1) * C * 2 + C * (K + 1) * 4
+    gbs = pbytes / (pre * 1e-3) / 1e9
+    return {"prefill_ms": round(pre, 4), "prefill_tokens_per_s": round(b * L / (pre * 1e-3), 1),
+            "prefill_bytes": pbytes, "prefill_gbps": round(gbs, 1), "prefill_frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+            "step_ms": round(step, 5), "step_bytes": sbytes,
+            "step_gbps": round(sbytes / (step * 1e-3) / 1e9, 1),
+            "what": "causal conv1d width 4 + SiLU over xBC (C=%d) split into x/B/C: prefill b%d L%d, "
+                    "decode step b%d; bf16 in/out, eager back-to-back" % (C, b, L, bd)}
+
+
 def _source_digest():
     """sha256 of the kernel sources, to tell whether counters are stale."""
     import hashlib
@@ -468,6 +518,8 @@ def main():
     dvr = decode_vs_recompute(torch, ssd)
     log("windowed exact decode vs ordinary decode")
     dwin = decode_window(torch, ssd, wd)
+    log("causal conv1d")
+    dconv = conv1d_measure(torch, ssd, wl, wd)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -508,6 +560,7 @@ def main():
         "step_ms_prefill_plus_decode": round(prefill_ms + decode_ms, 4),
         "decode_vs_recompute": dvr,
         "decode_window": dwin,
+        "conv1d": dconv,
         "prefill_dt_activation": {"ms_per_step": round(act_ms, 4), "tokens_per_s": round(tokens / (act_ms * 1e-3), 1),
                                   "plain_ms_per_step": round(plain_b2b_ms, 4),
                                   "what": "same prefill through ssd_chunked_scan_dt_act (softplus fused into "

@@ -205,6 +205,86 @@ ssd_status ssd_decode_window_step(float* state, const void* x, const float* dt, 
                                   const ssd_shape* shape, void* stream);
 
 /*
+ * Causal depthwise conv1d with optional SiLU, the step before the scan in the
+ * Mamba-2 block ("Engineering Hybrid State-Space Models", section 3,
+ * architecture figure: a width-4 1D convolution + SiLU), with its cache of
+ * the K-1 most recent inputs per channel (same page, section 4: the conv state
+ * [dConv - 1, channels] of each layer's state buffer).  Per sequence, channel
+ * c and token t, over the padded sequence xp = [conv state (K-1 rows, oldest
+ * first); x]:
+ *
+ *     v[t, c] = bias[c] + sum_{k<K} weight[c, k] * xp[t + k, c]
+ *     out[t, c] = activation ? v / (1 + exp(-v)) : v
+ *
+ * so weight[c, K-1] multiplies the current token.  The state after a
+ * sequence is the last K-1 rows of xp.
+ *
+ * Shape:
+ *   batch        sequences (>= 0)
+ *   seqlen       dense (cu_seqlens == NULL): tokens per sequence, rows =
+ *                batch*seqlen in [batch, seqlen] order; packed: total tokens T,
+ *                sequence s owns rows [cu_seqlens[s], cu_seqlens[s+1])
+ *   channels     C, a multiple of 8, at most 2^20
+ *   width        K in [2, 4]
+ *   dtype        ssd_dtype of x and of the conv states
+ *   ydtype       ssd_dtype of the outputs
+ *   activation   0: none; 1: SiLU
+ *   reserved     must be 0
+ *
+ * Outputs: the C channels of a row are split into nparts (1 to 3) contiguous
+ * channel ranges, in order, each written to its own dense buffer: part p is
+ * [rows, channels[p]] in ydtype, channels[p] a multiple of 8, the channels
+ * summing to C.  (With the Mamba-2 channel order x | B | C, the three parts
+ * are the scan's x, B and C inputs, written with no separate split pass.)
+ * Unused entries must be 0 / NULL.
+ */
+typedef struct ssd_conv_shape {
+    int64_t batch;
+    int64_t seqlen;
+    int32_t channels;
+    int32_t width;
+    int32_t dtype;
+    int32_t ydtype;
+    int32_t activation;
+    int32_t reserved;
+    const int32_t* cu_seqlens;      /* device int32 [batch+1], or NULL (dense) */
+    const int32_t* cu_seqlens_host; /* optional host copy; validated when given */
+} ssd_conv_shape;
+
+typedef struct ssd_conv_outputs {
+    int32_t nparts;
+    int32_t channels[3];
+    void* out[3];
+} ssd_conv_outputs;
+
+/*
+ *   x              [rows, C]        dtype
+ *   weight         [C, K]           fp32
+ *   bias           [C]              fp32, or NULL (zero)
+ *   conv_state_in  [batch, K-1, C]  dtype, or NULL (zero history)
+ *   conv_state_out [batch, K-1, C]  dtype, or NULL (not written); may equal
+ *                  conv_state_in (it is written after every read of it)
+ *   out            the output parts (above); no part may alias an input
+ * Errors: SSD_ERR_NULL, SSD_ERR_ALIGN, SSD_ERR_DTYPE, SSD_ERR_SHAPE (sizes,
+ * parts, aliasing), SSD_ERR_VALUE (activation), SSD_ERR_SEQLENS (host copy
+ * of cu_seqlens), SSD_ERR_HIP.
+ */
+ssd_status ssd_causal_conv1d(const void* x, const float* weight, const float* bias,
+                             const void* conv_state_in, void* conv_state_out,
+                             const ssd_conv_outputs* out, const ssd_conv_shape* shape, void* stream);
+
+/*
+ * One decode token per sequence, the conv state updated in place (oldest row
+ * dropped, the token appended):
+ *   conv_state [batch, K-1, C] dtype, read and overwritten
+ *   x          [batch, C]      dtype
+ *   weight, bias, out as ssd_causal_conv1d, with rows = batch
+ * shape->seqlen and shape->cu_seqlens are ignored.  Same errors.
+ */
+ssd_status ssd_causal_conv1d_step(void* conv_state, const void* x, const float* weight, const float* bias,
+                                  const ssd_conv_outputs* out, const ssd_conv_shape* shape, void* stream);
+
+/*
  * Measurement helper, for benchmarks only: does what ssd_chunked_scan does,
  * with a HIP event recorded on `stream` before and after every kernel stage,
  * then waits for the last event and writes each stage's elapsed time in

@@ -20,7 +20,8 @@ import ctypes
 import os
 from typing import Optional, Sequence, Tuple
 
-__all__ = ["chunked_scan", "decode_step", "workspace_size", "SsdError", "library_path", "load"]
+__all__ = ["chunked_scan", "decode_step", "decode_window_step", "causal_conv1d", "conv1d_step",
+           "workspace_size", "SsdError", "library_path", "load"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_NAME = "libssd_mi355x.so"
@@ -45,6 +46,17 @@ class _Shape(ctypes.Structure):
                 ("reserved", ctypes.c_int32 * 2),
                 ("cu_seqlens", ctypes.c_void_p),
                 ("cu_seqlens_host", ctypes.c_void_p)]
+
+
+class _ConvShape(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64), ("channels", ctypes.c_int32),
+                ("width", ctypes.c_int32), ("dtype", ctypes.c_int32), ("ydtype", ctypes.c_int32),
+                ("activation", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("cu_seqlens", ctypes.c_void_p), ("cu_seqlens_host", ctypes.c_void_p)]
+
+
+class _ConvOutputs(ctypes.Structure):
+    _fields_ = [("nparts", ctypes.c_int32), ("channels", ctypes.c_int32 * 3), ("out", ctypes.c_void_p * 3)]
 
 
 class _DtAct(ctypes.Structure):
@@ -86,6 +98,12 @@ def load():
         lib.ssd_decode_window_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int32, ctypes.c_int32,
                                                ctypes.c_int32, ap, sp, vp]
         lib.ssd_decode_window_step.restype = ctypes.c_int32
+        csp = ctypes.POINTER(_ConvShape)
+        cop = ctypes.POINTER(_ConvOutputs)
+        lib.ssd_causal_conv1d.argtypes = [vp, vp, vp, vp, vp, cop, csp, vp]
+        lib.ssd_causal_conv1d.restype = ctypes.c_int32
+        lib.ssd_causal_conv1d_step.argtypes = [vp, vp, vp, vp, cop, csp, vp]
+        lib.ssd_causal_conv1d_step.restype = ctypes.c_int32
         lib.ssd_status_string.argtypes = [ctypes.c_int32]
         lib.ssd_status_string.restype = ctypes.c_char_p
         lib.ssd_last_error_detail.argtypes = []
@@ -362,3 +380,100 @@ def decode_window_step(state, x, dt, A, B, C, D, t: int, flush: bool, *, y=None,
                                        _stream_handle(x))
     _check(st, "ssd_decode_window_step")
     return y
+
+
+def _conv_outputs(lead, C, split, outs, y_dtype, device):
+    """The output parts: given tensors, or new ones [*lead, channels_p]."""
+    torch = _torch()
+    split = [C] if split is None else [int(c) for c in split]
+    if sum(split) != C:
+        raise ValueError("split %s does not add up to %d channels" % (split, C))
+    if outs is None:
+        outs = [torch.empty(tuple(lead) + (c,), dtype=y_dtype, device=device) for c in split]
+    if len(outs) != len(split):
+        raise ValueError("%d output tensors for %d parts" % (len(outs), len(split)))
+    co = _ConvOutputs()
+    co.nparts = len(split)
+    for p, (c, o) in enumerate(zip(split, outs)):
+        _expect(o, tuple(lead) + (c,), o.dtype, "output part %d" % p)
+        if o.dtype != y_dtype:
+            raise TypeError("output part %d has dtype %s, expected %s" % (p, o.dtype, y_dtype))
+        co.channels[p] = c
+        co.out[p] = _ptr(o)
+    return co, outs
+
+
+def causal_conv1d(x, weight, bias=None, *, cu_seqlens=None, cu_seqlens_host=None, conv_state=None,
+                  final_conv_state=None, activation: bool = True, split: Optional[Sequence[int]] = None,
+                  outs=None, y_dtype=None):
+    """Causal depthwise conv1d (+ SiLU) over whole sequences.
+
+    x: dense [b, L, C] or packed [T, C] with ``cu_seqlens`` int32 [b+1];
+    weight [C, K] fp32 (tap K-1 on the current token); bias [C] fp32 or None;
+    conv_state [b, K-1, C] (x's dtype) or None; final_conv_state, if given,
+    receives the state after each sequence (it may be conv_state itself).
+    ``split`` lists channel counts of consecutive output parts (default: one
+    part of C channels); returns the list of parts [*x.shape[:-1], c_p]."""
+    torch = _torch()
+    _need_cuda(x, weight, bias, conv_state, final_conv_state, cu_seqlens)
+    C = x.shape[-1]
+    K = weight.shape[-1]
+    if y_dtype is None:
+        y_dtype = x.dtype if outs is None else outs[0].dtype
+    _expect(weight, (C, K), torch.float32, "weight")
+    _expect(bias, (C,), torch.float32, "bias")
+    sh = _ConvShape()
+    keep = None
+    if cu_seqlens is None:
+        if x.dim() != 3:
+            raise ValueError("dense x must be [b, L, C]")
+        sh.batch, sh.seqlen = x.shape[0], x.shape[1]
+    else:
+        if x.dim() != 2:
+            raise ValueError("packed x must be [T, C]")
+        _expect(cu_seqlens, (cu_seqlens.shape[0],), torch.int32, "cu_seqlens")
+        sh.batch, sh.seqlen = cu_seqlens.shape[0] - 1, x.shape[0]
+        sh.cu_seqlens = cu_seqlens.data_ptr()
+        if cu_seqlens_host is not None:
+            import numpy as np
+            keep = np.ascontiguousarray(np.asarray(cu_seqlens_host, dtype=np.int32))
+            sh.cu_seqlens_host = keep.ctypes.data
+    nseq = sh.batch
+    _expect(conv_state, (nseq, K - 1, C), x.dtype, "conv_state")
+    _expect(final_conv_state, (nseq, K - 1, C), x.dtype, "final_conv_state")
+    sh.channels, sh.width = C, K
+    sh.dtype = _dtype_code(x)
+    sh.ydtype = _dtype_code_of(y_dtype)
+    sh.activation = 1 if activation else 0
+    co, outs = _conv_outputs(x.shape[:-1], C, split, outs, y_dtype, x.device)
+    st = load().ssd_causal_conv1d(_ptr(x), _ptr(weight), _ptr(bias), _ptr(conv_state), _ptr(final_conv_state),
+                                  ctypes.byref(co), ctypes.byref(sh), _stream_handle(x))
+    del keep
+    _check(st, "ssd_causal_conv1d")
+    return outs
+
+
+def conv1d_step(conv_state, x, weight, bias=None, *, activation: bool = True,
+                split: Optional[Sequence[int]] = None, outs=None, y_dtype=None):
+    """One decode token per sequence: x [b, C]; conv_state [b, K-1, C] is
+    shifted in place (oldest row out, x in).  Returns the output parts [b, c_p]."""
+    torch = _torch()
+    _need_cuda(conv_state, x, weight, bias)
+    b, C = x.shape
+    K = weight.shape[-1]
+    if y_dtype is None:
+        y_dtype = x.dtype if outs is None else outs[0].dtype
+    _expect(weight, (C, K), torch.float32, "weight")
+    _expect(bias, (C,), torch.float32, "bias")
+    _expect(conv_state, (b, K - 1, C), x.dtype, "conv_state")
+    sh = _ConvShape()
+    sh.batch, sh.seqlen = b, 1
+    sh.channels, sh.width = C, K
+    sh.dtype = _dtype_code(x)
+    sh.ydtype = _dtype_code_of(y_dtype)
+    sh.activation = 1 if activation else 0
+    co, outs = _conv_outputs((b,), C, split, outs, y_dtype, x.device)
+    st = load().ssd_causal_conv1d_step(_ptr(conv_state), _ptr(x), _ptr(weight), _ptr(bias), ctypes.byref(co),
+                                       ctypes.byref(sh), _stream_handle(x))
+    _check(st, "ssd_causal_conv1d_step")
+    return outs

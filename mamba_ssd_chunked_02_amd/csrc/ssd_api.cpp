@@ -453,3 +453,145 @@ SSD_API ssd_status ssd_decode_window_step(float* state, const void* x, const flo
         return fail(SSD_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(err));
     return ok();
 }
+
+// ------------------------------------------------------------------ conv1d
+namespace {
+
+constexpr int32_t kMaxConvChannels = 1 << 20;
+
+ssd_status check_cu_host(const int32_t* cu, int64_t nseq, int64_t T) {
+    if (cu[0] != 0) return fail(SSD_ERR_SEQLENS, "cu_seqlens[0] must be 0 (got %d)", cu[0]);
+    for (int64_t s = 0; s < nseq; ++s)
+        if (cu[s + 1] < cu[s]) return fail(SSD_ERR_SEQLENS, "cu_seqlens decreases at %lld", (long long)s);
+    if (cu[nseq] != T)
+        return fail(SSD_ERR_SEQLENS, "cu_seqlens[batch] = %d differs from seqlen %lld", cu[nseq], (long long)T);
+    return SSD_OK;
+}
+
+// Validates what the prefill and the step share and fills `a` (rows = T for
+// the prefill, batch for the step).
+ssd_status conv_prepare(const void* x, const float* weight, const float* bias, const ssd_conv_outputs* out,
+                        const ssd_conv_shape* sh, bool step, ssd::ConvArgs* a) {
+    if (!sh) return fail(SSD_ERR_NULL, "shape is NULL");
+    if (!out) return fail(SSD_ERR_NULL, "out is NULL");
+    if (sh->dtype != SSD_F32 && sh->dtype != SSD_BF16)
+        return fail(SSD_ERR_DTYPE, "dtype %d is neither SSD_F32 (0) nor SSD_BF16 (1)", sh->dtype);
+    if (sh->ydtype != SSD_F32 && sh->ydtype != SSD_BF16)
+        return fail(SSD_ERR_DTYPE, "ydtype %d is neither SSD_F32 (0) nor SSD_BF16 (1)", sh->ydtype);
+    if (sh->reserved != 0) return fail(SSD_ERR_SHAPE, "reserved must be 0");
+    if (sh->activation != 0 && sh->activation != 1)
+        return fail(SSD_ERR_VALUE, "activation %d is neither 0 (none) nor 1 (SiLU)", sh->activation);
+    if (sh->channels < 8 || sh->channels > kMaxConvChannels || sh->channels % 8 != 0)
+        return fail(SSD_ERR_SHAPE, "channels %d must be a multiple of 8 in [8, 2^20]", sh->channels);
+    if (sh->width < 2 || sh->width > 4) return fail(SSD_ERR_SHAPE, "width %d must be in [2, 4]", sh->width);
+    if (sh->batch < 0 || sh->batch > (1 << 24)) return fail(SSD_ERR_SHAPE, "batch must be in [0, 2^24]");
+    const bool packed = !step && sh->cu_seqlens != nullptr;
+    if (!step && sh->seqlen < 0) return fail(SSD_ERR_SHAPE, "seqlen must be >= 0");
+    const int64_t rows = step ? sh->batch : packed ? sh->seqlen : sh->batch * sh->seqlen;
+    if (rows > ((int64_t)1 << 31) || rows * (int64_t)sh->channels > ((int64_t)1 << 40))
+        return fail(SSD_ERR_SHAPE, "tensor too large");
+    if (!step) {
+        if (!packed && sh->cu_seqlens_host)
+            return fail(SSD_ERR_SHAPE, "cu_seqlens_host given without the device cu_seqlens");
+        if (packed && sh->cu_seqlens_host) {
+            const ssd_status st = check_cu_host(sh->cu_seqlens_host, sh->batch, rows);
+            if (st != SSD_OK) return st;
+        }
+    }
+    if (out->nparts < 1 || out->nparts > 3) return fail(SSD_ERR_SHAPE, "nparts %d must be 1, 2 or 3", out->nparts);
+    int64_t sum = 0;
+    for (int p = 0; p < 3; ++p) {
+        if (p >= out->nparts) {
+            if (out->channels[p] != 0 || out->out[p] != nullptr)
+                return fail(SSD_ERR_SHAPE, "unused output part %d must be 0 / NULL", p);
+            continue;
+        }
+        if (out->channels[p] < 8 || out->channels[p] % 8 != 0)
+            return fail(SSD_ERR_SHAPE, "output part %d has %d channels (a positive multiple of 8 is needed)", p,
+                        out->channels[p]);
+        sum += out->channels[p];
+        if (!out->out[p] && rows > 0) return fail(SSD_ERR_NULL, "output part %d is NULL", p);
+        if (!aligned16(out->out[p])) return fail(SSD_ERR_ALIGN, "output part %d is not 16-byte aligned", p);
+    }
+    if (sum != sh->channels)
+        return fail(SSD_ERR_SHAPE, "output parts hold %lld channels, not %d", (long long)sum, sh->channels);
+    if (!weight) return fail(SSD_ERR_NULL, "weight is NULL");
+    if (!x && rows > 0) return fail(SSD_ERR_NULL, "x is NULL");
+    struct {
+        const void* p;
+        const char* name;
+    } in[] = {{x, "x"}, {weight, "weight"}, {bias, "bias"}};
+    for (auto& q : in)
+        if (q.p && !aligned16(q.p)) return fail(SSD_ERR_ALIGN, "%s is not 16-byte aligned", q.name);
+    for (int p = 0; p < out->nparts; ++p)
+        for (auto& q : in)
+            if (q.p && out->out[p] == q.p) return fail(SSD_ERR_SHAPE, "output part %d aliases %s", p, q.name);
+    a->x = x;
+    a->weight = weight;
+    a->bias = bias;
+    a->state_in = nullptr;
+    a->state_out = nullptr;
+    a->cu = packed ? sh->cu_seqlens : nullptr;
+    for (int p = 0; p < 3; ++p) {
+        a->out[p] = out->out[p];
+        a->part_ch[p] = out->channels[p];
+    }
+    a->nparts = out->nparts;
+    a->nseq = sh->batch;
+    a->L = step ? 1 : (packed ? 0 : sh->seqlen);
+    a->T = rows;
+    a->C = sh->channels;
+    a->K = sh->width;
+    a->dtype = sh->dtype;
+    a->y_f32 = sh->ydtype == SSD_F32 ? 1 : 0;
+    a->silu = sh->activation;
+    return SSD_OK;
+}
+
+bool aliases_output(const ssd_conv_outputs* out, const void* p) {
+    for (int q = 0; q < out->nparts; ++q)
+        if (p && out->out[q] == p) return true;
+    return false;
+}
+
+}  // namespace
+
+SSD_API ssd_status ssd_causal_conv1d(const void* x, const float* weight, const float* bias,
+                                     const void* conv_state_in, void* conv_state_out,
+                                     const ssd_conv_outputs* out, const ssd_conv_shape* shape, void* stream) {
+    ssd::ConvArgs a;
+    ssd_status st = conv_prepare(x, weight, bias, out, shape, false, &a);
+    if (st != SSD_OK) return st;
+    if (shape->cu_seqlens && shape->batch == 0 && a.T > 0)
+        return fail(SSD_ERR_SHAPE, "packed rows without sequences");
+    if (conv_state_in && !aligned16(conv_state_in)) return fail(SSD_ERR_ALIGN, "conv_state_in is not 16-byte aligned");
+    if (conv_state_out && !aligned16(conv_state_out))
+        return fail(SSD_ERR_ALIGN, "conv_state_out is not 16-byte aligned");
+    if (aliases_output(out, conv_state_in) || aliases_output(out, conv_state_out))
+        return fail(SSD_ERR_SHAPE, "an output part aliases a conv state");
+    if (conv_state_out && (conv_state_out == x || conv_state_out == (const void*)weight ||
+                           conv_state_out == (const void*)bias))
+        return fail(SSD_ERR_SHAPE, "conv_state_out aliases an input");
+    a.state_in = conv_state_in;
+    a.state_out = conv_state_out;
+    const hipError_t err = ssd::launch_conv1d(a, (hipStream_t)stream);
+    if (err != hipSuccess) return fail(SSD_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(err));
+    return ok();
+}
+
+SSD_API ssd_status ssd_causal_conv1d_step(void* conv_state, const void* x, const float* weight, const float* bias,
+                                          const ssd_conv_outputs* out, const ssd_conv_shape* shape,
+                                          void* stream) {
+    ssd::ConvArgs a;
+    ssd_status st = conv_prepare(x, weight, bias, out, shape, true, &a);
+    if (st != SSD_OK) return st;
+    if (!conv_state && a.nseq > 0) return fail(SSD_ERR_NULL, "conv_state is NULL");
+    if (!aligned16(conv_state)) return fail(SSD_ERR_ALIGN, "conv_state is not 16-byte aligned");
+    if (aliases_output(out, conv_state) || (conv_state && (conv_state == x || conv_state == (const void*)weight ||
+                                                          conv_state == (const void*)bias)))
+        return fail(SSD_ERR_SHAPE, "conv_state aliases another argument");
+    a.state_out = conv_state;
+    const hipError_t err = ssd::launch_conv1d_step(a, (hipStream_t)stream);
+    if (err != hipSuccess) return fail(SSD_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(err));
+    return ok();
+}

@@ -101,6 +101,21 @@ struct WindowArgs {
     DtAct act;
 };
 
+struct ConvArgs {
+    const void* x;           // [rows, C]
+    const float* weight;     // [C, K]
+    const float* bias;       // [C] or NULL
+    const void* state_in;    // [nseq, K-1, C] or NULL
+    void* state_out;         // [nseq, K-1, C] or NULL (the step: the state, in place)
+    const int32_t* cu;       // device [nseq+1] or NULL (dense)
+    void* out[3];            // output parts [rows, part_ch[p]]
+    int32_t part_ch[3];
+    int32_t nparts;
+    int64_t nseq, L, T;      // sequences, dense length, total rows
+    int32_t C, K;
+    int32_t dtype, y_f32, silu;
+};
+
 // dstate padded to the 32-row tiles the kernels use.
 inline int padded_dstate(int N) { return N <= 32 ? 32 : N <= 64 ? 64 : N <= 128 ? 128 : 256; }
 
@@ -120,5 +135,11 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 
 // Queue the windowed decode kernel (window <= 16).
 hipError_t launch_decode_window(const WindowArgs& a, hipStream_t stream);
+
+// Queue the conv1d prefill (and the final-state pass when a.state_out is set).
+hipError_t launch_conv1d(const ConvArgs& a, hipStream_t stream);
+
+// Queue the conv1d decode step (state in a.state_out, updated in place).
+hipError_t launch_conv1d_step(const ConvArgs& a, hipStream_t stream);
 
 }  // namespace ssd

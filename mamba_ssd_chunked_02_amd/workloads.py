@@ -193,3 +193,43 @@ def small_workload(*, batch=1, seqlen=0, seqlens=None, H=4, P=16, N=16, G=1, chu
                     P=P, N=N, G=G, dtype=dtype, batch=batch, seqlen=seqlen,
                     seqlens=None if seqlens is None else tuple(seqlens), chunk=chunk,
                     init_var=init_var, decode_steps=decode_steps, decode_batch=decode_batch)
+
+
+# ---------------------------------------------------------------- conv1d inputs
+@dataclasses.dataclass
+class ConvInputs:
+    """Host inputs of the causal conv1d (fp32 arrays holding exactly the values
+    the GPU receives)."""
+    x: np.ndarray                     # [b, L, C] dense or [T, C] packed
+    weight: np.ndarray                # [C, K]
+    bias: Optional[np.ndarray]        # [C]
+    state: Optional[np.ndarray]       # [nseq, K-1, C]
+    cu_seqlens: Optional[np.ndarray]  # int32 [nseq+1] when packed
+
+
+def conv_inputs(seed: int, *, C: int, K: int = 4, batch: int = 1, seqlen: int = 0,
+                seqlens: Optional[Sequence[int]] = None, dtype: str = "bf16", bias: bool = True,
+                state: bool = True) -> ConvInputs:
+    """Draw conv1d inputs.  x and the incoming states ~ N(0,1); weight and
+    bias ~ U(-1/sqrt(K), 1/sqrt(K)) (the usual fan-in bound of a depthwise
+    conv).  Draw order: x, weight, bias, state.  Dense [batch, seqlen, C]
+    unless ``seqlens`` is given (packed [T, C] with cu_seqlens)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    if seqlens is not None:
+        cu = np.concatenate([[0], np.cumsum(seqlens)]).astype(np.int32)
+        lead = (int(cu[-1]),)
+        nseq = len(seqlens)
+    else:
+        cu = None
+        lead = (batch, seqlen)
+        nseq = batch
+    bound = np.float32(1.0 / math.sqrt(K))
+    x = _normal(rng, lead + (C,), 1.0)
+    w = rng.uniform(-bound, bound, size=(C, K)).astype(np.float32)
+    b = rng.uniform(-bound, bound, size=C).astype(np.float32) if bias else None
+    st = _normal(rng, (nseq, K - 1, C), 1.0) if state else None
+    if dtype == "bf16":
+        x = round_bf16(x)
+        if st is not None:
+            st = round_bf16(st)
+    return ConvInputs(x, w, b, st, cu)

@@ -34,7 +34,8 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ["ssd_chunked_scan", "ssd_decode_step", "ssd_chunked_scan_workspace_size",
               "ssd_status_string", "ssd_last_error_detail", "ssd_chunked_scan_dt_act",
-              "ssd_decode_step_dt_act"]:
+              "ssd_decode_step_dt_act", "ssd_decode_window_step", "ssd_causal_conv1d",
+              "ssd_causal_conv1d_step"]:
         assert n in names
 
 
@@ -228,3 +229,93 @@ def test_window_step_errors(lib):
     a = ssd._DtAct()
     a.dt_bias, a.dt_min, a.dt_max = None, -1.0, 1.0
     assert win(act=ctypes.byref(a)) == E_VALUE
+
+
+def conv_shape(**kw):
+    s = ssd._ConvShape()
+    d = dict(batch=2, seqlen=100, channels=64, width=4, dtype=1, ydtype=1, activation=1, reserved=0)
+    d.update(kw)
+    for k, v in d.items():
+        setattr(s, k, v)
+    return s
+
+
+def conv_outs(parts=(64,), base=FAKE + 4096):
+    o = ssd._ConvOutputs()
+    o.nparts = len(parts)
+    for i, c in enumerate(parts):
+        o.channels[i] = c
+        o.out[i] = base + 1024 * i
+    return o
+
+
+def test_conv1d_argument_errors(lib):
+    X, Wt, Bs, S0, S1 = FAKE, FAKE + 16, FAKE + 32, FAKE + 48, FAKE + 64
+
+    def conv(x=X, w=Wt, b=Bs, s0=S0, s1=S1, out=None, sh=None):
+        out = conv_outs() if out is None else out
+        sh = conv_shape() if sh is None else sh
+        return lib.ssd_causal_conv1d(x, w, b, s0, s1, ctypes.byref(out), ctypes.byref(sh), None)
+
+    def step(state=S0, x=X, w=Wt, b=Bs, out=None, sh=None):
+        out = conv_outs() if out is None else out
+        sh = conv_shape() if sh is None else sh
+        return lib.ssd_causal_conv1d_step(state, x, w, b, ctypes.byref(out), ctypes.byref(sh), None)
+
+    assert lib.ssd_causal_conv1d(X, Wt, Bs, S0, S1, None, ctypes.byref(conv_shape()), None) == E_NULL
+    assert lib.ssd_causal_conv1d(X, Wt, Bs, S0, S1, ctypes.byref(conv_outs()), None, None) == E_NULL
+    for f in (conv, step):
+        assert f(sh=conv_shape(dtype=2)) == E_DTYPE
+        assert f(sh=conv_shape(ydtype=-1)) == E_DTYPE
+        assert f(sh=conv_shape(activation=2)) == E_VALUE
+        assert f(sh=conv_shape(reserved=1)) == E_SHAPE
+        for c in (0, 4, 12, 2 ** 20 + 8):
+            assert f(sh=conv_shape(channels=c), out=conv_outs((max(c, 8),))) == E_SHAPE, c
+        for k in (0, 1, 5):
+            assert f(sh=conv_shape(width=k)) == E_SHAPE, k
+        assert f(sh=conv_shape(batch=-1)) == E_SHAPE
+        # output parts: count, sizes, sum, unused entries, NULL, alignment, aliasing
+        o = conv_outs(); o.nparts = 0
+        assert f(out=o) == E_SHAPE
+        assert f(out=conv_outs((32, 24))) == E_SHAPE      # sums to 56, not 64
+        assert f(out=conv_outs((60, 4))) == E_SHAPE       # not multiples of 8
+        o = conv_outs((64,)); o.channels[1] = 8
+        assert f(out=o) == E_SHAPE
+        o = conv_outs((32, 32)); o.out[1] = None
+        assert f(out=o) == E_NULL
+        o = conv_outs((32, 32)); o.out[1] = FAKE + 4104
+        assert f(out=o) == E_ALIGN
+        o = conv_outs((64,)); o.out[0] = X
+        assert f(out=o) == E_SHAPE
+        assert f(w=None) == E_NULL
+        assert f(x=None) == E_NULL
+        assert f(x=X + 8) == E_ALIGN
+        assert f(w=Wt + 4) == E_ALIGN
+        assert f(b=Bs + 4) == E_ALIGN
+    # prefill-only checks: seqlen, packed offsets, state alignment and aliasing
+    assert conv(sh=conv_shape(seqlen=-1)) == E_SHAPE
+    assert conv(s0=S0 + 8) == E_ALIGN
+    assert conv(s1=S1 + 8) == E_ALIGN
+    assert conv(s1=X) == E_SHAPE
+    o = conv_outs((64,)); o.out[0] = S1
+    assert conv(out=o) == E_SHAPE
+    sh = conv_shape(batch=3, seqlen=10)
+    host = (ctypes.c_int32 * 4)(0, 4, 3, 10)
+    sh.cu_seqlens = FAKE + 256
+    sh.cu_seqlens_host = ctypes.addressof(host)
+    assert conv(sh=sh) == E_SEQ
+    host2 = (ctypes.c_int32 * 4)(0, 4, 6, 9)
+    sh.cu_seqlens_host = ctypes.addressof(host2)
+    assert conv(sh=sh) == E_SEQ
+    sh = conv_shape(batch=0, seqlen=10)
+    sh.cu_seqlens = FAKE + 256
+    assert conv(sh=sh) == E_SHAPE
+    sh = conv_shape()
+    sh.cu_seqlens_host = ctypes.addressof(host2)
+    assert conv(sh=sh) == E_SHAPE
+    # step-only checks: the state pointer
+    assert step(state=None) == E_NULL
+    assert step(state=S0 + 8) == E_ALIGN
+    assert step(state=X) == E_SHAPE
+    o = conv_outs((64,)); o.out[0] = S0
+    assert step(out=o) == E_SHAPE
