@@ -322,6 +322,9 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="leave out the reports beside the timed step (decode loop vs recompute, windowed\n"
+                         "decode, conv1d, fused dt activation); the timed step and its rooflines are unchanged")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic_chunk_scan_2p7b.txt"),
                     help="rocprofv3 FETCH_SIZE/WRITE_SIZE summary of the dominant kernel")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -427,8 +430,8 @@ def main():
         a1.synchronize()
         return a0.elapsed_time(a1) / args.steps
 
-    plain_b2b_ms = back_to_back(False)
-    act_ms = back_to_back(True)
+    plain_b2b_ms = back_to_back(False) if not args.no_extras else None
+    act_ms = back_to_back(True) if not args.no_extras else None
     del raw
 
     # per-kernel durations: the same prefill through the measuring entry point
@@ -514,12 +517,14 @@ def main():
     copy_gbs = 2 * state.numel() * 4 / (copy_ms * 1e-3) / 1e9
     del src, dst
 
-    log("cached decode vs full-prefix recompute")
-    dvr = decode_vs_recompute(torch, ssd)
-    log("windowed exact decode vs ordinary decode")
-    dwin = decode_window(torch, ssd, wd)
-    log("causal conv1d")
-    dconv = conv1d_measure(torch, ssd, wl, wd)
+    dvr = dwin = dconv = None
+    if not args.no_extras:
+        log("cached decode vs full-prefix recompute")
+        dvr = decode_vs_recompute(torch, ssd)
+        log("windowed exact decode vs ordinary decode")
+        dwin = decode_window(torch, ssd, wd)
+        log("causal conv1d")
+        dconv = conv1d_measure(torch, ssd, wl, wd)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -561,11 +566,11 @@ def main():
         "decode_vs_recompute": dvr,
         "decode_window": dwin,
         "conv1d": dconv,
-        "prefill_dt_activation": {"ms_per_step": round(act_ms, 4), "tokens_per_s": round(tokens / (act_ms * 1e-3), 1),
-                                  "plain_ms_per_step": round(plain_b2b_ms, 4),
-                                  "what": "same prefill through ssd_chunked_scan_dt_act (softplus fused into "
-                                          "the cumsum kernel) and through ssd_chunked_scan, back-to-back "
-                                          "calls each"},
+        "prefill_dt_activation": None if act_ms is None else {
+            "ms_per_step": round(act_ms, 4), "tokens_per_s": round(tokens / (act_ms * 1e-3), 1),
+            "plain_ms_per_step": round(plain_b2b_ms, 4),
+            "what": "same prefill through ssd_chunked_scan_dt_act (softplus fused into the cumsum kernel) "
+                    "and through ssd_chunked_scan, back-to-back calls each"},
         "tflops_contraction_kernels": round(contraction_tf, 2),
         "frac_bf16_peak_contraction_kernels": round(contraction_tf / BF16_PEAK_TFLOPS, 4),
         "roofline": roof,
