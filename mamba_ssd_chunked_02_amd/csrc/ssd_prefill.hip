@@ -126,13 +126,21 @@ __global__ __launch_bounds__(kThreads) void ssd_cumsum_kernel(Plan pl, const flo
     if (cd.seq < 0) return;
     const int Q = pl.Q, H = pl.H, h0 = blockIdx.y * kCumHeads;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    // thread (token q = tid/16 + 16i, head h0 + tid%16)
+    // thread (token q = tid/16 + 16i, head h0 + tid%16): all of its loads go
+    // out before any is used (indices clamped into the chunk, masked after)
     {
-        const int hh = tid % kCumHeads;
+        constexpr int QS = kThreads / kCumHeads;  // token stride
+        constexpr int PER = 256 / QS;             // tokens per thread for the largest chunk
+        const int hh = tid % kCumHeads, q0 = tid / kCumHeads;
+        const int hc = min(h0 + hh, H - 1);
         const bool hok = h0 + hh < H;
-        for (int q = tid / kCumHeads; q < Q; q += kThreads / kCumHeads) {
-            const bool ok = hok && q < cd.len;
-            sdt[hh * SP + q] = ok ? dt_activate(act, dt[(cd.row0 + q) * H + h0 + hh], h0 + hh) : 0.f;
+        float v[PER];
+#pragma unroll
+        for (int i = 0; i < PER; ++i) v[i] = dt[(cd.row0 + min(q0 + i * QS, cd.len - 1)) * H + hc];
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int q = q0 + i * QS;
+            if (q < Q) sdt[hh * SP + q] = (hok && q < cd.len) ? dt_activate(act, v[i], h0 + hh) : 0.f;
         }
     }
     __syncthreads();
@@ -161,13 +169,22 @@ __global__ __launch_bounds__(kThreads) void ssd_cumsum_kernel(Plan pl, const flo
         float* csr = cs + ((size_t)k * H + h) * Q;
         float* dtr = dtc + ((size_t)k * H + h) * Q;
         float* wsr = wst + ((size_t)k * H + h) * Q;
+        if (ppl == 4) {
+            // 256-token chunks: four consecutive positions per lane, 16-byte stores
+            const int q = 4 * lane;
+            *(f32x4*)(csr + q) = f32x4{c[0], c[1], c[2], c[3]};
+            *(f32x4*)(dtr + q) = f32x4{d[0], d[1], d[2], d[3]};
+            *(f32x4*)(wsr + q) = f32x4{__expf(last - c[0]) * d[0], __expf(last - c[1]) * d[1],
+                                       __expf(last - c[2]) * d[2], __expf(last - c[3]) * d[3]};
+        } else {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int q = lane * ppl + i;
-            if (i < ppl && q < Q) {
-                csr[q] = c[i];
-                dtr[q] = d[i];
-                wsr[q] = __expf(last - c[i]) * d[i];
+            for (int i = 0; i < 4; ++i) {
+                const int q = lane * ppl + i;
+                if (i < ppl && q < Q) {
+                    csr[q] = c[i];
+                    dtr[q] = d[i];
+                    wsr[q] = __expf(last - c[i]) * d[i];
+                }
             }
         }
     }
