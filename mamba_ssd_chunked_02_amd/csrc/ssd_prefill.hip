@@ -284,6 +284,110 @@ __global__ __launch_bounds__(64) void ssd_cb_kernel(Plan pl, const T* __restrict
     }
 }
 
+// Whole-chunk variant, grid (chunks, G), four waves: the chunk's B rows are
+// staged once in LDS ([token][n], pitch NT + EPC, zero past the chunk end and
+// past N) and wave w computes the causal tiles of output blocks w and
+// NTI-1-w (nine 32 x 32 tiles each for 256-token chunks), with its C rows in
+// registers and the B operand read from LDS.  The products, their operand
+// order and the stored values are those of ssd_cb_kernel; B^T fragments are
+// read from the staged rows.  Used when the staged chunk fits in LDS.
+template <typename T>
+__host__ __device__ constexpr size_t cb_chunk_lds_bytes(int NT, int Q) {
+    return (size_t)Q * (NT + 16 / sizeof(T)) * sizeof(T) + (size_t)4 * 32 * (32 + 16 / sizeof(T)) * sizeof(T);
+}
+
+template <typename T, int NT>
+__global__ __launch_bounds__(256) void ssd_cb_chunk_kernel(Plan pl, const T* __restrict__ B, const T* __restrict__ C,
+                                                          T* __restrict__ cb, T* __restrict__ bt) {
+    extern __shared__ __align__(16) char smem[];
+    constexpr int EPC = 16 / sizeof(T);
+    constexpr int BP = NT + EPC, TP = 32 + EPC;
+    typedef typename Tr<T>::v8 v8;
+    const int k = blockIdx.x, g = blockIdx.y;
+    const ChunkDesc cd = uniform_desc(chunk_desc(pl, k));
+    if (cd.seq < 0) return;
+    const int Q = pl.Q, N = pl.N, G = pl.G, NTI = Q / 32;
+    const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63, half = lane >> 5, col = lane & 31;
+    T* bs = (T*)smem;
+    T* ls = bs + (size_t)Q * BP + wave * 32 * TP;
+    // output blocks of this wave: w and NTI-1-w
+    const int b0 = wave, b1 = NTI - 1 - wave;
+    const bool do0 = b0 < NTI && b0 <= b1, do1 = b1 > b0;
+    // C rows of both blocks, then the chunk's B rows: every load goes out first
+    auto load_c = [&](int ti, v8 (&a)[NT / 16]) {
+        const int t = 32 * ti + col;
+        const T* crow = C + ((cd.row0 + (t < cd.len ? t : 0)) * G + g) * N;
+#pragma unroll
+        for (int s = 0; s < NT / 16; ++s) {
+            const int n = 16 * s + 8 * half;
+            a[s] = Tr<T>::ld8(crow + (n < N ? n : 0));
+        }
+#pragma unroll
+        for (int s = 0; s < NT / 16; ++s)
+            if (!(t < cd.len && 16 * s + 8 * half < N)) a[s] = v8{};
+    };
+    v8 a0[NT / 16], a1[NT / 16];
+    if (do0) load_c(b0, a0);
+    if (do1) load_c(b1, a1);
+    {
+        // piece c = 256 i + tid is 8 elements (token c / PR, n = 8 (c % PR));
+        // batches of 8 loads go out before their LDS writes
+        constexpr int PR = NT / 8;  // pieces per staged row; PR rounds of 256 cover 256 tokens
+        constexpr int BATCH = PR < 8 ? PR : 8;
+#pragma unroll
+        for (int i0 = 0; i0 < PR; i0 += BATCH) {
+            v8 v[BATCH];
+#pragma unroll
+            for (int u = 0; u < BATCH; ++u) {
+                const int c = 256 * (i0 + u) + tid, t = c / PR, n = 8 * (c % PR);
+                const bool ok = t < cd.len && n < N;
+                v[u] = Tr<T>::ld8(B + ((cd.row0 + (ok ? t : 0)) * G + g) * N + (ok ? n : 0));
+            }
+#pragma unroll
+            for (int u = 0; u < BATCH; ++u) {
+                const int c = 256 * (i0 + u) + tid, t = c / PR, n = 8 * (c % PR);
+                if (t < Q) Tr<T>::st8(bs + t * BP + n, (t < cd.len && n < N) ? v[u] : v8{});
+            }
+        }
+    }
+    __syncthreads();
+    auto tiles = [&](int ti, const v8 (&a)[NT / 16]) {
+        for (int kj = 0; kj <= ti; ++kj) {
+            const T* brow = bs + (32 * kj + col) * BP + 8 * half;
+            f32x16 acc = {};
+#pragma unroll
+            for (int s = 0; s < NT / 16; ++s) mma16(acc, a[s], Tr<T>::ld8(brow + 16 * s));
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int r = acc_row(v, lane);
+                const float e = acc[v];
+                ls[r * TP + col] = (T)((kj < ti || col <= r) ? e : 0.f);
+            }
+            T* out = cb + ((size_t)k * G + g) * Q * Q + (size_t)(32 * ti) * Q + 32 * kj;
+#pragma unroll
+            for (int i = 0; i < 32 * 32 / EPC / 64; ++i) {
+                const int c = i * 64 + lane, r = c / (32 / EPC), c0 = (c % (32 / EPC)) * EPC;
+                *(u32x4*)(out + (size_t)r * Q + c0) = *(const u32x4*)(ls + r * TP + c0);
+            }
+        }
+    };
+    if (do0) tiles(b0, a0);
+    if (do1) tiles(b1, a1);
+    // B^T fragments: n-tiles wave, wave + 4, ... of every 16-token step
+    T* btk = bt + ((size_t)k * G + g) * NT * Q;
+    for (int nt = wave; nt < NT / 32; nt += 4) {
+        const int n = 32 * nt + col;
+        for (int st = 0; st < 2 * NTI; ++st) {
+            const int t0 = 16 * st + 8 * half;
+            v8 bv;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) bv[j] = bs[(t0 + j) * BP + n];
+            Tr<T>::st8(btk + bt_frag(Q, nt, st, lane), bv);
+        }
+    }
+}
+
 // ------------------------------------------------------------------ shared pieces
 // Operand precision.  x, B, C are exact in their dtype.  Three products are
 // rounded to the operand dtype: C.B^T (once, by the cb kernel), x scaled by a
@@ -1066,7 +1170,6 @@ __device__ __forceinline__ void scan_wave(const Plan& pl, const Item& it, const 
         }
     }
     const int HP = H * P;
-    const int p = 32 * pt + col;
     const __amdgpu_buffer_rsrc_t ry = buffer_rsrc(y + cd.row0 * HP, (uint32_t)(cd.len * HP * sizeof(TY)));
     // per-head inputs, loaded one head ahead by the staging waves
     TabIn tin;
@@ -1214,9 +1317,17 @@ hipError_t run_prefill(const Plan& pl, const Layout& lay, const ScanArgs& a, hip
     }
     if ((err = mark(2)) != hipSuccess) return err;
     if (pl.nchunk_ub > 0) {
-        auto* k1 = ssd_cb_kernel<T, NT>;
-        hipLaunchKernelGGL(k1, dim3(pl.nchunk_ub, pl.G, NTI * (NTI + 1) / 2), dim3(64), cb_lds_bytes<T>(NT),
-                           stream, pl, B, C, cbm, bt);
+        if (cb_chunk_lds_bytes<T>(NT, Q) <= 160 * 1024) {
+            auto* k1 = ssd_cb_chunk_kernel<T, NT>;
+            const size_t lds = cb_chunk_lds_bytes<T>(NT, Q);
+            if ((err = allow_lds(k1, lds)) != hipSuccess) return err;
+            hipLaunchKernelGGL(k1, dim3(pl.nchunk_ub, pl.G), dim3(256), lds, stream, pl, B, C, cbm, bt);
+        } else {
+            // the staged chunk would not fit (fp32, dstate > 128, 256-token chunks)
+            auto* k1 = ssd_cb_kernel<T, NT>;
+            hipLaunchKernelGGL(k1, dim3(pl.nchunk_ub, pl.G, NTI * (NTI + 1) / 2), dim3(64), cb_lds_bytes<T>(NT),
+                               stream, pl, B, C, cbm, bt);
+        }
         if ((err = hipGetLastError()) != hipSuccess) return err;
     }
     if ((err = mark(3)) != hipSuccess) return err;

@@ -74,6 +74,8 @@ SMALL = [
     (1, 513, 2, 64, 256, 1, 128, "bf16", 0.1),
     (1, 96, 2, 64, 256, 1, 32, "bf16", 0.1),
     (1, 160, 2, 128, 128, 2, 32, "bf16", 0.1),
+    (1, 300, 2, 32, 256, 1, 256, "f32", 0.1),
+    (2, 290, 2, 64, 256, 1, 256, "bf16", 0.1),
 ]
 
 
