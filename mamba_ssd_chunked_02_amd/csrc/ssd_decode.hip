@@ -152,7 +152,7 @@ constexpr int kWinMax = 16;
 constexpr int kWinPitch = kWinMax + 4;  // floats per x row of the window in LDS (16-byte aligned rows)
 
 // Every step streams the state block once for y (and, with FLUSH, writes the
-// new state in the same pass).  The prologue reduces the window to per-lane
+// new state in the same pass), with the streaming cache hint on its loads.  The prologue reduces the window to per-lane
 // constants: C_t, the decay exp(cs_t), y's intra-window part per row (LDS) and,
 // with FLUSH, u_s = exp(cs_t - cs_s) dt_s B_s and the window's x rows
 // (LDS, one row of W values per p).  Rows are streamed as in the decode step:
@@ -192,7 +192,8 @@ __global__ __launch_bounds__(kDecThreads, FLUSH ? 2 : (sizeof(T) == 2 ? 4 : 3)) 
 #pragma unroll
         for (int u = 0; u < kBatch; ++u) {
             const int p = min(p0 + u * RPI + rsub, P - 1);
-            dst[u] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (p * N + n) * 4, 0, 0));
+            dst[u] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (p * N + n) * 4, 0,
+                                                                                   kNonTemporal));
         }
     };
     // the first state rows go out first: their latency covers the window set-up
