@@ -34,6 +34,21 @@ __device__ inline f32x8 ld_row8(const T* p) {
     return Tr<T>::widen(Tr<T>::ld8(p));
 }
 
+// Eight channels of x with the streaming cache hint (x is read once; only the
+// K-1 rows before a block are read again, by that block).
+template <typename T>
+__device__ inline typename Tr<T>::v8 ld_stream8(const T* p);
+template <>
+__device__ inline bf16x8 ld_stream8<bf16_t>(const bf16_t* p) {
+    return __builtin_bit_cast(bf16x8, __builtin_nontemporal_load((const f32x4*)p));
+}
+template <>
+__device__ inline f32x8 ld_stream8<float>(const float* p) {
+    const f32x4 a = __builtin_nontemporal_load((const f32x4*)p);
+    const f32x4 b = __builtin_nontemporal_load((const f32x4*)(p + 4));
+    return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
 template <typename Y>
 __device__ inline void st_row8(Y* p, f32x8 v);
 template <>
@@ -172,7 +187,7 @@ __global__ __launch_bounds__(kConvThreads) void ssd_conv1d_kernel(ConvArgs a) {
     typename Tr<T>::v8 cur[kRowBatch], nxt[kRowBatch];
     auto load = [&](int64_t rb, typename Tr<T>::v8 (&dst)[kRowBatch]) {
 #pragma unroll
-        for (int u = 0; u < kRowBatch; ++u) dst[u] = Tr<T>::ld8(xb + min(rb + u, r1 - 1) * a.C);
+        for (int u = 0; u < kRowBatch; ++u) dst[u] = ld_stream8<T>(xb + min(rb + u, r1 - 1) * a.C);
     };
     // A batch of rows with no sequence start and no block end inside takes
     // the straight path; the others check every row.
