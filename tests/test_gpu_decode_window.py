@@ -25,6 +25,7 @@ def say(*a):
     ("f32", 32, 64, 2, 5, False),
     ("bf16", 24, 40, 3, 1, False),
     ("f32", 64, 128, 2, 16, True),
+    ("bf16", 128, 256, 1, 16, False),
 ])
 def test_window_session_matches_sequential_decode(dtype, P, N, G, window, act):
     steps = 2 * window + 3 if window > 1 else 4  # two full windows and a partial one
@@ -80,3 +81,26 @@ def test_window_step_without_flush_leaves_state_unchanged():
                          tdev(inp.D))
     torch.cuda.synchronize()
     assert_close(host(y), host(y1).astype(np.float64), "f32", "window of one vs decode step")
+
+
+def test_window_step_bf16_output_is_the_rounded_fp32_output():
+    """y in bf16 is the same kernel's fp32 y rounded to nearest even, for a
+    read-only and a flush step."""
+    wl = W.small_workload(batch=3, seqlen=0, H=4, P=64, N=128, G=1, dtype="bf16", init_var=0.1,
+                          decode_steps=4, decode_batch=3)
+    inp = W.generate(wl, 71)
+    W_ = 4
+    xw = torch.stack([tdev(d["x"], "bf16") for d in inp.decode], dim=1).contiguous()
+    dtw = torch.stack([tdev(d["dt"]) for d in inp.decode], dim=1).contiguous()
+    Bw = torch.stack([tdev(d["B"], "bf16") for d in inp.decode], dim=1).contiguous()
+    Cw = torch.stack([tdev(d["C"], "bf16") for d in inp.decode], dim=1).contiguous()
+    A, D = tdev(inp.A), tdev(inp.D)
+    for t, flush in ((1, False), (W_ - 1, True)):
+        s32 = tdev(inp.init)
+        s16 = tdev(inp.init)
+        y32 = ssd.decode_window_step(s32, xw, dtw, A, Bw, Cw, D, t, flush)
+        y16 = ssd.decode_window_step(s16, xw, dtw, A, Bw, Cw, D, t, flush, y_dtype=torch.bfloat16)
+        torch.cuda.synchronize()
+        assert y16.dtype == torch.bfloat16
+        assert torch.equal(y16, y32.to(torch.bfloat16)), (t, flush)
+        assert torch.equal(s16, s32)
