@@ -268,14 +268,18 @@ def conv1d_measure(torch, ssd, wl, wd, reps=20):
                     "decode step b%d; bf16 in/out, eager back-to-back" % (C, b, L, bd)}
 
 
+# the sources that define and launch the prefill kernels (the counters in the
+# traffic summary describe those kernels only)
+PREFILL_SOURCES = ("ssd_api.cpp", "ssd_device.h", "ssd_internal.h", "ssd_prefill.hip")
+
+
 def _source_digest():
-    """sha256 of the kernel sources, to tell whether counters are stale."""
+    """sha256 of the prefill kernel sources, to tell whether counters are stale."""
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "mamba_ssd_chunked_02_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
-        if f.endswith((".hip", ".h", ".cpp")):
-            h.update(open(os.path.join(csrc, f), "rb").read())
+    for f in PREFILL_SOURCES:
+        h.update(open(os.path.join(csrc, f), "rb").read())
     return h.hexdigest()[:16]
 
 

@@ -61,14 +61,17 @@ __device__ inline void st_row8<float>(float* p, f32x8 v) {
     __builtin_nontemporal_store(__builtin_shufflevector(v, v, 4, 5, 6, 7), (f32x4*)(p + 4));
 }
 
-// First row, end row of sequence s.
+// First row, end row of sequence s.  Device offsets are clamped into
+// [0, T] with the end no earlier than the start (an offset list that
+// decreases or leaves the stream makes that sequence empty), so no row or
+// state index derived from them leaves its array.
 __device__ inline void seq_rows(const ConvArgs& a, int64_t s, int64_t& r0, int64_t& r1) {
     if (!a.cu) {
         r0 = s * a.L;
         r1 = r0 + a.L;
     } else {
-        r0 = a.cu[s];
-        r1 = a.cu[s + 1];
+        r0 = min(max((int64_t)a.cu[s], (int64_t)0), a.T);
+        r1 = min(max((int64_t)a.cu[s + 1], r0), a.T);
     }
 }
 
@@ -178,9 +181,11 @@ __global__ __launch_bounds__(kConvThreads) void ssd_conv1d_kernel(ConvArgs a) {
     seq_rows(a, s, sb, se);
 #pragma unroll
     for (int j = 0; j < K - 1; ++j) {
-        const int64_t i = r0 - sb + j;  // padded index of the j-th previous input
-        hist[j] = i < K - 1 ? (a.state_in ? ld_row8((const T*)a.state_in + (s * (K - 1) + i) * a.C + c0)
-                                          : f32x8{})
+        // padded index of the j-th previous input (negative only when the
+        // offsets are invalid and r0 lies outside every sequence)
+        const int64_t i = r0 - sb + j;
+        hist[j] = i < K - 1 ? ((a.state_in && i >= 0) ? ld_row8((const T*)a.state_in + (s * (K - 1) + i) * a.C + c0)
+                                                     : f32x8{})
                             : ld_row8(xb + (r0 + j - (K - 1)) * a.C);
     }
 
