@@ -17,6 +17,15 @@ namespace ssd {
 namespace {
 
 constexpr int kDecThreads = 256;  // four waves, one (sequence, head) state block each
+
+// dt_activate with the head's bias already loaded (0 when there is none), so
+// the kernel can issue that load together with its others.
+__device__ inline float dt_activate_b(const DtAct& a, float raw, float bias) {
+    if (!a.on) return raw;
+    const float v = raw + bias;
+    const float sp = v > 20.f ? v : log1pf(expf(v));
+    return fminf(fmaxf(sp, a.lo), a.hi);
+}
 constexpr int kBatch = 8;         // 128-bit state loads in flight per lane
 
 // Sum over aligned groups of TPR lanes with DPP moves (no LDS): quad swaps,
@@ -68,11 +77,6 @@ __global__ __launch_bounds__(kDecThreads) void ssd_decode_kernel(
     const int j = lane % TPR, rsub = lane / TPR;
     const bool nv = 4 * j < N;
     const int n = nv ? 4 * j : N - 4;
-    const float d = dt_activate(act, dt[bh], h);
-    const float a = __expf(d * A[h]);
-    const float Dh = D[h];
-    const f32x4 bv = nv ? Tr<T>::ld4(B + (b * G + g) * N + n) : f32x4{};
-    const f32x4 cv = nv ? Tr<T>::ld4(C + (b * G + g) * N + n) : f32x4{};
     float* sb = state + bh * P * N;
     const T* xb = x + bh * P;
     const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(sb, (uint32_t)(P * N * sizeof(float)));
@@ -88,7 +92,17 @@ __global__ __launch_bounds__(kDecThreads) void ssd_decode_kernel(
             xd[u] = (float)xb[p];
         }
     };
+    // the first state rows go out first; then every per-step operand, with
+    // no load waiting on another (B, C columns clamped in range, masked after)
     load(0, s, xv);
+    const float draw = dt[bh], Ah = A[h], Dh = D[h];
+    const float braw = *(act.bias ? act.bias + h : A + h);
+    const typename Tr<T>::v4 bq = Tr<T>::ld4raw(B + (b * G + g) * N + n);
+    const typename Tr<T>::v4 cq = Tr<T>::ld4raw(C + (b * G + g) * N + n);
+    const float d = dt_activate_b(act, draw, act.bias ? braw : 0.f);
+    const float a = __expf(d * Ah);
+    const f32x4 bv = nv ? Tr<T>::widen4(bq) : f32x4{};
+    const f32x4 cv = nv ? Tr<T>::widen4(cq) : f32x4{};
     for (int p0 = 0; p0 < P; p0 += RPB) {
         load(min(p0 + RPB, P - 1), sn, xn);  // next batch (repeats the last rows at the end)
 #pragma unroll
