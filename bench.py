@@ -335,7 +335,7 @@ def main():
                     help="only run a plain device copy of known size (for counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path (the scan shards "
+        print("bench.py measures one GPU only: the library has no multi-GPU path (the scan shards "
               "over independent (sequence, head) pairs with no exchange; see the design notes). "
               "Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)

@@ -7,8 +7,9 @@ shares no code with the GPU library (no kernels, headers, helpers or tables).
 Contents
 --------
 ``scan`` / ``decode``
-    The judged reference: the plain sequential fp64 recurrence, written in C
-    (``ssd_oracle.c``) and run with OpenMP over (sequence, head) pairs.  It
+    The reference the GPU results are compared with: the plain sequential fp64
+    recurrence, written in C (``ssd_oracle.c``) and run with OpenMP over
+    (sequence, head) pairs.  It
     follows the per-token recurrence of "Engineering hybrid state-space models"
     (innvotechnologies blog), section 2, with Abar = exp(dt*A) and the input
     term dt*B*x, plus the D skip term of the continuous SSM (lesty.tech Mamba
