@@ -64,10 +64,25 @@ int heads_per_workgroup(const ssd::Plan& pl, int64_t target, int64_t max_heads) 
 // Chunk states and the passing between chunks in one launch when there are
 // enough (sequence, head, column tile) walks to fill the chip: each walk is
 // sequential over its sequence's chunks, so with few of them the separate
-// kernels, parallel over chunks, finish first.
-bool fuse_state_passing(const ssd::Plan& pl) {
+// kernels, parallel over chunks, finish first.  A walk also lasts as long as
+// its sequence: when the host copy of a packed batch's offsets shows the
+// longest sequence with more than 1.5 times the mean chunk count of the
+// non-empty ones, the chunk-parallel kernels finish first too.
+bool fuse_state_passing(const ssd::Plan& pl, const ssd_shape* sh) {
     const int64_t npt = (pl.P + 31) / 32;
-    return (int64_t)pl.nseq * pl.H * npt >= kFusedMinWalks;
+    if ((int64_t)pl.nseq * pl.H * npt < kFusedMinWalks) return false;
+    if (!pl.dense && sh->cu_seqlens_host) {
+        const int32_t* cu = sh->cu_seqlens_host;
+        int64_t total = 0, longest = 0, nonempty = 0;
+        for (int64_t s = 0; s < pl.nseq; ++s) {
+            const int64_t nc = ((int64_t)cu[s + 1] - cu[s] + pl.Q - 1) / pl.Q;
+            total += nc;
+            longest = std::max(longest, nc);
+            nonempty += nc > 0;
+        }
+        if (nonempty > 0 && 2 * longest * nonempty > 3 * total) return false;
+    }
+    return true;
 }
 
 ssd_status check_head_dims(const ssd_shape* sh) {
@@ -251,7 +266,7 @@ ssd_status scan_impl(const void* x, const float* dt, const float* A, const void*
     a.y_f32 = shape->ydtype == SSD_F32 ? 1 : 0;
     a.hpw = heads_per_workgroup(pr.plan, kScanWorkgroups, pr.plan.hpg);
     a.hpw_state = heads_per_workgroup(pr.plan, kStateWorkgroups, kStateMaxHeads);
-    a.fused = fuse_state_passing(pr.plan) ? 1 : 0;
+    a.fused = fuse_state_passing(pr.plan, shape) ? 1 : 0;
     a.act = act ? *act : ssd::DtAct{nullptr, 0.f, 0.f, 0};
     if (fused_out) *fused_out = a.fused;
     pr.plan.seq_tab = (int32_t*)(a.ws + pr.lay.seq_tab);

@@ -236,6 +236,27 @@ def test_fused_walk_equals_separate_runs():
         assert_close(fin[s], host(fs)[0], "f32", "seq %d final" % s)
 
 
+@pytest.mark.parametrize("lens,walk", [((300, 280, 310, 290), True), ((64, 64, 64, 1000), False)],
+                         ids=["balanced", "one-long-sequence"])
+def test_state_path_follows_sequence_balance(lens, walk):
+    """With the host copy of the offsets, a packed batch takes the walk only
+    when no sequence has more than 1.5x the mean chunk count (the walk lasts
+    as long as the longest sequence); both choices match the oracle."""
+    wl = W.small_workload(seqlens=lens, H=32, P=64, N=64, G=2, chunk=64, dtype="bf16", init_var=0.1)
+    inp = W.generate(wl, 91)
+    say("case: state path for", lens)
+    g = to_gpu(inp)
+    st = []
+    y, fin = ssd.chunked_scan(g["x"], g["dt"], g["A"], g["B"], g["C"], g["D"], 64, init_state=g["init"],
+                              cu_seqlens=[int(v) for v in inp.cu_seqlens], stage_ms=st)
+    torch.cuda.synchronize()
+    took_walk = st[ssd.STAGES.index("state_passing")] == 0.0
+    assert took_walk == walk, st
+    yr, fr = oracle_scan(inp)
+    assert_close(host(y), yr, "bf16", "y")
+    assert_close(host(fin), fr, "bf16", "final")
+
+
 # ------------------------------------------------------------------ fused dt activation
 # Raw step sizes (softplus argument) with a per-head bias; the kernels apply
 # clamp(softplus(raw + bias), lo, hi) where dt enters (cumsum, decode) and the
