@@ -268,6 +268,52 @@ def conv1d_measure(torch, ssd, wl, wd, reps=20):
                     "decode step b%d; bf16 in/out, eager back-to-back" % (C, b, L, bd)}
 
 
+def other_prefill(torch, ssd, reps=20):
+    """Prefill throughput of the other two prefill configurations, through the
+    plain entry point: the 130M-shaped layer (b1 L4096 H24 P64 N128 G1) and
+    the packed grouped batch ({1024, 4096, 12288, 32768} tokens, H128 P64
+    N128 G8, offsets given with their host copy).  bf16 x/B/C, fp32 dt/A/D,
+    initial states ~N(0, 0.1), chunk 256; inputs drawn on the GPU."""
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device="cpu").manual_seed(23)
+    out = {}
+    for name, lens, H, G, dense in (("130m_layer_b1_L4096", [4096], 24, 1, True),
+                                    ("varlen_h128_g8_4seqs", [1024, 4096, 12288, 32768], 128, 8, False)):
+        P, N = 64, 128
+        T = sum(lens)
+        lead = (1, T) if dense else (T,)
+        x = torch.randn(*lead, H, P, generator=g).to(torch.bfloat16).to(dev)
+        dt = (torch.rand(*lead, H, generator=g) * 0.099 + 0.001).to(dev)
+        A = (-torch.exp(torch.rand(H, generator=g) * np.log(16.0))).to(dev)
+        B = (torch.randn(*lead, G, N, generator=g) / N ** 0.5).to(torch.bfloat16).to(dev)
+        C = (torch.randn(*lead, G, N, generator=g) / N ** 0.5).to(torch.bfloat16).to(dev)
+        D = torch.randn(H, generator=g).to(dev)
+        init = (torch.randn(len(lens), H, P, N, generator=g) * 0.1 ** 0.5).to(dev)
+        cu_host = None if dense else [0] + list(np.cumsum(lens))
+        cu = None if dense else torch.tensor(cu_host, dtype=torch.int32, device=dev)
+        y = torch.empty(tuple(x.shape), device=dev)
+        fin = torch.empty_like(init)
+        ws = torch.empty(ssd.workspace_size(x, B, 256, cu_seqlens=cu), dtype=torch.uint8, device=dev)
+
+        def run():
+            ssd.chunked_scan(x, dt, A, B, C, D, 256, init_state=init, cu_seqlens=cu, cu_seqlens_host=cu_host,
+                             y=y, final_state=fin, workspace=ws)
+        for _ in range(3):
+            run()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            run()
+        e1.record()
+        e1.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        out[name] = {"ms": round(ms, 4), "tokens_per_s": round(T / (ms * 1e-3), 1)}
+        del x, dt, B, C, y, ws
+    out["what"] = "plain-entry-point prefill, back-to-back calls, the other two prefill configurations"
+    return out
+
+
 # the sources that define and launch the prefill kernels (the counters in the
 # traffic summary describe those kernels only)
 PREFILL_SOURCES = ("ssd_api.cpp", "ssd_device.h", "ssd_internal.h", "ssd_prefill.hip")
@@ -521,7 +567,7 @@ def main():
     copy_gbs = 2 * state.numel() * 4 / (copy_ms * 1e-3) / 1e9
     del src, dst
 
-    dvr = dwin = dconv = None
+    dvr = dwin = dconv = dother = None
     if not args.no_extras:
         log("cached decode vs full-prefix recompute")
         dvr = decode_vs_recompute(torch, ssd)
@@ -529,6 +575,8 @@ def main():
         dwin = decode_window(torch, ssd, wd)
         log("causal conv1d")
         dconv = conv1d_measure(torch, ssd, wl, wd)
+        log("other prefill configurations")
+        dother = other_prefill(torch, ssd)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -570,6 +618,7 @@ def main():
         "decode_vs_recompute": dvr,
         "decode_window": dwin,
         "conv1d": dconv,
+        "other_prefill": dother,
         "prefill_dt_activation": None if act_ms is None else {
             "ms_per_step": round(act_ms, 4), "tokens_per_s": round(tokens / (act_ms * 1e-3), 1),
             "plain_ms_per_step": round(plain_b2b_ms, 4),
