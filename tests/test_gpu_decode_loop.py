@@ -8,6 +8,7 @@ import pytest
 import torch
 
 import oracle
+import mamba_ssd_chunked_02_amd as ssd
 from mamba_ssd_chunked_02_amd import workloads as W
 from mamba_ssd_chunked_02_amd.decode_loop import DecodeLoop
 from parity import assert_close, host, tdev
@@ -89,3 +90,44 @@ def test_consecutive_replays_advance_the_state():
         yk, ref = oracle.decode(ref, d["x"], d["dt"], inp.A, d["B"], d["C"], inp.D)
         assert_close(ys[j // steps][j % steps], yk, "f32", "y token %d" % j)
     assert_close(host(loop.state), ref, "f32", "state")
+
+
+@pytest.mark.parametrize("b,L,H", [(4, 300, 32), (2, 300, 4)], ids=["walk", "chunk-parallel"])
+def test_prefill_graph_replays_equal_eager(b, L, H):
+    """The prefill allocates, clears and synchronizes nothing, so it can be
+    captured in a HIP graph: every replay (with unrelated eager work and
+    synchronizations between them) equals the eager call bitwise."""
+    wl = W.small_workload(batch=b, seqlen=L, H=H, P=64, N=128, G=2, chunk=128, dtype="bf16", init_var=0.1)
+    inp = W.generate(wl, 97)
+    dev = torch.device("cuda:0")
+
+    def t(a, bf=False):
+        x = torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+        return x.to(torch.bfloat16) if bf else x
+    x, dt, A, B, C, D, init = (t(inp.x, True), t(inp.dt), t(inp.A), t(inp.B, True), t(inp.C, True), t(inp.D),
+                               t(inp.init))
+    ws = torch.empty(ssd.workspace_size(x, B, 128), dtype=torch.uint8, device=dev)
+    y = torch.empty(tuple(x.shape), device=dev)
+    fin = torch.empty_like(init)
+
+    def run():
+        ssd.chunked_scan(x, dt, A, B, C, D, 128, init_state=init, y=y, final_state=fin, workspace=ws)
+    run()
+    torch.cuda.synchronize()
+    y_ref, f_ref = y.clone(), fin.clone()
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph, stream=side):
+            run()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for k in range(3):
+        y.fill_(float("nan"))
+        fin.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, y_ref) and torch.equal(fin, f_ref), "replay %d" % k
+        _ = (x.float() * 2).sum().item()  # unrelated eager work between replays
