@@ -8,12 +8,15 @@
 // One multiply-add per tap and element: the prefill is an HBM stream (read x
 // once, write the output once), so it is laid out for bandwidth, not MFMA.
 // Rows are token-major [rows, C].  A lane owns 8 consecutive channels (one
-// 16-byte bf16 vector) and walks a block of kTokBlock tokens keeping the K-1
-// previous inputs in registers; a wave covers 512 channels of a row, so every
-// wave load and store is 1 KB (bf16) of contiguous row.  The next 8 rows are
-// in flight while the current 8 are computed.  Sequence starts inside a block
-// are the same for the whole wave (rows are uniform), so the switch to the
-// next sequence's incoming state is a scalar branch.
+// 16-byte bf16 vector) and walks a block of kTokBlock tokens; a wave covers
+// 512 channels of a row, so every wave load and store is 1 KB (bf16) of
+// contiguous row.  Rows go in batches of 8, the next batch in flight while
+// the current one is computed; one register array holds the K-1 inputs
+// before the batch and the batch's 8 rows, so every tap is a compile-time
+// index.  A batch with no sequence start inside takes a path with no
+// per-row test; otherwise sequence starts, which are the same for the whole
+// wave (rows are uniform), switch to the next sequence's incoming state on a
+// scalar branch.
 #include <type_traits>
 
 #include "ssd_device.h"
