@@ -290,9 +290,11 @@ ssd_status ssd_causal_conv1d_step(void* conv_state, const void* x, const float* 
  * then waits for the last event and writes each stage's elapsed time in
  * milliseconds to stage_ms[SSD_PREFILL_STAGES], in the order plan, cumsum,
  * cb, chunk_state, state_passing, chunk_scan (0 for a stage that did not
- * run: with enough (sequence, head, 32-column tile) walks, 256 or more, the
- * state passing runs inside the chunk_state stage and state_passing reads
- * 0).  Unlike ssd_chunked_scan it blocks the calling thread until the
+ * run: with enough (sequence, head, 32-column tile) walks, 256 or more, and
+ * sequences of similar length (with a host copy of a packed batch's
+ * offsets, no sequence over 1.5 times the mean chunk count), the state
+ * passing runs inside the chunk_state stage and state_passing reads 0).
+ * Unlike ssd_chunked_scan it blocks the calling thread until the
  * kernels finish.  Same arguments and errors as ssd_chunked_scan, plus
  * SSD_ERR_NULL when stage_ms is NULL.
  */
