@@ -565,6 +565,12 @@ def main():
     c1.synchronize()
     copy_ms = c0.elapsed_time(c1) / 10
     copy_gbs = 2 * state.numel() * 4 / (copy_ms * 1e-3) / 1e9
+    # the same rooflines against what this device streams in practice
+    for r in [roof, roof_dec] + list(roofs.values()):
+        if r["unit"] == "GB/s":
+            r["frac_of_copy_rate"] = round(r["achieved"] / copy_gbs, 4)
+        elif r.get("hbm_frac") is not None:
+            r["frac_of_copy_rate"] = round(r["hbm_frac"] * HBM_PEAK_GBS / copy_gbs, 4)
     del src, dst
 
     dvr = dwin = dconv = dother = None
