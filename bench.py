@@ -621,6 +621,9 @@ def main():
                    "steady_gbps": round(dbytes / (decode_steady_ms * 1e-3) / 1e9, 1),
                    "steady": "100 back-to-back steps after the timed region"},
         "step_ms_prefill_plus_decode": round(prefill_ms + decode_ms, 4),
+        "ms_per_step_note": "each timed step is one prefill then one decode step, each between HIP events; "
+                            "ms_per_step and value cover the prefill part (the metric is prefill tokens/s), "
+                            "decode.ms_per_step the decode part, step_ms_prefill_plus_decode both",
         "decode_vs_recompute": dvr,
         "decode_window": dwin,
         "conv1d": dconv,
