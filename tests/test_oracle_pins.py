@@ -2,7 +2,7 @@
 
 The sequential fp64 recurrence (oracle.scan / oracle.decode) is checked
 against things other than itself:
-  * hand-derived values (tests/golden/scalar_by_hand.json),
+  * hand-derived values (tests/golden/scalar_by_hand.json, tests/golden/conv1d_by_hand.json),
   * the brute-force quadratic (duality) form, built from explicit decay
     products ("Engineering hybrid state-space models", section 2),
   * scipy.signal.lfilter in the linear time-invariant special case
@@ -433,3 +433,16 @@ def test_conv1d_steps_equal_prefill_and_packed_batch():
         yt, st = oconv.conv1d_step(st, xs[t:t + 1], w, bias)
         assert np.allclose(yt[0], y[cu[3] + t], rtol=1e-14, atol=1e-14)
     assert np.array_equal(st[0], fin[3])
+
+
+def test_conv1d_hand_values():
+    g = json.load(open(os.path.join(GOLDEN, "conv1d_by_hand.json")))
+    w, bias, st = np.array(g["weight"]), np.array(g["bias"]), np.array(g["state"])
+    for case in g["cases"]:
+        y, fin = oconv.causal_conv1d(np.array(case["x"]), w, bias, st, activation=False)
+        assert np.array_equal(y, np.array(case["y"])), case["steps"]
+        assert np.array_equal(fin, np.array(case["final"]))
+        if "decode" in case:
+            d = case["decode"]
+            yd, sd = oconv.conv1d_step(fin[None], np.array(d["x"])[None], w, bias, activation=False)
+            assert np.array_equal(yd[0], np.array(d["y"])) and np.array_equal(sd[0], np.array(d["state"]))
