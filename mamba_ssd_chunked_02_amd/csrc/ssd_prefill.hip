@@ -1317,13 +1317,15 @@ hipError_t run_prefill(const Plan& pl, const Layout& lay, const ScanArgs& a, hip
     }
     if ((err = mark(2)) != hipSuccess) return err;
     if (pl.nchunk_ub > 0) {
-        if (cb_chunk_lds_bytes<T>(NT, Q) <= 160 * 1024) {
+        // the whole-chunk form needs enough (chunk, group) pairs to fill the
+        // chip; below that the tile-per-wave form's 36x more workgroups finish first
+        if (cb_chunk_lds_bytes<T>(NT, Q) <= 160 * 1024 && (int64_t)pl.nchunk_ub * pl.G >= 256) {
             auto* k1 = ssd_cb_chunk_kernel<T, NT>;
             const size_t lds = cb_chunk_lds_bytes<T>(NT, Q);
             if ((err = allow_lds(k1, lds)) != hipSuccess) return err;
             hipLaunchKernelGGL(k1, dim3(pl.nchunk_ub, pl.G), dim3(256), lds, stream, pl, B, C, cbm, bt);
         } else {
-            // the staged chunk would not fit (fp32, dstate > 128, 256-token chunks)
+            // few chunks, or a staged chunk that would not fit (fp32, dstate > 128, 256-token chunks)
             auto* k1 = ssd_cb_kernel<T, NT>;
             hipLaunchKernelGGL(k1, dim3(pl.nchunk_ub, pl.G, NTI * (NTI + 1) / 2), dim3(64), cb_lds_bytes<T>(NT),
                                stream, pl, B, C, cbm, bt);
