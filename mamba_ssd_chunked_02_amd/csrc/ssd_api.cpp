@@ -37,9 +37,10 @@ constexpr int64_t kMaxGrid = ((int64_t)1 << 31) - 8;
 // chunk-parallel chunk_state: ~8 workgroups per CU (three fit at once), at most 16 heads each
 constexpr int64_t kStateWorkgroups = 2048;
 constexpr int64_t kStateMaxHeads = 16;
-// chunk_scan: one 8-wave workgroup fits per CU; two per CU, each walking as
-// many heads as that allows, amortize the per-workgroup block operands best
-constexpr int64_t kScanWorkgroups = 512;
+// chunk_scan: one 8-wave workgroup fits per CU; one per CU, each walking as
+// many heads as that allows (up to the whole group), amortizes the
+// per-workgroup block operands and prologue best
+constexpr int64_t kScanWorkgroups = 256;
 constexpr int64_t kFusedMinWalks = 256;  // one per CU
 
 struct Prepared {
