@@ -76,6 +76,9 @@ SMALL = [
     (1, 160, 2, 128, 128, 2, 32, "bf16", 0.1),
     (1, 300, 2, 32, 256, 1, 256, "f32", 0.1),
     (2, 290, 2, 64, 256, 1, 256, "bf16", 0.1),
+    # 256 or more (chunk, group) pairs: the whole-chunk C.B^T kernel
+    (8, 1000, 4, 32, 64, 2, 64, "bf16", 0.1),
+    (4, 2000, 8, 16, 32, 4, 128, "f32", 0.1),
 ]
 
 
