@@ -79,6 +79,9 @@ SMALL = [
     # 256 or more (chunk, group) pairs: the whole-chunk C.B^T kernel
     (8, 1000, 4, 32, 64, 2, 64, "bf16", 0.1),
     (4, 2000, 8, 16, 32, 4, 128, "f32", 0.1),
+    # the largest head (P 128, N 256) at the largest chunk
+    (1, 300, 2, 128, 256, 1, 256, "bf16", 0.1),
+    (1, 300, 2, 128, 256, 2, 256, "f32", 0.1),
 ]
 
 
@@ -137,15 +140,20 @@ def test_no_initial_state_equals_zero_initial_state():
     assert torch.equal(y0, y1) and torch.equal(f0, f1)
 
 
-def test_final_state_may_alias_initial_state():
-    wl = W.small_workload(batch=2, seqlen=400, H=2, P=32, N=32, G=1, chunk=64, dtype="f32",
-                          init_var=0.1)
+@pytest.mark.parametrize("H,walk", [(2, False), (64, True)])
+def test_final_state_may_alias_initial_state(H, walk):
+    """final_state == init_state on both state paths: 4 and 256 (sequence,
+    head, column tile) walks."""
+    wl = W.small_workload(batch=2, seqlen=400, H=H, P=64 if walk else 32, N=32, G=1, chunk=64,
+                          dtype="f32", init_var=0.1)
     inp = W.generate(wl, 61)
     g = to_gpu(inp)
     st = g["init"].clone()
+    stages = []
     y, fin = ssd.chunked_scan(g["x"], g["dt"], g["A"], g["B"], g["C"], g["D"], 64, init_state=st,
-                              final_state=st)
+                              final_state=st, stage_ms=stages)
     torch.cuda.synchronize()
+    assert (stages[ssd.STAGES.index("state_passing")] == 0.0) == walk, stages
     yr, fr = oracle.scan(inp.x, inp.dt, inp.A, inp.B, inp.C, inp.D, init=inp.init)
     assert_close(host(st), fr, "f32", "aliased final")
     assert_close(host(y), yr, "f32", "y")
@@ -375,7 +383,7 @@ def test_decode_state_roundtrip_through_host_is_bitwise():
 
 
 @pytest.mark.parametrize("P,N,dt", [(16, 16, "f32"), (64, 128, "bf16"), (32, 256, "bf16"), (128, 8, "f32"),
-                                    (24, 40, "bf16")])
+                                    (24, 40, "bf16"), (128, 256, "bf16"), (128, 256, "f32")])
 def test_decode_shapes(P, N, dt):
     wl = W.small_workload(batch=5, seqlen=0, H=6, P=P, N=N, G=3, dtype=dt, init_var=0.1,
                           decode_steps=3, decode_batch=5)
