@@ -391,6 +391,10 @@ ssd_status check_decode(const float* state, const void* x, const float* dt, cons
         return fail(SSD_ERR_SHAPE, "y aliases an input");
     if (shape->batch * (int64_t)shape->nheads * shape->headdim > ((int64_t)1 << 40))
         return fail(SSD_ERR_SHAPE, "tensor too large");
+    // one wave per (sequence, head) block, at least one per workgroup
+    if (shape->batch * (int64_t)shape->nheads > kMaxGrid)
+        return fail(SSD_ERR_SHAPE, "batch * nheads %lld too large for one launch grid",
+                    (long long)(shape->batch * (int64_t)shape->nheads));
     return SSD_OK;
 }
 

@@ -161,6 +161,9 @@ def test_decode_errors(lib):
     assert lib.ssd_decode_step(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE + 16,
                                ctypes.byref(bad), None) == E_SHAPE
     assert lib.ssd_decode_step(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None) == E_NULL
+    # more (sequence, head) blocks than one launch grid holds
+    assert dec(sh=shape(batch=1 << 30, nheads=8, headdim=8)) == E_SHAPE
+    assert "launch grid" in lib.ssd_last_error_detail().decode()
 
 
 def test_status_strings(lib):
