@@ -17,9 +17,8 @@ namespace ssd {
 namespace {
 
 // Decode step: two waves per workgroup, one (sequence, head) state block
-// each.  At the 2.7B decode shape (20 480 blocks, 3 waves per SIMD) this
-// streams about 1% faster than four or three waves per workgroup and 3%
-// faster than one.
+// each.  At the 2.7B decode shape (20 480 blocks) this streamed about 1%
+// faster than four or three waves per workgroup and 3% faster than one.
 constexpr int kDecThreads = 128;
 // Windowed step: four waves per workgroup, one state block each.
 constexpr int kWinThreads = 256;
@@ -59,14 +58,18 @@ __device__ inline __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t 
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kBufferWord3);
 }
 
-// Wave w of block L updates the state block (b, h) = 4L + w: P rows of N
+// Wave w of block L updates the state block (b, h) = 2L + w: P rows of N
 // floats, contiguous.  Lane l owns columns n = 4 (l % TPR) .. +3 of the rows
 // p = RPI i + l / TPR, so each wave instruction moves 64 x 16 contiguous bytes
 // and B, C, dt, A are loaded once per lane.  Rows go in batches of kBatch
 // instructions; the next batch is loaded before the current one is stored,
-// and every lane issues every store (rows past P, columns past N and the
-// lanes that do not own a y element get an out-of-range offset), so the wait
-// for a batch never includes the previous batch's stores.
+// and every lane issues every state store (rows past P and columns past N get
+// an out-of-range offset), so the wait for a batch never includes the
+// previous batch's stores.  The block's x (P <= 128 values) is loaded once
+// into the wave's LDS row and its y collected there, then stored with one
+// coalesced store per 64 rows: per batch the wave issues only the state's
+// loads and stores to memory.  The wave index is made uniform so the buffer
+// descriptors are scalar.
 template <typename T, int TPR>
 __global__ __launch_bounds__(kDecThreads) void ssd_decode_kernel(
     int64_t nbh, int H, int P, int N, int G, float* __restrict__ state, const T* __restrict__ x,
@@ -75,7 +78,8 @@ __global__ __launch_bounds__(kDecThreads) void ssd_decode_kernel(
     constexpr int RPI = 64 / TPR;  // rows per wave instruction
     constexpr int RPB = RPI * kBatch;  // rows per batch
     const int lane = threadIdx.x & 63;
-    const int64_t bh = (int64_t)blockIdx.x * (kDecThreads / 64) + (threadIdx.x >> 6);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t bh = (int64_t)blockIdx.x * (kDecThreads / 64) + wave;
     if (bh >= nbh) return;
     const int h = (int)(bh % H);
     const int64_t b = bh / H;
@@ -88,19 +92,25 @@ __global__ __launch_bounds__(kDecThreads) void ssd_decode_kernel(
     const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(sb, (uint32_t)(P * N * sizeof(float)));
     const __amdgpu_buffer_rsrc_t ry =
         buffer_rsrc((char*)y + bh * P * (y_f32 ? 4 : 2), (uint32_t)(P * (y_f32 ? 4 : 2)));
+    __shared__ float xsh[kDecThreads / 64][128];
+    __shared__ float ysh[kDecThreads / 64][128];
+    float* xs = xsh[wave];
+    float* ys = ysh[wave];
+    const float xl0 = (float)xb[min(lane, P - 1)];
+    const float xl1 = (float)xb[min(lane + 64, P - 1)];
     f32x4 s[kBatch], sn[kBatch];
-    float xv[kBatch], xn[kBatch];
-    auto load = [&](int p0, f32x4 (&dst)[kBatch], float (&xd)[kBatch]) {
+    auto load = [&](int p0, f32x4 (&dst)[kBatch]) {
 #pragma unroll
         for (int u = 0; u < kBatch; ++u) {
             const int p = min(p0 + u * RPI + rsub, P - 1);
             dst[u] = __builtin_nontemporal_load((const f32x4*)(sb + (int64_t)p * N + n));
-            xd[u] = (float)xb[p];
         }
     };
     // the first state rows go out first; then every per-step operand, with
     // no load waiting on another (B, C columns clamped in range, masked after)
-    load(0, s, xv);
+    load(0, s);
+    xs[lane] = xl0;
+    xs[lane + 64] = xl1;
     const float draw = dt[bh], Ah = A[h], Dh = D[h];
     const float braw = *(act.bias ? act.bias + h : A + h);
     const typename Tr<T>::v4 bq = Tr<T>::ld4raw(B + (b * G + g) * N + n);
@@ -110,28 +120,32 @@ __global__ __launch_bounds__(kDecThreads) void ssd_decode_kernel(
     const f32x4 bv = nv ? Tr<T>::widen4(bq) : f32x4{};
     const f32x4 cv = nv ? Tr<T>::widen4(cq) : f32x4{};
     for (int p0 = 0; p0 < P; p0 += RPB) {
-        load(min(p0 + RPB, P - 1), sn, xn);  // next batch (repeats the last rows at the end)
+        load(min(p0 + RPB, P - 1), sn);  // next batch (repeats the last rows at the end)
 #pragma unroll
         for (int u = 0; u < kBatch; ++u) {
             const int p = p0 + u * RPI + rsub;
-            const f32x4 ns = a * s[u] + (d * xv[u]) * bv;
+            const float xp = xs[min(p, P - 1)];
+            const f32x4 ns = a * s[u] + (d * xp) * bv;
             const float tot = group_sum<TPR>(ns[0] * cv[0] + ns[1] * cv[1] + ns[2] * cv[2] + ns[3] * cv[3]);
             __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, ns), rs,
                                                    (p < P && nv) ? (p * N + n) * 4 : kOutOfRange, 0, kNonTemporal);
-            const float o = tot + Dh * xv[u];
-            const bool yo = j == TPR - 1 && p < P;
-            if (y_f32)
-                __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, o), ry, yo ? p * 4 : kOutOfRange,
-                                                      0, kNonTemporal);
-            else
-                __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, (bf16_t)o), ry,
-                                                      yo ? p * 2 : kOutOfRange, 0, kNonTemporal);
+            const float o = tot + Dh * xp;
+            if (j == TPR - 1 && p < P) ys[p] = o;
         }
 #pragma unroll
-        for (int u = 0; u < kBatch; ++u) {
-            s[u] = sn[u];
-            xv[u] = xn[u];
-        }
+        for (int u = 0; u < kBatch; ++u) s[u] = sn[u];
+    }
+    const float y0 = ys[min(lane, P - 1)], y1 = ys[min(lane + 64, P - 1)];
+    if (y_f32) {
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, y0), ry, lane < P ? lane * 4 : kOutOfRange,
+                                              0, kNonTemporal);
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, y1), ry,
+                                              lane + 64 < P ? (lane + 64) * 4 : kOutOfRange, 0, kNonTemporal);
+    } else {
+        __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, (bf16_t)y0), ry,
+                                              lane < P ? lane * 2 : kOutOfRange, 0, kNonTemporal);
+        __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, (bf16_t)y1), ry,
+                                              lane + 64 < P ? (lane + 64) * 2 : kOutOfRange, 0, kNonTemporal);
     }
 }
 
