@@ -186,12 +186,14 @@ constexpr int kWinMax = 16;
 constexpr int kWinPitch = kWinMax + 4;  // floats per x row of the window in LDS (16-byte aligned rows)
 
 // Every step streams the state block once for y (and, with FLUSH, writes the
-// new state in the same pass), with the streaming cache hint on its loads.  The prologue reduces the window to per-lane
-// constants: C_t, the decay exp(cs_t), y's intra-window part per row (LDS) and,
-// with FLUSH, u_s = exp(cs_t - cs_s) dt_s B_s and the window's x rows
-// (LDS, one row of W values per p).  Rows are streamed as in the decode step:
-// batches of kBatch 128-bit loads, the next batch in flight while the current
-// one is used.
+// new state in the same pass), with the streaming cache hint on its loads.
+// The prologue reduces the window to per-lane constants: C_t, the decay
+// exp(cs_t), y's intra-window part per row (LDS) and, with FLUSH,
+// u_s = exp(cs_t - cs_s) dt_s B_s and the window's x rows (LDS, one row of W
+// values per p).  Rows are streamed as in the decode step: batches of kBatch
+// 128-bit loads, the next batch in flight while the current one is used.
+// Each row's y replaces its intra-window part in LDS, and the block's y goes
+// out at the end with one coalesced store per 64 rows.
 template <typename T, int TPR, bool FLUSH>
 __global__ __launch_bounds__(kWinThreads, FLUSH ? 2 : (sizeof(T) == 2 ? 4 : 3)) void ssd_decode_window_kernel(
     int64_t nbh, int H, int P, int N, int G, int W, int t, float* __restrict__ state,
@@ -302,13 +304,7 @@ __global__ __launch_bounds__(kWinThreads, FLUSH ? 2 : (sizeof(T) == 2 ? 4 : 3)) 
             const int pc = min(p, P - 1);
             const float tot = group_sum<TPR>(s0[u][0] * ct[0] + s0[u][1] * ct[1] + s0[u][2] * ct[2] + s0[u][3] * ct[3]);
             const float o = et * tot + yi[pc];
-            const bool yo = j == TPR - 1 && p < P;
-            if (y_f32)
-                __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, o), ry, yo ? p * 4 : kOutOfRange,
-                                                      0, kNonTemporal);
-            else
-                __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, (bf16_t)o), ry,
-                                                      yo ? p * 2 : kOutOfRange, 0, kNonTemporal);
+            if (j == TPR - 1 && p < P) yi[p] = o;
             if constexpr (FLUSH) {
                 const f32x4* xr = (const f32x4*)xt[pc];
                 f32x4 ns = et * s0[u];
@@ -324,6 +320,19 @@ __global__ __launch_bounds__(kWinThreads, FLUSH ? 2 : (sizeof(T) == 2 ? 4 : 3)) 
         }
 #pragma unroll
         for (int u = 0; u < kBatch; ++u) s0[u] = sn[u];
+    }
+    __builtin_amdgcn_wave_barrier();
+    const float y0 = yi[min(lane, P - 1)], y1 = yi[min(lane + 64, P - 1)];
+    if (y_f32) {
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, y0), ry, lane < P ? lane * 4 : kOutOfRange,
+                                              0, kNonTemporal);
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, y1), ry,
+                                              lane + 64 < P ? (lane + 64) * 4 : kOutOfRange, 0, kNonTemporal);
+    } else {
+        __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, (bf16_t)y0), ry,
+                                              lane < P ? lane * 2 : kOutOfRange, 0, kNonTemporal);
+        __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, (bf16_t)y1), ry,
+                                              lane + 64 < P ? (lane + 64) * 2 : kOutOfRange, 0, kNonTemporal);
     }
 }
 
