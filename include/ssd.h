@@ -131,7 +131,9 @@ ssd_status ssd_chunked_scan(const void* x, const float* dt, const float* A, cons
  *   A, D  [H]            fp32
  *   B, C  [batch, G, N]  dtype
  *   y     [batch, H, P]  ydtype   output; must not alias any input
- * shape->seqlen and shape->cu_seqlens are ignored.
+ * shape->seqlen and shape->cu_seqlens are ignored.  batch * H may be at most
+ * 2^31 - 8 (one launch grid, one wave per (sequence, head)); larger batches
+ * return SSD_ERR_SHAPE.
  */
 ssd_status ssd_decode_step(float* state, const void* x, const float* dt, const float* A,
                            const void* B, const void* C, const float* D, void* y,
@@ -195,9 +197,9 @@ ssd_status ssd_decode_step_dt_act(float* state, const void* x, const float* dt_r
  *   y      [batch, H, P]    ydtype output of token t; must not alias an input
  *   window W in [1, 16]; t in [0, W); flush 0 or 1
  *   act    NULL, or the dt activation of ssd_decode_step_dt_act
- * shape->seqlen and shape->cu_seqlens are ignored.  Errors as ssd_decode_step,
- * plus SSD_ERR_VALUE for window, t or flush out of range (and the activation
- * errors).
+ * shape->seqlen and shape->cu_seqlens are ignored.  Errors (and the batch * H
+ * limit) as ssd_decode_step, plus SSD_ERR_VALUE for window, t or flush out of
+ * range (and the activation errors).
  */
 ssd_status ssd_decode_window_step(float* state, const void* x, const float* dt, const float* A,
                                   const void* B, const void* C, const float* D, void* y, int32_t window,
