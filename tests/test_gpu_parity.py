@@ -438,6 +438,35 @@ def test_bf16_output_is_the_rounded_fp32_output():
     assert torch.equal(yd16, yd32.to(torch.bfloat16)) and torch.equal(s1, s2)
 
 
+@pytest.mark.parametrize("P", [24, 128])
+def test_decode_bf16_output_rows_past_64(P):
+    """The decode kernels store y with one coalesced store per 64 rows: bf16
+    y is the rounded fp32 y for P below 64 and for rows 64..127, for the
+    decode step and the windowed step."""
+    wl = W.small_workload(batch=3, seqlen=0, H=4, P=P, N=64, G=2, dtype="bf16", init_var=0.1,
+                          decode_steps=3, decode_batch=3)
+    inp = W.generate(wl, 130 + P)
+    A, D = tdev(inp.A), tdev(inp.D)
+    d = inp.decode[0]
+    args = (tdev(d["x"], "bf16"), tdev(d["dt"]), A, tdev(d["B"], "bf16"), tdev(d["C"], "bf16"), D)
+    s1, s2 = tdev(inp.init), tdev(inp.init)
+    y32 = ssd.decode_step(s1, *args)
+    y16 = ssd.decode_step(s2, *args, y_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert torch.equal(y16, y32.to(torch.bfloat16)) and torch.equal(s1, s2)
+    ref_y, _ = oracle.decode(inp.init, d["x"], d["dt"], inp.A, d["B"], d["C"], inp.D)
+    assert_close(host(y32), ref_y, "bf16", "decode y")
+    win = [torch.stack([tdev(e[k], dt) for e in inp.decode], dim=1).contiguous()
+           for k, dt in (("x", "bf16"), ("dt", "f32"), ("B", "bf16"), ("C", "bf16"))]
+    for flush in (False, True):
+        w1, w2 = tdev(inp.init), tdev(inp.init)
+        y32 = ssd.decode_window_step(w1, win[0], win[1], A, win[2], win[3], D, 2, flush)
+        y16 = ssd.decode_window_step(w2, win[0], win[1], A, win[2], win[3], D, 2, flush,
+                                     y_dtype=torch.bfloat16)
+        torch.cuda.synchronize()
+        assert torch.equal(y16, y32.to(torch.bfloat16)) and torch.equal(w1, w2), flush
+
+
 def test_empty_batch_is_a_no_op():
     x = torch.zeros((0, 10, 2, 16), device="cuda")
     y, fin = ssd.chunked_scan(x, torch.zeros((0, 10, 2), device="cuda"), torch.zeros(2, device="cuda"),
