@@ -462,11 +462,16 @@ def main():
     # inverse softplus of the workload's dt, so the kernels see the same dt)
     raw = up(np.log(np.expm1(inp.dt.astype(np.float64))).astype(np.float32))
 
+    y16 = None if args.no_extras else torch.empty(tuple(x.shape), dtype=torch.bfloat16, device=dev)
+
     def back_to_back(act):
         def one():
-            if act:
+            if act == "softplus":
                 ssd.chunked_scan(x, raw, A, Bm, Cm, D, wl.chunk, init_state=init, y=y, final_state=fin,
                                  workspace=ws, dt_softplus=True)
+            elif act == "bf16_y":
+                ssd.chunked_scan(x, dtt, A, Bm, Cm, D, wl.chunk, init_state=init, y=y16, final_state=fin,
+                                 workspace=ws)
             else:
                 prefill()
         for _ in range(3):
@@ -480,9 +485,10 @@ def main():
         a1.synchronize()
         return a0.elapsed_time(a1) / args.steps
 
-    plain_b2b_ms = back_to_back(False) if not args.no_extras else None
-    act_ms = back_to_back(True) if not args.no_extras else None
-    del raw
+    plain_b2b_ms = back_to_back(None) if not args.no_extras else None
+    act_ms = back_to_back("softplus") if not args.no_extras else None
+    y16_ms = back_to_back("bf16_y") if not args.no_extras else None
+    del raw, y16
 
     # per-kernel durations: the same prefill through the measuring entry point
     # (HIP events before and after every stage on the same stream)
@@ -633,6 +639,11 @@ def main():
             "plain_ms_per_step": round(plain_b2b_ms, 4),
             "what": "same prefill through ssd_chunked_scan_dt_act (softplus fused into the cumsum kernel) "
                     "and through ssd_chunked_scan, back-to-back calls each"},
+        "prefill_bf16_y": None if y16_ms is None else {
+            "ms_per_step": round(y16_ms, 4), "tokens_per_s": round(tokens / (y16_ms * 1e-3), 1),
+            "plain_ms_per_step": round(plain_b2b_ms, 4),
+            "what": "same prefill with y stored in bf16 (RNE of the fp32 y; 671 MB less written), "
+                    "back-to-back calls; context only, value is the fp32-y default"},
         "tflops_contraction_kernels": round(contraction_tf, 2),
         "frac_bf16_peak_contraction_kernels": round(contraction_tf / BF16_PEAK_TFLOPS, 4),
         "roofline": roof,
