@@ -73,9 +73,12 @@ def kernel_work(wl, es=2, ys=4, fused=True):
     return {"chunk_state": ks, "chunk_scan": kc, "state_passing": kp}
 
 
-def decode_bytes(wd, es=2):
+def decode_bytes(wd, es=2, ys=4):
+    """HBM bytes of one decode step: the fp32 state read and written, x (es
+    bytes per element), y (ys, fp32 by default), B and C, dt, A and D."""
     b, H, P, N, G = wd.nseq, wd.H, wd.P, wd.N, wd.G
-    return 2 * b * H * P * N * 4 + 2 * b * H * P * es + 2 * b * G * N * es + b * H * 4 + 2 * H * 4
+    return (2 * b * H * P * N * 4 + b * H * P * es + b * H * P * ys + 2 * b * G * N * es + b * H * 4
+            + 2 * H * 4)
 
 
 def cpu_baseline(inp, max_seqs=None):

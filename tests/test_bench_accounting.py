@@ -1,0 +1,52 @@
+"""The algorithmic bytes and FLOPs behind the benchmark's roofline figures,
+checked against the same quantities written out from the shapes of the
+2.7B-shaped workloads (prefill b8 L8192 H80 P64 N128 G1 chunk 256 with bf16
+x/B/C and fp32 y; decode b256 with fp32 state and y)."""
+import importlib.util
+import os
+
+from mamba_ssd_chunked_02_amd import workloads as W
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+_spec = importlib.util.spec_from_file_location("bench_under_test", os.path.join(ROOT, "bench.py"))
+bench = importlib.util.module_from_spec(_spec)
+_spec.loader.exec_module(bench)
+
+MB = 1e6
+b, L, H, P, N, Q = 8, 8192, 80, 64, 128, 256
+chunks = b * L // Q                      # 256 chunks of 256 tokens
+x_bytes = b * L * H * P * 2              # bf16 x, read once
+y_bytes = b * L * H * P * 4              # fp32 y, written once
+state_slots = chunks * H * P * N * 4     # one fp32 state per (chunk, head)
+tables = 2 * chunks * H * Q * 4          # two fp32 per-token tables per (chunk, head)
+
+
+def test_workload_is_the_2p7b_prefill():
+    wl = W.CONFIGS[3]
+    assert (wl.batch, wl.seqlen, wl.H, wl.P, wl.N, wl.G, wl.chunk) == (b, L, H, P, N, 1, Q)
+
+
+def test_chunk_state_walk_bytes_and_flops():
+    ks = bench.kernel_work(W.CONFIGS[3])["chunk_state"]
+    bt = chunks * N * Q * 2              # B^T of every chunk, bf16
+    init_final = 2 * b * H * P * N * 4
+    assert ks["bytes"] == x_bytes + bt + state_slots + tables + init_final == 1_442_840_576
+    assert ks["flops"] == chunks * H * 2 * Q * N * P == 85_899_345_920
+
+
+def test_chunk_scan_bytes_and_flops():
+    kc = bench.kernel_work(W.CONFIGS[3])["chunk_scan"]
+    c_rows = b * L * N * 2
+    cb_causal = chunks * (8 * 9 // 2) * 32 * 32 * 2   # 36 causal 32x32 tiles per chunk, bf16
+    assert kc["bytes"] == x_bytes + y_bytes + c_rows + state_slots + cb_causal + tables
+    assert abs(kc["bytes"] / MB - 2761.9) < 0.05
+    assert kc["flops"] == chunks * H * (2 * Q * N * P + 2 * Q * Q * P) == 257_698_037_760
+
+
+def test_decode_step_bytes():
+    wd = W.CONFIGS[2]
+    nb = 256
+    state = nb * H * P * N * 4
+    assert state == 671_088_640
+    expect = 2 * state + nb * H * P * 2 + nb * H * P * 4 + 2 * nb * N * 2 + nb * H * 4 + 2 * H * 4
+    assert bench.decode_bytes(wd) == expect == 1_350_255_232
