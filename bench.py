@@ -29,6 +29,7 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
+MFMA_TARGET = 0.40              # the prefill's contraction kernels: fraction of the bf16 peak asked for
 
 
 def log(*a):
@@ -62,15 +63,39 @@ def kernel_work(wl, es=2, ys=4, fused=True):
     nti = Q // 32
     state = nch * H * P * N * 4
     ks = {"flops": nch * H * 2 * Q * N * P,
+          "flops_causal": nch * H * 2 * Q * N * P,
           "bytes": T * H * P * es + nch * G * N * Q * es + state + 2 * nch * H * Q * 4}
     kc = {"flops": nch * H * (2 * Q * N * P + 2 * Q * Q * P),
+          "flops_causal": nch * H * (2 * Q * N * P + Q * (Q + 1) * P),
           "bytes": (T * H * P * es + T * H * P * ys + T * G * N * es + state
                     + nch * G * nti * (nti + 1) // 2 * 1024 * es + 2 * nch * H * Q * 4)}
-    kp = {"flops": 0, "bytes": 2 * state + nch * H * 4 + 2 * b * H * P * N * 4}
+    kp = {"flops": 0, "flops_causal": 0, "bytes": 2 * state + nch * H * 4 + 2 * b * H * P * N * 4}
     if fused:
         ks["bytes"] += 2 * b * H * P * N * 4
         return {"chunk_state": ks, "chunk_scan": kc}
     return {"chunk_state": ks, "chunk_scan": kc, "state_passing": kp}
+
+
+def roofline_of(wk, ms, kernel):
+    """Roofline of one kernel launch from its algorithmic work and measured
+    duration.  The roof that bounds it is the one its arithmetic intensity
+    (algorithmic FLOPs per HBM byte) selects against the ridge point
+    (bf16 peak / HBM peak); both fractions are reported either way."""
+    gbs = wk["bytes"] / (ms * 1e-3) / 1e9
+    tfl = wk["flops"] / (ms * 1e-3) / 1e12
+    tfl_c = wk["flops_causal"] / (ms * 1e-3) / 1e12
+    fh, fm = gbs / HBM_PEAK_GBS, tfl / BF16_PEAK_TFLOPS
+    ai = wk["flops"] / wk["bytes"]
+    ridge = BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    r = ({"bound": "mfma", "achieved": round(tfl, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+          "frac": round(fm, 4)} if ai > ridge else
+         {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(fh, 4)})
+    r.update({"traffic": None, "kernel": kernel, "avg_ms": round(ms, 4),
+              "algorithmic_flops": wk["flops"], "algorithmic_flops_causal": wk["flops_causal"],
+              "algorithmic_bytes": wk["bytes"], "flop_per_byte": round(ai, 1), "ridge_flop_per_byte": round(ridge, 1),
+              "tflops": round(tfl, 2), "mfma_frac": round(fm, 4), "tflops_causal": round(tfl_c, 2),
+              "mfma_frac_causal": round(tfl_c / BF16_PEAK_TFLOPS, 4), "hbm_frac": round(fh, 4)})
+    return r
 
 
 def decode_bytes(wd, es=2, ys=4):
@@ -81,27 +106,48 @@ def decode_bytes(wd, es=2, ys=4):
             + 2 * H * 4)
 
 
-def cpu_baseline(inp, max_seqs=None):
+def cpu_model():
+    """The host CPU's model name from /proc/cpuinfo (None if unreadable)."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.lower().startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def cpu_baseline(inp, max_seqs=None, one_core_seqs=1):
     """The fp64 oracle (sequential recurrence, OpenMP over (sequence, head))
-    on the prefill workload's own inputs: all heads of the first `max_seqs`
-    sequences (all of them by default, ~30 core-seconds on 16 cores), scaled
-    to tokens/s of the whole layer."""
+    on the prefill workload's own inputs, timed twice: on all the host threads
+    OpenMP gets, over all heads of the first `max_seqs` sequences (all of them
+    by default, ~20 core-seconds), and on one thread over all heads of the
+    first `one_core_seqs` sequences (~3 s).  Both are scaled to tokens/s of
+    the whole layer (every head of a token)."""
     import oracle
     wl = inp.wl
     nseq = wl.batch if max_seqs is None else min(max_seqs, wl.batch)
     threads = oracle.threads()
-    init = None if inp.init is None else inp.init[:nseq]
-    t0 = time.perf_counter()
-    cpu0 = time.process_time()
-    oracle.scan(inp.x[:nseq], inp.dt[:nseq], inp.A, inp.B[:nseq], inp.C[:nseq], inp.D, init=init)
-    t = time.perf_counter() - t0
-    cpu_s = time.process_time() - cpu0
+
+    def timed(n, nthreads):
+        init = None if inp.init is None else inp.init[:n]
+        t0 = time.perf_counter()
+        cpu0 = time.process_time()
+        oracle.scan(inp.x[:n], inp.dt[:n], inp.A, inp.B[:n], inp.C[:n], inp.D, init=init, nthreads=nthreads)
+        return time.perf_counter() - t0, time.process_time() - cpu0
+
+    t, cpu_s = timed(nseq, 0)
+    n1 = min(one_core_seqs, wl.batch)
+    t1, _ = timed(n1, 1)
     return {"value": nseq * wl.seqlen / t, "unit": "tokens/s", "cores": int(threads),
-            "host_cpus": len(os.sched_getaffinity(0)), "kind": "oracle", "seconds": round(t, 3),
-            "cpu_seconds": round(cpu_s, 1),
+            "host_cpus": len(os.sched_getaffinity(0)), "cpu_model": cpu_model(), "kind": "oracle",
+            "seconds": round(t, 3), "cpu_seconds": round(cpu_s, 1),
             "sample": "fp64 sequential oracle (C, OpenMP over (sequence, head)) on %d of %d "
                       "sequences x all %d heads x %d tokens of the prefill workload"
-                      % (nseq, wl.batch, wl.H, wl.seqlen)}
+                      % (nseq, wl.batch, wl.H, wl.seqlen),
+            "one_core": {"value": n1 * wl.seqlen / t1, "unit": "tokens/s", "cores": 1, "seconds": round(t1, 3),
+                         "sample": "the same oracle on one thread: %d sequence x all %d heads x %d tokens"
+                                   % (n1, wl.H, wl.seqlen)}}
 
 
 def decode_vs_recompute(torch, ssd, context=4096, steps=64, reps=20):
@@ -535,23 +581,24 @@ def main():
     roofs = {}
     for k, wk in work.items():
         ms = float(stage_mean[ssd.STAGES.index(k)])
-        gbs = wk["bytes"] / (ms * 1e-3) / 1e9
-        tfl = wk["flops"] / (ms * 1e-3) / 1e12
-        fh, fm = gbs / HBM_PEAK_GBS, tfl / BF16_PEAK_TFLOPS
-        r = ({"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-              "frac": round(fh, 4)} if fh >= fm else
-             {"bound": "mfma", "achieved": round(tfl, 1), "peak": BF16_PEAK_TFLOPS,
-              "unit": "TFLOP/s", "frac": round(fm, 4)})
-        r.update({"traffic": None, "kernel": names[k], "avg_ms": round(ms, 4),
-                  "algorithmic_flops": wk["flops"], "algorithmic_bytes": wk["bytes"],
-                  "tflops": round(tfl, 2), "mfma_frac": round(fm, 4), "hbm_frac": round(fh, 4)})
-        roofs[k] = r
+        roofs[k] = roofline_of(wk, ms, names[k])
     dominant = max(roofs, key=lambda k: roofs[k]["avg_ms"])
     roof = dict(roofs[dominant])
     if args.traffic:
         roof["traffic"] = _traffic(args.traffic, names[dominant], roof["algorithmic_bytes"])
     mfma_ms = float(stage_mean[ssd.STAGES.index("chunk_state")] + stage_mean[ssd.STAGES.index("chunk_scan")])
     contraction_tf = (work["chunk_state"]["flops"] + work["chunk_scan"]["flops"]) / (mfma_ms * 1e-3) / 1e12
+    contraction_tf_c = ((work["chunk_state"]["flops_causal"] + work["chunk_scan"]["flops_causal"])
+                        / (mfma_ms * 1e-3) / 1e12)
+    # the contraction kernels against the 40% bf16 target, beside the dominant
+    # kernel's own roofline (which is the HBM roof: its arithmetic intensity
+    # sits left of the ridge)
+    roof["contraction_kernels"] = {
+        "ms": round(mfma_ms, 4), "tflops_dense": round(contraction_tf, 2),
+        "mfma_frac_dense": round(contraction_tf / BF16_PEAK_TFLOPS, 4),
+        "tflops_causal": round(contraction_tf_c, 2),
+        "mfma_frac_causal": round(contraction_tf_c / BF16_PEAK_TFLOPS, 4),
+        "mfma_target": MFMA_TARGET}
     dbytes = decode_bytes(wd)
     dgbs = dbytes / (decode_ms * 1e-3) / 1e9
     roof_dec = {"bound": "hbm", "achieved": round(dgbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",

@@ -22,7 +22,10 @@
  *     global state: calls are reentrant and asynchronous on `stream` (a
  *     hipStream_t passed as void*, NULL = the null stream).
  *   - Tensors are dense row-major with the innermost index last, as listed per
- *     argument.  Every tensor pointer must be 16-byte aligned.
+ *     argument.  Tensor pointers must be 16-byte aligned, except the fp32
+ *     vectors dt, A, D and dt_bias, which the kernels read one element at a
+ *     time and which need only 4-byte alignment (so a per-step slice of a
+ *     [steps, batch, H] dt buffer can be passed as is).
  *   - Validation runs on the host before any launch.  On any error nothing is
  *     launched and nothing is written; the returned code says why and
  *     ssd_last_error_detail() gives a sentence (thread-local).
@@ -47,7 +50,7 @@ typedef enum ssd_status {
     SSD_ERR_NULL = -1,        /* a required pointer is NULL */
     SSD_ERR_SHAPE = -2,       /* a size is out of range or inconsistent */
     SSD_ERR_DTYPE = -3,       /* unknown dtype code */
-    SSD_ERR_ALIGN = -4,       /* a tensor pointer is not 16-byte aligned */
+    SSD_ERR_ALIGN = -4,       /* a tensor pointer is not aligned as required */
     SSD_ERR_CHUNK = -5,       /* chunk not in {32, 64, 128, 256} */
     SSD_ERR_WORKSPACE = -6,   /* workspace NULL or smaller than the query says */
     SSD_ERR_HIP = -7,         /* the HIP runtime reported an error at launch */
@@ -69,8 +72,25 @@ typedef enum ssd_dtype { SSD_F32 = 0, SSD_BF16 = 1 } ssd_dtype;
  *     initial state through unchanged.
  *   headdim P in [8, 128] and dstate N in [8, 256], both multiples of 8;
  *   ngroups G >= 1 divides nheads H; head h reads B/C group h / (H/G).
+ *   path: which kernels compute the chunk states, their passing and y
+ *     (ssd_path; SSD_PATH_AUTO, i.e. 0, lets the library choose).  Every path
+ *     computes the same result up to fp32 rounding order; the others exist
+ *     for tests and measurements.  The workspace size depends on the path:
+ *     query it with the same shape the call uses.
  *   reserved: must be zero.
  */
+typedef enum ssd_path {
+    SSD_PATH_AUTO = 0,
+    SSD_PATH_CHUNK_PARALLEL = 1, /* chunk states, state passing and outputs as three
+                                    launches, each parallel over chunks */
+    SSD_PATH_STATE_WALK = 2,     /* one walk per (sequence, head, 32-column tile) for the
+                                    states and their passing, then the outputs */
+    SSD_PATH_SCAN_WALK = 3       /* one walk per (sequence, group, slice of heads) that also
+                                    writes y, so no per-chunk state leaves the chip; bf16
+                                    inputs, chunk 256 and dstate in (64, 128] only
+                                    (SSD_ERR_UNSUPPORTED otherwise) */
+} ssd_path;
+
 typedef struct ssd_shape {
     int64_t batch;
     int64_t seqlen;
@@ -80,7 +100,8 @@ typedef struct ssd_shape {
     int32_t ngroups;
     int32_t dtype;               /* ssd_dtype of x, B, C */
     int32_t ydtype;              /* ssd_dtype of y (0 = SSD_F32, the default) */
-    int32_t reserved[2];         /* must be 0 */
+    int32_t path;                /* ssd_path (0 = the library's choice) */
+    int32_t reserved;            /* must be 0 */
     const int32_t* cu_seqlens;      /* device int32 [batch+1], or NULL (dense) */
     const int32_t* cu_seqlens_host; /* optional host copy; validated when given */
 } ssd_shape;
@@ -108,8 +129,9 @@ ssd_status ssd_chunked_scan_workspace_size(const ssd_shape* shape, int32_t chunk
  *              init_state (each element is read before it is written)
  *   workspace  device scratch of at least the queried size, owned by the
  *              caller, contents undefined on entry and exit.  It holds the
- *              per-chunk tables and one fp32 (P x N) state per (chunk, head),
- *              about 4*P*N*H/chunk bytes per token.
+ *              per-chunk decay tables and C.B^T, and (every path but the scan
+ *              walk) one fp32 (P x N) state per (chunk, head), about
+ *              4*P*N*H/chunk bytes per token.
  *   stream     hipStream_t (as void*) the kernels are queued on
  * Returns SSD_OK once the kernels are queued (asynchronous).
  */
@@ -152,7 +174,7 @@ ssd_status ssd_decode_step(float* state, const void* x, const float* dt, const f
  * prefill, the decode step).  Everything else is exactly ssd_chunked_scan /
  * ssd_decode_step; the `dt` argument holds dt_raw.
  *
- *   dt_bias  [H] fp32 device pointer, 16-byte aligned, or NULL for no bias
+ *   dt_bias  [H] fp32 device pointer, 4-byte aligned, or NULL for no bias
  *   dt_min   lower clamp: finite and >= 0
  *   dt_max   upper clamp: >= dt_min (INFINITY: no upper clamp)
  * Errors as the plain entry points, plus SSD_ERR_NULL for a NULL `act` and
@@ -291,16 +313,21 @@ ssd_status ssd_causal_conv1d_step(void* conv_state, const void* x, const float* 
  * with a HIP event recorded on `stream` before and after every kernel stage,
  * then waits for the last event and writes each stage's elapsed time in
  * milliseconds to stage_ms[SSD_PREFILL_STAGES], in the order plan, cumsum,
- * cb, chunk_state, state_passing, chunk_scan (0 for a stage that did not
- * run: with enough (sequence, head, 32-column tile) walks, 256 or more, and
- * sequences of similar length (with a host copy of a packed batch's
- * offsets, no sequence over 1.5 times the mean chunk count), the state
- * passing runs inside the chunk_state stage and state_passing reads 0).
- * Unlike ssd_chunked_scan it blocks the calling thread until the
- * kernels finish.  Same arguments and errors as ssd_chunked_scan, plus
- * SSD_ERR_NULL when stage_ms is NULL.
+ * cb, chunk_state, state_passing, chunk_scan, scan_walk.  A stage the path
+ * does not run reads exactly 0:
+ *   SSD_PATH_CHUNK_PARALLEL  scan_walk
+ *   SSD_PATH_STATE_WALK      state_passing (the passing runs inside the
+ *                            chunk_state stage), scan_walk
+ *   SSD_PATH_SCAN_WALK       chunk_state, state_passing, chunk_scan
+ * With SSD_PATH_AUTO the library takes a walk when there are enough
+ * (sequence, head, 32-column tile) walks, 256 or more, and sequences of
+ * similar length (with a host copy of a packed batch's offsets, no sequence
+ * over 1.5 times the mean chunk count), else the chunk-parallel path.
+ * Unlike ssd_chunked_scan it blocks the calling thread until the kernels
+ * finish.  Same arguments and errors as ssd_chunked_scan, plus SSD_ERR_NULL
+ * when stage_ms is NULL.
  */
-#define SSD_PREFILL_STAGES 6
+#define SSD_PREFILL_STAGES 7
 ssd_status ssd_chunked_scan_profiled(const void* x, const float* dt, const float* A,
                                      const void* B, const void* C, const float* D, int32_t chunk,
                                      const float* init_state, void* y, float* final_state,

@@ -43,7 +43,7 @@ class _Shape(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64), ("nheads", ctypes.c_int32),
                 ("headdim", ctypes.c_int32), ("dstate", ctypes.c_int32),
                 ("ngroups", ctypes.c_int32), ("dtype", ctypes.c_int32), ("ydtype", ctypes.c_int32),
-                ("reserved", ctypes.c_int32 * 2),
+                ("path", ctypes.c_int32), ("reserved", ctypes.c_int32),
                 ("cu_seqlens", ctypes.c_void_p),
                 ("cu_seqlens_host", ctypes.c_void_p)]
 
@@ -178,9 +178,12 @@ def _stream_handle(t) -> int:
 
 
 def make_shape(x, B, cu_seqlens=None, cu_seqlens_host=None, nseq: Optional[int] = None,
-               y_dtype=None) -> Tuple[_Shape, object]:
+               y_dtype=None, path: str = "auto") -> Tuple[_Shape, object]:
     """Build the C shape struct from tensors.  Returns (shape, keepalive)."""
     sh = _Shape()
+    if path not in PATHS:
+        raise ValueError("path must be one of %s" % sorted(PATHS))
+    sh.path = PATHS[path]
     keep = None
     if cu_seqlens is None:
         b, L, H, P = x.shape
@@ -201,15 +204,23 @@ def make_shape(x, B, cu_seqlens=None, cu_seqlens_host=None, nseq: Optional[int] 
     return sh, keep
 
 
-def workspace_size(x, B, chunk: int, cu_seqlens=None) -> int:
-    sh, _ = make_shape(x, B, cu_seqlens, None)
+def workspace_size(x, B, chunk: int, cu_seqlens=None, cu_seqlens_host=None, path: str = "auto",
+                   y_dtype=None) -> int:
+    """Workspace bytes for a chunked_scan call with the same arguments (the
+    kernel path, and so the size, can depend on the host copy of the offsets)."""
+    sh, keep = make_shape(x, B, cu_seqlens, cu_seqlens_host, y_dtype=y_dtype, path=path)
     n = ctypes.c_size_t(0)
     _check(load().ssd_chunked_scan_workspace_size(ctypes.byref(sh), int(chunk), ctypes.byref(n)),
            "ssd_chunked_scan_workspace_size")
+    del keep
     return int(n.value)
 
 
-STAGES = ("plan", "cumsum", "cb", "chunk_state", "state_passing", "chunk_scan")
+STAGES = ("plan", "cumsum", "cb", "chunk_state", "state_passing", "chunk_scan", "scan_walk")
+
+# Kernel paths of the prefill (ssd_path in include/ssd.h); "auto" lets the
+# library choose.
+PATHS = {"auto": 0, "chunk_parallel": 1, "state_walk": 2, "scan_walk": 3}
 
 
 def _dt_act(dt_softplus, dt_bias, dt_limit, H):
@@ -233,8 +244,12 @@ def chunked_scan(x, dt, A, B, C, D, chunk: int = 256, init_state=None, cu_seqlen
                  y=None, final_state=None, want_final: bool = True, workspace=None,
                  cu_seqlens_host: Optional[Sequence[int]] = None,
                  stage_ms: Optional[list] = None, y_dtype=None,
-                 dt_softplus: bool = False, dt_bias=None, dt_limit=None):
+                 dt_softplus: bool = False, dt_bias=None, dt_limit=None, path: str = "auto"):
     """Chunked prefill.  Returns (y, final_state or None).
+
+    ``path``: one of ``PATHS`` ("auto" by default), the kernels that compute
+    the chunk states, their passing and y (the same result up to fp32
+    rounding order).
 
     ``dt_softplus``: ``dt`` holds raw step sizes and the kernels use
     ``clamp(softplus(dt + dt_bias[h]), *dt_limit)`` (``dt_bias`` [H] fp32 or
@@ -259,7 +274,7 @@ def chunked_scan(x, dt, A, B, C, D, chunk: int = 256, init_state=None, cu_seqlen
         raise TypeError("cu_seqlens must be int32")
     if y_dtype is None:
         y_dtype = torch.float32 if y is None else y.dtype
-    sh, keep = make_shape(x, B, cu_seqlens, host_cu, y_dtype=y_dtype)
+    sh, keep = make_shape(x, B, cu_seqlens, host_cu, y_dtype=y_dtype, path=path)
     nseq = sh.batch
     H, P, N = sh.nheads, sh.headdim, sh.dstate
     lead = tuple(x.shape[:-2])

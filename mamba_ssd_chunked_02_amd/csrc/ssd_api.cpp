@@ -29,6 +29,30 @@ ssd_status ok() {
 }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
+
+// Alignment each pointer argument needs: dt, A, D and the dt bias are fp32
+// vectors that every kernel reads one element at a time (4 bytes); every
+// other tensor is read or written with 16-byte accesses.
+struct PtrArg {
+    const void* p;
+    const char* name;
+    bool required;
+    int align;
+};
+
+ssd_status check_ptrs(const PtrArg* args, int n) {
+    for (int i = 0; i < n; ++i) {
+        const PtrArg& q = args[i];
+        if (!q.p && q.required) {
+            if (q.name[0] == 'w') return fail(SSD_ERR_WORKSPACE, "workspace is NULL");
+            return fail(SSD_ERR_NULL, "%s is NULL", q.name);
+        }
+        if (q.p && ((uintptr_t)q.p & (uintptr_t)(q.align - 1)) != 0)
+            return fail(SSD_ERR_ALIGN, "%s is not %d-byte aligned", q.name, q.align);
+    }
+    return SSD_OK;
+}
 
 size_t up256(size_t v) { return (v + 255) & ~(size_t)255; }
 
@@ -42,11 +66,33 @@ constexpr int64_t kStateMaxHeads = 16;
 // per-workgroup block operands and prologue best
 constexpr int64_t kScanWorkgroups = 256;
 constexpr int64_t kFusedMinWalks = 256;  // one per CU
+// whether the library's own choice may take the scan walk where it applies
+constexpr bool kAutoScanWalk = false;
 
 struct Prepared {
     ssd::Plan plan;
     ssd::Layout lay;
+    int32_t path;       // ssd::kPath*
+    int32_t walk_nus;    // scan walk: units per workgroup
+    int32_t walk_nslice; // scan walk: workgroups per (sequence, group)
 };
+
+// The scan walk's work split: about one workgroup per CU, each walking at
+// most kWalkMaxUnits (head, column tile) units of one group; the group's
+// units are cut into equal slices.
+constexpr int64_t kWalkWorkgroups = 256;
+constexpr int64_t kWalkMaxUnits = 6;
+
+void walk_split(const ssd::Plan& pl, int32_t* nus, int32_t* nslice) {
+    const int64_t npt = (pl.P + 31) / 32;
+    const int64_t upg = (int64_t)pl.hpg * npt;
+    const int64_t units = (int64_t)pl.nseq * pl.G * upg;
+    int64_t n = std::max<int64_t>(1, std::min<int64_t>(kWalkMaxUnits, units / kWalkWorkgroups));
+    n = std::min(n, upg);
+    const int64_t ns = (upg + n - 1) / n;
+    *nslice = (int32_t)ns;
+    *nus = (int32_t)((upg + ns - 1) / ns);
+}
 
 // Heads of one group that a chunk_state / chunk_scan workgroup walks: the
 // group's per-chunk operands are loaded once per workgroup, so more heads per
@@ -91,8 +137,9 @@ ssd_status check_head_dims(const ssd_shape* sh) {
         return fail(SSD_ERR_DTYPE, "dtype %d is neither SSD_F32 (0) nor SSD_BF16 (1)", sh->dtype);
     if (sh->ydtype != SSD_F32 && sh->ydtype != SSD_BF16)
         return fail(SSD_ERR_DTYPE, "ydtype %d is neither SSD_F32 (0) nor SSD_BF16 (1)", sh->ydtype);
-    if (sh->reserved[0] != 0 || sh->reserved[1] != 0)
-        return fail(SSD_ERR_SHAPE, "reserved fields must be 0");
+    if (sh->reserved != 0) return fail(SSD_ERR_SHAPE, "reserved must be 0");
+    if (sh->path < SSD_PATH_AUTO || sh->path > SSD_PATH_SCAN_WALK)
+        return fail(SSD_ERR_VALUE, "path %d is not one of the SSD_PATH_* values", sh->path);
     if (sh->nheads < 1) return fail(SSD_ERR_SHAPE, "nheads must be >= 1 (got %d)", sh->nheads);
     if (sh->ngroups < 1 || sh->nheads % sh->ngroups != 0)
         return fail(SSD_ERR_SHAPE, "ngroups %d must be >= 1 and divide nheads %d", sh->ngroups,
@@ -170,6 +217,17 @@ ssd_status prepare(const ssd_shape* sh, int32_t chunk, Prepared* out) {
         return fail(SSD_ERR_SHAPE, "nheads * headdim %lld too large", (long long)sh->nheads * sh->headdim);
     pl.nchunk_ub = (int32_t)nchunks;
 
+    // kernel path: the caller's, or the library's choice
+    const bool walk_ok = ssd::scan_walk_supported(sh->dtype, sh->dstate, chunk);
+    if (sh->path == SSD_PATH_SCAN_WALK && !walk_ok)
+        return fail(SSD_ERR_UNSUPPORTED,
+                    "the scan walk needs bf16 inputs, 256-token chunks and dstate in (64, 128]");
+    if (sh->path != SSD_PATH_AUTO) out->path = sh->path;
+    else if (!fuse_state_passing(pl, sh)) out->path = ssd::kPathChunkParallel;
+    else out->path = (walk_ok && kAutoScanWalk) ? ssd::kPathScanWalk : ssd::kPathStateWalk;
+    walk_split(pl, &out->walk_nus, &out->walk_nslice);
+    const bool scan_walk = out->path == ssd::kPathScanWalk;
+
     ssd::Layout& L = out->lay;
     const size_t es = sh->dtype == SSD_BF16 ? 2 : 4;
     size_t off = 0;
@@ -182,10 +240,10 @@ ssd_status prepare(const ssd_shape* sh, int32_t chunk, Prepared* out) {
     L.chunk_tab = take(packed ? (size_t)pl.nchunk_ub * 16 : 0);
     L.cs = take((size_t)pl.nchunk_ub * pl.H * chunk * 4);
     L.dtc = take((size_t)pl.nchunk_ub * pl.H * chunk * 4);
-    L.wst = take((size_t)pl.nchunk_ub * pl.H * chunk * 4);
+    L.wst = take(scan_walk ? 0 : (size_t)pl.nchunk_ub * pl.H * chunk * 4);
     L.cb = take((size_t)pl.nchunk_ub * pl.G * chunk * chunk * es);
     L.bt = take((size_t)pl.nchunk_ub * pl.G * ssd::padded_dstate(pl.N) * chunk * es);
-    L.states = take((size_t)pl.nchunk_ub * pl.H * pl.P * pl.N * 4);
+    L.states = take(scan_walk ? 0 : (size_t)pl.nchunk_ub * pl.H * pl.P * pl.N * 4);
     L.total = std::max<size_t>(off, 256);
     return SSD_OK;
 }
@@ -198,7 +256,7 @@ SSD_API const char* ssd_status_string(int32_t status) {
         case SSD_ERR_NULL: return "a required pointer is NULL";
         case SSD_ERR_SHAPE: return "a size is out of range or inconsistent";
         case SSD_ERR_DTYPE: return "unknown dtype";
-        case SSD_ERR_ALIGN: return "a tensor pointer is not 16-byte aligned";
+        case SSD_ERR_ALIGN: return "a tensor pointer is not aligned as required";
         case SSD_ERR_CHUNK: return "chunk must be 32, 64, 128 or 256";
         case SSD_ERR_WORKSPACE: return "workspace missing or too small";
         case SSD_ERR_HIP: return "HIP runtime error";
@@ -227,26 +285,18 @@ ssd_status scan_impl(const void* x, const float* dt, const float* A, const void*
                      const float* D, int32_t chunk, const float* init_state, void* y,
                      float* final_state, const ssd_shape* shape, void* workspace,
                      size_t workspace_bytes, void* stream, hipEvent_t* marks,
-                     int* fused_out = nullptr, const ssd::DtAct* act = nullptr) {
+                     int* path_out = nullptr, const ssd::DtAct* act = nullptr) {
     Prepared pr;
     ssd_status st = prepare(shape, chunk, &pr);
     if (st != SSD_OK) return st;
     const bool any_tokens = pr.plan.T > 0;
-    struct {
-        const void* p;
-        const char* name;
-        bool required;
-    } ptrs[] = {{x, "x", any_tokens},   {dt, "dt", any_tokens},     {A, "A", true},
-                {B, "B", any_tokens},   {C, "C", any_tokens},       {D, "D", true},
-                {y, "y", any_tokens},   {init_state, "init_state", false},
-                {final_state, "final_state", false},             {workspace, "workspace", true}};
-    for (auto& q : ptrs) {
-        if (!q.p && q.required) {
-            if (q.name[0] == 'w') return fail(SSD_ERR_WORKSPACE, "workspace is NULL");
-            return fail(SSD_ERR_NULL, "%s is NULL", q.name);
-        }
-        if (q.p && !aligned16(q.p)) return fail(SSD_ERR_ALIGN, "%s is not 16-byte aligned", q.name);
-    }
+    const PtrArg ptrs[] = {{x, "x", any_tokens, 16},          {dt, "dt", any_tokens, 4},
+                           {A, "A", true, 4},                 {B, "B", any_tokens, 16},
+                           {C, "C", any_tokens, 16},          {D, "D", true, 4},
+                           {y, "y", any_tokens, 16},          {init_state, "init_state", false, 16},
+                           {final_state, "final_state", false, 16}, {workspace, "workspace", true, 16}};
+    st = check_ptrs(ptrs, (int)(sizeof(ptrs) / sizeof(ptrs[0])));
+    if (st != SSD_OK) return st;
     if (workspace_bytes < pr.lay.total)
         return fail(SSD_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes,
                     pr.lay.total);
@@ -267,9 +317,11 @@ ssd_status scan_impl(const void* x, const float* dt, const float* A, const void*
     a.y_f32 = shape->ydtype == SSD_F32 ? 1 : 0;
     a.hpw = heads_per_workgroup(pr.plan, kScanWorkgroups, pr.plan.hpg);
     a.hpw_state = heads_per_workgroup(pr.plan, kStateWorkgroups, kStateMaxHeads);
-    a.fused = fuse_state_passing(pr.plan, shape) ? 1 : 0;
+    a.path = pr.path;
+    a.walk_nus = pr.walk_nus;
+    a.walk_nslice = pr.walk_nslice;
     a.act = act ? *act : ssd::DtAct{nullptr, 0.f, 0.f, 0};
-    if (fused_out) *fused_out = a.fused;
+    if (path_out) *path_out = a.path;
     pr.plan.seq_tab = (int32_t*)(a.ws + pr.lay.seq_tab);
     pr.plan.chunk_tab = (int32_t*)(a.ws + pr.lay.chunk_tab);
     if (pr.plan.nseq == 0 && !marks) return ok();
@@ -297,6 +349,7 @@ SSD_API ssd_status ssd_chunked_scan_profiled(const void* x, const float* dt, con
                                              void* workspace, size_t workspace_bytes, void* stream,
                                              float* stage_ms) {
     if (!stage_ms) return fail(SSD_ERR_NULL, "stage_ms is NULL");
+    static_assert(SSD_PREFILL_STAGES == ssd::kPrefillStages, "stage count");
     constexpr int kMarks = SSD_PREFILL_STAGES + 1;
     hipEvent_t ev[kMarks] = {};
     hipError_t err = hipSuccess;
@@ -307,13 +360,18 @@ SSD_API ssd_status ssd_chunked_scan_profiled(const void* x, const float* dt, con
         st = fail(SSD_ERR_HIP, "hipEventCreate failed: %s", hipGetErrorString(err));
         --made;
     } else {
-        int fused = 0;
+        int path = 0;
         st = scan_impl(x, dt, A, B, C, D, chunk, init_state, y, final_state, shape, workspace,
-                       workspace_bytes, stream, ev, &fused);
+                       workspace_bytes, stream, ev, &path);
         if (st == SSD_OK) err = hipEventSynchronize(ev[kMarks - 1]);
         for (int i = 0; st == SSD_OK && err == hipSuccess && i < SSD_PREFILL_STAGES; ++i)
             err = hipEventElapsedTime(&stage_ms[i], ev[i], ev[i + 1]);
-        if (st == SSD_OK && err == hipSuccess && fused) stage_ms[4] = 0.f;  // folded into chunk_state
+        // stages a path does not run read exactly 0 (their marks are back to back)
+        if (st == SSD_OK && err == hipSuccess) {
+            if (path == ssd::kPathStateWalk) stage_ms[4] = 0.f;  // inside chunk_state
+            if (path == ssd::kPathScanWalk) stage_ms[3] = stage_ms[4] = stage_ms[5] = 0.f;
+            if (path != ssd::kPathScanWalk) stage_ms[6] = 0.f;
+        }
         if (st == SSD_OK && err != hipSuccess)
             st = fail(SSD_ERR_HIP, "event timing failed: %s", hipGetErrorString(err));
     }
@@ -326,7 +384,7 @@ namespace {
 // Validated copy of an activation argument.
 ssd_status dt_act_of(const ssd_dt_activation* act, ssd::DtAct* out) {
     if (!act) return fail(SSD_ERR_NULL, "act is NULL");
-    if (act->dt_bias && !aligned16(act->dt_bias)) return fail(SSD_ERR_ALIGN, "dt_bias is not 16-byte aligned");
+    if (act->dt_bias && !aligned4(act->dt_bias)) return fail(SSD_ERR_ALIGN, "dt_bias is not 4-byte aligned");
     const float lo = act->dt_min, hi = act->dt_max;
     if (!(lo >= 0.f) || lo > 3.0e38f) return fail(SSD_ERR_VALUE, "dt_min %g must be finite and >= 0", (double)lo);
     if (!(hi >= lo)) return fail(SSD_ERR_VALUE, "dt_max %g must be >= dt_min %g", (double)hi, (double)lo);
@@ -377,16 +435,11 @@ ssd_status check_decode(const float* state, const void* x, const float* dt, cons
     ssd_status st = check_head_dims(shape);
     if (st != SSD_OK) return st;
     const bool any = shape->batch > 0;
-    struct {
-        const void* p;
-        const char* name;
-        bool required;
-    } ptrs[] = {{state, "state", any}, {x, "x", any}, {dt, "dt", any}, {A, "A", true},
-                {B, "B", any},         {C, "C", any}, {D, "D", true},  {y, "y", any}};
-    for (auto& q : ptrs) {
-        if (!q.p && q.required) return fail(SSD_ERR_NULL, "%s is NULL", q.name);
-        if (q.p && !aligned16(q.p)) return fail(SSD_ERR_ALIGN, "%s is not 16-byte aligned", q.name);
-    }
+    const PtrArg ptrs[] = {{state, "state", any, 16}, {x, "x", any, 16}, {dt, "dt", any, 4},
+                           {A, "A", true, 4},          {B, "B", any, 16}, {C, "C", any, 16},
+                           {D, "D", true, 4},          {y, "y", any, 16}};
+    st = check_ptrs(ptrs, (int)(sizeof(ptrs) / sizeof(ptrs[0])));
+    if (st != SSD_OK) return st;
     if (y && (y == x || y == B || y == C || y == (const void*)state))
         return fail(SSD_ERR_SHAPE, "y aliases an input");
     if (shape->batch * (int64_t)shape->nheads * shape->headdim > ((int64_t)1 << 40))

@@ -119,6 +119,8 @@ __global__ __launch_bounds__(kDecThreads) void ssd_decode_kernel(
     const float a = __expf(d * Ah);
     const f32x4 bv = nv ? Tr<T>::widen4(bq) : f32x4{};
     const f32x4 cv = nv ? Tr<T>::widen4(cq) : f32x4{};
+    // xs is read across lanes below: keep its writes ahead of those reads
+    __builtin_amdgcn_wave_barrier();
     for (int p0 = 0; p0 < P; p0 += RPB) {
         load(min(p0 + RPB, P - 1), sn);  // next batch (repeats the last rows at the end)
 #pragma unroll
@@ -135,6 +137,8 @@ __global__ __launch_bounds__(kDecThreads) void ssd_decode_kernel(
 #pragma unroll
         for (int u = 0; u < kBatch; ++u) s[u] = sn[u];
     }
+    // ys rows were written by other lanes
+    __builtin_amdgcn_wave_barrier();
     const float y0 = ys[min(lane, P - 1)], y1 = ys[min(lane + 64, P - 1)];
     if (y_f32) {
         __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, y0), ry, lane < P ? lane * 4 : kOutOfRange,

@@ -35,9 +35,11 @@ struct Layout {
     size_t cs;      // f32 [nchunk_ub][H][Q]   inclusive sums of dt A within each chunk
     size_t dtc;     // f32 [nchunk_ub][H][Q]   dt per chunk and head, 0 past the chunk end
     size_t wst;     // f32 [nchunk_ub][H][Q]   exp(cs_last - cs) dt, each token's weight in the chunk state
+                    //                         (not used by the scan walk: empty there)
     size_t cb;      // elem [nchunk_ub][G][Q][Q] C_t . B_k within each chunk
     size_t bt;      // elem [nchunk_ub][G][NT * Q] B transposed per chunk in MFMA fragment order, 0 past the end and N
     size_t states;  // f32 [nchunk_ub][H][P][N] chunk states, then the states entering each chunk
+                    //                         (not used by the scan walk: empty there)
     size_t total;
 };
 
@@ -64,9 +66,50 @@ struct ScanArgs {
     int32_t y_f32;     // 1: y is fp32, 0: y is bf16
     int32_t hpw;       // heads per workgroup of chunk_scan (within one group)
     int32_t hpw_state; // heads per workgroup of the chunk-parallel chunk_state
-    int32_t fused;     // 1: chunk states and state passing in one launch per (sequence, head, tile)
+    int32_t path;      // kPathChunkParallel, kPathStateWalk or kPathScanWalk
+    int32_t walk_nus;  // scan walk: units (head, column tile) per workgroup
+    int32_t walk_nslice; // scan walk: workgroups per (sequence, group)
     DtAct act;
 };
+
+// How the prefill computes the chunk states, the passing between chunks and
+// the outputs:
+//   kPathChunkParallel  chunk_state, state_passing, chunk_scan: three launches,
+//                       each parallel over chunks (the per-chunk states round
+//                       trip through the workspace)
+//   kPathStateWalk      one walk per (sequence, head, column tile) for the
+//                       states and their passing, then chunk_scan
+//   kPathScanWalk       one walk per (sequence, group, slice of units) that
+//                       also writes y: no per-chunk state leaves the chip
+//                       (bf16 inputs, 256-token chunks, dstate in (64, 128])
+constexpr int32_t kPathChunkParallel = 1;
+constexpr int32_t kPathStateWalk = 2;
+constexpr int32_t kPathScanWalk = 3;
+
+// Arguments of the scan walk launch.
+struct WalkArgs {
+    const void* x;
+    const float* cs;
+    const float* dtc;
+    const void* C;
+    const void* cb;
+    const void* bt;
+    const float* D;
+    const float* init;
+    float* final_state;
+    void* y;
+    int32_t per_xcd, npt, nslice, nus;
+    int32_t y_f32;
+};
+
+// Whether the scan walk kernel covers this dtype, dstate and chunk.
+bool scan_walk_supported(int dtype, int N, int Q);
+
+// LDS bytes per workgroup of the scan walk.
+size_t scan_walk_lds_bytes();
+
+// Queue the scan walk (after the cumsum and C.B^T kernels).
+hipError_t launch_scan_walk(const Plan& plan, const WalkArgs& a, hipStream_t stream);
 
 struct DecodeArgs {
     float* state;
@@ -124,9 +167,11 @@ size_t prefill_lds_bytes(int dtype, int N, int Q);
 
 // Queue the prefill kernels.  Returns hipSuccess or the launch error.
 // When `marks` is non-NULL, an event is recorded before the first stage and
-// after each of the six stages (plan, cumsum, cb, chunk_state, state_passing,
-// chunk_scan), seven events in all.  With a.fused the chunk_state stage
-// includes the state passing and the state_passing stage is empty.
+// after each of the seven stages (plan, cumsum, cb, chunk_state,
+// state_passing, chunk_scan, scan_walk), eight events in all.  Stages a path
+// does not run are empty: the state walk runs inside chunk_state, and the
+// scan walk alone replaces chunk_state, state_passing and chunk_scan.
+constexpr int kPrefillStages = 7;
 hipError_t launch_prefill(const Plan& plan, const Layout& lay, const ScanArgs& a,
                           hipStream_t stream, hipEvent_t* marks = nullptr);
 

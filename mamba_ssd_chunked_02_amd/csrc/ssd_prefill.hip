@@ -33,7 +33,7 @@
 // fp32 accumulation everywhere.
 #include <algorithm>
 
-#include "ssd_device.h"
+#include "ssd_prefill_shared.h"
 
 namespace ssd {
 
@@ -111,7 +111,7 @@ __global__ __launch_bounds__(kThreads) void ssd_plan_kernel(Plan pl) {
 //            end repeat the last value (dt = 0 there)
 //   dtc[q] = dt with zeros past the end
 //   wst[q] = exp(cs[Q-1] - cs[q]) dt[q], each token's weight in the chunk
-//            state (<= dt, 0 past the end)
+//            state (<= dt, 0 past the end); not written when wst is NULL
 constexpr int kCumHeads = 16;
 
 __global__ __launch_bounds__(kThreads) void ssd_cumsum_kernel(Plan pl, const float* __restrict__ dt,
@@ -164,18 +164,29 @@ __global__ __launch_bounds__(kThreads) void ssd_cumsum_kernel(Plan pl, const flo
             run += d[i] * a;
             c[i] = run;
         }
-        // cs[Q-1], from the lane that holds it
-        const float last = __shfl(run, (Q - 1) / ppl);
+        // The sums past the chunk end add only zeros, but the lane totals
+        // reach later lanes through the scan tree in another order, so they
+        // can differ from cs[len-1] in the last bit; once |cs| is large
+        // (a flushing decay) exp() turns that bit into a visible factor.
+        // Every position past the end, and cs_last, therefore takes the
+        // bits of cs[len-1] itself.
+        const int il = (cd.len - 1) % ppl;
+        const float mine = il == 0 ? c[0] : il == 1 ? c[1] : il == 2 ? c[2] : c[3];
+        const float last = __shfl(mine, (cd.len - 1) / ppl);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            if (lane * ppl + i >= cd.len) c[i] = last;
         float* csr = cs + ((size_t)k * H + h) * Q;
         float* dtr = dtc + ((size_t)k * H + h) * Q;
-        float* wsr = wst + ((size_t)k * H + h) * Q;
         if (ppl == 4) {
             // 256-token chunks: four consecutive positions per lane, 16-byte stores
             const int q = 4 * lane;
             *(f32x4*)(csr + q) = f32x4{c[0], c[1], c[2], c[3]};
             *(f32x4*)(dtr + q) = f32x4{d[0], d[1], d[2], d[3]};
-            *(f32x4*)(wsr + q) = f32x4{__expf(last - c[0]) * d[0], __expf(last - c[1]) * d[1],
-                                       __expf(last - c[2]) * d[2], __expf(last - c[3]) * d[3]};
+            if (wst)
+                *(f32x4*)(wst + ((size_t)k * H + h) * Q + q) =
+                    f32x4{__expf(last - c[0]) * d[0], __expf(last - c[1]) * d[1], __expf(last - c[2]) * d[2],
+                          __expf(last - c[3]) * d[3]};
         } else {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -183,27 +194,14 @@ __global__ __launch_bounds__(kThreads) void ssd_cumsum_kernel(Plan pl, const flo
                 if (i < ppl && q < Q) {
                     csr[q] = c[i];
                     dtr[q] = d[i];
-                    wsr[q] = __expf(last - c[i]) * d[i];
+                    if (wst) wst[((size_t)k * H + h) * Q + q] = __expf(last - c[i]) * d[i];
                 }
             }
         }
     }
 }
 
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-
 // ------------------------------------------------------------------ C.B^T
-// B^T of a chunk is kept in the order the chunk_state MFMAs consume it: for
-// n-tile nt (32 values of n), k-step s (16 tokens) and lane l = 32 half + col
-// the eight tokens 16 s + 8 half + j (j < 8) of row n = 32 nt + col are
-// consecutive, so each wave-wide 16-byte-per-lane load reads one contiguous
-// fragment.  Element (n, t) of chunk k, group g sits at
-//   bt[(k G + g) ntp Q + ((nt (Q/16) + s) 64 + l) 8 + j].
-__host__ __device__ constexpr int bt_frag(int Q, int nt, int s, int lane) {
-    return ((nt * (Q / 16) + s) * 64 + lane) * 8;
-}
-
 // grid (chunks, G, NTI (NTI + 1) / 2), one wave per causal 32 x 32 tile
 // (ti, kj <= ti) of cb = C B^T, stored in the input dtype, the part the chunk
 // scan reads; the diagonal tile's entries above the diagonal are zero, rows
@@ -400,62 +398,6 @@ template <typename T>
 struct Split {
     static constexpr bool on = !__is_same(T, float);
 };
-
-// Grid order: item i of a chunk-major work list runs as workgroup L with
-// i = (L % 8) * per_xcd + L / 8.  Workgroups are dealt to the 8 XCDs round
-// robin, so each XCD walks a contiguous range of items: the heads and column
-// tiles of one chunk run together and share its C.B^T, C and B^T in that
-// XCD's L2.
-__device__ inline int64_t xcd_item(int per_xcd) {
-    return (int64_t)(blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
-}
-
-// Raw buffer access (gfx9 descriptor: untyped 32-bit data format word).
-constexpr int kBufferWord3 = 0x00020000;
-
-__device__ inline __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kBufferWord3);
-}
-
-// A raw buffer offset past any descriptor's range (accesses there are dropped).
-constexpr int kOutOfRange = 0x7ffffff0;
-
-// Four consecutive outputs through a raw buffer descriptor (byte offset voff).
-// These stores carry the non-temporal hint: y and the per-chunk states are
-// written once and not read again by the same kernel, so they should not
-// displace its inputs from the caches.
-constexpr int kNonTemporal = 2;  // cache-policy bit of gfx9.4+ buffer instructions
-template <typename TY>
-__device__ inline void buffer_store4(f32x4 v, __amdgpu_buffer_rsrc_t r, int voff);
-template <>
-__device__ inline void buffer_store4<float>(f32x4 v, __amdgpu_buffer_rsrc_t r, int voff) {
-    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, voff, 0, kNonTemporal);
-}
-template <>
-__device__ inline void buffer_store4<bf16_t>(f32x4 v, __amdgpu_buffer_rsrc_t r, int voff) {
-    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, Tr<bf16_t>::narrow4(v)), r, voff, 0,
-                                          kNonTemporal);
-}
-
-// Eight consecutive elements through a raw buffer descriptor (byte offset voff).
-template <typename T>
-__device__ inline typename Tr<T>::v8 buffer_ld8(__amdgpu_buffer_rsrc_t r, int voff);
-template <>
-__device__ inline bf16x8 buffer_ld8<bf16_t>(__amdgpu_buffer_rsrc_t r, int voff) {
-    return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0));
-}
-template <>
-__device__ inline f32x8 buffer_ld8<float>(__amdgpu_buffer_rsrc_t r, int voff) {
-    const f32x4 a = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0));
-    const f32x4 b = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff + 16, 0, 0));
-    return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
-}
-
-// The x rows of one chunk as a buffer: uniform base, 32-bit lane offsets.
-template <typename T>
-__device__ inline __amdgpu_buffer_rsrc_t chunk_x_rsrc(const T* x, const ChunkDesc& cd, int H, int P) {
-    return buffer_rsrc(x + (size_t)cd.row0 * H * P, (uint32_t)((size_t)cd.len * H * P * sizeof(T)));
-}
 
 // Per-wave LDS tile for the output transpose: 32 tokens x 32 columns fp32.
 constexpr int kEpPitch = 36;
@@ -1312,7 +1254,7 @@ hipError_t run_prefill(const Plan& pl, const Layout& lay, const ScanArgs& a, hip
     if ((err = mark(1)) != hipSuccess) return err;
     if (pl.nchunk_ub > 0) {
         hipLaunchKernelGGL(ssd_cumsum_kernel, dim3(pl.nchunk_ub, (pl.H + kCumHeads - 1) / kCumHeads), dim3(kThreads), 0,
-                           stream, pl, a.dt, a.A, cs, dtc, wst, a.act);
+                           stream, pl, a.dt, a.A, cs, dtc, a.path == kPathScanWalk ? nullptr : wst, a.act);
         if ((err = hipGetLastError()) != hipSuccess) return err;
     }
     if ((err = mark(2)) != hipSuccess) return err;
@@ -1333,7 +1275,32 @@ hipError_t run_prefill(const Plan& pl, const Layout& lay, const ScanArgs& a, hip
         if ((err = hipGetLastError()) != hipSuccess) return err;
     }
     if ((err = mark(3)) != hipSuccess) return err;
-    if (a.fused) {
+    if (a.path == kPathScanWalk) {
+        // one launch: states, their passing and y, per (sequence, group, slice of units)
+        if ((err = mark(4)) != hipSuccess) return err;
+        if ((err = mark(5)) != hipSuccess) return err;
+        if ((err = mark(6)) != hipSuccess) return err;
+        WalkArgs wa;
+        wa.x = a.x;
+        wa.cs = cs;
+        wa.dtc = dtc;
+        wa.C = a.C;
+        wa.cb = cbm;
+        wa.bt = bt;
+        wa.D = a.D;
+        wa.init = a.init;
+        wa.final_state = a.final_state;
+        wa.y = a.y;
+        wa.npt = npt;
+        wa.nslice = a.walk_nslice;
+        wa.nus = a.walk_nus;
+        const int64_t nwalk = (int64_t)pl.nseq * pl.G * a.walk_nslice;
+        wa.per_xcd = (int)((nwalk + 7) / 8);
+        wa.y_f32 = a.y_f32;
+        if ((err = launch_scan_walk(pl, wa, stream)) != hipSuccess) return err;
+        return mark(7);
+    }
+    if (a.path == kPathStateWalk) {
         // one launch walks every sequence: chunk states and the passing between them
         const int64_t nfused = (int64_t)pl.nseq * pl.H * npt;
         const int fper_xcd = (int)((nfused + 7) / 8);
@@ -1377,7 +1344,7 @@ hipError_t run_prefill(const Plan& pl, const Layout& lay, const ScanArgs& a, hip
         if ((err = hipGetLastError()) != hipSuccess) return err;
     }
     if ((err = mark(6)) != hipSuccess) return err;
-    return hipSuccess;
+    return mark(7);
 }
 
 template <typename T, typename TY>

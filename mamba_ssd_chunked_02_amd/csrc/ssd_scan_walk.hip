@@ -1,0 +1,584 @@
+// Fused chunked scan on gfx950: chunk states, the passing between chunks and
+// the chunk outputs of one sequence in a single walk over its chunks, so the
+// state entering each chunk never leaves the chip and x is read once.
+//
+// The computation is the chunked regrouping of the recurrence
+//   S_t = exp(dt_t A) S_{t-1} + dt_t x_t (outer) B_t,   y_t = S_t C_t + D x_t
+// ("Engineering hybrid state-space models", section 2: the duality
+// Y = (M o CB^T) X over chunks of Q tokens; "Compiler-First State Space
+// Duality...", abstract: fixed-size chunking, einsum-shaped contractions).
+// Per chunk c with entering state h_c, inclusive decay sums cs inside the
+// chunk and the chunk cut into 32-token blocks j:
+//   y_t     = exp(cs_t) C_t h_c^T + sum_{s<=t} (C_t . B_s) exp(cs_t - cs_s) dt_s x_s + D x_t
+//   h_{c+1} = Horner over the blocks: H <- gam_j H + sum_{s in j} wb_s x_s (outer) B_s,
+//             starting from H = h_c, with gam_j = exp(decay across block j) <= 1
+//             and wb_s = exp(cs_end(j) - cs_s) dt_s <= dt_s,
+// so h_{c+1} = exp(cs_last) h_c + sum_s exp(cs_last - cs_s) dt_s x_s (outer) B_s.
+//
+// Work item: one sequence, one group, and a slice of up to NU units, a unit
+// being (head of the group, 32-column tile of P).  The workgroup walks the
+// sequence's chunks in order and, inside a chunk, its units in order: one
+// step per (chunk, unit).  Eight waves with two roles:
+//   waves 0-3  output blocks (w, 7-w) of y: they hold the chunk's C.B^T rows
+//              and C rows of their two blocks in registers for every unit of
+//              the chunk, and read the unit's staged x and state from LDS;
+//   waves 4-7  n-tile w-4 of every unit's state, kept in MFMA accumulators
+//              across the whole walk (the transposed tile h^T[n][p]); per step
+//              they advance the current unit's tile over the chunk, write the
+//              next step's state as a hi/lo bf16 pair to LDS, stage the next
+//              step's x and decay tables in LDS and load the step after that.
+// LDS holds two staging buffers and two state buffers (141 KB); one barrier
+// per step separates the step that reads a buffer from the one that refills
+// it.  Only bf16 inputs, 256-token chunks and dstate in (64, 128] take this
+// kernel; the host picks the separate kernels for everything else.
+#include "ssd_prefill_shared.h"
+
+namespace ssd {
+
+namespace {
+
+constexpr int kQ = 256;          // chunk length
+constexpr int kNTI = kQ / 32;    // 32-token blocks per chunk
+constexpr int kNT = 128;         // dstate rows, padded
+constexpr int kLP = kQ + 8;      // token pitch (elements) of the transposed x tiles
+constexpr int kNS = kNT + 8;     // n pitch (elements) of the state tiles
+constexpr float kFastDecay = 60.f;  // same bound as the chunk scan's Horner scheme
+
+// One staging buffer: tables | (x wb)^T hi | (x wb)^T lo | x^T, the tiles
+// [32 columns p][kLP tokens] in bf16.
+constexpr size_t kTabBytes = (size_t)(4 * kQ + 16) * 4;
+constexpr size_t kTileBytes = (size_t)32 * kLP * 2;
+constexpr size_t kStageBytes = kTabBytes + 3 * kTileBytes;
+// One state buffer: h hi, h lo as [32 columns p][kNS] bf16.
+constexpr size_t kStateBytes = (size_t)2 * 32 * kNS * 2;
+constexpr size_t kWalkLds = 2 * kStageBytes + 2 * kStateBytes;
+static_assert(kWalkLds <= 160 * 1024, "scan walk LDS");
+
+struct WalkTables {
+    float* cs;   // [Q] cs_t
+    float* dt;   // [Q] dt_t (0 past the chunk end)
+    float* ul;   // [Q] exp(cs_t - cs before t's block)          (<= 1)
+    float* ue;   // [Q] exp(min(cs_t - cs at t's block end, 60))   (>= 1)
+    float* gam;  // [8] decay across each block                   (<= 1)
+    int* fast;   // [8] block decay below kFastDecay
+};
+
+__device__ inline WalkTables walk_tables(char* base) {
+    WalkTables t;
+    t.cs = (float*)base;
+    t.dt = t.cs + kQ;
+    t.ul = t.dt + kQ;
+    t.ue = t.ul + kQ;
+    t.gam = t.ue + kQ;
+    t.fast = (int*)(t.gam + 8);
+    return t;
+}
+
+struct WalkBufs {
+    char* smem;
+    __device__ char* stage(int b) const { return smem + b * kStageBytes; }
+    __device__ bf16_t* xh(int b) const { return (bf16_t*)(stage(b) + kTabBytes); }
+    __device__ bf16_t* xl(int b) const { return xh(b) + 32 * kLP; }
+    __device__ bf16_t* xr(int b) const { return xl(b) + 32 * kLP; }
+    __device__ bf16_t* sh(int b) const { return (bf16_t*)(smem + 2 * kStageBytes + b * kStateBytes); }
+    __device__ bf16_t* sl(int b) const { return sh(b) + 32 * kNS; }
+};
+
+// The walk of one workgroup: sequence s, group g, units [u0, u0 + nu) of the
+// group's hpg * npt units (unit u: head g hpg + u / npt, column tile u % npt).
+struct Walk {
+    int s, g, u0, nu, npt;
+    int chunk0, nck, len;  // first chunk, chunk count, tokens of the sequence
+    int64_t row0;          // first token row of the sequence
+    __device__ int head(const Plan& pl, int j) const { return g * pl.hpg + (u0 + j) / npt; }
+    __device__ int tile(int j) const { return (u0 + j) % npt; }
+    __device__ ChunkDesc chunk(int c) const {
+        ChunkDesc d;
+        d.seq = s;
+        d.idx = c;
+        d.row0 = row0 + (int64_t)c * kQ;
+        d.len = min(kQ, len - c * kQ);
+        return d;
+    }
+};
+
+__device__ inline bool walk_of(const Plan& pl, int per_xcd, int npt, int nslice, int nus, Walk& w) {
+    const int64_t item = xcd_item(per_xcd);
+    if (item >= (int64_t)pl.nseq * pl.G * nslice) return false;
+    const int slice = (int)(item % nslice);
+    const int64_t r = item / nslice;
+    w.g = (int)(r % pl.G);
+    w.s = (int)(r / pl.G);
+    w.npt = npt;
+    w.u0 = slice * nus;
+    w.nu = min(nus, pl.hpg * npt - w.u0);
+    const SeqExtent se = seq_extent(pl, w.s);
+    w.chunk0 = __builtin_amdgcn_readfirstlane(se.chunk0);
+    w.nck = __builtin_amdgcn_readfirstlane(se.nchunks);
+    w.len = __builtin_amdgcn_readfirstlane(se.len);
+    w.row0 = (int64_t)__builtin_amdgcn_readfirstlane((int)se.row0);
+    return w.nu > 0;
+}
+
+// ------------------------------------------------------------------ staging (waves 4-7)
+// Thread tau of the 256 staging threads owns 4 consecutive tokens k0..k0+3
+// and 8 columns 8 pb..8 pb+7 of the unit's tile: it loads 4 x 16 bytes of x
+// plus the tokens' decay sums and steps, and writes the column-major tiles
+// (4 tokens = 8 bytes per column).  The threads of pb = 0 also write the
+// decay tables of their 4 tokens, and of their block when k0 starts one.
+struct StageRegs {
+    bf16x8 raw[4];
+    f32x4 cs4, dt4;
+    float ce, c0;  // cs at the end of the tokens' block, cs before its start
+};
+
+__device__ inline int stage_pb(int tau) { return (tau >> 4) & 3; }
+__device__ inline int stage_k0(int tau) { return 4 * ((tau & 15) + 16 * (tau >> 6)); }
+
+__device__ inline void stage_load(StageRegs& r, const Plan& pl, const Walk& w, int c, int j, const bf16_t* x,
+                                  const float* cs, const float* dtc, int tau) {
+    const ChunkDesc d = w.chunk(c);
+    const int k = w.chunk0 + c, h = w.head(pl, j), pt = w.tile(j);
+    const int H = pl.H, P = pl.P;
+    const int pb = stage_pb(tau), k0 = stage_k0(tau);
+    const int pc = 32 * pt + 8 * pb;
+    const int p0 = pc < P ? pc : 0;
+    const __amdgpu_buffer_rsrc_t rx = chunk_x_rsrc(x, d, H, P);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int kk = min(k0 + i, d.len - 1);
+        r.raw[i] = buffer_ld8<bf16_t>(rx, ((kk * H + h) * P + p0) * 2);
+    }
+    const float* csk = cs + ((size_t)k * H + h) * kQ;
+    const float* dtk = dtc + ((size_t)k * H + h) * kQ;
+    r.cs4 = *(const f32x4*)(csk + k0);
+    r.dt4 = *(const f32x4*)(dtk + k0);
+    r.ce = csk[k0 | 31];
+    r.c0 = csk[max((k0 & ~31) - 1, 0)];
+}
+
+__device__ inline void stage_store(const StageRegs& r, const Plan& pl, const Walk& w, const WalkBufs& bufs, int c,
+                                   int j, int b, int tau) {
+    const ChunkDesc d = w.chunk(c);
+    const int pb = stage_pb(tau), k0 = stage_k0(tau);
+    const bool pok = 32 * w.tile(j) + 8 * pb < pl.P;
+    const float c0 = k0 >= 32 ? r.c0 : 0.f;
+    float wb[4];
+    bf16x8 xm[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        wb[i] = pok ? __expf(r.ce - r.cs4[i]) * r.dt4[i] : 0.f;  // dt is 0 past the chunk end
+        xm[i] = (pok && k0 + i < d.len) ? r.raw[i] : bf16x8{};
+    }
+    bf16_t* xh = bufs.xh(b) + (8 * pb) * kLP + k0;
+    bf16_t* xl = bufs.xl(b) + (8 * pb) * kLP + k0;
+    bf16_t* xr = bufs.xr(b) + (8 * pb) * kLP + k0;
+#pragma unroll
+    for (int col = 0; col < 8; ++col) {
+        const f32x4 o = {(float)xm[0][col] * wb[0], (float)xm[1][col] * wb[1], (float)xm[2][col] * wb[2],
+                         (float)xm[3][col] * wb[3]};
+        const bf16x4 hi = Tr<bf16_t>::narrow4(o);
+        Tr<bf16_t>::st4raw(xh + col * kLP, hi);
+        Tr<bf16_t>::st4raw(xl + col * kLP, Tr<bf16_t>::narrow4(o - Tr<bf16_t>::widen4(hi)));
+        Tr<bf16_t>::st4raw(xr + col * kLP, bf16x4{xm[0][col], xm[1][col], xm[2][col], xm[3][col]});
+    }
+    if (pb == 0) {
+        const WalkTables tb = walk_tables(bufs.stage(b));
+        *(f32x4*)(tb.cs + k0) = r.cs4;
+        *(f32x4*)(tb.dt + k0) = r.dt4;
+        f32x4 ul, ue;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            ul[i] = __expf(r.cs4[i] - c0);
+            ue[i] = __expf(fminf(r.cs4[i] - r.ce, kFastDecay));
+        }
+        *(f32x4*)(tb.ul + k0) = ul;
+        *(f32x4*)(tb.ue + k0) = ue;
+        if ((k0 & 31) == 0) {
+            tb.gam[k0 >> 5] = __expf(r.ce - c0);
+            tb.fast[k0 >> 5] = (c0 - r.ce) < kFastDecay ? 1 : 0;
+        }
+    }
+}
+
+// ------------------------------------------------------------------ state tiles (waves 4-7)
+// acc holds h^T[n][p] for n in n-tile nt (row 8 (v/4) + 4 half + v%4 of the
+// tile) and p = 32 pt + lane%32.  Written to a state buffer as [p][n]
+// hi/lo pairs: 4 consecutive n per lane and register group, 8 bytes each.
+__device__ inline void put_state(const f32x16& acc, const WalkBufs& bufs, int b, int nt) {
+    const int lane = threadIdx.x & 63, half = lane >> 5, col = lane & 31;
+    bf16_t* sh = bufs.sh(b) + col * kNS + 32 * nt + 4 * half;
+    bf16_t* sl = bufs.sl(b) + col * kNS + 32 * nt + 4 * half;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const f32x4 v = {acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]};
+        const bf16x4 hi = Tr<bf16_t>::narrow4(v);
+        Tr<bf16_t>::st4raw(sh + 8 * q, hi);
+        Tr<bf16_t>::st4raw(sl + 8 * q, Tr<bf16_t>::narrow4(v - Tr<bf16_t>::widen4(hi)));
+    }
+}
+
+// Byte offset of element (p, n) of a P x N state for the lane's accumulator
+// register v, or an offset past the descriptor when (p, n) is padding.
+__device__ inline int state_off(int v, int pt, int nt, int P, int N) {
+    const int lane = threadIdx.x & 63;
+    const int p = 32 * pt + (lane & 31);
+    const int n = 32 * nt + acc_row(v, lane);
+    return (p < P && n < N) ? (p * N + n) * 4 : kOutOfRange;
+}
+
+// One chunk of the state walk for the current unit: H <- Horner over the 8
+// blocks, as two interleaved chains so the MFMAs of one overlap the scaling
+// of the other:  O: h_c (as block -1), blocks 1, 3, 5, 7;  E: blocks 0, 2, 4, 6;
+// each chain scales by the decay across the two blocks it skips; at the end
+// H = O + gam_7 E.  A = the chunk's B^T fragments (n-tile rows), B = the
+// staged (x wb)^T hi and lo tiles.
+__device__ inline void walk_advance(f32x16& acc, const bf16x8 (&bf)[kQ / 16], const WalkBufs& bufs, int b) {
+    const int lane = threadIdx.x & 63, half = lane >> 5, col = lane & 31;
+    const WalkTables tb = walk_tables(bufs.stage(b));
+    const bf16_t* hrow = bufs.xh(b) + col * kLP + 8 * half;
+    const bf16_t* lrow = bufs.xl(b) + col * kLP + 8 * half;
+    const f32x4 g0 = *(const f32x4*)tb.gam;
+    const f32x4 g1 = *(const f32x4*)(tb.gam + 4);
+    const float gm[8] = {g0[0], g0[1], g0[2], g0[3], g1[0], g1[1], g1[2], g1[3]};
+    f32x16 e = {};
+    auto block = [&](f32x16& ch, int jb) {
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            const int s = 2 * jb + ks;
+            mma16(ch, bf[s], Tr<bf16_t>::ld8(hrow + 16 * s));
+            mma16(ch, bf[s], Tr<bf16_t>::ld8(lrow + 16 * s));
+        }
+    };
+    block(e, 0);
+#pragma unroll
+    for (int jb = 1; jb < kNTI; ++jb) {
+        if (jb & 1) {
+            acc *= gm[jb - 1] * gm[jb];
+            block(acc, jb);
+        } else {
+            e *= gm[jb - 1] * gm[jb];
+            block(e, jb);
+        }
+    }
+    acc += gm[kNTI - 1] * e;
+}
+
+template <int NU>
+__device__ void walk_states(const Plan& pl, const Walk& w, const WalkBufs& bufs, const bf16_t* __restrict__ x,
+                            const float* __restrict__ cs, const float* __restrict__ dtc,
+                            const bf16_t* __restrict__ bt, const float* __restrict__ init, float* __restrict__ fin) {
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int nt = __builtin_amdgcn_readfirstlane((tid >> 6) - 4);
+    const int tau = tid - 256;
+    const int P = pl.P, N = pl.N, H = pl.H, G = pl.G;
+    const int nu = w.nu;
+    const int total = w.nck * nu;
+    f32x16 acc[NU];
+#pragma unroll
+    for (int j = 0; j < NU; ++j) {
+        acc[j] = f32x16{};
+        if (j < nu && init) {
+            const int h = w.head(pl, j), pt = w.tile(j);
+            const __amdgpu_buffer_rsrc_t ri =
+                buffer_rsrc(init + ((size_t)w.s * H + h) * P * N, (uint32_t)(P * N * 4));
+#pragma unroll
+            for (int v = 0; v < 16; ++v)
+                acc[j][v] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                          ri, state_off(v, pt, nt, P, N), 0, 0));
+        }
+    }
+    bf16x8 bf[kQ / 16];
+    const int boff = bt_frag(kQ, nt, 0, lane) * 2;
+    auto load_bt = [&](int c) {
+        const __amdgpu_buffer_rsrc_t rb =
+            buffer_rsrc(bt + ((size_t)(w.chunk0 + c) * G + w.g) * kNT * kQ, (uint32_t)(kNT * kQ * 2));
+#pragma unroll
+        for (int s = 0; s < kQ / 16; ++s) bf[s] = buffer_ld8<bf16_t>(rb, boff + 512 * s * 2);
+    };
+    StageRegs sr;
+    auto load_step = [&](int i) {  // i < total
+        const int c = i / nu;
+        stage_load(sr, pl, w, c, i - c * nu, x, cs, dtc, tau);
+    };
+    if (total > 0) {
+        load_bt(0);
+        load_step(0);
+        stage_store(sr, pl, w, bufs, 0, 0, 0, tau);
+        put_state(acc[0], bufs, 0, nt);
+        load_step(min(1, total - 1));
+    }
+    __syncthreads();
+    for (int c = 0; c < w.nck; ++c) {
+#pragma unroll
+        for (int j = 0; j < NU; ++j) {
+            if (j < nu) {
+                const int i = c * nu + j, b = i & 1;
+                walk_advance(acc[j], bf, bufs, b);
+                if (j == nu - 1 && c + 1 < w.nck) load_bt(c + 1);
+                if (i + 1 < total) {
+                    // the next step's unit: j + 1 of this chunk, or unit 0 of
+                    // the next chunk (already advanced past this one)
+                    if (j + 1 < nu) put_state(acc[(j + 1) % NU], bufs, b ^ 1, nt);
+                    else put_state(acc[0], bufs, b ^ 1, nt);
+                    const int cn = j + 1 < nu ? c : c + 1, jn = j + 1 < nu ? j + 1 : 0;
+                    stage_store(sr, pl, w, bufs, cn, jn, b ^ 1, tau);
+                }
+                // unconditional (the last step repeats itself), so the wait
+                // counts never cover a path without these loads
+                load_step(min(i + 2, total - 1));
+                __syncthreads();
+            }
+        }
+    }
+    if (fin) {
+#pragma unroll
+        for (int j = 0; j < NU; ++j) {
+            if (j < nu) {
+                const int h = w.head(pl, j), pt = w.tile(j);
+                const __amdgpu_buffer_rsrc_t rf =
+                    buffer_rsrc(fin + ((size_t)w.s * H + h) * P * N, (uint32_t)(P * N * 4));
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    // the element goes through a scalar first: a bit cast of a
+                    // vector element expression compiles to element 0
+                    const float e = acc[j][v];
+                    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, e), rf,
+                                                          state_off(v, pt, nt, P, N), 0, 0);
+                }
+            }
+        }
+    }
+}
+
+// ------------------------------------------------------------------ outputs (waves 0-3)
+template <typename TY>
+__device__ inline void store_y(float v, __amdgpu_buffer_rsrc_t r, int voff);
+template <>
+__device__ inline void store_y<float>(float v, __amdgpu_buffer_rsrc_t r, int voff) {
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, voff, 0, kNonTemporal);
+}
+template <>
+__device__ inline void store_y<bf16_t>(float v, __amdgpu_buffer_rsrc_t r, int voff) {
+    __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, (bf16_t)v), r, voff, 0, kNonTemporal);
+}
+
+// Output block TI (tokens 32 TI .. 32 TI + 31, the tile's 32 columns) of one
+// unit: the state term C_rows . h_c^T from the staged hi/lo state.  The intra-chunk
+// term is the Horner scheme of the chunk scan: two chains over the blocks
+// kj <= TI with the (C.B^T) rows ga as A and the staged (x wb)^T as B, the
+// diagonal block inside the scheme when its decay is below kFastDecay (then
+// scaled by ue), else added with exact per-element factors after scaling by
+// ul.  y leaves from the accumulator layout: each register v is one row,
+// the wave's store covering two 128-byte row pieces.
+template <typename TY, int TI>
+__device__ __forceinline__ void walk_block(const bf16x8 (&ga)[TI + 1][2], const bf16x8 (&ca)[kNT / 16],
+                                           bool has_state, const bf16_t* shrow, const bf16_t* slrow,
+                                           const WalkTables& tb, const bf16_t* xhrow, const bf16_t* xrrow,
+                                           __amdgpu_buffer_rsrc_t ry, int ybase, int rowb, int len, bool cok,
+                                           float Dh) {
+    const int lane = threadIdx.x & 63, half = lane >> 5, col = lane & 31;
+    // the state term C_rows . h_c^T (hi and lo), a chain of its own
+    f32x16 sacc = {};
+    if (has_state) {
+#pragma unroll
+        for (int s = 0; s < kNT / 16; ++s) {
+            mma16(sacc, ca[s], Tr<bf16_t>::ld8(shrow + 16 * s));
+            mma16(sacc, ca[s], Tr<bf16_t>::ld8(slrow + 16 * s));
+        }
+    }
+    const bool fast = tb.fast[TI] != 0;
+    // blocks kj < TI: two chains (even and odd blocks), each stepping two
+    // blocks at a time with the product of their decays
+    f32x16 ce = {}, co = {};
+#pragma unroll
+    for (int kj = 0; kj < TI; ++kj) {
+        f32x16& ch = (kj & 1) ? co : ce;
+        if (kj >= 2) ch *= tb.gam[kj - 1] * tb.gam[kj];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) mma16(ch, ga[kj][ks], Tr<bf16_t>::ld8(xhrow + 32 * kj + 16 * ks));
+    }
+    // the chain that ends at the last included block K is complete; the other
+    // one still takes the decay across block K.  K is TI (diagonal block in
+    // the scheme) or TI - 1, so each branch knows both chains' roles.
+    f32x16 acc;
+    if (fast) {
+        f32x16& ch = (TI & 1) ? co : ce;
+        if (TI >= 2) ch *= tb.gam[TI - 1] * tb.gam[TI];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) mma16(ch, ga[TI][ks], Tr<bf16_t>::ld8(xhrow + 32 * TI + 16 * ks));
+        if (TI == 0) acc = ce;
+        else if (TI & 1) acc = co + tb.gam[TI] * ce;
+        else acc = ce + tb.gam[TI] * co;
+    } else {
+        if (TI <= 1) acc = ce;  // block 0 alone (TI = 1) or nothing (TI = 0, ce is zero)
+        else if ((TI - 1) & 1) acc = co + tb.gam[TI - 1] * ce;
+        else acc = ce + tb.gam[TI - 1] * co;
+    }
+    if (has_state) {
+        const int e = fast ? 32 * TI + 31 : 32 * TI - 1;
+        const float dec = e >= 0 ? __expf(tb.cs[e]) : 1.f;
+        acc += dec * sacc;
+    }
+    const float* scale = fast ? tb.ue : tb.ul;
+#pragma unroll
+    for (int vg = 0; vg < 4; ++vg) {
+        const f32x4 u = *(const f32x4*)(scale + 32 * TI + 8 * vg + 4 * half);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[4 * vg + i] *= u[i];
+    }
+    if (!fast) {
+        const float cst = tb.cs[32 * TI + col];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            const int k0 = 32 * TI + 16 * ks + 8 * half;
+            const f32x8 gv = Tr<bf16_t>::widen(ga[TI][ks]);
+            f32x8 m;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) m[i] = gv[i] * (__expf(fminf(cst - tb.cs[k0 + i], 0.f)) * tb.dt[k0 + i]);
+            mma16(acc, Tr<bf16_t>::narrow(m), Tr<bf16_t>::ld8(xrrow + k0));
+        }
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const f32x4 xv = Tr<bf16_t>::ld4(xrrow + 32 * TI + 8 * q + 4 * half);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[4 * q + i] += Dh * xv[i];
+    }
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+        const int r = 8 * (v >> 2) + (v & 3);  // + 4 half, folded into ybase
+        const bool ok = cok && 32 * TI + 4 * half + r < len;
+        store_y<TY>(acc[v], ry, ok ? ybase + r * rowb : kOutOfRange);
+    }
+}
+
+template <typename TY, int TA, int TB>
+__device__ void walk_outputs(const Plan& pl, const Walk& w, const WalkBufs& bufs, const bf16_t* __restrict__ Cm,
+                             const bf16_t* __restrict__ cb, const float* __restrict__ D, bool has_init,
+                             TY* __restrict__ y) {
+    const int lane = threadIdx.x & 63, half = lane >> 5, col = lane & 31;
+    const int H = pl.H, P = pl.P, N = pl.N, G = pl.G, HP = H * P;
+    bf16x8 ga_a[TA + 1][2], ga_b[TB + 1][2], ca_a[kNT / 16], ca_b[kNT / 16];
+    auto load_ops = [&](int c) {
+        const ChunkDesc d = w.chunk(c);
+        const bf16_t* cbk = cb + ((size_t)(w.chunk0 + c) * G + w.g) * kQ * kQ + 8 * half;
+        const bf16_t* ra = cbk + (size_t)(32 * TA + col) * kQ;
+        const bf16_t* rb = cbk + (size_t)(32 * TB + col) * kQ;
+#pragma unroll
+        for (int kj = 0; kj <= TA; ++kj)
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) ga_a[kj][ks] = Tr<bf16_t>::ld8(ra + 32 * kj + 16 * ks);
+#pragma unroll
+        for (int kj = 0; kj <= TB; ++kj)
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) ga_b[kj][ks] = Tr<bf16_t>::ld8(rb + 32 * kj + 16 * ks);
+        // C rows through a buffer over the chunk's rows: one 32-bit offset
+        // per block, the k-steps as immediate offsets; columns n >= N (the
+        // padding of a dstate below 128) are zeroed after the load
+        const __amdgpu_buffer_rsrc_t rc =
+            buffer_rsrc(Cm + d.row0 * G * N, (uint32_t)((size_t)d.len * G * N * 2));
+        const int oa = ((min(32 * TA + col, d.len - 1) * G + w.g) * N + 8 * half) * 2;
+        const int ob = ((min(32 * TB + col, d.len - 1) * G + w.g) * N + 8 * half) * 2;
+#pragma unroll
+        for (int s = 0; s < kNT / 16; ++s) {
+            ca_a[s] = buffer_ld8<bf16_t>(rc, oa + 32 * s);
+            ca_b[s] = buffer_ld8<bf16_t>(rc, ob + 32 * s);
+        }
+#pragma unroll
+        for (int s = 0; s < kNT / 16; ++s) {
+            if (16 * s + 8 * half >= N) {
+                ca_a[s] = bf16x8{};
+                ca_b[s] = bf16x8{};
+            }
+        }
+    };
+    if (w.nck > 0) load_ops(0);
+    __syncthreads();
+    for (int c = 0; c < w.nck; ++c) {
+        const ChunkDesc d = w.chunk(c);
+        const bool has_state = c > 0 || has_init;
+        const __amdgpu_buffer_rsrc_t ry =
+            buffer_rsrc(y + d.row0 * HP, (uint32_t)((size_t)d.len * HP * sizeof(TY)));
+        for (int j = 0; j < w.nu; ++j) {
+            const int i = c * w.nu + j, b = i & 1;
+            const int h = w.head(pl, j), pt = w.tile(j);
+            const float Dh = D[h];
+            const bf16_t* shrow = bufs.sh(b) + col * kNS + 8 * half;
+            const bf16_t* slrow = bufs.sl(b) + col * kNS + 8 * half;
+            const WalkTables tb = walk_tables(bufs.stage(b));
+            const bf16_t* xhrow = bufs.xh(b) + col * kLP + 8 * half;
+            const bf16_t* xrrow = bufs.xr(b) + col * kLP;
+            const bool cok = 32 * pt + col < P;
+            const int rowb = HP * (int)sizeof(TY);
+            const int yb = (h * P + 32 * pt + col) * (int)sizeof(TY) + 4 * half * rowb;
+            walk_block<TY, TA>(ga_a, ca_a, has_state, shrow, slrow, tb, xhrow, xrrow, ry, yb + 32 * TA * rowb, rowb,
+                               d.len, cok, Dh);
+            // one block at a time: overlapping the two would need both blocks'
+            // accumulators at once
+            __builtin_amdgcn_sched_barrier(0);
+            walk_block<TY, TB>(ga_b, ca_b, has_state, shrow, slrow, tb, xhrow, xrrow, ry, yb + 32 * TB * rowb, rowb,
+                               d.len, cok, Dh);
+            __builtin_amdgcn_sched_barrier(0);
+            if (j == w.nu - 1 && c + 1 < w.nck) load_ops(c + 1);
+            __syncthreads();
+        }
+    }
+}
+
+template <typename TY, int NU>
+__global__ __launch_bounds__(512, 1) void ssd_scan_walk_kernel(
+    Plan pl, int per_xcd, int npt, int nslice, int nus, const bf16_t* __restrict__ x, const float* __restrict__ cs,
+    const float* __restrict__ dtc, const bf16_t* __restrict__ Cm, const bf16_t* __restrict__ cb,
+    const bf16_t* __restrict__ bt, const float* __restrict__ D, const float* __restrict__ init,
+    float* __restrict__ fin, TY* __restrict__ y) {
+    extern __shared__ __align__(16) char smem[];
+    Walk w;
+    if (!walk_of(pl, per_xcd, npt, nslice, nus, w)) return;
+    const WalkBufs bufs{smem};
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    switch (wave) {
+        case 0: walk_outputs<TY, 0, 7>(pl, w, bufs, Cm, cb, D, init != nullptr, y); break;
+        case 1: walk_outputs<TY, 1, 6>(pl, w, bufs, Cm, cb, D, init != nullptr, y); break;
+        case 2: walk_outputs<TY, 2, 5>(pl, w, bufs, Cm, cb, D, init != nullptr, y); break;
+        case 3: walk_outputs<TY, 3, 4>(pl, w, bufs, Cm, cb, D, init != nullptr, y); break;
+        default: walk_states<NU>(pl, w, bufs, x, cs, dtc, bt, init, fin); break;
+    }
+}
+
+template <typename TY, int NU>
+hipError_t run_walk(const Plan& pl, const WalkArgs& a, hipStream_t stream) {
+    auto* k = ssd_scan_walk_kernel<TY, NU>;
+    hipError_t err = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kWalkLds);
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL(k, dim3(8 * a.per_xcd), dim3(512), kWalkLds, stream, pl, a.per_xcd, a.npt, a.nslice, a.nus,
+                       (const bf16_t*)a.x, a.cs, a.dtc, (const bf16_t*)a.C, (const bf16_t*)a.cb,
+                       (const bf16_t*)a.bt, a.D, a.init, a.final_state, (TY*)a.y);
+    return hipGetLastError();
+}
+
+template <typename TY>
+hipError_t dispatch_walk(const Plan& pl, const WalkArgs& a, hipStream_t stream) {
+    switch (a.nus) {
+        case 1: return run_walk<TY, 1>(pl, a, stream);
+        case 2: return run_walk<TY, 2>(pl, a, stream);
+        case 3: return run_walk<TY, 3>(pl, a, stream);
+        case 4: return run_walk<TY, 4>(pl, a, stream);
+        case 5: return run_walk<TY, 5>(pl, a, stream);
+        case 6: return run_walk<TY, 6>(pl, a, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+bool scan_walk_supported(int dtype, int N, int Q) { return dtype == 1 && Q == kQ && N > 64 && N <= kNT; }
+
+size_t scan_walk_lds_bytes() { return kWalkLds; }
+
+hipError_t launch_scan_walk(const Plan& pl, const WalkArgs& a, hipStream_t stream) {
+    if (a.per_xcd <= 0) return hipSuccess;
+    return a.y_f32 ? dispatch_walk<float>(pl, a, stream) : dispatch_walk<bf16_t>(pl, a, stream);
+}
+
+}  // namespace ssd

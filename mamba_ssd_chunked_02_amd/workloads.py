@@ -127,11 +127,14 @@ def _normal(rng, shape, var: float) -> np.ndarray:
 
 
 def generate(wl: Workload, seed: int, *, A_range=None, A_zero: bool = False,
-             x_zero: bool = False, decode_steps: Optional[int] = None,
-             init_var: Optional[float] = None) -> Inputs:
+             A_values: Optional[Sequence[float]] = None, x_zero: bool = False,
+             decode_steps: Optional[int] = None, init_var: Optional[float] = None) -> Inputs:
     """Draw one workload.  Variants used by the tests:
-    ``A_range=(lo, hi)`` draws A uniformly in [lo, hi] (slow decay),
-    ``A_zero`` sets A = 0, ``x_zero`` zeroes x (initial-state path only)."""
+    ``A_range=(lo, hi)`` draws A uniformly in [lo, hi] (slow or strong decay),
+    ``A_values`` gives A per head (cycled over the heads), ``A_zero`` sets
+    A = 0, ``x_zero`` zeroes x (initial-state path only).  ``A_range`` draws
+    its values right after u, so the later tensors differ from the plain
+    draw's; the other variants leave every other tensor as drawn."""
     rng = np.random.Generator(np.random.PCG64(seed))
     H, P, N, G = wl.H, wl.P, wl.N, wl.G
     if wl.varlen:
@@ -159,6 +162,8 @@ def generate(wl: Workload, seed: int, *, A_range=None, A_zero: bool = False,
         A = rng.uniform(A_range[0], A_range[1], size=H).astype(np.float32)
     if A_zero:
         A = np.zeros(H, np.float32)
+    if A_values is not None:
+        A = np.resize(np.asarray(A_values, np.float32), H).astype(np.float32)
     if lead is not None:
         B = _normal(rng, lead + (G, N), 1.0 / N)
         C = _normal(rng, lead + (G, N), 1.0 / N)

@@ -151,13 +151,19 @@ def dt_activation(dt_raw, dt_bias=None, dt_limit=(0.0, float("inf"))) -> np.ndar
     return np.minimum(np.maximum(np.logaddexp(0.0, v), lo), hi)
 
 
-def decode(state, x, dt, A, B, C, D, nthreads: int = 0) -> Tuple[np.ndarray, np.ndarray]:
+def decode(state, x, dt, A, B, C, D, nthreads: int = 0, inplace: bool = False
+           ) -> Tuple[np.ndarray, np.ndarray]:
     """One cached decode step: returns (y [b,H,P], new_state [b,H,P,N]) in fp64.
 
     state [b,H,P,N], x [b,H,P], dt [b,H], B/C [b,G,N].  The input state is not
-    modified.
+    modified, unless ``inplace`` is set and it is already a C-contiguous fp64
+    array: then it is updated in place and returned (long decode runs over
+    large batches avoid a copy of the state per step).
     """
-    st = _f64(state).copy()
+    if inplace and isinstance(state, np.ndarray) and state.dtype == np.float64 and state.flags.c_contiguous:
+        st = state
+    else:
+        st = _f64(state).copy()
     x = _f64(x)
     dt = _f64(dt)
     A = _f64(A)

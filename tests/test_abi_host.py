@@ -55,12 +55,11 @@ def test_only_the_abi_is_exported(lib):
 
 def shape(**kw):
     s = ssd._Shape()
-    d = dict(batch=1, seqlen=512, nheads=4, headdim=16, dstate=16, ngroups=1, dtype=0, ydtype=0)
-    res = kw.pop("reserved", (0, 0))
+    d = dict(batch=1, seqlen=512, nheads=4, headdim=16, dstate=16, ngroups=1, dtype=0, ydtype=0, path=0,
+             reserved=0)
     d.update(kw)
     for k, v in d.items():
         setattr(s, k, v)
-    s.reserved[0], s.reserved[1] = res
     return s
 
 
@@ -77,13 +76,28 @@ def test_workspace_size_valid(lib):
     assert st2 == OK and n2 > n
     st3, n3 = ws_size(lib, shape(batch=8, seqlen=8192, nheads=80, headdim=64, dstate=128, dtype=1), 256)
     assert st3 == OK and n3 < 2 ** 31
+    # the scan walk keeps the per-chunk states on chip: its workspace has no
+    # [chunks, H, P, N] fp32 region and no per-token weight table
+    big = dict(batch=8, seqlen=8192, nheads=80, headdim=64, dstate=128, dtype=1)
+    sizes = {p: ws_size(lib, shape(path=p, **big), 256) for p in (1, 2, 3)}
+    assert all(v[0] == OK for v in sizes.values())
+    states = 8 * 32 * 80 * 64 * 128 * 4
+    weights = 8 * 32 * 80 * 256 * 4
+    assert sizes[1][1] == sizes[2][1]
+    assert sizes[2][1] - sizes[3][1] == states + weights
 
 
 @pytest.mark.parametrize("kw,chunk,code", [
     (dict(dtype=7), 64, E_DTYPE),
     (dict(ydtype=2), 64, E_DTYPE),
-    (dict(reserved=(1, 0)), 64, E_SHAPE),
-    (dict(reserved=(0, 3)), 64, E_SHAPE),
+    (dict(reserved=1), 64, E_SHAPE),
+    (dict(path=-1), 64, E_VALUE),
+    (dict(path=4), 64, E_VALUE),
+    # the scan walk covers bf16 inputs, 256-token chunks and dstate in (64, 128] only
+    (dict(path=3), 64, E_UNSUP),
+    (dict(path=3, dtype=1, dstate=128), 128, E_UNSUP),
+    (dict(path=3, dtype=1, dstate=64), 256, E_UNSUP),
+    (dict(path=3, dtype=0, dstate=128), 256, E_UNSUP),
     (dict(nheads=0), 64, E_SHAPE),
     (dict(nheads=6, ngroups=4), 64, E_SHAPE),
     (dict(headdim=12), 64, E_SHAPE),
@@ -136,8 +150,12 @@ def test_scan_pointer_errors(lib):
     for name in ["x", "dt", "A", "B", "C", "D", "y"]:
         assert scan(lib, sh, **{name: None}) == E_NULL, name
     assert scan(lib, sh, ws=None) == E_WS
-    for name in ["x", "dt", "A", "B", "C", "D", "y", "init", "final", "ws"]:
+    for name in ["x", "B", "C", "y", "init", "final", "ws"]:
         assert scan(lib, sh, **{name: FAKE + 8}) == E_ALIGN, name
+    # dt, A and D are read one fp32 element at a time: 4-byte alignment suffices
+    for name in ["dt", "A", "D"]:
+        assert scan(lib, sh, **{name: FAKE + 2}) == E_ALIGN, name
+        assert scan(lib, sh, ws_bytes=1, **{name: FAKE + 4}) == E_WS, name
     n = ws_size(lib, sh)[1]
     assert scan(lib, sh, ws_bytes=n - 1) == E_WS
     assert scan(lib, sh, y=FAKE) == E_SHAPE  # y aliases x
@@ -155,7 +173,13 @@ def test_decode_errors(lib):
 
     for name in ["state", "x", "dt", "A", "B", "C", "D", "y"]:
         assert dec(**{name: None}) == E_NULL
+    for name in ["state", "x", "B", "C", "y"]:
         assert dec(**{name: FAKE + 8}) == E_ALIGN
+    # per-step slices of a [steps, batch, H] dt buffer sit at multiples of
+    # 4 * batch * H bytes: dt, A and D need only 4-byte alignment
+    for name in ["dt", "A", "D"]:
+        assert dec(**{name: FAKE + 2}) == E_ALIGN
+        assert dec(y=FAKE + 16, **{name: FAKE + 4 + {"dt": 32, "A": 48, "D": 96}[name]}) == E_SHAPE
     assert dec(y=FAKE + 16) == E_SHAPE
     bad = shape(batch=2, ngroups=3)
     assert lib.ssd_decode_step(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE + 16,
@@ -204,7 +228,7 @@ def test_dt_activation_argument_errors(lib):
 
     for call in (scan_act, dec_act):
         assert call(None) == E_NULL
-        assert call(act(bias=FAKE + 4)) == E_ALIGN
+        assert call(act(bias=FAKE + 2)) == E_ALIGN
         for lo, hi in [(-0.1, 1.0), (nan, 1.0), (0.0, nan), (inf, inf), (0.5, 0.1)]:
             assert call(act(lo=lo, hi=hi)) == E_VALUE, (lo, hi)
             assert lib.ssd_last_error_detail().decode()
@@ -227,7 +251,7 @@ def test_window_step_errors(lib):
         assert win(window, t, flush) == E_VALUE, (window, t, flush)
     for name in ["state", "x", "dt", "A", "B", "C", "D", "y"]:
         assert win(**{name: None}) == E_NULL, name
-        assert win(**{name: FAKE + 8}) == E_ALIGN, name
+        assert win(**{name: FAKE + (2 if name in ("dt", "A", "D") else 8)}) == E_ALIGN, name
     assert win(y=FAKE + 16) == E_SHAPE  # y aliases x
     a = ssd._DtAct()
     a.dt_bias, a.dt_min, a.dt_max = None, -1.0, 1.0

@@ -1,0 +1,122 @@
+"""GPU parity in the strong-decay regime and at the memoryless limit.
+
+A large step flushes the state: with dt*A far below zero the decay factor
+exp(dt*A) underflows and each output keeps only its own token's contribution
+("Mamba and Selective State Space Models...", section 4, the selection
+mechanism: a large step resets the state, a small one keeps it).  The chunk
+scan evaluates the intra-chunk term block by block with per-block decay
+factors; a 32-token block whose decay exceeds the kernel's fast-path bound
+takes an exact per-element path.  These cases drive both paths, and their
+mix across heads, on every state path, against the fp64 oracle element by
+element, then continue with decode steps.
+
+Workloads: the standard distributions with A drawn from a wider range:
+  A in [-1e3, -60]   every block decays past the bound (dt up to 0.1)
+  A = -10 / -300     alternating heads: blocks that stay on the fast path
+                     and blocks that do not
+  A = -1e6           dt*A <= -1000: exp underflows to 0 in fp32 and fp64
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import mamba_ssd_chunked_02_amd as ssd
+from mamba_ssd_chunked_02_amd import workloads as W
+from parity import assert_close, host, oracle_scan, tdev, to_gpu
+
+pytestmark = pytest.mark.gpu
+
+REGIMES = {"strong": dict(A_range=(-1e3, -60.0)), "mixed": dict(A_values=(-10.0, -300.0)),
+           "flush": dict(A_range=(-1e6, -1e6))}
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def block_decays(inp, chunk):
+    """Largest decay A * sum(dt) over the 32-token blocks of any chunk, per head
+    (dense batches): tells which heads cross the fast-path bound."""
+    dt = inp.dt.astype(np.float64)
+    b, L, H = dt.shape
+    out = np.zeros(H)
+    for t0 in range(0, L, 32):
+        seg = dt[:, t0:min(L, t0 + 32)].sum(axis=1)  # [b, H]
+        out = np.maximum(out, (-inp.A.astype(np.float64) * seg).max(axis=0))
+    return out
+
+
+CASES = [
+    # (batch, L, H, P, N, G, chunk, dtype, regime); H*P/32*batch >= 256 takes the walk
+    (2, 700, 4, 64, 128, 2, 256, "bf16", "strong"),
+    (2, 700, 4, 64, 128, 2, 256, "bf16", "flush"),
+    (1, 600, 8, 64, 128, 2, 128, "bf16", "mixed"),
+    (2, 333, 4, 32, 64, 1, 64, "f32", "strong"),
+    (2, 333, 4, 32, 64, 1, 64, "f32", "flush"),
+    (1, 520, 8, 32, 32, 4, 128, "f32", "mixed"),
+    (4, 600, 32, 64, 128, 2, 256, "bf16", "strong"),
+    (4, 600, 32, 64, 128, 2, 256, "bf16", "mixed"),
+    (4, 600, 32, 64, 128, 2, 256, "bf16", "flush"),
+    (8, 300, 32, 32, 64, 4, 64, "f32", "mixed"),
+    (4, 300, 32, 64, 128, 1, 128, "bf16", "flush"),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "b%d-L%d-H%d-P%d-N%d-G%d-Q%d-%s-%s" % c)
+def test_strong_decay_prefill_then_decode(case):
+    b, L, H, P, N, G, Q, dt, regime = case
+    wl = W.small_workload(batch=b, seqlen=L, H=H, P=P, N=N, G=G, chunk=Q, dtype=dt, init_var=0.1,
+                          decode_steps=3, decode_batch=b)
+    inp = W.generate(wl, 300 + L + H, **REGIMES[regime])
+    dec = block_decays(inp, Q)
+    say("case:", case, "block decay min %.1f max %.1f" % (dec.min(), dec.max()))
+    if regime == "strong":
+        assert dec.min() > 60.0
+    if regime == "mixed":
+        assert dec.min() < 60.0 < dec.max()
+    g = to_gpu(inp)
+    st = []
+    y, fin = ssd.chunked_scan(g["x"], g["dt"], g["A"], g["B"], g["C"], g["D"], Q, init_state=g["init"],
+                              stage_ms=st)
+    torch.cuda.synchronize()
+    say("  stages", ["%.3f" % v for v in st])
+    yr, fr = oracle_scan(inp)
+    say("  y err %.3e" % assert_close(host(y), yr, dt, "y"))
+    say("  final err %.3e" % assert_close(host(fin), fr, dt, "final"))
+    state, ref = fin, fr
+    for k, d in enumerate(inp.decode):
+        yd = ssd.decode_step(state, tdev(d["x"], dt), tdev(d["dt"]), g["A"], tdev(d["B"], dt),
+                             tdev(d["C"], dt), g["D"])
+        yref, ref = oracle.decode(ref, d["x"], d["dt"], inp.A, d["B"], d["C"], inp.D)
+        assert_close(host(yd), yref, dt, "decode y %d" % k)
+    torch.cuda.synchronize()
+    assert_close(host(state), ref, dt, "decode state")
+
+
+@pytest.mark.parametrize("dt,walk", [("bf16", False), ("f32", False), ("bf16", True)])
+def test_memoryless_limit_closed_form(dt, walk):
+    """At A = -1e6 every decay factor is 0, so y_t = dt_t (C_t . B_t) x_t + D x_t
+    and the final state is dt_T x_T (outer) B_T of the last token: checked
+    against that closed form directly (fp64 from the same inputs), not only
+    against the recurrence."""
+    b, H = (4, 32) if walk else (2, 4)
+    wl = W.small_workload(batch=b, seqlen=300, H=H, P=64, N=64, G=2, chunk=128, dtype=dt, init_var=0.1)
+    inp = W.generate(wl, 400 + H, **REGIMES["flush"])
+    g = to_gpu(inp)
+    st = []
+    y, fin = ssd.chunked_scan(g["x"], g["dt"], g["A"], g["B"], g["C"], g["D"], 128, init_state=g["init"],
+                              stage_ms=st)
+    torch.cuda.synchronize()
+    say("case: memoryless", dt, "walk" if walk else "chunk-parallel", ["%.3f" % v for v in st])
+    x, dtt, B, C, D = (np.asarray(v, np.float64) for v in (inp.x, inp.dt, inp.B, inp.C, inp.D))
+    heads = np.arange(H)
+    grp = heads // (H // 2)
+    cb = np.einsum("blgn,blgn->blg", C, B)[:, :, grp]            # [b, L, H]
+    y_cf = (dtt * cb)[..., None] * x + D[None, None, :, None] * x
+    f_cf = (dtt[:, -1][..., None, None] * x[:, -1][..., :, None] * B[:, -1][:, grp][:, :, None, :])
+    assert_close(host(y), y_cf, dt, "y vs closed form")
+    assert_close(host(fin), f_cf, dt, "final vs closed form")

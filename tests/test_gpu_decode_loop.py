@@ -131,3 +131,26 @@ def test_prefill_graph_replays_equal_eager(b, L, H):
         torch.cuda.synchronize()
         assert torch.equal(y, y_ref) and torch.equal(fin, f_ref), "replay %d" % k
         _ = (x.float() * 2).sum().item()  # unrelated eager work between replays
+
+
+def test_odd_batch_times_heads():
+    """batch * H = 15: the per-step dt slices sit at multiples of 60 bytes
+    (4-byte, not 16-byte, aligned), which dt accepts; the loop still equals
+    the oracle's steps."""
+    steps = 3
+    wl = W.small_workload(batch=3, seqlen=0, H=5, P=32, N=64, G=1, dtype="bf16", init_var=0.1,
+                          decode_steps=steps, decode_batch=3)
+    inp = W.generate(wl, 41)
+    say("case: decode loop, batch 3 x 5 heads")
+    A, D = tdev(inp.A), tdev(inp.D)
+    loop = DecodeLoop(steps, 3, 5, 32, 64, 1, A, D, dtype=torch.bfloat16)
+    fill(loop, inp, "bf16")
+    assert loop.dt[1].data_ptr() % 16 != 0
+    loop.state.copy_(tdev(inp.init))
+    loop.replay()
+    torch.cuda.synchronize()
+    ref = inp.init.astype(np.float64)
+    for k, d in enumerate(inp.decode):
+        yk, ref = oracle.decode(ref, d["x"], d["dt"], inp.A, d["B"], d["C"], inp.D)
+        assert_close(host(loop.y[k]), yk, "bf16", "y step %d" % k)
+    assert_close(host(loop.state), ref, "bf16", "state")

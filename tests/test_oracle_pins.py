@@ -446,3 +446,20 @@ def test_conv1d_hand_values():
             d = case["decode"]
             yd, sd = oconv.conv1d_step(fin[None], np.array(d["x"])[None], w, bias, activation=False)
             assert np.array_equal(yd[0], np.array(d["y"])) and np.array_equal(sd[0], np.array(d["state"]))
+
+
+def test_decode_in_place_equals_copying_decode():
+    """The in-place form of the decode glue updates the given fp64 state and
+    returns the same values as the copying form (same C routine)."""
+    rng = np.random.default_rng(3)
+    b, H, P, N, G = 3, 4, 8, 16, 2
+    st = rng.normal(size=(b, H, P, N))
+    x, dt = rng.normal(size=(b, H, P)), rng.uniform(0.001, 0.1, size=(b, H))
+    A, D = -rng.uniform(1, 16, size=H), rng.normal(size=H)
+    B, C = rng.normal(size=(b, G, N)), rng.normal(size=(b, G, N))
+    y1, s1 = oracle.decode(st, x, dt, A, B, C, D)
+    st2 = st.copy()
+    y2, s2 = oracle.decode(st2, x, dt, A, B, C, D, inplace=True)
+    assert s2 is st2
+    assert np.array_equal(y1, y2) and np.array_equal(s1, s2)
+    assert not np.array_equal(st, st2)
