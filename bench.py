@@ -70,6 +70,17 @@ def kernel_work(wl, es=2, ys=4, fused=True):
           "bytes": (T * H * P * es + T * H * P * ys + T * G * N * es + state
                     + nch * G * nti * (nti + 1) // 2 * 1024 * es + 2 * nch * H * Q * 4)}
     kp = {"flops": 0, "flops_causal": 0, "bytes": 2 * state + nch * H * 4 + 2 * b * H * P * N * 4}
+    if fused == "scan_walk":
+        # one launch: the chunk states, their passing and y; it reads x, C,
+        # B^T, the causal C.B^T tiles, the decay sums and steps and the
+        # initial states, and writes y and the final states.  No per-chunk
+        # state and no per-token weight table reach memory.
+        nt = 128 if N <= 128 else 256
+        kw = {"flops": ks["flops"] + kc["flops"], "flops_causal": ks["flops_causal"] + kc["flops_causal"],
+              "bytes": (T * H * P * es + T * H * P * ys + T * G * N * es + nch * G * nt * Q * es
+                        + nch * G * nti * (nti + 1) // 2 * 1024 * es + 2 * nch * H * Q * 4
+                        + 2 * b * H * P * N * 4)}
+        return {"scan_walk": kw}
     if fused:
         ks["bytes"] += 2 * b * H * P * N * 4
         return {"chunk_state": ks, "chunk_scan": kc}
@@ -365,7 +376,8 @@ def other_prefill(torch, ssd, reps=20):
 
 # the sources that define and launch the prefill kernels (the counters in the
 # traffic summary describe those kernels only)
-PREFILL_SOURCES = ("ssd_api.cpp", "ssd_device.h", "ssd_internal.h", "ssd_prefill.hip")
+PREFILL_SOURCES = ("ssd_api.cpp", "ssd_device.h", "ssd_internal.h", "ssd_prefill.hip", "ssd_prefill_shared.h",
+                   "ssd_scan_walk.hip")
 
 
 def _source_digest():
@@ -424,7 +436,7 @@ def main():
     ap.add_argument("--no-extras", action="store_true",
                     help="leave out the reports beside the timed step (decode loop vs recompute, windowed\n"
                          "decode, conv1d, fused dt activation); the timed step and its rooflines are unchanged")
-    ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic_chunk_scan_2p7b.txt"),
+    ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic_scan_walk_2p7b.txt"),
                     help="rocprofv3 FETCH_SIZE/WRITE_SIZE summary of the dominant kernel")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of known size (for counter calibration)")
@@ -569,15 +581,19 @@ def main():
     dense_tf = prefill_flops(wl) / (prefill_ms * 1e-3) / 1e12
     causal_tf = prefill_flops(wl, causal=True) / (prefill_ms * 1e-3) / 1e12
 
-    # rooflines of the prefill kernels; the slowest one is the reported one
-    # the library folds state passing into chunk_state when it has enough
-    # (sequence, head, tile) walks; the passing stage then reads 0
-    fused = float(stage_mean[ssd.STAGES.index("state_passing")]) == 0.0
+    # rooflines of the prefill kernels; the slowest one is the reported one.
+    # The stages that ran tell the path: the scan walk alone, the state walk
+    # (state passing inside chunk_state) + chunk_scan, or all three
+    if float(stage_mean[ssd.STAGES.index("scan_walk")]) > 0.0:
+        fused = "scan_walk"
+    else:
+        fused = float(stage_mean[ssd.STAGES.index("state_passing")]) == 0.0
     work = kernel_work(wl, fused=fused)
     names = {"chunk_state": ("ssd_chunk_state_passing_kernel<bf16,NT=128,Q=256>" if fused else
                              "ssd_chunk_state_kernel<bf16,NT=128,Q=256>"),
              "state_passing": "ssd_state_passing_kernel",
-             "chunk_scan": "ssd_chunk_scan_kernel<bf16,f32,NT=128,Q=256>"}
+             "chunk_scan": "ssd_chunk_scan_kernel<bf16,f32,NT=128,Q=256>",
+             "scan_walk": "ssd_scan_walk_kernel<f32 y,NU=5>"}
     roofs = {}
     for k, wk in work.items():
         ms = float(stage_mean[ssd.STAGES.index(k)])
@@ -586,10 +602,12 @@ def main():
     roof = dict(roofs[dominant])
     if args.traffic:
         roof["traffic"] = _traffic(args.traffic, names[dominant], roof["algorithmic_bytes"])
-    mfma_ms = float(stage_mean[ssd.STAGES.index("chunk_state")] + stage_mean[ssd.STAGES.index("chunk_scan")])
-    contraction_tf = (work["chunk_state"]["flops"] + work["chunk_scan"]["flops"]) / (mfma_ms * 1e-3) / 1e12
-    contraction_tf_c = ((work["chunk_state"]["flops_causal"] + work["chunk_scan"]["flops_causal"])
-                        / (mfma_ms * 1e-3) / 1e12)
+    # the contraction kernels: chunk_state and chunk_scan, or the scan walk
+    # that does both (state_passing has no contraction)
+    mk = [k for k in work if k != "state_passing"]
+    mfma_ms = float(sum(stage_mean[ssd.STAGES.index(k)] for k in mk))
+    contraction_tf = sum(work[k]["flops"] for k in mk) / (mfma_ms * 1e-3) / 1e12
+    contraction_tf_c = sum(work[k]["flops_causal"] for k in mk) / (mfma_ms * 1e-3) / 1e12
     # the contraction kernels against the 40% bf16 target, beside the dominant
     # kernel's own roofline (which is the HBM roof: its arithmetic intensity
     # sits left of the ridge)
@@ -696,6 +714,7 @@ def main():
                     "back-to-back calls; context only, value is the fp32-y default"},
         "tflops_contraction_kernels": round(contraction_tf, 2),
         "frac_bf16_peak_contraction_kernels": round(contraction_tf / BF16_PEAK_TFLOPS, 4),
+        "prefill_path": fused if isinstance(fused, str) else ("state_walk" if fused else "chunk_parallel"),
         "roofline": roof,
         "roofline_kernels": roofs,
         "roofline_decode": roof_dec,

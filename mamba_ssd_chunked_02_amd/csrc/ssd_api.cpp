@@ -66,8 +66,10 @@ constexpr int64_t kStateMaxHeads = 16;
 // per-workgroup block operands and prologue best
 constexpr int64_t kScanWorkgroups = 256;
 constexpr int64_t kFusedMinWalks = 256;  // one per CU
-// whether the library's own choice may take the scan walk where it applies
-constexpr bool kAutoScanWalk = false;
+// where the scan walk applies (bf16, chunk 256, dstate in (64, 128]) and a
+// walk is the right shape, the library's own choice takes it: it moves
+// about half the bytes of the state walk followed by chunk_scan
+constexpr bool kAutoScanWalk = true;
 
 struct Prepared {
     ssd::Plan plan;

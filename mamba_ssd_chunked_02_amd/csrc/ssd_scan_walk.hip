@@ -27,10 +27,13 @@
 //              they advance the current unit's tile over the chunk, write the
 //              next step's state as a hi/lo bf16 pair to LDS, stage the next
 //              step's x and decay tables in LDS and load the step after that.
-// LDS holds two staging buffers and two state buffers (141 KB); one barrier
+// LDS holds two staging buffers, two state buffers and the output waves'
+// transpose tiles (159 KB); one barrier
 // per step separates the step that reads a buffer from the one that refills
 // it.  Only bf16 inputs, 256-token chunks and dstate in (64, 128] take this
 // kernel; the host picks the separate kernels for everything else.
+#include <type_traits>
+
 #include "ssd_prefill_shared.h"
 
 namespace ssd {
@@ -51,7 +54,11 @@ constexpr size_t kTileBytes = (size_t)32 * kLP * 2;
 constexpr size_t kStageBytes = kTabBytes + 3 * kTileBytes;
 // One state buffer: h hi, h lo as [32 columns p][kNS] bf16.
 constexpr size_t kStateBytes = (size_t)2 * 32 * kNS * 2;
-constexpr size_t kWalkLds = 2 * kStageBytes + 2 * kStateBytes;
+// Per output wave: a 32 x 32 fp32 tile that turns a block's accumulator
+// layout into 16-byte row pieces for the y stores.
+constexpr int kEpPitch = 36;
+constexpr size_t kEpBytes = (size_t)32 * kEpPitch * 4;
+constexpr size_t kWalkLds = 2 * kStageBytes + 2 * kStateBytes + 4 * kEpBytes;
 static_assert(kWalkLds <= 160 * 1024, "scan walk LDS");
 
 struct WalkTables {
@@ -82,6 +89,7 @@ struct WalkBufs {
     __device__ bf16_t* xr(int b) const { return xl(b) + 32 * kLP; }
     __device__ bf16_t* sh(int b) const { return (bf16_t*)(smem + 2 * kStageBytes + b * kStateBytes); }
     __device__ bf16_t* sl(int b) const { return sh(b) + 32 * kNS; }
+    __device__ float* ep(int w) const { return (float*)(smem + 2 * kStageBytes + 2 * kStateBytes + w * kEpBytes); }
 };
 
 // The walk of one workgroup: sequence s, group g, units [u0, u0 + nu) of the
@@ -102,6 +110,10 @@ struct Walk {
     }
 };
 
+// Items are (sequence, group, slice) with the slice fastest: the XCD-ordered
+// grid gives each XCD a contiguous range, so the walks of one sequence run on
+// one XCD and share each chunk's C.B^T, C and B^T in its L2.  (Slice-major
+// order, which spreads every XCD over all sequences, measured 6% slower.)
 __device__ inline bool walk_of(const Plan& pl, int per_xcd, int npt, int nslice, int nus, Walk& w) {
     const int64_t item = xcd_item(per_xcd);
     if (item >= (int64_t)pl.nseq * pl.G * nslice) return false;
@@ -296,17 +308,20 @@ __device__ void walk_states(const Plan& pl, const Walk& w, const WalkBufs& bufs,
 #pragma unroll
         for (int s = 0; s < kQ / 16; ++s) bf[s] = buffer_ld8<bf16_t>(rb, boff + 512 * s * 2);
     };
-    StageRegs sr;
-    auto load_step = [&](int i) {  // i < total
+    // staging registers: sr holds the next step's inputs (loaded a step
+    // ago), sn receives the inputs of the step after it, loaded at the start
+    // of a step so their latency spans the whole step
+    StageRegs sr, sn;
+    auto load_step = [&](StageRegs& r, int i) {  // i < total
         const int c = i / nu;
-        stage_load(sr, pl, w, c, i - c * nu, x, cs, dtc, tau);
+        stage_load(r, pl, w, c, i - c * nu, x, cs, dtc, tau);
     };
     if (total > 0) {
         load_bt(0);
-        load_step(0);
+        load_step(sr, 0);
         stage_store(sr, pl, w, bufs, 0, 0, 0, tau);
         put_state(acc[0], bufs, 0, nt);
-        load_step(min(1, total - 1));
+        load_step(sr, min(1, total - 1));
     }
     __syncthreads();
     for (int c = 0; c < w.nck; ++c) {
@@ -314,19 +329,23 @@ __device__ void walk_states(const Plan& pl, const Walk& w, const WalkBufs& bufs,
         for (int j = 0; j < NU; ++j) {
             if (j < nu) {
                 const int i = c * nu + j, b = i & 1;
-                walk_advance(acc[j], bf, bufs, b);
-                if (j == nu - 1 && c + 1 < w.nck) load_bt(c + 1);
-                if (i + 1 < total) {
-                    // the next step's unit: j + 1 of this chunk, or unit 0 of
-                    // the next chunk (already advanced past this one)
-                    if (j + 1 < nu) put_state(acc[(j + 1) % NU], bufs, b ^ 1, nt);
-                    else put_state(acc[0], bufs, b ^ 1, nt);
-                    const int cn = j + 1 < nu ? c : c + 1, jn = j + 1 < nu ? j + 1 : 0;
-                    stage_store(sr, pl, w, bufs, cn, jn, b ^ 1, tau);
-                }
                 // unconditional (the last step repeats itself), so the wait
                 // counts never cover a path without these loads
-                load_step(min(i + 2, total - 1));
+                load_step(sn, min(i + 2, total - 1));
+                // the next step's unit is j + 1 of this chunk, whose state is
+                // ready, or unit 0 of the next chunk, whose state is ready
+                // once this step has advanced it (with one unit per
+                // workgroup it is the unit advanced here)
+                const bool more = i + 1 < total;
+                const int cn = j + 1 < nu ? c : c + 1, jn = j + 1 < nu ? j + 1 : 0;
+                if (more) {
+                    if (j + 1 < nu) put_state(acc[(j + 1) % NU], bufs, b ^ 1, nt);
+                    stage_store(sr, pl, w, bufs, cn, jn, b ^ 1, tau);
+                }
+                walk_advance(acc[j], bf, bufs, b);
+                if (more && j + 1 == nu) put_state(acc[0], bufs, b ^ 1, nt);
+                if (j == nu - 1 && c + 1 < w.nck) load_bt(c + 1);
+                sr = sn;
                 __syncthreads();
             }
         }
@@ -352,31 +371,19 @@ __device__ void walk_states(const Plan& pl, const Walk& w, const WalkBufs& bufs,
 }
 
 // ------------------------------------------------------------------ outputs (waves 0-3)
-template <typename TY>
-__device__ inline void store_y(float v, __amdgpu_buffer_rsrc_t r, int voff);
-template <>
-__device__ inline void store_y<float>(float v, __amdgpu_buffer_rsrc_t r, int voff) {
-    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, voff, 0, kNonTemporal);
-}
-template <>
-__device__ inline void store_y<bf16_t>(float v, __amdgpu_buffer_rsrc_t r, int voff) {
-    __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, (bf16_t)v), r, voff, 0, kNonTemporal);
-}
-
 // Output block TI (tokens 32 TI .. 32 TI + 31, the tile's 32 columns) of one
 // unit: the state term C_rows . h_c^T from the staged hi/lo state.  The intra-chunk
 // term is the Horner scheme of the chunk scan: two chains over the blocks
 // kj <= TI with the (C.B^T) rows ga as A and the staged (x wb)^T as B, the
 // diagonal block inside the scheme when its decay is below kFastDecay (then
 // scaled by ue), else added with exact per-element factors after scaling by
-// ul.  y leaves from the accumulator layout: each register v is one row,
-// the wave's store covering two 128-byte row pieces.
+// ul.  y leaves through the wave's LDS tile as 16-byte row pieces.
 template <typename TY, int TI>
 __device__ __forceinline__ void walk_block(const bf16x8 (&ga)[TI + 1][2], const bf16x8 (&ca)[kNT / 16],
                                            bool has_state, const bf16_t* shrow, const bf16_t* slrow,
                                            const WalkTables& tb, const bf16_t* xhrow, const bf16_t* xrrow,
-                                           __amdgpu_buffer_rsrc_t ry, int ybase, int rowb, int len, bool cok,
-                                           float Dh) {
+                                           float* ep, __amdgpu_buffer_rsrc_t ry, int yb0, int rowb, int len,
+                                           int pcols, float Dh) {
     const int lane = threadIdx.x & 63, half = lane >> 5, col = lane & 31;
     // the state term C_rows . h_c^T (hi and lo), a chain of its own
     f32x16 sacc = {};
@@ -445,12 +452,21 @@ __device__ __forceinline__ void walk_block(const bf16x8 (&ga)[TI + 1][2], const 
 #pragma unroll
         for (int i = 0; i < 4; ++i) acc[4 * q + i] += Dh * xv[i];
     }
+    // through the wave's LDS tile: lane (column) writes its 16 rows, then
+    // each lane reads 4 consecutive columns of one row (one wave: its LDS
+    // operations complete in order); every lane stores, an output outside
+    // the chunk or past P getting an offset beyond the descriptor
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-        const int r = 8 * (v >> 2) + (v & 3);  // + 4 half, folded into ybase
-        const bool ok = cok && 32 * TI + 4 * half + r < len;
-        store_y<TY>(acc[v], ry, ok ? ybase + r * rowb : kOutOfRange);
+    for (int v = 0; v < 16; ++v) ep[acc_row(v, lane) * kEpPitch + col] = acc[v];
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+        const int tr = (lane >> 3) + 8 * it, c4 = 4 * (lane & 7);
+        const f32x4 r = *(const f32x4*)(ep + tr * kEpPitch + c4);
+        const bool ok = 32 * TI + tr < len && c4 < pcols;
+        buffer_store4<TY>(r, ry, ok ? (32 * TI + tr) * rowb + yb0 + c4 * (int)sizeof(TY) : kOutOfRange);
     }
+    __builtin_amdgcn_wave_barrier();
 }
 
 template <typename TY, int TA, int TB>
@@ -460,40 +476,35 @@ __device__ void walk_outputs(const Plan& pl, const Walk& w, const WalkBufs& bufs
     const int lane = threadIdx.x & 63, half = lane >> 5, col = lane & 31;
     const int H = pl.H, P = pl.P, N = pl.N, G = pl.G, HP = H * P;
     bf16x8 ga_a[TA + 1][2], ga_b[TB + 1][2], ca_a[kNT / 16], ca_b[kNT / 16];
-    auto load_ops = [&](int c) {
+    // the chunk's operands of one output block: its C.B^T rows (A of the
+    // intra-chunk term) and C rows (A of the state term).  C goes through a
+    // buffer over the chunk's rows (one 32-bit offset, the k-steps as
+    // immediate offsets); columns n >= N (the padding of a dstate below 128)
+    // are zeroed after the load.
+    auto load_block = [&](int c, auto ti, auto& ga, bf16x8 (&ca)[kNT / 16]) {
+        constexpr int TI = decltype(ti)::value;
         const ChunkDesc d = w.chunk(c);
-        const bf16_t* cbk = cb + ((size_t)(w.chunk0 + c) * G + w.g) * kQ * kQ + 8 * half;
-        const bf16_t* ra = cbk + (size_t)(32 * TA + col) * kQ;
-        const bf16_t* rb = cbk + (size_t)(32 * TB + col) * kQ;
+        const bf16_t* row = cb + ((size_t)(w.chunk0 + c) * G + w.g) * kQ * kQ + (size_t)(32 * TI + col) * kQ +
+                            8 * half;
 #pragma unroll
-        for (int kj = 0; kj <= TA; ++kj)
+        for (int kj = 0; kj <= TI; ++kj)
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks) ga_a[kj][ks] = Tr<bf16_t>::ld8(ra + 32 * kj + 16 * ks);
-#pragma unroll
-        for (int kj = 0; kj <= TB; ++kj)
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) ga_b[kj][ks] = Tr<bf16_t>::ld8(rb + 32 * kj + 16 * ks);
-        // C rows through a buffer over the chunk's rows: one 32-bit offset
-        // per block, the k-steps as immediate offsets; columns n >= N (the
-        // padding of a dstate below 128) are zeroed after the load
+            for (int ks = 0; ks < 2; ++ks) ga[kj][ks] = Tr<bf16_t>::ld8(row + 32 * kj + 16 * ks);
         const __amdgpu_buffer_rsrc_t rc =
             buffer_rsrc(Cm + d.row0 * G * N, (uint32_t)((size_t)d.len * G * N * 2));
-        const int oa = ((min(32 * TA + col, d.len - 1) * G + w.g) * N + 8 * half) * 2;
-        const int ob = ((min(32 * TB + col, d.len - 1) * G + w.g) * N + 8 * half) * 2;
+        const int off = ((min(32 * TI + col, d.len - 1) * G + w.g) * N + 8 * half) * 2;
 #pragma unroll
-        for (int s = 0; s < kNT / 16; ++s) {
-            ca_a[s] = buffer_ld8<bf16_t>(rc, oa + 32 * s);
-            ca_b[s] = buffer_ld8<bf16_t>(rc, ob + 32 * s);
-        }
+        for (int s = 0; s < kNT / 16; ++s) ca[s] = buffer_ld8<bf16_t>(rc, off + 32 * s);
 #pragma unroll
-        for (int s = 0; s < kNT / 16; ++s) {
-            if (16 * s + 8 * half >= N) {
-                ca_a[s] = bf16x8{};
-                ca_b[s] = bf16x8{};
-            }
-        }
+        for (int s = 0; s < kNT / 16; ++s)
+            if (16 * s + 8 * half >= N) ca[s] = bf16x8{};
     };
-    if (w.nck > 0) load_ops(0);
+    using IA = std::integral_constant<int, TA>;
+    using IB = std::integral_constant<int, TB>;
+    if (w.nck > 0) {
+        load_block(0, IA{}, ga_a, ca_a);
+        load_block(0, IB{}, ga_b, ca_b);
+    }
     __syncthreads();
     for (int c = 0; c < w.nck; ++c) {
         const ChunkDesc d = w.chunk(c);
@@ -509,18 +520,25 @@ __device__ void walk_outputs(const Plan& pl, const Walk& w, const WalkBufs& bufs
             const WalkTables tb = walk_tables(bufs.stage(b));
             const bf16_t* xhrow = bufs.xh(b) + col * kLP + 8 * half;
             const bf16_t* xrrow = bufs.xr(b) + col * kLP;
-            const bool cok = 32 * pt + col < P;
+            const int pcols = P - 32 * pt;
             const int rowb = HP * (int)sizeof(TY);
-            const int yb = (h * P + 32 * pt + col) * (int)sizeof(TY) + 4 * half * rowb;
-            walk_block<TY, TA>(ga_a, ca_a, has_state, shrow, slrow, tb, xhrow, xrrow, ry, yb + 32 * TA * rowb, rowb,
-                               d.len, cok, Dh);
+            const int yb0 = (h * P + 32 * pt) * (int)sizeof(TY);
+            float* ep = bufs.ep(threadIdx.x >> 6);
             // one block at a time: overlapping the two would need both blocks'
-            // accumulators at once
+            // accumulators at once.  After the chunk's last unit each block's
+            // registers are refilled with the next chunk's operands as soon as
+            // the block is done, so the reload spreads over the step instead
+            // of leaving together at its end.
+            const bool reload = j == w.nu - 1 && c + 1 < w.nck;
+            walk_block<TY, TA>(ga_a, ca_a, has_state, shrow, slrow, tb, xhrow, xrrow, ep, ry, yb0, rowb, d.len,
+                               pcols, Dh);
             __builtin_amdgcn_sched_barrier(0);
-            walk_block<TY, TB>(ga_b, ca_b, has_state, shrow, slrow, tb, xhrow, xrrow, ry, yb + 32 * TB * rowb, rowb,
-                               d.len, cok, Dh);
+            if (reload) load_block(c + 1, IA{}, ga_a, ca_a);
             __builtin_amdgcn_sched_barrier(0);
-            if (j == w.nu - 1 && c + 1 < w.nck) load_ops(c + 1);
+            walk_block<TY, TB>(ga_b, ca_b, has_state, shrow, slrow, tb, xhrow, xrrow, ep, ry, yb0, rowb, d.len,
+                               pcols, Dh);
+            __builtin_amdgcn_sched_barrier(0);
+            if (reload) load_block(c + 1, IB{}, ga_b, ca_b);
             __syncthreads();
         }
     }

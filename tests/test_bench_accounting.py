@@ -50,3 +50,29 @@ def test_decode_step_bytes():
     assert state == 671_088_640
     expect = 2 * state + nb * H * P * 2 + nb * H * P * 4 + 2 * nb * N * 2 + nb * H * 4 + 2 * H * 4
     assert bench.decode_bytes(wd) == expect == 1_350_255_232
+
+
+def test_scan_walk_bytes_and_flops():
+    """The fused walk: x and y once, C rows, B^T, the causal C.B^T tiles, the
+    decay sums and steps, the initial and final states; no per-chunk state."""
+    kw = bench.kernel_work(W.CONFIGS[3], fused="scan_walk")["scan_walk"]
+    bt = chunks * N * Q * 2
+    c_rows = b * L * N * 2
+    cb_causal = chunks * (8 * 9 // 2) * 32 * 32 * 2
+    init_final = 2 * b * H * P * N * 4
+    assert kw["bytes"] == x_bytes + y_bytes + c_rows + bt + cb_causal + tables + init_final
+    assert abs(kw["bytes"] / MB - 2149.6) < 0.1
+    assert kw["flops"] == 85_899_345_920 + 257_698_037_760
+    causal_pairs = Q * (Q + 1) // 2
+    assert kw["flops_causal"] == chunks * H * (2 * Q * N * P + 2 * Q * N * P + 2 * causal_pairs * P)
+
+
+def test_roofline_bound_follows_arithmetic_intensity():
+    """The roof is chosen by flops per byte against the ridge (bf16 peak / HBM
+    peak), not by whichever fraction is larger."""
+    kw = bench.kernel_work(W.CONFIGS[3], fused="scan_walk")["scan_walk"]
+    r = bench.roofline_of(kw, 0.8, "k")
+    assert r["bound"] == "hbm" and r["unit"] == "GB/s"
+    assert r["flop_per_byte"] < r["ridge_flop_per_byte"] == 312.5
+    dense = {"flops": 10 ** 15, "flops_causal": 10 ** 15, "bytes": 10 ** 9}
+    assert bench.roofline_of(dense, 1.0, "k")["bound"] == "mfma"

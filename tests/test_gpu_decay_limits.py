@@ -66,8 +66,15 @@ CASES = [
 ]
 
 
-@pytest.mark.parametrize("case", CASES, ids=lambda c: "b%d-L%d-H%d-P%d-N%d-G%d-Q%d-%s-%s" % c)
-def test_strong_decay_prefill_then_decode(case):
+# the walk-sized bf16 cases at chunk 256 run on both walks: the library's
+# choice there (the scan walk) and the state walk forced
+RUNS = [(c, "auto") for c in CASES] + [(c, "state_walk") for c in CASES
+                                       if c[0] * c[2] * ((c[3] + 31) // 32) >= 256 and c[6] == 256]
+
+
+@pytest.mark.parametrize("case,path", RUNS, ids=lambda v: v if isinstance(v, str) else
+                         "b%d-L%d-H%d-P%d-N%d-G%d-Q%d-%s-%s" % v)
+def test_strong_decay_prefill_then_decode(case, path):
     b, L, H, P, N, G, Q, dt, regime = case
     wl = W.small_workload(batch=b, seqlen=L, H=H, P=P, N=N, G=G, chunk=Q, dtype=dt, init_var=0.1,
                           decode_steps=3, decode_batch=b)
@@ -81,9 +88,9 @@ def test_strong_decay_prefill_then_decode(case):
     g = to_gpu(inp)
     st = []
     y, fin = ssd.chunked_scan(g["x"], g["dt"], g["A"], g["B"], g["C"], g["D"], Q, init_state=g["init"],
-                              stage_ms=st)
+                              stage_ms=st, path=path)
     torch.cuda.synchronize()
-    say("  stages", ["%.3f" % v for v in st])
+    say("  path", path, "stages", ["%.3f" % v for v in st])
     yr, fr = oracle_scan(inp)
     say("  y err %.3e" % assert_close(host(y), yr, dt, "y"))
     say("  final err %.3e" % assert_close(host(fin), fr, dt, "final"))

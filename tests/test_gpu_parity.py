@@ -20,19 +20,19 @@ def say(*a):
     sys.stdout.flush()
 
 
-def run_gpu(inp, chunk=None, want_final=True):
+def run_gpu(inp, chunk=None, want_final=True, path="auto"):
     g = to_gpu(inp)
     chunk = chunk or inp.wl.chunk
     y, fin = ssd.chunked_scan(g["x"], g["dt"], g["A"], g["B"], g["C"], g["D"], chunk,
-                              init_state=g["init"], cu_seqlens=g.get("cu"), want_final=want_final)
+                              init_state=g["init"], cu_seqlens=g.get("cu"), want_final=want_final, path=path)
     torch.cuda.synchronize()
     return host(y), None if fin is None else host(fin)
 
 
-def check_scan(inp, chunk=None, what=""):
+def check_scan(inp, chunk=None, what="", path="auto"):
     dt = inp.wl.dtype
-    say("case:", inp.wl.name, "chunk", chunk, what)
-    y, fin = run_gpu(inp, chunk)
+    say("case:", inp.wl.name, "chunk", chunk, what, path)
+    y, fin = run_gpu(inp, chunk, path=path)
     yr, fr = oracle_scan(inp)
     ey = assert_close(y, yr, dt, "y " + what)
     ef = assert_close(fin, fr, dt, "final " + what)
@@ -192,7 +192,9 @@ def test_packed_equals_separate_dense_runs():
 # ------------------------------------------------------------------ one walk per (sequence, head, tile)
 # With at least 256 (sequence, head, 32-column tile) walks the chunk states
 # and the passing between chunks run as one kernel that walks each
-# sequence's chunks in order; these shapes take that path.
+# sequence's chunks in order.  Where the scan walk applies (bf16, chunk 256,
+# dstate in (64, 128]) the library takes that instead; these tests force the
+# state walk so that it keeps its coverage at those shapes too.
 FUSED = [
     # (batch, L, H, P, N, G, chunk, dtype, init)
     (4, 300, 32, 64, 128, 2, 64, "bf16", 0.1),
@@ -209,19 +211,20 @@ FUSED = [
 def test_fused_state_walk_shapes(case):
     b, L, H, P, N, G, Q, dt, iv = case
     wl = W.small_workload(batch=b, seqlen=L, H=H, P=P, N=N, G=G, chunk=Q, dtype=dt, init_var=iv)
-    check_scan(W.generate(wl, 13 + L), what=str(case))
+    check_scan(W.generate(wl, 13 + L), what=str(case), path="state_walk")
 
 
 def test_fused_state_walk_slow_decay_long_sequences():
     wl = W.small_workload(batch=4, seqlen=2300, H=32, P=64, N=128, G=1, chunk=128, dtype="bf16",
                           init_var=0.1)
-    check_scan(W.generate(wl, 23, A_range=(-0.02, -0.001)), what="slow decay")
+    check_scan(W.generate(wl, 23, A_range=(-0.02, -0.001)), what="slow decay", path="state_walk")
 
 
-def test_fused_state_walk_packed_with_empty_sequences():
+@pytest.mark.parametrize("path", ["state_walk", "auto"])
+def test_fused_state_walk_packed_with_empty_sequences(path):
     lens = (100, 0, 513, 1, 256, 0, 700, 64, 65, 300, 0, 7, 1024, 33, 0, 250)
     wl = W.small_workload(seqlens=lens, H=8, P=64, N=128, G=2, chunk=256, dtype="bf16", init_var=0.1)
-    check_scan(W.generate(wl, 71), what="packed, %d sequences" % len(lens))
+    check_scan(W.generate(wl, 71), what="packed, %d sequences" % len(lens), path=path)
 
 
 def test_fused_walk_equals_separate_runs():
