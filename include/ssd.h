@@ -334,6 +334,34 @@ ssd_status ssd_chunked_scan_profiled(const void* x, const float* dt, const float
                                      const ssd_shape* shape, void* workspace,
                                      size_t workspace_bytes, void* stream, float* stage_ms);
 
+/*
+ * Allocation-free prefill, for callers that cannot allocate device memory:
+ * code under stream capture, tight serving loops, harnesses that forbid
+ * allocation.  It does exactly what ssd_chunked_scan does, with the
+ * workspace taken from a device array inside the library instead of an
+ * argument: SSD_NOALLOC_SCRATCH_BYTES bytes on every device it runs on, held
+ * until the process ends.
+ *   - The array of the current device (hipGetDevice) is used; `stream` must
+ *     belong to that device.  Its address is looked up (hipGetSymbolAddress)
+ *     on the first call with a device current and kept.
+ *   - Every call on a device shares that device's array.  Calls that overlap
+ *     on one device (other host threads, or streams with no ordering between
+ *     them) race; the caller orders them.  Nothing in the array has to start
+ *     at zero.
+ *   - A shape whose workspace (ssd_chunked_scan_workspace_size with the same
+ *     shape and chunk) exceeds the array returns SSD_ERR_WORKSPACE before
+ *     anything is launched.
+ *   - It calls nothing that allocates or frees device memory.
+ * Same arguments as ssd_chunked_scan without workspace and workspace_bytes;
+ * same errors, plus SSD_ERR_HIP if the device or the array's address cannot
+ * be queried.
+ */
+#define SSD_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+ssd_status ssd_chunked_scan_noalloc(const void* x, const float* dt, const float* A, const void* B,
+                                    const void* C, const float* D, int32_t chunk,
+                                    const float* init_state, void* y, float* final_state,
+                                    const ssd_shape* shape, void* stream);
+
 /* Static English name of a status code. */
 const char* ssd_status_string(int32_t status);
 

@@ -20,8 +20,8 @@ import ctypes
 import os
 from typing import Optional, Sequence, Tuple
 
-__all__ = ["chunked_scan", "decode_step", "decode_window_step", "causal_conv1d", "conv1d_step",
-           "workspace_size", "SsdError", "library_path", "load"]
+__all__ = ["chunked_scan", "chunked_scan_noalloc", "decode_step", "decode_window_step", "causal_conv1d",
+           "conv1d_step", "workspace_size", "SsdError", "library_path", "load"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_NAME = "libssd_mi355x.so"
@@ -87,6 +87,8 @@ def load():
         lib.ssd_chunked_scan_profiled.argtypes = lib.ssd_chunked_scan.argtypes + [
             ctypes.POINTER(ctypes.c_float)]
         lib.ssd_chunked_scan_profiled.restype = ctypes.c_int32
+        lib.ssd_chunked_scan_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_int32, vp, vp, vp, sp, vp]
+        lib.ssd_chunked_scan_noalloc.restype = ctypes.c_int32
         lib.ssd_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, sp, vp]
         lib.ssd_decode_step.restype = ctypes.c_int32
         ap = ctypes.POINTER(_DtAct)
@@ -317,6 +319,37 @@ def chunked_scan(x, dt, A, B, C, D, chunk: int = 256, init_state=None, cu_seqlen
         out = (ctypes.c_float * len(STAGES))()
         _check(lib.ssd_chunked_scan_profiled(*args, out), "ssd_chunked_scan_profiled")
         stage_ms[:] = [float(v) for v in out]
+    del keep
+    return y, final_state
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20  # SSD_NOALLOC_SCRATCH_BYTES of include/ssd.h
+
+
+def chunked_scan_noalloc(x, dt, A, B, C, D, chunk: int, y, final_state=None, init_state=None,
+                         cu_seqlens=None, cu_seqlens_host: Optional[Sequence[int]] = None, path: str = "auto"):
+    """ssd_chunked_scan_noalloc: the chunked prefill with the library's own
+    device scratch array as its workspace (no allocation anywhere: ``y`` and,
+    when wanted, ``final_state`` are given by the caller).  Same shapes as
+    ``chunked_scan``; ``cu_seqlens`` must already be a GPU int32 tensor."""
+    torch = _torch()
+    _need_cuda(x, dt, A, B, C, D, init_state, y, final_state)
+    if cu_seqlens is not None and not (hasattr(cu_seqlens, "is_cuda") and cu_seqlens.is_cuda):
+        raise ValueError("cu_seqlens must be a GPU tensor here (copying it would allocate)")
+    sh, keep = make_shape(x, B, cu_seqlens, cu_seqlens_host, y_dtype=y.dtype, path=path)
+    H, P, N = sh.nheads, sh.headdim, sh.dstate
+    lead = tuple(x.shape[:-2])
+    _expect(dt, lead + (H,), torch.float32, "dt")
+    _expect(B, lead + (sh.ngroups, N), x.dtype, "B")
+    _expect(C, lead + (sh.ngroups, N), x.dtype, "C")
+    _expect(A, (H,), torch.float32, "A")
+    _expect(D, (H,), torch.float32, "D")
+    _expect(init_state, (sh.batch, H, P, N), torch.float32, "init_state")
+    _expect(y, tuple(x.shape), y.dtype, "y")
+    _expect(final_state, (sh.batch, H, P, N), torch.float32, "final_state")
+    _check(load().ssd_chunked_scan_noalloc(_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), int(chunk),
+                                           _ptr(init_state), _ptr(y), _ptr(final_state), ctypes.byref(sh),
+                                           _stream_handle(x)), "ssd_chunked_scan_noalloc")
     del keep
     return y, final_state
 

@@ -21,7 +21,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_NAME = "libssd_mi355x.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
-SOURCES = ["ssd_api.cpp", "ssd_prefill.hip", "ssd_scan_walk.hip", "ssd_decode.hip", "ssd_conv.hip"]
+SOURCES = ["ssd_api.cpp", "ssd_prefill.hip", "ssd_scan_walk.hip", "ssd_decode.hip", "ssd_conv.hip",
+           "ssd_noalloc.hip"]
 ARCH = "gfx950"
 
 

@@ -28,6 +28,22 @@ ssd_status ok() {
     return SSD_OK;
 }
 
+}  // namespace
+
+namespace ssd {
+
+int32_t set_error_detail(int32_t st, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_detail, sizeof(g_detail), fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+}  // namespace ssd
+
+namespace {
+
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
 

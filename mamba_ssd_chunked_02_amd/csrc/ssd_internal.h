@@ -159,6 +159,10 @@ struct ConvArgs {
     int32_t dtype, y_f32, silu;
 };
 
+// Sets the sentence ssd_last_error_detail() returns on this thread (for
+// entry points outside ssd_api.cpp); returns st.
+int32_t set_error_detail(int32_t st, const char* fmt, ...);
+
 // dstate padded to the 32-row tiles the kernels use.
 inline int padded_dstate(int N) { return N <= 32 ? 32 : N <= 64 ? 64 : N <= 128 ? 128 : 256; }
 

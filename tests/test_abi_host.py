@@ -346,3 +346,18 @@ def test_conv1d_argument_errors(lib):
     assert step(state=X) == E_SHAPE
     o = conv_outs((64,)); o.out[0] = S0
     assert step(out=o) == E_SHAPE
+
+
+def test_noalloc_rejects_before_any_device_call(lib):
+    """ssd_chunked_scan_noalloc validates the shape, then the workspace size
+    against the static array, before it touches the device."""
+    assert lib.ssd_chunked_scan_noalloc(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 64, None, FAKE + 4096, None,
+                                        ctypes.byref(shape(dtype=7)), None) == E_DTYPE
+    big = shape(batch=8, seqlen=8192, nheads=80, headdim=64, dstate=128, dtype=1)
+    assert lib.ssd_chunked_scan_noalloc(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 256, None, FAKE + 4096, None,
+                                        ctypes.byref(big), None) == E_WS
+    assert "static array" in lib.ssd_last_error_detail().decode()
+    assert ssd.NOALLOC_SCRATCH_BYTES == 64 << 20
+    import re
+    m = re.search(r"#define SSD_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", open(HEADER).read())
+    assert m and int(m.group(1)) << int(m.group(2)) == ssd.NOALLOC_SCRATCH_BYTES
