@@ -322,7 +322,9 @@ ssd_status ssd_causal_conv1d_step(void* conv_state, const void* x, const float* 
  * With SSD_PATH_AUTO the library takes a walk when there are enough
  * (sequence, head, 32-column tile) walks, 256 or more, and sequences of
  * similar length (with a host copy of a packed batch's offsets, no sequence
- * over 1.5 times the mean chunk count), else the chunk-parallel path.
+ * over 1.5 times the mean chunk count), else the chunk-parallel path.  The
+ * walk it takes is the scan walk where that path applies, else the state
+ * walk.
  * Unlike ssd_chunked_scan it blocks the calling thread until the kernels
  * finish.  Same arguments and errors as ssd_chunked_scan, plus SSD_ERR_NULL
  * when stage_ms is NULL.
