@@ -132,6 +132,17 @@ __device__ inline bool walk_of(const Plan& pl, int per_xcd, int npt, int nslice,
     return w.nu > 0;
 }
 
+// hi = rn(v) and lo = rn(v - hi) of four fp32 values as bf16 pairs packed in
+// 32-bit words (element 0 in the low half).  hi's fp32 value is read back from
+// its bits (a shift or a mask) rather than converted a second time.
+__device__ inline void split_hilo(const f32x4& v, u32x2& hi, u32x2& lo) {
+    hi = __builtin_bit_cast(u32x2, Tr<bf16_t>::narrow4(v));
+    const uint32_t h0 = hi[0], h1 = hi[1];
+    const f32x4 hf = {__builtin_bit_cast(float, h0 << 16), __builtin_bit_cast(float, h0 & 0xffff0000u),
+                      __builtin_bit_cast(float, h1 << 16), __builtin_bit_cast(float, h1 & 0xffff0000u)};
+    lo = __builtin_bit_cast(u32x2, Tr<bf16_t>::narrow4(v - hf));
+}
+
 // ------------------------------------------------------------------ staging (waves 4-7)
 // Thread tau of the 256 staging threads owns 4 consecutive tokens k0..k0+3
 // and 8 columns 8 pb..8 pb+7 of the unit's tile: it loads 4 x 16 bytes of x
@@ -189,9 +200,10 @@ __device__ inline void stage_store(const StageRegs& r, const Plan& pl, const Wal
     for (int col = 0; col < 8; ++col) {
         const f32x4 o = {(float)xm[0][col] * wb[0], (float)xm[1][col] * wb[1], (float)xm[2][col] * wb[2],
                          (float)xm[3][col] * wb[3]};
-        const bf16x4 hi = Tr<bf16_t>::narrow4(o);
-        Tr<bf16_t>::st4raw(xh + col * kLP, hi);
-        Tr<bf16_t>::st4raw(xl + col * kLP, Tr<bf16_t>::narrow4(o - Tr<bf16_t>::widen4(hi)));
+        u32x2 hi, lo;
+        split_hilo(o, hi, lo);
+        *(u32x2*)(xh + col * kLP) = hi;
+        *(u32x2*)(xl + col * kLP) = lo;
         Tr<bf16_t>::st4raw(xr + col * kLP, bf16x4{xm[0][col], xm[1][col], xm[2][col], xm[3][col]});
     }
     if (pb == 0) {
@@ -224,9 +236,10 @@ __device__ inline void put_state(const f32x16& acc, const WalkBufs& bufs, int b,
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
         const f32x4 v = {acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]};
-        const bf16x4 hi = Tr<bf16_t>::narrow4(v);
-        Tr<bf16_t>::st4raw(sh + 8 * q, hi);
-        Tr<bf16_t>::st4raw(sl + 8 * q, Tr<bf16_t>::narrow4(v - Tr<bf16_t>::widen4(hi)));
+        u32x2 hi, lo;
+        split_hilo(v, hi, lo);
+        *(u32x2*)(sh + 8 * q) = hi;
+        *(u32x2*)(sl + 8 * q) = lo;
     }
 }
 
@@ -239,12 +252,13 @@ __device__ inline int state_off(int v, int pt, int nt, int P, int N) {
     return (p < P && n < N) ? (p * N + n) * 4 : kOutOfRange;
 }
 
-// One chunk of the state walk for the current unit: H <- Horner over the 8
-// blocks, as two interleaved chains so the MFMAs of one overlap the scaling
-// of the other:  O: h_c (as block -1), blocks 1, 3, 5, 7;  E: blocks 0, 2, 4, 6;
-// each chain scales by the decay across the two blocks it skips; at the end
-// H = O + gam_7 E.  A = the chunk's B^T fragments (n-tile rows), B = the
-// staged (x wb)^T hi and lo tiles.
+// One chunk of the state walk for the current unit: the Horner scheme over
+// the 8 blocks, H <- gam_j H + X_j from H = h_c, X_j being block j's
+// contribution with its weights taken to the block's end.  A = the chunk's
+// B^T fragments (n-tile rows), B = the staged (x wb)^T hi and lo tiles.  The
+// operands of block j + 1 are read from LDS while block j's MFMAs run (the
+// scheduling barriers keep the reads ahead); the other wave on the SIMD fills
+// the matrix core while this one scales H.
 __device__ inline void walk_advance(f32x16& acc, const bf16x8 (&bf)[kQ / 16], const WalkBufs& bufs, int b) {
     const int lane = threadIdx.x & 63, half = lane >> 5, col = lane & 31;
     const WalkTables tb = walk_tables(bufs.stage(b));
@@ -253,27 +267,27 @@ __device__ inline void walk_advance(f32x16& acc, const bf16x8 (&bf)[kQ / 16], co
     const f32x4 g0 = *(const f32x4*)tb.gam;
     const f32x4 g1 = *(const f32x4*)(tb.gam + 4);
     const float gm[8] = {g0[0], g0[1], g0[2], g0[3], g1[0], g1[1], g1[2], g1[3]};
-    f32x16 e = {};
-    auto block = [&](f32x16& ch, int jb) {
+    bf16x8 op[2][4];
+    auto ld = [&](int jb, bf16x8 (&o)[4]) {
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-            const int s = 2 * jb + ks;
-            mma16(ch, bf[s], Tr<bf16_t>::ld8(hrow + 16 * s));
-            mma16(ch, bf[s], Tr<bf16_t>::ld8(lrow + 16 * s));
+            o[2 * ks] = Tr<bf16_t>::ld8(hrow + 16 * (2 * jb + ks));
+            o[2 * ks + 1] = Tr<bf16_t>::ld8(lrow + 16 * (2 * jb + ks));
         }
     };
-    block(e, 0);
+    ld(0, op[0]);
 #pragma unroll
-    for (int jb = 1; jb < kNTI; ++jb) {
-        if (jb & 1) {
-            acc *= gm[jb - 1] * gm[jb];
-            block(acc, jb);
-        } else {
-            e *= gm[jb - 1] * gm[jb];
-            block(e, jb);
+    for (int jb = 0; jb < kNTI; ++jb) {
+        if (jb + 1 < kNTI) ld(jb + 1, op[(jb + 1) & 1]);
+        __builtin_amdgcn_sched_barrier(0);
+        acc *= gm[jb];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            mma16(acc, bf[2 * jb + ks], op[jb & 1][2 * ks]);
+            mma16(acc, bf[2 * jb + ks], op[jb & 1][2 * ks + 1]);
         }
+        __builtin_amdgcn_sched_barrier(0);
     }
-    acc += gm[kNTI - 1] * e;
 }
 
 template <int NU>
