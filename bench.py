@@ -328,12 +328,35 @@ def conv1d_measure(torch, ssd, wl, wd, reps=20):
                     "decode step b%d; bf16 in/out, eager back-to-back" % (C, b, L, bd)}
 
 
+def environment(torch):
+    """What the numbers were measured on: device, HIP and torch versions, and
+    the clock levels rocm-smi reports at bench start (the device is idle
+    then, so sclk reads its idle level; None when rocm-smi is absent)."""
+    import subprocess
+    env = {"gpu": torch.cuda.get_device_name(0), "gcn_arch": torch.cuda.get_device_properties(0).gcnArchName,
+           "hip": torch.version.hip, "torch": torch.__version__, "clocks": None}
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True, timeout=20)
+        lines = [l.strip() for l in r.stdout.splitlines() if "sclk" in l or "mclk" in l or "fclk" in l]
+        env["clocks"] = lines[:6] or None
+    except Exception:  # pragma: no cover - rocm-smi absent or not permitted
+        pass
+    return env
+
+
+def _pct(v):
+    v = np.asarray(v)
+    return {"p10": round(float(np.percentile(v, 10)), 4), "p50": round(float(np.percentile(v, 50)), 4),
+            "p90": round(float(np.percentile(v, 90)), 4)}
+
+
 def other_prefill(torch, ssd, reps=20):
-    """Prefill throughput of the other two prefill configurations, through the
+    """Prefill throughput and TFLOPS of the other two prefill configurations, through the
     plain entry point: the 130M-shaped layer (b1 L4096 H24 P64 N128 G1) and
     the packed grouped batch ({1024, 4096, 12288, 32768} tokens, H128 P64
     N128 G8, offsets given with their host copy).  bf16 x/B/C, fp32 dt/A/D,
     initial states ~N(0, 0.1), chunk 256; inputs drawn on the GPU."""
+    from mamba_ssd_chunked_02_amd import workloads as W
     dev = torch.device("cuda:0")
     g = torch.Generator(device="cpu").manual_seed(23)
     out = {}
@@ -368,7 +391,11 @@ def other_prefill(torch, ssd, reps=20):
         e1.record()
         e1.synchronize()
         ms = e0.elapsed_time(e1) / reps
-        out[name] = {"ms": round(ms, 4), "tokens_per_s": round(T / (ms * 1e-3), 1)}
+        wl = W.CONFIGS[1] if dense else W.CONFIGS[4]
+        assert wl.tokens == T and wl.H == H and wl.G == G
+        out[name] = {"ms": round(ms, 4), "tokens_per_s": round(T / (ms * 1e-3), 1),
+                     "tflops_dense": round(prefill_flops(wl) / (ms * 1e-3) / 1e12, 2),
+                     "tflops_causal": round(prefill_flops(wl, causal=True) / (ms * 1e-3) / 1e12, 2)}
         del x, dt, B, C, y, ws
     out["what"] = "plain-entry-point prefill, back-to-back calls, the other two prefill configurations"
     return out
@@ -378,19 +405,21 @@ def other_prefill(torch, ssd, reps=20):
 # traffic summary describe those kernels only)
 PREFILL_SOURCES = ("ssd_api.cpp", "ssd_device.h", "ssd_internal.h", "ssd_prefill.hip", "ssd_prefill_shared.h",
                    "ssd_scan_walk.hip")
+# the sources that define and launch the decode kernel
+DECODE_SOURCES = ("ssd_api.cpp", "ssd_device.h", "ssd_internal.h", "ssd_decode.hip")
 
 
-def _source_digest():
-    """sha256 of the prefill kernel sources, to tell whether counters are stale."""
+def _source_digest(files=PREFILL_SOURCES):
+    """sha256 of kernel sources, to tell whether counters are stale."""
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "mamba_ssd_chunked_02_amd", "csrc")
-    for f in PREFILL_SOURCES:
+    for f in files:
         h.update(open(os.path.join(csrc, f), "rb").read())
     return h.hexdigest()[:16]
 
 
-def _traffic(path, kernel, alg_bytes):
+def _traffic(path, kernel, alg_bytes, files=PREFILL_SOURCES):
     """HBM bytes per launch of `kernel` from a committed counter summary:
     lines `key: value` with fetch_kib, write_kib (per dispatch, rocprofv3
     FETCH_SIZE / WRITE_SIZE), copy_fetch_factor and copy_write_factor (known
@@ -404,7 +433,7 @@ def _traffic(path, kernel, alg_bytes):
             k, v = line.split(":", 1)
             kv[k.strip()] = v.strip()
     try:
-        if kv.get("source_digest") != _source_digest():
+        if kv.get("source_digest") != _source_digest(files):
             return None
         fetch = float(kv["fetch_kib"]) * 1024 * float(kv["copy_fetch_factor"])
         write = float(kv["write_kib"]) * 1024 * float(kv["copy_write_factor"])
@@ -455,6 +484,7 @@ def main():
     from mamba_ssd_chunked_02_amd import workloads as W
 
     dev = torch.device("cuda:0")
+    env = environment(torch)
     wl = W.CONFIGS[3]
     wd = W.CONFIGS[2]
     log("generating prefill inputs:", wl.name)
@@ -620,7 +650,9 @@ def main():
     dbytes = decode_bytes(wd)
     dgbs = dbytes / (decode_ms * 1e-3) / 1e9
     roof_dec = {"bound": "hbm", "achieved": round(dgbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(dgbs / HBM_PEAK_GBS, 4), "traffic": None,
+                "frac": round(dgbs / HBM_PEAK_GBS, 4),
+                "traffic": _traffic(os.path.join(ROOT, "profiles", "traffic_decode_2p7b.txt"),
+                                    "ssd_decode_kernel", dbytes, DECODE_SOURCES),
                 "kernel": "ssd_decode_kernel<bf16,32>", "avg_ms": round(decode_ms, 4),
                 "algorithmic_bytes": dbytes}
 
@@ -723,6 +755,9 @@ def main():
                            "what": "torch device-to-device copy of a buffer the size of the decode state"},
         "cpu_baseline": cpu,
         "wall_s_timed_region": round(wall, 3),
+        "distribution_ms": {"prefill": _pct(pre_ms), "decode": _pct(dec_ms),
+                            "what": "p10 / median / p90 over the timed steps (HIP events per call)"},
+        "environment": env,
     }
     print(json.dumps(out), flush=True)
 

@@ -76,3 +76,19 @@ def test_roofline_bound_follows_arithmetic_intensity():
     assert r["flop_per_byte"] < r["ridge_flop_per_byte"] == 312.5
     dense = {"flops": 10 ** 15, "flops_causal": 10 ** 15, "bytes": 10 ** 9}
     assert bench.roofline_of(dense, 1.0, "k")["bound"] == "mfma"
+
+
+def test_traffic_summary_is_read_only_while_its_sources_match(tmp_path):
+    """A counter summary scales FETCH_SIZE / WRITE_SIZE (KiB) by the copy
+    calibration factors, and is ignored once the kernel sources it describes
+    have changed (a different digest)."""
+    good = bench._source_digest(bench.DECODE_SOURCES)
+    body = "kernel: k\nfetch_kib: 1000.0\nwrite_kib: 2000.0\ncopy_fetch_factor: 2.000\ncopy_write_factor: 1.000\n"
+    f = tmp_path / "t.txt"
+    f.write_text(body + "source_digest: %s\n" % good)
+    t = bench._traffic(str(f), "k", 6 * 1024 * 1000, bench.DECODE_SOURCES)
+    assert t["fetch_bytes"] == 2 * 1000 * 1024 and t["write_bytes"] == 2000 * 1024
+    assert t["over_algorithmic"] == round(4000 * 1024 / (6 * 1024 * 1000), 3)
+    f.write_text(body + "source_digest: 0000000000000000\n")
+    assert bench._traffic(str(f), "k", 1, bench.DECODE_SOURCES) is None
+    assert bench._source_digest(bench.DECODE_SOURCES) != bench._source_digest(bench.PREFILL_SOURCES)
