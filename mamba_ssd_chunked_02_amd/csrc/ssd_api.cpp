@@ -95,21 +95,33 @@ struct Prepared {
     int32_t walk_nslice; // scan walk: workgroups per (sequence, group)
 };
 
-// The scan walk's work split: about one workgroup per CU, each walking at
-// most kWalkMaxUnits (head, column tile) units of one group; the group's
-// units are cut into equal slices.
-constexpr int64_t kWalkWorkgroups = 256;
+// The scan walk's work split: each workgroup walks at most kWalkMaxUnits
+// (head, column tile) units of one group, the group's units cut into equal
+// slices.  One 8-wave workgroup fits per CU, so a launch runs in rounds of 32
+// workgroups per XCD, and a workgroup's chunk step costs about kWalkStepFixed
+// + n unit steps for n units (the output waves' per-chunk work is shared by
+// the units; measured 2.2 us + 4.15 us per unit at 2.1 GHz).  The split with
+// the least rounds x step cost wins, the one with more workgroups on a tie.
+constexpr int64_t kXcds = 8, kCusPerXcd = 32;
 constexpr int64_t kWalkMaxUnits = 6;
+constexpr double kWalkStepFixed = 0.53;
 
 void walk_split(const ssd::Plan& pl, int32_t* nus, int32_t* nslice) {
     const int64_t npt = (pl.P + 31) / 32;
     const int64_t upg = (int64_t)pl.hpg * npt;
-    const int64_t units = (int64_t)pl.nseq * pl.G * upg;
-    int64_t n = std::max<int64_t>(1, std::min<int64_t>(kWalkMaxUnits, units / kWalkWorkgroups));
-    n = std::min(n, upg);
-    const int64_t ns = (upg + n - 1) / n;
-    *nslice = (int32_t)ns;
-    *nus = (int32_t)((upg + ns - 1) / ns);
+    const int64_t walks = (int64_t)pl.nseq * pl.G;
+    double best = 0.0;
+    for (int64_t n = 1; n <= std::min(kWalkMaxUnits, upg); ++n) {
+        const int64_t ns = (upg + n - 1) / n, nu = (upg + ns - 1) / ns;
+        const int64_t per_xcd = (walks * ns + kXcds - 1) / kXcds;
+        const int64_t rounds = std::max<int64_t>(1, (per_xcd + kCusPerXcd - 1) / kCusPerXcd);
+        const double cost = (double)rounds * (kWalkStepFixed + (double)nu);
+        if (n == 1 || cost < best) {
+            best = cost;
+            *nslice = (int32_t)ns;
+            *nus = (int32_t)nu;
+        }
+    }
 }
 
 // Heads of one group that a chunk_state / chunk_scan workgroup walks: the

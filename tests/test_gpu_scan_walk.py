@@ -69,6 +69,8 @@ SHAPES = [
     (8, 260, 64, 64, 128, 4, 0.1),      # 1024 units: 4, four groups
     (8, 300, 80, 64, 128, 1, 0.1),      # 1280 units: 5 (the 2.7B-shaped layer's split)
     (8, 200, 96, 64, 128, 2, 0.1),      # 1536 units: 6
+    (2, 300, 80, 64, 128, 1, 0.1),      # 320 units: 2 (160 workgroups in one round, not 320 in two)
+    (4, 300, 80, 64, 128, 1, 0.1),      # 640 units: 3 (216 workgroups, the last slice of each group short)
     (2, 513, 8, 40, 96, 2, 0.1),        # partial column tile, dstate 96
     (2, 300, 6, 128, 72, 3, 0.1),       # four column tiles, dstate 72, three groups
     (3, 33, 8, 64, 128, 1, 0.1),        # one partial chunk of one full and one partial block
