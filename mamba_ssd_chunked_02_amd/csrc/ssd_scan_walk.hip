@@ -149,6 +149,10 @@ __device__ inline void split_hilo(const f32x4& v, u32x2& hi, u32x2& lo) {
 // plus the tokens' decay sums and steps, and writes the column-major tiles
 // (4 tokens = 8 bytes per column).  The threads of pb = 0 also write the
 // decay tables of their 4 tokens, and of their block when k0 starts one.
+// s_waitcnt vmcnt(0) with expcnt and lgkmcnt left alone (gfx9 encoding:
+// vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
+constexpr int kWaitVmcnt0 = 0x0F70;
+
 struct StageRegs {
     bf16x8 raw[4];
     f32x4 cs4, dt4;
@@ -358,6 +362,12 @@ __device__ void walk_states(const Plan& pl, const Walk& w, const WalkBufs& bufs,
                 }
                 walk_advance(acc[j], bf, bufs, b);
                 if (more && j + 1 == nu) put_state(acc[0], bufs, b ^ 1, nt);
+                // sn's loads, issued at the step's start, are waited for here
+                // on every path.  Otherwise the copy into sr, placed after
+                // the branch, waits on a count that must also hold on the
+                // path without the B^T reload, which on the reload path
+                // means waiting for most of those 16 younger loads.
+                __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
                 if (j == nu - 1 && c + 1 < w.nck) load_bt(c + 1);
                 sr = sn;
                 __syncthreads();
@@ -477,8 +487,13 @@ __device__ __forceinline__ void walk_block(const bf16x8 (&ga)[TI + 1][2], const 
     for (int it = 0; it < 4; ++it) {
         const int tr = (lane >> 3) + 8 * it, c4 = 4 * (lane & 7);
         const f32x4 r = *(const f32x4*)(ep + tr * kEpPitch + c4);
-        const bool ok = 32 * TI + tr < len && c4 < pcols;
-        buffer_store4<TY>(r, ry, ok ? (32 * TI + tr) * rowb + yb0 + c4 * (int)sizeof(TY) : kOutOfRange);
+        // the row bound and the offset as one lane term and a uniform one:
+        // folded together, each row group's lane offset is loop-invariant,
+        // gets hoisted, and the eight of them spill
+        const int rows = __builtin_amdgcn_readfirstlane(len - 32 * TI - 8 * it);
+        const int uoff = __builtin_amdgcn_readfirstlane((32 * TI + 8 * it) * rowb + yb0);
+        const bool ok = (lane >> 3) < rows && c4 < pcols;
+        buffer_store4<TY>(r, ry, ok ? (lane >> 3) * rowb + c4 * (int)sizeof(TY) + uoff : kOutOfRange);
     }
     __builtin_amdgcn_wave_barrier();
 }
@@ -494,24 +509,35 @@ __device__ void walk_outputs(const Plan& pl, const Walk& w, const WalkBufs& bufs
     // intra-chunk term) and C rows (A of the state term).  C goes through a
     // buffer over the chunk's rows (one 32-bit offset, the k-steps as
     // immediate offsets); columns n >= N (the padding of a dstate below 128)
-    // are zeroed after the load.
+    // are zeroed after the load.  That select waits for the loads, and the
+    // wait covers the y stores issued before them, so it sits behind a
+    // uniform branch that dstate 128 skips: there the loads are first used
+    // in the next step.
     auto load_block = [&](int c, auto ti, auto& ga, bf16x8 (&ca)[kNT / 16]) {
         constexpr int TI = decltype(ti)::value;
         const ChunkDesc d = w.chunk(c);
-        const bf16_t* row = cb + ((size_t)(w.chunk0 + c) * G + w.g) * kQ * kQ + (size_t)(32 * TI + col) * kQ +
-                            8 * half;
+        // buffers from the block's first row, so that the lane offsets are
+        // the same for both blocks and every chunk
+        const __amdgpu_buffer_rsrc_t rg = buffer_rsrc(
+            cb + (((size_t)(w.chunk0 + c) * G + w.g) * kQ + 32 * TI) * kQ, (uint32_t)(32 * kQ * 2));
+        const int goff = (col * kQ + 8 * half) * 2;
 #pragma unroll
         for (int kj = 0; kj <= TI; ++kj)
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks) ga[kj][ks] = Tr<bf16_t>::ld8(row + 32 * kj + 16 * ks);
-        const __amdgpu_buffer_rsrc_t rc =
-            buffer_rsrc(Cm + d.row0 * G * N, (uint32_t)((size_t)d.len * G * N * 2));
-        const int off = ((min(32 * TI + col, d.len - 1) * G + w.g) * N + 8 * half) * 2;
+            for (int ks = 0; ks < 2; ++ks) ga[kj][ks] = buffer_ld8<bf16_t>(rg, goff + (32 * kj + 16 * ks) * 2);
+        // C rows past the chunk's end read as zero (their y is not stored)
+        // (the byte count through readfirstlane: computed on the vector
+        // unit it would make the descriptor look divergent)
+        const int cbytes = __builtin_amdgcn_readfirstlane(max(d.len - 32 * TI, 0) * G * N * 2);
+        const __amdgpu_buffer_rsrc_t rc = buffer_rsrc(Cm + (d.row0 + 32 * TI) * G * N, (uint32_t)cbytes);
+        const int off = ((col * G + w.g) * N + 8 * half) * 2;
 #pragma unroll
         for (int s = 0; s < kNT / 16; ++s) ca[s] = buffer_ld8<bf16_t>(rc, off + 32 * s);
+        if (N < kNT) {
 #pragma unroll
-        for (int s = 0; s < kNT / 16; ++s)
-            if (16 * s + 8 * half >= N) ca[s] = bf16x8{};
+            for (int s = 0; s < kNT / 16; ++s)
+                if (16 * s + 8 * half >= N) ca[s] = bf16x8{};
+        }
     };
     using IA = std::integral_constant<int, TA>;
     using IB = std::integral_constant<int, TB>;
