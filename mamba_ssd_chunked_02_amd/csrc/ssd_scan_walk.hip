@@ -152,6 +152,7 @@ __device__ inline void split_hilo(const f32x4& v, u32x2& hi, u32x2& lo) {
 // s_waitcnt vmcnt(0) with expcnt and lgkmcnt left alone (gfx9 encoding:
 // vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
 constexpr int kWaitVmcnt0 = 0x0F70;
+constexpr int kWaitVmcnt4 = 0x0F74;
 
 struct StageRegs {
     bf16x8 raw[4];
@@ -570,14 +571,22 @@ __device__ void walk_outputs(const Plan& pl, const Walk& w, const WalkBufs& bufs
             // the block is done, so the reload spreads over the step instead
             // of leaving together at its end.
             const bool reload = j == w.nu - 1 && c + 1 < w.nck;
+            // Before each (conditional) reload, everything but the block's
+            // own 4 y stores is waited for, on both paths: the other block's
+            // operands, reloaded a block earlier, are then known to have
+            // arrived.  Without it the wait before their first use has to
+            // hold on the path without this reload too, and on the reload
+            // path it then also waits for most of these 16 younger loads.
             walk_block<TY, TA>(ga_a, ca_a, has_state, shrow, slrow, tb, xhrow, xrrow, ep, ry, yb0, rowb, d.len,
                                pcols, Dh);
             __builtin_amdgcn_sched_barrier(0);
+            __builtin_amdgcn_s_waitcnt(kWaitVmcnt4);
             if (reload) load_block(c + 1, IA{}, ga_a, ca_a);
             __builtin_amdgcn_sched_barrier(0);
             walk_block<TY, TB>(ga_b, ca_b, has_state, shrow, slrow, tb, xhrow, xrrow, ep, ry, yb0, rowb, d.len,
                                pcols, Dh);
             __builtin_amdgcn_sched_barrier(0);
+            __builtin_amdgcn_s_waitcnt(kWaitVmcnt4);
             if (reload) load_block(c + 1, IB{}, ga_b, ca_b);
             __syncthreads();
         }
