@@ -432,34 +432,35 @@ __device__ __forceinline__ void walk_block(const bf16x8 (&ga)[TI + 1][2], const 
     }
     // the chain that ends at the last included block K is complete; the other
     // one still takes the decay across block K.  K is TI (diagonal block in
-    // the scheme) or TI - 1, so each branch knows both chains' roles.
-    f32x16 acc;
+    // the scheme) or TI - 1, so each branch knows both chains' roles.  Each
+    // branch also adds the state term and applies its row scaling, and both
+    // leave the sum in the chain of TI's parity (acc): where the branches
+    // meet only acc is live, in the same registers on both paths.
+    f32x16& acc = (TI & 1) ? co : ce;
+    f32x16& other = (TI & 1) ? ce : co;
+    auto scale_rows = [&](const float* scale) {
+#pragma unroll
+        for (int vg = 0; vg < 4; ++vg) {
+            const f32x4 u = *(const f32x4*)(scale + 32 * TI + 8 * vg + 4 * half);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[4 * vg + i] *= u[i];
+        }
+    };
     if (fast) {
-        f32x16& ch = (TI & 1) ? co : ce;
-        if (TI >= 2) ch *= tb.gam[TI - 1] * tb.gam[TI];
+        // acc ends at TI - 2: across blocks TI - 1 and TI, then block TI
+        if (TI >= 2) acc *= tb.gam[TI - 1] * tb.gam[TI];
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) mma16(ch, ga[TI][ks], Tr<bf16_t>::ld8(xhrow + 32 * TI + 16 * ks));
-        if (TI == 0) acc = ce;
-        else if (TI & 1) acc = co + tb.gam[TI] * ce;
-        else acc = ce + tb.gam[TI] * co;
+        for (int ks = 0; ks < 2; ++ks) mma16(acc, ga[TI][ks], Tr<bf16_t>::ld8(xhrow + 32 * TI + 16 * ks));
+        if (TI >= 1) acc += tb.gam[TI] * other;
+        if (has_state) acc += __expf(tb.cs[32 * TI + 31]) * sacc;
+        scale_rows(tb.ue);
     } else {
-        if (TI <= 1) acc = ce;  // block 0 alone (TI = 1) or nothing (TI = 0, ce is zero)
-        else if ((TI - 1) & 1) acc = co + tb.gam[TI - 1] * ce;
-        else acc = ce + tb.gam[TI - 1] * co;
-    }
-    if (has_state) {
-        const int e = fast ? 32 * TI + 31 : 32 * TI - 1;
-        const float dec = e >= 0 ? __expf(tb.cs[e]) : 1.f;
-        acc += dec * sacc;
-    }
-    const float* scale = fast ? tb.ue : tb.ul;
-#pragma unroll
-    for (int vg = 0; vg < 4; ++vg) {
-        const f32x4 u = *(const f32x4*)(scale + 32 * TI + 8 * vg + 4 * half);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[4 * vg + i] *= u[i];
-    }
-    if (!fast) {
+        // K = TI - 1 ends other; acc (ends at TI - 2, or zero) takes block
+        // K's decay.  TI = 1: other is block 0's chain, acc zero.
+        if (TI >= 1) acc = other + tb.gam[TI - 1] * acc;
+        if (has_state) acc += (TI > 0 ? __expf(tb.cs[32 * TI - 1]) : 1.f) * sacc;
+        scale_rows(tb.ul);
+        // the diagonal block with exact per-element factors
         const float cst = tb.cs[32 * TI + col];
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
