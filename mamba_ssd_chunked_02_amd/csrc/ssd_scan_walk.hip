@@ -143,17 +143,17 @@ __device__ inline void split_hilo(const f32x4& v, u32x2& hi, u32x2& lo) {
     lo = __builtin_bit_cast(u32x2, Tr<bf16_t>::narrow4(v - hf));
 }
 
+// s_waitcnt vmcnt(0) and vmcnt(4) with expcnt and lgkmcnt left alone (gfx9 encoding:
+// vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
+constexpr int kWaitVmcnt0 = 0x0F70;
+constexpr int kWaitVmcnt4 = 0x0F74;
+
 // ------------------------------------------------------------------ staging (waves 4-7)
 // Thread tau of the 256 staging threads owns 4 consecutive tokens k0..k0+3
 // and 8 columns 8 pb..8 pb+7 of the unit's tile: it loads 4 x 16 bytes of x
 // plus the tokens' decay sums and steps, and writes the column-major tiles
 // (4 tokens = 8 bytes per column).  The threads of pb = 0 also write the
 // decay tables of their 4 tokens, and of their block when k0 starts one.
-// s_waitcnt vmcnt(0) with expcnt and lgkmcnt left alone (gfx9 encoding:
-// vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
-constexpr int kWaitVmcnt0 = 0x0F70;
-constexpr int kWaitVmcnt4 = 0x0F74;
-
 struct StageRegs {
     bf16x8 raw[4];
     f32x4 cs4, dt4;
@@ -577,7 +577,7 @@ __device__ void walk_outputs(const Plan& pl, const Walk& w, const WalkBufs& bufs
             // operands, reloaded a block earlier, are then known to have
             // arrived.  Without it the wait before their first use has to
             // hold on the path without this reload too, and on the reload
-            // path it then also waits for most of these 16 younger loads.
+            // path it then also waits for most of the younger reload loads.
             walk_block<TY, TA>(ga_a, ca_a, has_state, shrow, slrow, tb, xhrow, xrrow, ep, ry, yb0, rowb, d.len,
                                pcols, Dh);
             __builtin_amdgcn_sched_barrier(0);
