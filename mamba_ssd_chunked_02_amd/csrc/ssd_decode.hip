@@ -16,10 +16,11 @@ namespace ssd {
 
 namespace {
 
-// Decode step: two waves per workgroup, one (sequence, head) state block
-// each.  At the 2.7B decode shape (20 480 blocks) this streamed about 1%
-// faster than four or three waves per workgroup and 3% faster than one.
-constexpr int kDecThreads = 128;
+// Decode step: eight waves per workgroup, one (sequence, head) state block
+// each.  At the 2.7B decode shape (20 480 blocks), in interleaved A/B runs,
+// this streamed 1.5% faster than two waves per workgroup and 2.7% faster
+// than sixteen.
+constexpr int kDecThreads = 512;
 // Windowed step: four waves per workgroup, one state block each.
 constexpr int kWinThreads = 256;
 
@@ -58,7 +59,7 @@ __device__ inline __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t 
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kBufferWord3);
 }
 
-// Wave w of block L updates the state block (b, h) = 2L + w: P rows of N
+// Wave w of block L updates the state block (b, h) = 8L + w: P rows of N
 // floats, contiguous.  Lane l owns columns n = 4 (l % TPR) .. +3 of the rows
 // p = RPI i + l / TPR, so each wave instruction moves 64 x 16 contiguous bytes
 // and B, C, dt, A are loaded once per lane.  Rows go in batches of kBatch
