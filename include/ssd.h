@@ -324,7 +324,11 @@ ssd_status ssd_causal_conv1d_step(void* conv_state, const void* x, const float* 
  * similar length (with a host copy of a packed batch's offsets, no sequence
  * over 1.5 times the mean chunk count), else the chunk-parallel path.  The
  * walk it takes is the scan walk where that path applies, else the state
- * walk.
+ * walk.  For a packed batch of at most 256 sequences with a host copy of
+ * its offsets, where the scan walk applies, the library instead estimates
+ * the scan walk (which runs the longest sequences first) against the
+ * chunk-parallel path and takes the walk when it expects it to be at least
+ * 10% faster.
  * Unlike ssd_chunked_scan it blocks the calling thread until the kernels
  * finish.  Same arguments and errors as ssd_chunked_scan, plus SSD_ERR_NULL
  * when stage_ms is NULL.

@@ -97,15 +97,17 @@ struct Prepared {
 
 // The scan walk's work split: each workgroup walks at most kWalkMaxUnits
 // (head, column tile) units of one group, the group's units cut into equal
-// slices.  One 8-wave workgroup fits per CU, so a launch runs in rounds of 32
-// workgroups per XCD, and a workgroup's chunk step costs about kWalkStepFixed
-// + n unit steps for n units (the output waves' per-chunk work is shared by
-// the units; measured 2.2 us + 4.15 us per unit at 2.1 GHz).  The split with
-// the least rounds x step cost wins, the one with more workgroups on a tie.
+// slices.  A workgroup's chunk step takes about kWalkStepFixedUs + n
+// kWalkStepUnitUs for n units: the output waves' per-chunk work and the
+// operand reload are shared by the units (measured at the 2.7B shape: 21.3
+// us per step for 5 units, 7.0 us for 1).
 constexpr int64_t kXcds = 8, kCusPerXcd = 32;
 constexpr int64_t kWalkMaxUnits = 6;
-constexpr double kWalkStepFixed = 0.53;
+constexpr double kWalkStepFixedUs = 3.4, kWalkStepUnitUs = 3.6;
 
+// Sequences of equal length: one 8-wave workgroup fits per CU, so a launch
+// runs in rounds of 32 workgroups per XCD; the split with the least rounds x
+// step time wins, the one with more workgroups on a tie.
 void walk_split(const ssd::Plan& pl, int32_t* nus, int32_t* nslice) {
     const int64_t npt = (pl.P + 31) / 32;
     const int64_t upg = (int64_t)pl.hpg * npt;
@@ -115,13 +117,66 @@ void walk_split(const ssd::Plan& pl, int32_t* nus, int32_t* nslice) {
         const int64_t ns = (upg + n - 1) / n, nu = (upg + ns - 1) / ns;
         const int64_t per_xcd = (walks * ns + kXcds - 1) / kXcds;
         const int64_t rounds = std::max<int64_t>(1, (per_xcd + kCusPerXcd - 1) / kCusPerXcd);
-        const double cost = (double)rounds * (kWalkStepFixed + (double)nu);
+        const double cost = (double)rounds * (kWalkStepFixedUs + kWalkStepUnitUs * (double)nu);
         if (n == 1 || cost < best) {
             best = cost;
             *nslice = (int32_t)ns;
             *nus = (int32_t)nu;
         }
     }
+}
+
+// A packed batch whose lengths the host holds, with at most kOrderMaxSeq
+// sequences: the walk starts its longest pairs first (the plan kernel orders
+// the sequences by chunk count), so it takes about the longer of its longest
+// walks and its total work spread over the CUs.  The split with the least
+// such time wins.  The chunk-parallel kernels take about kChunkParallelNs per
+// token, head and 8192 state elements (measured 0.26-0.27 ns on the grouped
+// packed batch, on one 32K-token sequence and at the 2.7B shape) plus
+// kChunkParallelFixedUs (their launches; 20-90 us measured on smaller
+// batches); the library's choice walks when that is expected to be at least
+// 10% faster.
+constexpr double kChunkParallelNs = 0.265;
+constexpr double kChunkParallelFixedUs = 40.0;
+constexpr double kWalkMargin = 0.9;
+
+struct PackedWalk {
+    int32_t nus = 0, nslice = 0;
+    double us = 0.0;
+};
+
+PackedWalk packed_walk(const ssd::Plan& pl, const int32_t* cu) {
+    const int64_t npt = (pl.P + 31) / 32;
+    const int64_t upg = (int64_t)pl.hpg * npt;
+    int64_t total = 0, longest = 0, nlong = 0;
+    for (int64_t s = 0; s < pl.nseq; ++s) {
+        const int64_t nc = ((int64_t)cu[s + 1] - cu[s] + pl.Q - 1) / pl.Q;
+        total += nc;
+        if (nc > longest) longest = nc, nlong = 0;
+        if (nc == longest) ++nlong;
+    }
+    PackedWalk best;
+    const int64_t cus = kXcds * kCusPerXcd;
+    for (int64_t n = 1; n <= std::min(kWalkMaxUnits, upg); ++n) {
+        const int64_t ns = (upg + n - 1) / n, nu = (upg + ns - 1) / ns;
+        const double step = kWalkStepFixedUs + kWalkStepUnitUs * (double)nu;
+        // the longest sequences' workgroups start together, in rounds when
+        // they outnumber the CUs
+        const int64_t rounds = (nlong * pl.G * ns + cus - 1) / cus;
+        const double crit = (double)(rounds * longest) * step;
+        const double spread = (double)total * (double)(pl.G * ns) * step / (double)cus;
+        const double us = std::max(crit, spread);
+        if (n == 1 || us < best.us) {
+            best.nus = (int32_t)nu;
+            best.nslice = (int32_t)ns;
+            best.us = us;
+        }
+    }
+    return best;
+}
+
+double chunk_parallel_us(const ssd::Plan& pl) {
+    return kChunkParallelNs * 1e-3 * (double)pl.T * pl.H * ((double)pl.P * pl.N / 8192.0) + kChunkParallelFixedUs;
 }
 
 // Heads of one group that a chunk_state / chunk_scan workgroup walks: the
@@ -256,6 +311,19 @@ ssd_status prepare(const ssd_shape* sh, int32_t chunk, Prepared* out) {
     else if (!fuse_state_passing(pl, sh)) out->path = ssd::kPathChunkParallel;
     else out->path = (walk_ok && kAutoScanWalk) ? ssd::kPathScanWalk : ssd::kPathStateWalk;
     walk_split(pl, &out->walk_nus, &out->walk_nslice);
+    // a packed batch with its lengths on the host: the walk's split, and for
+    // the library's choice whether to walk, from the longest-first estimate
+    if (walk_ok && packed && sh->cu_seqlens_host && nseq <= ssd::kOrderMaxSeq &&
+        (sh->path == SSD_PATH_AUTO || sh->path == SSD_PATH_SCAN_WALK)) {
+        const PackedWalk pw = packed_walk(pl, sh->cu_seqlens_host);
+        if (sh->path == SSD_PATH_SCAN_WALK || pw.us < kWalkMargin * chunk_parallel_us(pl)) {
+            out->path = ssd::kPathScanWalk;
+            out->walk_nus = pw.nus;
+            out->walk_nslice = pw.nslice;
+        } else {
+            out->path = ssd::kPathChunkParallel;
+        }
+    }
     const bool scan_walk = out->path == ssd::kPathScanWalk;
 
     ssd::Layout& L = out->lay;
@@ -268,6 +336,7 @@ ssd_status prepare(const ssd_shape* sh, int32_t chunk, Prepared* out) {
     };
     L.seq_tab = take(packed ? (size_t)nseq * 16 : 0);
     L.chunk_tab = take(packed ? (size_t)pl.nchunk_ub * 16 : 0);
+    L.seq_order = take(packed && scan_walk ? (size_t)nseq * 4 : 0);
     L.cs = take((size_t)pl.nchunk_ub * pl.H * chunk * 4);
     L.dtc = take((size_t)pl.nchunk_ub * pl.H * chunk * 4);
     L.wst = take(scan_walk ? 0 : (size_t)pl.nchunk_ub * pl.H * chunk * 4);
@@ -354,6 +423,7 @@ ssd_status scan_impl(const void* x, const float* dt, const float* A, const void*
     if (path_out) *path_out = a.path;
     pr.plan.seq_tab = (int32_t*)(a.ws + pr.lay.seq_tab);
     pr.plan.chunk_tab = (int32_t*)(a.ws + pr.lay.chunk_tab);
+    pr.plan.seq_order = !pr.plan.dense && a.path == ssd::kPathScanWalk ? (int32_t*)(a.ws + pr.lay.seq_order) : nullptr;
     if (pr.plan.nseq == 0 && !marks) return ok();
     const hipError_t err = ssd::launch_prefill(pr.plan, pr.lay, a, (hipStream_t)stream, marks);
     if (err != hipSuccess)

@@ -27,11 +27,18 @@ struct Plan {
     const int32_t* cu; // packed: device cu_seqlens [nseq+1]
     int32_t* seq_tab;  // packed: per sequence {chunk0, nchunks, first row, tokens}
     int32_t* chunk_tab;// packed: per chunk {seq, row0, len, index in sequence}
+    int32_t* seq_order;// packed scan walk: sequences by chunk count, longest first
+                       // (filled by the plan kernel; NULL: in index order)
 };
+
+// The plan kernel orders the sequences by chunk count when there are at most
+// this many (one workgroup ranks them); more keep their index order.
+constexpr int32_t kOrderMaxSeq = 256;
 
 // Byte offsets of the workspace regions (all 256-byte aligned).
 struct Layout {
     size_t seq_tab, chunk_tab;  // int32 x4 entries
+    size_t seq_order;           // int32 [nseq] (packed batches)
     size_t cs;      // f32 [nchunk_ub][H][Q]   inclusive sums of dt A within each chunk
     size_t dtc;     // f32 [nchunk_ub][H][Q]   dt per chunk and head, 0 past the chunk end
     size_t wst;     // f32 [nchunk_ub][H][Q]   exp(cs_last - cs) dt, each token's weight in the chunk state
@@ -98,9 +105,21 @@ struct WalkArgs {
     const float* init;
     float* final_state;
     void* y;
-    int32_t per_xcd, npt, nslice, nus;
+    int32_t per_xcd, run, npt, nslice, nus;  // per_xcd, run: walk_grid
     int32_t y_f32;
 };
+
+// Grid of a walk over `items` (pair, slice) items: runs of `run` consecutive
+// items share an XCD, the runs dealt to the 8 XCDs in turn; per_xcd
+// workgroups per XCD (some past the last item, which return at once).  Up to
+// 256 items this is one contiguous range per XCD.
+inline void walk_grid(int64_t items, int32_t* run, int32_t* per_xcd) {
+    int64_t r = (items + 7) / 8;
+    r = r < 1 ? 1 : (r > 32 ? 32 : r);
+    const int64_t nruns = (items + r - 1) / r;
+    *run = (int32_t)r;
+    *per_xcd = (int32_t)(r * ((nruns + 7) / 8));
+}
 
 // Whether the scan walk kernel covers this dtype, dstate and chunk.
 bool scan_walk_supported(int dtype, int N, int Q);

@@ -82,6 +82,23 @@ __global__ __launch_bounds__(kThreads) void ssd_plan_kernel(Plan pl) {
         for (int s = tid; s < pl.nseq; s += kThreads) ((int4*)pl.seq_tab)[s] = make_int4(0, 0, 0, 0);
         nchunks = 0;
     }
+    // the scan walk's sequence order: by chunk count, longest first (ties in
+    // index order), so that its longest walks start first
+    if (pl.seq_order) {
+        __syncthreads();  // seq_tab complete (or cleared)
+        if (pl.nseq <= kOrderMaxSeq) {
+            if (tid < pl.nseq) s_a[tid] = nchunks > 0 ? ((const int4*)pl.seq_tab)[tid].y : 0;
+            __syncthreads();
+            if (tid < pl.nseq) {
+                const int mine = s_a[tid];
+                int rank = 0;
+                for (int t = 0; t < pl.nseq; ++t) rank += (s_a[t] > mine || (s_a[t] == mine && t < tid)) ? 1 : 0;
+                pl.seq_order[rank] = tid;
+            }
+        } else {
+            for (int s = tid; s < pl.nseq; s += kThreads) pl.seq_order[s] = s;
+        }
+    }
     // chunk entries; the owning sequence is the last one whose first chunk is
     // <= the entry (empty sequences share it with a successor)
     for (int k = tid; k < pl.nchunk_ub; k += kThreads) {
@@ -1295,7 +1312,7 @@ hipError_t run_prefill(const Plan& pl, const Layout& lay, const ScanArgs& a, hip
         wa.nslice = a.walk_nslice;
         wa.nus = a.walk_nus;
         const int64_t nwalk = (int64_t)pl.nseq * pl.G * a.walk_nslice;
-        wa.per_xcd = (int)((nwalk + 7) / 8);
+        walk_grid(nwalk, &wa.run, &wa.per_xcd);
         wa.y_f32 = a.y_f32;
         if ((err = launch_scan_walk(pl, wa, stream)) != hipSuccess) return err;
         return mark(7);

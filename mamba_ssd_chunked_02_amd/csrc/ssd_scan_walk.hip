@@ -110,17 +110,22 @@ struct Walk {
     }
 };
 
-// Items are (sequence, group, slice) with the slice fastest: the XCD-ordered
-// grid gives each XCD a contiguous range, so the walks of one sequence run on
-// one XCD and share each chunk's C.B^T, C and B^T in its L2.  (Slice-major
-// order, which spreads every XCD over all sequences, measured 6% slower.)
-__device__ inline bool walk_of(const Plan& pl, int per_xcd, int npt, int nslice, int nus, Walk& w) {
-    const int64_t item = xcd_item(per_xcd);
+// Items are (pair, slice) with the slice fastest, a pair being (sequence,
+// group) and the sequences in the order pl.seq_order gives (longest first,
+// for a packed batch) or in index order.  Runs of `run` consecutive items
+// share an XCD, so the walks of one pair read each chunk's C.B^T, C and B^T
+// from one L2; the runs are dealt to the XCDs in turn, so the longest pairs
+// start first, spread over the chip.  (Slice-major order, which spreads every
+// XCD over all sequences, measured 6% slower.)
+__device__ inline bool walk_of(const Plan& pl, int run, int npt, int nslice, int nus, Walk& w) {
+    const int64_t l = blockIdx.x >> 3;
+    const int64_t item = ((int64_t)(blockIdx.x & 7) + 8 * (l / run)) * run + l % run;
     if (item >= (int64_t)pl.nseq * pl.G * nslice) return false;
     const int slice = (int)(item % nslice);
     const int64_t r = item / nslice;
     w.g = (int)(r % pl.G);
-    w.s = (int)(r / pl.G);
+    const int rank = (int)(r / pl.G);
+    w.s = pl.seq_order ? __builtin_amdgcn_readfirstlane(pl.seq_order[rank]) : rank;
     w.npt = npt;
     w.u0 = slice * nus;
     w.nu = min(nus, pl.hpg * npt - w.u0);
@@ -596,13 +601,13 @@ __device__ void walk_outputs(const Plan& pl, const Walk& w, const WalkBufs& bufs
 
 template <typename TY, int NU>
 __global__ __launch_bounds__(512, 1) void ssd_scan_walk_kernel(
-    Plan pl, int per_xcd, int npt, int nslice, int nus, const bf16_t* __restrict__ x, const float* __restrict__ cs,
+    Plan pl, int run, int npt, int nslice, int nus, const bf16_t* __restrict__ x, const float* __restrict__ cs,
     const float* __restrict__ dtc, const bf16_t* __restrict__ Cm, const bf16_t* __restrict__ cb,
     const bf16_t* __restrict__ bt, const float* __restrict__ D, const float* __restrict__ init,
     float* __restrict__ fin, TY* __restrict__ y) {
     extern __shared__ __align__(16) char smem[];
     Walk w;
-    if (!walk_of(pl, per_xcd, npt, nslice, nus, w)) return;
+    if (!walk_of(pl, run, npt, nslice, nus, w)) return;
     const WalkBufs bufs{smem};
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     switch (wave) {
@@ -619,7 +624,7 @@ hipError_t run_walk(const Plan& pl, const WalkArgs& a, hipStream_t stream) {
     auto* k = ssd_scan_walk_kernel<TY, NU>;
     hipError_t err = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kWalkLds);
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(k, dim3(8 * a.per_xcd), dim3(512), kWalkLds, stream, pl, a.per_xcd, a.npt, a.nslice, a.nus,
+    hipLaunchKernelGGL(k, dim3(8 * a.per_xcd), dim3(512), kWalkLds, stream, pl, a.run, a.npt, a.nslice, a.nus,
                        (const bf16_t*)a.x, a.cs, a.dtc, (const bf16_t*)a.C, (const bf16_t*)a.cb,
                        (const bf16_t*)a.bt, a.D, a.init, a.final_state, (TY*)a.y);
     return hipGetLastError();
