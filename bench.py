@@ -328,13 +328,17 @@ def conv1d_measure(torch, ssd, wl, wd, reps=20):
                     "decode step b%d; bf16 in/out, eager back-to-back" % (C, b, L, bd)}
 
 
-def environment(torch):
+def environment(torch, clocks=True):
     """What the numbers were measured on: device, HIP and torch versions, and
     the clock levels rocm-smi reports at bench start (the device is idle
-    then, so sclk reads its idle level; None when rocm-smi is absent)."""
+    then, so sclk reads its idle level; None when rocm-smi is absent or
+    clocks is False: under a profiler that preloads itself into every child,
+    rocm-smi's interpreter would start as a GPU process)."""
     import subprocess
     env = {"gpu": torch.cuda.get_device_name(0), "gcn_arch": torch.cuda.get_device_properties(0).gcnArchName,
            "hip": torch.version.hip, "torch": torch.__version__, "clocks": None}
+    if not clocks:
+        return env
     try:
         r = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True, timeout=20)
         lines = [l.strip() for l in r.stdout.splitlines() if "sclk" in l or "mclk" in l or "fclk" in l]
@@ -464,7 +468,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
                     help="leave out the reports beside the timed step (decode loop vs recompute, windowed\n"
-                         "decode, conv1d, fused dt activation); the timed step and its rooflines are unchanged")
+                         "decode, conv1d, fused dt activation) and the rocm-smi clock query; the timed step\n"
+                         "and its rooflines are unchanged")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic_scan_walk_2p7b.txt"),
                     help="rocprofv3 FETCH_SIZE/WRITE_SIZE summary of the dominant kernel")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -484,7 +489,7 @@ def main():
     from mamba_ssd_chunked_02_amd import workloads as W
 
     dev = torch.device("cuda:0")
-    env = environment(torch)
+    env = environment(torch, clocks=not args.no_extras)
     wl = W.CONFIGS[3]
     wd = W.CONFIGS[2]
     log("generating prefill inputs:", wl.name)

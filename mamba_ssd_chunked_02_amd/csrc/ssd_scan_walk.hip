@@ -14,6 +14,12 @@
 //             starting from H = h_c, with gam_j = exp(decay across block j) <= 1
 //             and wb_s = exp(cs_end(j) - cs_s) dt_s <= dt_s,
 // so h_{c+1} = exp(cs_last) h_c + sum_s exp(cs_last - cs_s) dt_s x_s (outer) B_s.
+// A chunk that decays by less than kWeakDecay over its whole length takes that
+// last form directly (weakly decaying chunks): the weights go to the chunk's
+// end, wc_s = exp(cs_last - cs_s) dt_s, the state is scaled once and the
+// advance is a plain sum, and y's intra-chunk term is one unscaled sum
+//   y_t = exp(cs_t - cs_last) (sum_{s<=t} (C_t . B_s) wc_s x_s + exp(cs_last) C_t h_c^T) + D x_t,
+// whose row factor stays below exp(kWeakDecay).
 //
 // Work item: one sequence, one group, and a slice of up to NU units, a unit
 // being (head of the group, 32-column tile of P).  The workgroup walks the
@@ -46,6 +52,7 @@ constexpr int kNT = 128;         // dstate rows, padded
 constexpr int kLP = kQ + 8;      // token pitch (elements) of the transposed x tiles
 constexpr int kNS = kNT + 8;     // n pitch (elements) of the state tiles
 constexpr float kFastDecay = 60.f;  // same bound as the chunk scan's Horner scheme
+constexpr float kWeakDecay = 60.f;  // whole-chunk decay below which the weights go to the chunk's end
 
 // One staging buffer: tables | (x wb)^T hi | (x wb)^T lo | x^T, the tiles
 // [32 columns p][kLP tokens] in bf16.
@@ -61,13 +68,16 @@ constexpr size_t kEpBytes = (size_t)32 * kEpPitch * 4;
 constexpr size_t kWalkLds = 2 * kStageBytes + 2 * kStateBytes + 4 * kEpBytes;
 static_assert(kWalkLds <= 160 * 1024, "scan walk LDS");
 
+// A weakly decaying chunk (flag bit 1 of every fast[] entry) stores
+// exp(cs_t - cs_last) in ue and exp(cs_last) in every gam entry; ul is not
+// read then, and all its blocks are fast.
 struct WalkTables {
     float* cs;   // [Q] cs_t
     float* dt;   // [Q] dt_t (0 past the chunk end)
     float* ul;   // [Q] exp(cs_t - cs before t's block)          (<= 1)
     float* ue;   // [Q] exp(min(cs_t - cs at t's block end, 60))   (>= 1)
     float* gam;  // [8] decay across each block                   (<= 1)
-    int* fast;   // [8] block decay below kFastDecay
+    int* fast;   // [8] bit 0: block decay below kFastDecay; bit 1: weakly decaying chunk
 };
 
 __device__ inline WalkTables walk_tables(char* base) {
@@ -163,6 +173,7 @@ struct StageRegs {
     bf16x8 raw[4];
     f32x4 cs4, dt4;
     float ce, c0;  // cs at the end of the tokens' block, cs before its start
+    float cl;      // cs at the chunk's last token (positions past the end hold it too)
 };
 
 __device__ inline int stage_pb(int tau) { return (tau >> 4) & 3; }
@@ -188,6 +199,7 @@ __device__ inline void stage_load(StageRegs& r, const Plan& pl, const Walk& w, i
     r.dt4 = *(const f32x4*)(dtk + k0);
     r.ce = csk[k0 | 31];
     r.c0 = csk[max((k0 & ~31) - 1, 0)];
+    r.cl = csk[kQ - 1];
 }
 
 __device__ inline void stage_store(const StageRegs& r, const Plan& pl, const Walk& w, const WalkBufs& bufs, int c,
@@ -196,11 +208,14 @@ __device__ inline void stage_store(const StageRegs& r, const Plan& pl, const Wal
     const int pb = stage_pb(tau), k0 = stage_k0(tau);
     const bool pok = 32 * w.tile(j) + 8 * pb < pl.P;
     const float c0 = k0 >= 32 ? r.c0 : 0.f;
+    // every thread reads the same cs_last, so all take the same form
+    const bool weak = -r.cl < kWeakDecay;
+    const float ref = weak ? r.cl : r.ce;
     float wb[4];
     bf16x8 xm[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        wb[i] = pok ? __expf(r.ce - r.cs4[i]) * r.dt4[i] : 0.f;  // dt is 0 past the chunk end
+        wb[i] = pok ? __expf(ref - r.cs4[i]) * r.dt4[i] : 0.f;  // dt is 0 past the chunk end
         xm[i] = (pok && k0 + i < d.len) ? r.raw[i] : bf16x8{};
     }
     bf16_t* xh = bufs.xh(b) + (8 * pb) * kLP + k0;
@@ -224,13 +239,13 @@ __device__ inline void stage_store(const StageRegs& r, const Plan& pl, const Wal
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             ul[i] = __expf(r.cs4[i] - c0);
-            ue[i] = __expf(fminf(r.cs4[i] - r.ce, kFastDecay));
+            ue[i] = weak ? __expf(r.cs4[i] - r.cl) : __expf(fminf(r.cs4[i] - r.ce, kFastDecay));
         }
         *(f32x4*)(tb.ul + k0) = ul;
         *(f32x4*)(tb.ue + k0) = ue;
         if ((k0 & 31) == 0) {
-            tb.gam[k0 >> 5] = __expf(r.ce - c0);
-            tb.fast[k0 >> 5] = (c0 - r.ce) < kFastDecay ? 1 : 0;
+            tb.gam[k0 >> 5] = weak ? __expf(r.cl) : __expf(r.ce - c0);
+            tb.fast[k0 >> 5] = weak ? 3 : (c0 - r.ce) < kFastDecay ? 1 : 0;
         }
     }
 }
@@ -268,8 +283,11 @@ __device__ inline int state_off(int v, int pt, int nt, int P, int N) {
 // B^T fragments (n-tile rows), B = the staged (x wb)^T hi and lo tiles.  The
 // operands of block j + 1 are read from LDS while block j's MFMAs run (the
 // scheduling barriers keep the reads ahead); the other wave on the SIMD fills
-// the matrix core while this one scales H.
-__device__ inline void walk_advance(f32x16& acc, const bf16x8 (&bf)[kQ / 16], const WalkBufs& bufs, int b) {
+// the matrix core while this one scales H.  A weakly decaying chunk's staged
+// weights already reach the chunk's end: H is scaled once, by exp(cs_last),
+// and the blocks are a plain sum.
+__device__ inline void walk_advance(f32x16& acc, const bf16x8 (&bf)[kQ / 16], const WalkBufs& bufs, int b,
+                                    bool weak) {
     const int lane = threadIdx.x & 63, half = lane >> 5, col = lane & 31;
     const WalkTables tb = walk_tables(bufs.stage(b));
     const bf16_t* hrow = bufs.xh(b) + col * kLP + 8 * half;
@@ -286,11 +304,12 @@ __device__ inline void walk_advance(f32x16& acc, const bf16x8 (&bf)[kQ / 16], co
         }
     };
     ld(0, op[0]);
+    if (weak) acc *= gm[0];
 #pragma unroll
     for (int jb = 0; jb < kNTI; ++jb) {
         if (jb + 1 < kNTI) ld(jb + 1, op[(jb + 1) & 1]);
         __builtin_amdgcn_sched_barrier(0);
-        acc *= gm[jb];
+        if (!weak) acc *= gm[jb];
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
             mma16(acc, bf[2 * jb + ks], op[jb & 1][2 * ks]);
@@ -366,7 +385,8 @@ __device__ void walk_states(const Plan& pl, const Walk& w, const WalkBufs& bufs,
                     if (j + 1 < nu) put_state(acc[(j + 1) % NU], bufs, b ^ 1, nt);
                     stage_store(sr, pl, w, bufs, cn, jn, b ^ 1, tau);
                 }
-                walk_advance(acc[j], bf, bufs, b);
+                walk_advance(acc[j], bf, bufs, b,
+                             (__builtin_amdgcn_readfirstlane(walk_tables(bufs.stage(b)).fast[0]) & 2) != 0);
                 if (more && j + 1 == nu) put_state(acc[0], bufs, b ^ 1, nt);
                 // sn's loads, issued at the step's start, are waited for here
                 // on every path.  Otherwise the copy into sr, placed after
@@ -424,23 +444,11 @@ __device__ __forceinline__ void walk_block(const bf16x8 (&ga)[TI + 1][2], const 
             mma16(sacc, ca[s], Tr<bf16_t>::ld8(slrow + 16 * s));
         }
     }
-    const bool fast = tb.fast[TI] != 0;
-    // blocks kj < TI: two chains (even and odd blocks), each stepping two
-    // blocks at a time with the product of their decays
+    const int flags = __builtin_amdgcn_readfirstlane(tb.fast[TI]);
+    // Every branch below leaves the sum in the chain of TI's parity (acc):
+    // where the branches meet only acc is live, in the same registers on all
+    // paths.
     f32x16 ce = {}, co = {};
-#pragma unroll
-    for (int kj = 0; kj < TI; ++kj) {
-        f32x16& ch = (kj & 1) ? co : ce;
-        if (kj >= 2) ch *= tb.gam[kj - 1] * tb.gam[kj];
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) mma16(ch, ga[kj][ks], Tr<bf16_t>::ld8(xhrow + 32 * kj + 16 * ks));
-    }
-    // the chain that ends at the last included block K is complete; the other
-    // one still takes the decay across block K.  K is TI (diagonal block in
-    // the scheme) or TI - 1, so each branch knows both chains' roles.  Each
-    // branch also adds the state term and applies its row scaling, and both
-    // leave the sum in the chain of TI's parity (acc): where the branches
-    // meet only acc is live, in the same registers on both paths.
     f32x16& acc = (TI & 1) ? co : ce;
     f32x16& other = (TI & 1) ? ce : co;
     auto scale_rows = [&](const float* scale) {
@@ -451,30 +459,56 @@ __device__ __forceinline__ void walk_block(const bf16x8 (&ga)[TI + 1][2], const 
             for (int i = 0; i < 4; ++i) acc[4 * vg + i] *= u[i];
         }
     };
-    if (fast) {
-        // acc ends at TI - 2: across blocks TI - 1 and TI, then block TI
-        if (TI >= 2) acc *= tb.gam[TI - 1] * tb.gam[TI];
+    if (flags & 2) {
+        // weakly decaying chunk: weights to the chunk's end, one unscaled
+        // chain over the blocks kj <= TI (the C.B^T tiles are causal), the
+        // state term scaled by exp(cs_last), rows by exp(cs_t - cs_last)
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) mma16(acc, ga[TI][ks], Tr<bf16_t>::ld8(xhrow + 32 * TI + 16 * ks));
-        if (TI >= 1) acc += tb.gam[TI] * other;
-        if (has_state) acc += __expf(tb.cs[32 * TI + 31]) * sacc;
+        for (int kj = 0; kj <= TI; ++kj)
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) mma16(acc, ga[kj][ks], Tr<bf16_t>::ld8(xhrow + 32 * kj + 16 * ks));
+        if (has_state) acc += tb.gam[0] * sacc;
         scale_rows(tb.ue);
     } else {
-        // K = TI - 1 ends other; acc (ends at TI - 2, or zero) takes block
-        // K's decay.  TI = 1: other is block 0's chain, acc zero.
-        if (TI >= 1) acc = other + tb.gam[TI - 1] * acc;
-        if (has_state) acc += (TI > 0 ? __expf(tb.cs[32 * TI - 1]) : 1.f) * sacc;
-        scale_rows(tb.ul);
-        // the diagonal block with exact per-element factors
-        const float cst = tb.cs[32 * TI + col];
+        const bool fast = flags & 1;
+        // blocks kj < TI: two chains (even and odd blocks), each stepping two
+        // blocks at a time with the product of their decays
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            const int k0 = 32 * TI + 16 * ks + 8 * half;
-            const f32x8 gv = Tr<bf16_t>::widen(ga[TI][ks]);
-            f32x8 m;
+        for (int kj = 0; kj < TI; ++kj) {
+            f32x16& ch = (kj & 1) ? co : ce;
+            if (kj >= 2) ch *= tb.gam[kj - 1] * tb.gam[kj];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) m[i] = gv[i] * (__expf(fminf(cst - tb.cs[k0 + i], 0.f)) * tb.dt[k0 + i]);
-            mma16(acc, Tr<bf16_t>::narrow(m), Tr<bf16_t>::ld8(xrrow + k0));
+            for (int ks = 0; ks < 2; ++ks) mma16(ch, ga[kj][ks], Tr<bf16_t>::ld8(xhrow + 32 * kj + 16 * ks));
+        }
+        // the chain that ends at the last included block K is complete; the other
+        // one still takes the decay across block K.  K is TI (diagonal block in
+        // the scheme) or TI - 1, so each branch knows both chains' roles.  Each
+        // branch also adds the state term and applies its row scaling.
+        if (fast) {
+            // acc ends at TI - 2: across blocks TI - 1 and TI, then block TI
+            if (TI >= 2) acc *= tb.gam[TI - 1] * tb.gam[TI];
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) mma16(acc, ga[TI][ks], Tr<bf16_t>::ld8(xhrow + 32 * TI + 16 * ks));
+            if (TI >= 1) acc += tb.gam[TI] * other;
+            if (has_state) acc += __expf(tb.cs[32 * TI + 31]) * sacc;
+            scale_rows(tb.ue);
+        } else {
+            // K = TI - 1 ends other; acc (ends at TI - 2, or zero) takes block
+            // K's decay.  TI = 1: other is block 0's chain, acc zero.
+            if (TI >= 1) acc = other + tb.gam[TI - 1] * acc;
+            if (has_state) acc += (TI > 0 ? __expf(tb.cs[32 * TI - 1]) : 1.f) * sacc;
+            scale_rows(tb.ul);
+            // the diagonal block with exact per-element factors
+            const float cst = tb.cs[32 * TI + col];
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                const int k0 = 32 * TI + 16 * ks + 8 * half;
+                const f32x8 gv = Tr<bf16_t>::widen(ga[TI][ks]);
+                f32x8 m;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) m[i] = gv[i] * (__expf(fminf(cst - tb.cs[k0 + i], 0.f)) * tb.dt[k0 + i]);
+                mma16(acc, Tr<bf16_t>::narrow(m), Tr<bf16_t>::ld8(xrrow + k0));
+            }
         }
     }
 #pragma unroll

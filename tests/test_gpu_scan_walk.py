@@ -14,7 +14,9 @@ cases span:
   * dstate 72, 96 and 128; one group or several;
   * zero and nonzero initial states, a final state aliasing the initial one;
   * fp32 and bf16 y;
-  * slow decay, strong decay past the fast-path bound, and the flush limit.
+  * slow decay, strong decay past the fast-path bound, and the flush limit;
+  * chunks on both sides of the whole-chunk decay bound of the single
+    reference form.
 """
 import sys
 
@@ -97,6 +99,32 @@ def test_scan_walk_decay_regimes(variant):
               strong=dict(A_range=(-1e3, -60.0)), mixed=dict(A_values=(-10.0, -300.0)),
               flush=dict(A_range=(-1e6, -1e6)))[variant]
     check(W.generate(wl, 21, **kw), what=variant)
+
+
+def test_scan_walk_chunks_on_both_sides_of_the_single_reference_bound():
+    """A chunk whose whole decay stays below 60 takes its weights to the
+    chunk's end (one scaling of the state, unscaled sums); others take the
+    per-block Horner scheme.  Here each (sequence, chunk, head) gets its own
+    total decay, drawn from U(35, 85), so the two forms alternate along one
+    head's walk and between the heads of one step, over full and ragged
+    chunks (1000 tokens: three full chunks and one of 232)."""
+    wl = W.small_workload(batch=4, seqlen=1000, H=16, P=64, N=128, G=2, chunk=256, dtype="bf16",
+                          init_var=0.1)
+    inp = W.generate(wl, 91)
+    rng = np.random.default_rng(92)
+    b, L, H = inp.dt.shape
+    dt = np.empty_like(inp.dt)
+    decay = []
+    for c0 in range(0, L, 256):
+        c1 = min(c0 + 256, L)
+        r = rng.uniform(0.5, 1.5, size=(b, c1 - c0, H))
+        total = rng.uniform(35.0, 85.0, size=(b, 1, H))
+        dt[:, c0:c1] = (r / r.sum(axis=1, keepdims=True) * total / -inp.A[None, None, :]).astype(np.float32)
+        decay.append(-(dt[:, c0:c1].astype(np.float64) * inp.A).sum(axis=1))
+    decay = np.concatenate(decay)
+    assert (decay < 58).sum() > 50 and (decay > 62).sum() > 50, "both forms must occur"
+    inp.dt = dt
+    check(inp, what="decay U(35, 85) per chunk")
 
 
 def test_scan_walk_bf16_y_is_rounded_fp32_y():
