@@ -637,6 +637,7 @@ def main():
     roof = dict(roofs[dominant])
     if args.traffic:
         roof["traffic"] = _traffic(args.traffic, names[dominant], roof["algorithmic_bytes"])
+        roofs[dominant]["traffic"] = roof["traffic"]
     # the contraction kernels: chunk_state and chunk_scan, or the scan walk
     # that does both (state_passing has no contraction)
     mk = [k for k in work if k != "state_passing"]
