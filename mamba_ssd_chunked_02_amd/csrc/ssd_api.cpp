@@ -99,11 +99,14 @@ struct Prepared {
 // (head, column tile) units of one group, the group's units cut into equal
 // slices.  A workgroup's chunk step takes about kWalkStepFixedUs + n
 // kWalkStepUnitUs for n units: the output waves' per-chunk work and the
-// operand reload are shared by the units (measured at the 2.7B shape: 21.3
-// us per step for 5 units, 7.0 us for 1).
+// operand reload are shared by the units.  Measured on the 2.7B-shaped layer
+// (L8192 H80), one round of workgroups each: at batch 4, 6, 8 and 9 (216 to
+// 256 busy CUs, 3 to 6 units) 14.2, 18.3, 22.5 and 26.0 us per chunk step,
+// whose least-squares line is 2.34 + 3.98 n; at batch 2 (160 CUs, 2 units)
+// 9.35 us, below the line, as fewer CUs share L2 and HBM.
 constexpr int64_t kXcds = 8, kCusPerXcd = 32;
 constexpr int64_t kWalkMaxUnits = 6;
-constexpr double kWalkStepFixedUs = 3.4, kWalkStepUnitUs = 3.6;
+constexpr double kWalkStepFixedUs = 2.34, kWalkStepUnitUs = 3.98;
 
 // Sequences of equal length: one 8-wave workgroup fits per CU, so a launch
 // runs in rounds of 32 workgroups per XCD; the split with the least rounds x
