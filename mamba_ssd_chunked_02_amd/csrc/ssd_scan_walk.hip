@@ -25,7 +25,7 @@
 // being (head of the group, 32-column tile of P).  The workgroup walks the
 // sequence's chunks in order and, inside a chunk, its units in order: one
 // step per (chunk, unit).  Eight waves with two roles:
-//   waves 0-3  output blocks (w, 7-w) of y: they hold the chunk's C.B^T rows
+//   waves 0-3  output blocks w and 7-w of y: they hold the chunk's C.B^T rows
 //              and C rows of their two blocks in registers for every unit of
 //              the chunk, and read the unit's staged x and state from LDS;
 //   waves 4-7  n-tile w-4 of every unit's state, kept in MFMA accumulators
@@ -644,11 +644,20 @@ __global__ __launch_bounds__(512, 1) void ssd_scan_walk_kernel(
     if (!walk_of(pl, run, npt, nslice, nus, w)) return;
     const WalkBufs bufs{smem};
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    // Output wave w takes blocks w and 7 - w.  With several units per
+    // workgroup the larger block goes first: at a chunk switch its reload
+    // then leaves first and has the most time to arrive, while the smaller
+    // block's reload is needed only after the larger block's work in the next
+    // step.  With one unit every step switches chunks, and the smaller block
+    // goes first, so that the larger block's reload has the smaller block's
+    // work, not its own, to hide behind.
+    constexpr bool kLargeFirst = NU > 1;
+    const bool has_init = init != nullptr;
     switch (wave) {
-        case 0: walk_outputs<TY, 0, 7>(pl, w, bufs, Cm, cb, D, init != nullptr, y); break;
-        case 1: walk_outputs<TY, 1, 6>(pl, w, bufs, Cm, cb, D, init != nullptr, y); break;
-        case 2: walk_outputs<TY, 2, 5>(pl, w, bufs, Cm, cb, D, init != nullptr, y); break;
-        case 3: walk_outputs<TY, 3, 4>(pl, w, bufs, Cm, cb, D, init != nullptr, y); break;
+        case 0: walk_outputs<TY, kLargeFirst ? 7 : 0, kLargeFirst ? 0 : 7>(pl, w, bufs, Cm, cb, D, has_init, y); break;
+        case 1: walk_outputs<TY, kLargeFirst ? 6 : 1, kLargeFirst ? 1 : 6>(pl, w, bufs, Cm, cb, D, has_init, y); break;
+        case 2: walk_outputs<TY, kLargeFirst ? 5 : 2, kLargeFirst ? 2 : 5>(pl, w, bufs, Cm, cb, D, has_init, y); break;
+        case 3: walk_outputs<TY, kLargeFirst ? 4 : 3, kLargeFirst ? 3 : 4>(pl, w, bufs, Cm, cb, D, has_init, y); break;
         default: walk_states<NU>(pl, w, bufs, x, cs, dtc, bt, init, fin); break;
     }
 }
