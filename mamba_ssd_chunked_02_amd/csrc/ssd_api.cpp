@@ -346,6 +346,7 @@ ssd_status prepare(const ssd_shape* sh, int32_t chunk, Prepared* out) {
     L.cb = take((size_t)pl.nchunk_ub * pl.G * chunk * chunk * es);
     L.bt = take((size_t)pl.nchunk_ub * pl.G * ssd::padded_dstate(pl.N) * chunk * es);
     L.states = take(scan_walk ? 0 : (size_t)pl.nchunk_ub * pl.H * pl.P * pl.N * 4);
+    L.tail = take(scan_walk ? (size_t)pl.nchunk_ub * pl.H * 8 : 0);
     L.total = std::max<size_t>(off, 256);
     return SSD_OK;
 }

@@ -47,6 +47,8 @@ struct Layout {
     size_t bt;      // elem [nchunk_ub][G][NT * Q] B transposed per chunk in MFMA fragment order, 0 past the end and N
     size_t states;  // f32 [nchunk_ub][H][P][N] chunk states, then the states entering each chunk
                     //                         (not used by the scan walk: empty there)
+    size_t tail;    // f32 [nchunk_ub][H][2]   scan walk only: cs_last of each chunk and the decay
+                    //                         from its end to its sequence's end
     size_t total;
 };
 
@@ -98,6 +100,7 @@ struct WalkArgs {
     const void* x;
     const float* cs;
     const float* dtc;
+    float* tail;  // [nchunk_ub][H][2], written by launch_walk_tails
     const void* C;
     const void* cb;
     const void* bt;
@@ -127,7 +130,8 @@ bool scan_walk_supported(int dtype, int N, int Q);
 // LDS bytes per workgroup of the scan walk.
 size_t scan_walk_lds_bytes();
 
-// Queue the scan walk (after the cumsum and C.B^T kernels).
+// Queue the scan walk (after the cumsum and C.B^T kernels): first the
+// per-(chunk, head) table a.tail from a.cs, then the walk.
 hipError_t launch_scan_walk(const Plan& plan, const WalkArgs& a, hipStream_t stream);
 
 struct DecodeArgs {

@@ -1301,6 +1301,7 @@ hipError_t run_prefill(const Plan& pl, const Layout& lay, const ScanArgs& a, hip
         wa.x = a.x;
         wa.cs = cs;
         wa.dtc = dtc;
+        wa.tail = (float*)(ws + lay.tail);
         wa.C = a.C;
         wa.cb = cbm;
         wa.bt = bt;

@@ -20,6 +20,12 @@
 // advance is a plain sum, and y's intra-chunk term is one unscaled sum
 //   y_t = exp(cs_t - cs_last) (sum_{s<=t} (C_t . B_s) wc_s x_s + exp(cs_last) C_t h_c^T) + D x_t,
 // whose row factor stays below exp(kWeakDecay).
+// The state advance contracts x wb as a hi/lo bf16 pair, so that the state
+// keeps the accuracy the final state needs.  A chunk whose sequence decays by
+// kLoSkipDecay or more after it contributes to the final state only through
+// that decay (below exp(-kLoSkipDecay)); its advance takes the hi half alone,
+// the single rounding that y's intra-chunk term uses too.  A small kernel
+// before the walk gives each (chunk, head) the decay still to come.
 //
 // Work item: one sequence, one group, and a slice of up to NU units, a unit
 // being (head of the group, 32-column tile of P).  The workgroup walks the
@@ -46,6 +52,8 @@ namespace ssd {
 
 namespace {
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
 constexpr int kQ = 256;          // chunk length
 constexpr int kNTI = kQ / 32;    // 32-token blocks per chunk
 constexpr int kNT = 128;         // dstate rows, padded
@@ -53,6 +61,7 @@ constexpr int kLP = kQ + 8;      // token pitch (elements) of the transposed x t
 constexpr int kNS = kNT + 8;     // n pitch (elements) of the state tiles
 constexpr float kFastDecay = 60.f;  // same bound as the chunk scan's Horner scheme
 constexpr float kWeakDecay = 60.f;  // whole-chunk decay below which the weights go to the chunk's end
+constexpr float kLoSkipDecay = 8.f;  // decay after a chunk from which its advance drops the lo half
 
 // One staging buffer: tables | (x wb)^T hi | (x wb)^T lo | x^T, the tiles
 // [32 columns p][kLP tokens] in bf16.
@@ -70,14 +79,17 @@ static_assert(kWalkLds <= 160 * 1024, "scan walk LDS");
 
 // A weakly decaying chunk (flag bit 1 of every fast[] entry) stores
 // exp(cs_t - cs_last) in ue and exp(cs_last) in every gam entry; ul is not
-// read then, and all its blocks are fast.
+// read then, and all its blocks are fast.  Flag bit 2 (every entry): the
+// chunk's advance takes the hi half of x wb alone, and the lo tile is not
+// written.
 struct WalkTables {
     float* cs;   // [Q] cs_t
     float* dt;   // [Q] dt_t (0 past the chunk end)
     float* ul;   // [Q] exp(cs_t - cs before t's block)          (<= 1)
     float* ue;   // [Q] exp(min(cs_t - cs at t's block end, 60))   (>= 1)
     float* gam;  // [8] decay across each block                   (<= 1)
-    int* fast;   // [8] bit 0: block decay below kFastDecay; bit 1: weakly decaying chunk
+    int* fast;   // [8] bit 0: block decay below kFastDecay; bit 1: weakly decaying chunk;
+                 //     bit 2: hi half alone in the advance
 };
 
 __device__ inline WalkTables walk_tables(char* base) {
@@ -174,13 +186,14 @@ struct StageRegs {
     f32x4 cs4, dt4;
     float ce, c0;  // cs at the end of the tokens' block, cs before its start
     float cl;      // cs at the chunk's last token (positions past the end hold it too)
+    float after;   // decay from the chunk's end to its sequence's end
 };
 
 __device__ inline int stage_pb(int tau) { return (tau >> 4) & 3; }
 __device__ inline int stage_k0(int tau) { return 4 * ((tau & 15) + 16 * (tau >> 6)); }
 
 __device__ inline void stage_load(StageRegs& r, const Plan& pl, const Walk& w, int c, int j, const bf16_t* x,
-                                  const float* cs, const float* dtc, int tau) {
+                                  const float* cs, const float* dtc, const float* tail, int tau) {
     const ChunkDesc d = w.chunk(c);
     const int k = w.chunk0 + c, h = w.head(pl, j), pt = w.tile(j);
     const int H = pl.H, P = pl.P;
@@ -199,7 +212,9 @@ __device__ inline void stage_load(StageRegs& r, const Plan& pl, const Walk& w, i
     r.dt4 = *(const f32x4*)(dtk + k0);
     r.ce = csk[k0 | 31];
     r.c0 = csk[max((k0 & ~31) - 1, 0)];
-    r.cl = csk[kQ - 1];
+    const f32x2 t = *(const f32x2*)(tail + 2 * ((size_t)k * H + h));
+    r.cl = t[0];
+    r.after = t[1];
 }
 
 __device__ inline void stage_store(const StageRegs& r, const Plan& pl, const Walk& w, const WalkBufs& bufs, int c,
@@ -210,6 +225,7 @@ __device__ inline void stage_store(const StageRegs& r, const Plan& pl, const Wal
     const float c0 = k0 >= 32 ? r.c0 : 0.f;
     // every thread reads the same cs_last, so all take the same form
     const bool weak = -r.cl < kWeakDecay;
+    const bool hi_only = r.after >= kLoSkipDecay;  // false for a NaN
     const float ref = weak ? r.cl : r.ce;
     float wb[4];
     bf16x8 xm[4];
@@ -225,10 +241,14 @@ __device__ inline void stage_store(const StageRegs& r, const Plan& pl, const Wal
     for (int col = 0; col < 8; ++col) {
         const f32x4 o = {(float)xm[0][col] * wb[0], (float)xm[1][col] * wb[1], (float)xm[2][col] * wb[2],
                          (float)xm[3][col] * wb[3]};
-        u32x2 hi, lo;
-        split_hilo(o, hi, lo);
-        *(u32x2*)(xh + col * kLP) = hi;
-        *(u32x2*)(xl + col * kLP) = lo;
+        if (hi_only) {
+            *(u32x2*)(xh + col * kLP) = __builtin_bit_cast(u32x2, Tr<bf16_t>::narrow4(o));
+        } else {
+            u32x2 hi, lo;
+            split_hilo(o, hi, lo);
+            *(u32x2*)(xh + col * kLP) = hi;
+            *(u32x2*)(xl + col * kLP) = lo;
+        }
         Tr<bf16_t>::st4raw(xr + col * kLP, bf16x4{xm[0][col], xm[1][col], xm[2][col], xm[3][col]});
     }
     if (pb == 0) {
@@ -245,7 +265,7 @@ __device__ inline void stage_store(const StageRegs& r, const Plan& pl, const Wal
         *(f32x4*)(tb.ue + k0) = ue;
         if ((k0 & 31) == 0) {
             tb.gam[k0 >> 5] = weak ? __expf(r.cl) : __expf(r.ce - c0);
-            tb.fast[k0 >> 5] = weak ? 3 : (c0 - r.ce) < kFastDecay ? 1 : 0;
+            tb.fast[k0 >> 5] = (weak ? 3 : (c0 - r.ce) < kFastDecay ? 1 : 0) | (hi_only ? 4 : 0);
         }
     }
 }
@@ -286,8 +306,15 @@ __device__ inline int state_off(int v, int pt, int nt, int P, int N) {
 // the matrix core while this one scales H.  A weakly decaying chunk's staged
 // weights already reach the chunk's end: H is scaled once, by exp(cs_last),
 // and the blocks are a plain sum.
+// LO: whether the lo half is contracted too; RUNTIME: take that from lo_rt
+// instead, one loop with the choice inside.  The six-unit instance takes that
+// form because its registers do not hold two copies of the loop, and the
+// one-unit instance because it measured faster (every one of its steps
+// switches chunks).
+template <bool LO, bool RUNTIME>
 __device__ inline void walk_advance(f32x16& acc, const bf16x8 (&bf)[kQ / 16], const WalkBufs& bufs, int b,
-                                    bool weak) {
+                                    bool weak, bool lo_rt) {
+    const bool lo_too = RUNTIME ? lo_rt : LO;
     const int lane = threadIdx.x & 63, half = lane >> 5, col = lane & 31;
     const WalkTables tb = walk_tables(bufs.stage(b));
     const bf16_t* hrow = bufs.xh(b) + col * kLP + 8 * half;
@@ -300,7 +327,7 @@ __device__ inline void walk_advance(f32x16& acc, const bf16x8 (&bf)[kQ / 16], co
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
             o[2 * ks] = Tr<bf16_t>::ld8(hrow + 16 * (2 * jb + ks));
-            o[2 * ks + 1] = Tr<bf16_t>::ld8(lrow + 16 * (2 * jb + ks));
+            if (lo_too) o[2 * ks + 1] = Tr<bf16_t>::ld8(lrow + 16 * (2 * jb + ks));
         }
     };
     ld(0, op[0]);
@@ -313,7 +340,7 @@ __device__ inline void walk_advance(f32x16& acc, const bf16x8 (&bf)[kQ / 16], co
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
             mma16(acc, bf[2 * jb + ks], op[jb & 1][2 * ks]);
-            mma16(acc, bf[2 * jb + ks], op[jb & 1][2 * ks + 1]);
+            if (lo_too) mma16(acc, bf[2 * jb + ks], op[jb & 1][2 * ks + 1]);
         }
         __builtin_amdgcn_sched_barrier(0);
     }
@@ -322,7 +349,8 @@ __device__ inline void walk_advance(f32x16& acc, const bf16x8 (&bf)[kQ / 16], co
 template <int NU>
 __device__ void walk_states(const Plan& pl, const Walk& w, const WalkBufs& bufs, const bf16_t* __restrict__ x,
                             const float* __restrict__ cs, const float* __restrict__ dtc,
-                            const bf16_t* __restrict__ bt, const float* __restrict__ init, float* __restrict__ fin) {
+                            const float* __restrict__ tail, const bf16_t* __restrict__ bt,
+                            const float* __restrict__ init, float* __restrict__ fin) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int nt = __builtin_amdgcn_readfirstlane((tid >> 6) - 4);
     const int tau = tid - 256;
@@ -357,7 +385,7 @@ __device__ void walk_states(const Plan& pl, const Walk& w, const WalkBufs& bufs,
     StageRegs sr, sn;
     auto load_step = [&](StageRegs& r, int i) {  // i < total
         const int c = i / nu;
-        stage_load(r, pl, w, c, i - c * nu, x, cs, dtc, tau);
+        stage_load(r, pl, w, c, i - c * nu, x, cs, dtc, tail, tau);
     };
     if (total > 0) {
         load_bt(0);
@@ -385,8 +413,15 @@ __device__ void walk_states(const Plan& pl, const Walk& w, const WalkBufs& bufs,
                     if (j + 1 < nu) put_state(acc[(j + 1) % NU], bufs, b ^ 1, nt);
                     stage_store(sr, pl, w, bufs, cn, jn, b ^ 1, tau);
                 }
-                walk_advance(acc[j], bf, bufs, b,
-                             (__builtin_amdgcn_readfirstlane(walk_tables(bufs.stage(b)).fast[0]) & 2) != 0);
+                const int flags = __builtin_amdgcn_readfirstlane(walk_tables(bufs.stage(b)).fast[0]);
+                const bool weak = (flags & 2) != 0, lo = (flags & 4) == 0;
+                if constexpr (NU >= 6 || NU == 1) {
+                    walk_advance<true, true>(acc[j], bf, bufs, b, weak, lo);
+                } else if (lo) {
+                    walk_advance<true, false>(acc[j], bf, bufs, b, weak, true);
+                } else {
+                    walk_advance<false, false>(acc[j], bf, bufs, b, weak, false);
+                }
                 if (more && j + 1 == nu) put_state(acc[0], bufs, b ^ 1, nt);
                 // sn's loads, issued at the step's start, are waited for here
                 // on every path.  Otherwise the copy into sr, placed after
@@ -633,10 +668,38 @@ __device__ void walk_outputs(const Plan& pl, const Walk& w, const WalkBufs& bufs
     }
 }
 
+// Per (sequence, head), one wave: for each chunk, its cs_last and the decay
+// from its end to the sequence's end (the sum of -cs_last over the later
+// chunks), in windows of 64 chunks from the sequence's end, lane c of a
+// window holding chunk base + c.  cs_last is copied bit for bit; the decay
+// only decides whether the advance takes the lo half.
+__global__ __launch_bounds__(256) void ssd_walk_tail_kernel(Plan pl, const float* __restrict__ cs,
+                                                            float* __restrict__ tail) {
+    const int lane = threadIdx.x & 63;
+    const int64_t pair = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (pair >= (int64_t)pl.nseq * pl.H) return;
+    const int H = pl.H;
+    const int s = (int)(pair / H), h = (int)(pair % H);
+    const SeqExtent se = seq_extent(pl, s);
+    float later = 0.f;  // decay of the chunks after the current window
+    for (int end = se.nchunks; end > 0; end -= 64) {
+        const int c = end - 64 + lane;
+        const bool ok = c >= 0;
+        const size_t k = (size_t)se.chunk0 + (ok ? c : 0);
+        const float cl = ok ? cs[(k * H + h) * kQ + kQ - 1] : 0.f;
+        const float v = -cl;
+        const float incl = wave_inclusive_scan(v);  // the window's chunks up to c
+        const float total = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, incl), 63));
+        if (ok) *(f32x2*)(tail + 2 * (k * H + h)) = f32x2{cl, later + (total - incl)};
+        later += total;
+    }
+}
+
 template <typename TY, int NU>
 __global__ __launch_bounds__(512, 1) void ssd_scan_walk_kernel(
     Plan pl, int run, int npt, int nslice, int nus, const bf16_t* __restrict__ x, const float* __restrict__ cs,
-    const float* __restrict__ dtc, const bf16_t* __restrict__ Cm, const bf16_t* __restrict__ cb,
+    const float* __restrict__ dtc, const float* __restrict__ tail, const bf16_t* __restrict__ Cm,
+    const bf16_t* __restrict__ cb,
     const bf16_t* __restrict__ bt, const float* __restrict__ D, const float* __restrict__ init,
     float* __restrict__ fin, TY* __restrict__ y) {
     extern __shared__ __align__(16) char smem[];
@@ -658,7 +721,7 @@ __global__ __launch_bounds__(512, 1) void ssd_scan_walk_kernel(
         case 1: walk_outputs<TY, kLargeFirst ? 6 : 1, kLargeFirst ? 1 : 6>(pl, w, bufs, Cm, cb, D, has_init, y); break;
         case 2: walk_outputs<TY, kLargeFirst ? 5 : 2, kLargeFirst ? 2 : 5>(pl, w, bufs, Cm, cb, D, has_init, y); break;
         case 3: walk_outputs<TY, kLargeFirst ? 4 : 3, kLargeFirst ? 3 : 4>(pl, w, bufs, Cm, cb, D, has_init, y); break;
-        default: walk_states<NU>(pl, w, bufs, x, cs, dtc, bt, init, fin); break;
+        default: walk_states<NU>(pl, w, bufs, x, cs, dtc, tail, bt, init, fin); break;
     }
 }
 
@@ -668,7 +731,7 @@ hipError_t run_walk(const Plan& pl, const WalkArgs& a, hipStream_t stream) {
     hipError_t err = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kWalkLds);
     if (err != hipSuccess) return err;
     hipLaunchKernelGGL(k, dim3(8 * a.per_xcd), dim3(512), kWalkLds, stream, pl, a.run, a.npt, a.nslice, a.nus,
-                       (const bf16_t*)a.x, a.cs, a.dtc, (const bf16_t*)a.C, (const bf16_t*)a.cb,
+                       (const bf16_t*)a.x, a.cs, a.dtc, a.tail, (const bf16_t*)a.C, (const bf16_t*)a.cb,
                        (const bf16_t*)a.bt, a.D, a.init, a.final_state, (TY*)a.y);
     return hipGetLastError();
 }
@@ -694,6 +757,11 @@ size_t scan_walk_lds_bytes() { return kWalkLds; }
 
 hipError_t launch_scan_walk(const Plan& pl, const WalkArgs& a, hipStream_t stream) {
     if (a.per_xcd <= 0) return hipSuccess;
+    const int64_t pairs = (int64_t)pl.nseq * pl.H;
+    hipLaunchKernelGGL(ssd_walk_tail_kernel, dim3((unsigned)((pairs + 3) / 4)), dim3(256), 0, stream, pl, a.cs,
+                       a.tail);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
     return a.y_f32 ? dispatch_walk<float>(pl, a, stream) : dispatch_walk<bf16_t>(pl, a, stream);
 }
 

@@ -77,14 +77,16 @@ def test_workspace_size_valid(lib):
     st3, n3 = ws_size(lib, shape(batch=8, seqlen=8192, nheads=80, headdim=64, dstate=128, dtype=1), 256)
     assert st3 == OK and n3 < 2 ** 31
     # the scan walk keeps the per-chunk states on chip: its workspace has no
-    # [chunks, H, P, N] fp32 region and no per-token weight table
+    # [chunks, H, P, N] fp32 region and no per-token weight table, only a
+    # [chunks, H] table of (cs_last, decay to the sequence's end) pairs
     big = dict(batch=8, seqlen=8192, nheads=80, headdim=64, dstate=128, dtype=1)
     sizes = {p: ws_size(lib, shape(path=p, **big), 256) for p in (1, 2, 3)}
     assert all(v[0] == OK for v in sizes.values())
     states = 8 * 32 * 80 * 64 * 128 * 4
     weights = 8 * 32 * 80 * 256 * 4
+    tails = 8 * 32 * 80 * 2 * 4
     assert sizes[1][1] == sizes[2][1]
-    assert sizes[2][1] - sizes[3][1] == states + weights
+    assert sizes[2][1] - sizes[3][1] == states + weights - tails
 
 
 @pytest.mark.parametrize("kw,chunk,code", [
