@@ -470,13 +470,23 @@ __device__ __forceinline__ void walk_block(const bf16x8 (&ga)[TI + 1][2], const 
                                            float* ep, __amdgpu_buffer_rsrc_t ry, int yb0, int rowb, int len,
                                            int pcols, float Dh) {
     const int lane = threadIdx.x & 63, half = lane >> 5, col = lane & 31;
-    // the state term C_rows . h_c^T (hi and lo), a chain of its own
+    // the state term C_rows . h_c^T, a chain of its own: hi and lo, or hi
+    // alone once the block's first token has decayed by kLoSkipDecay since
+    // the chunk's start (every row of the term is then scaled by less than
+    // exp(-kLoSkipDecay); a NaN keeps both)
     f32x16 sacc = {};
     if (has_state) {
+        const float cs0 = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(
+                                                        __builtin_bit_cast(int, tb.cs[32 * TI])));
+        if (!(cs0 <= -kLoSkipDecay)) {
 #pragma unroll
-        for (int s = 0; s < kNT / 16; ++s) {
-            mma16(sacc, ca[s], Tr<bf16_t>::ld8(shrow + 16 * s));
-            mma16(sacc, ca[s], Tr<bf16_t>::ld8(slrow + 16 * s));
+            for (int s = 0; s < kNT / 16; ++s) {
+                mma16(sacc, ca[s], Tr<bf16_t>::ld8(shrow + 16 * s));
+                mma16(sacc, ca[s], Tr<bf16_t>::ld8(slrow + 16 * s));
+            }
+        } else {
+#pragma unroll
+            for (int s = 0; s < kNT / 16; ++s) mma16(sacc, ca[s], Tr<bf16_t>::ld8(shrow + 16 * s));
         }
     }
     const int flags = __builtin_amdgcn_readfirstlane(tb.fast[TI]);
