@@ -62,6 +62,7 @@ constexpr int kNS = kNT + 8;     // n pitch (elements) of the state tiles
 constexpr float kFastDecay = 60.f;  // same bound as the chunk scan's Horner scheme
 constexpr float kWeakDecay = 60.f;  // whole-chunk decay below which the weights go to the chunk's end
 constexpr float kLoSkipDecay = 8.f;  // decay after a chunk from which its advance drops the lo half
+constexpr float kBlockSkipDecay = 16.f;  // decay to the chunk's end past which a block leaves the advance
 
 // One staging buffer: tables | (x wb)^T hi | (x wb)^T lo | x^T, the tiles
 // [32 columns p][kLP tokens] in bf16.
@@ -89,7 +90,8 @@ struct WalkTables {
     float* ue;   // [Q] exp(min(cs_t - cs at t's block end, 60))   (>= 1)
     float* gam;  // [8] decay across each block                   (<= 1)
     int* fast;   // [8] bit 0: block decay below kFastDecay; bit 1: weakly decaying chunk;
-                 //     bit 2: hi half alone in the advance
+                 //     bit 2: hi half alone in the advance; bit 3: the block decays by
+                 //     kBlockSkipDecay or more before the chunk's end
 };
 
 __device__ inline WalkTables walk_tables(char* base) {
@@ -265,7 +267,8 @@ __device__ inline void stage_store(const StageRegs& r, const Plan& pl, const Wal
         *(f32x4*)(tb.ue + k0) = ue;
         if ((k0 & 31) == 0) {
             tb.gam[k0 >> 5] = weak ? __expf(r.cl) : __expf(r.ce - c0);
-            tb.fast[k0 >> 5] = (weak ? 3 : (c0 - r.ce) < kFastDecay ? 1 : 0) | (hi_only ? 4 : 0);
+            tb.fast[k0 >> 5] = (weak ? 3 : (c0 - r.ce) < kFastDecay ? 1 : 0) | (hi_only ? 4 : 0) |
+                               (r.ce - r.cl >= kBlockSkipDecay ? 8 : 0);
         }
     }
 }
@@ -311,7 +314,11 @@ __device__ inline int state_off(int v, int pt, int nt, int P, int N) {
 // form because its registers do not hold two copies of the loop, and the
 // one-unit instance because it measured faster (every one of its steps
 // switches chunks).
-template <bool LO, bool RUNTIME>
+// JB0: the first block contracted.  The blocks before it decay by
+// kBlockSkipDecay or more before the chunk's end, so their tokens reach the
+// state scaled by less than exp(-kBlockSkipDecay) and are left out; the
+// Horner scheme still applies their decays.
+template <bool LO, bool RUNTIME, int JB0>
 __device__ inline void walk_advance(f32x16& acc, const bf16x8 (&bf)[kQ / 16], const WalkBufs& bufs, int b,
                                     bool weak, bool lo_rt) {
     const bool lo_too = RUNTIME ? lo_rt : LO;
@@ -330,10 +337,17 @@ __device__ inline void walk_advance(f32x16& acc, const bf16x8 (&bf)[kQ / 16], co
             if (lo_too) o[2 * ks + 1] = Tr<bf16_t>::ld8(lrow + 16 * (2 * jb + ks));
         }
     };
-    ld(0, op[0]);
-    if (weak) acc *= gm[0];
+    ld(JB0, op[JB0 & 1]);
+    if (weak) {
+        acc *= gm[0];
+    } else if (JB0 > 0) {
+        float g = gm[0];
 #pragma unroll
-    for (int jb = 0; jb < kNTI; ++jb) {
+        for (int jb = 1; jb < JB0; ++jb) g *= gm[jb];
+        acc *= g;
+    }
+#pragma unroll
+    for (int jb = JB0; jb < kNTI; ++jb) {
         if (jb + 1 < kNTI) ld(jb + 1, op[(jb + 1) & 1]);
         __builtin_amdgcn_sched_barrier(0);
         if (!weak) acc *= gm[jb];
@@ -416,11 +430,24 @@ __device__ void walk_states(const Plan& pl, const Walk& w, const WalkBufs& bufs,
                 const int flags = __builtin_amdgcn_readfirstlane(walk_tables(bufs.stage(b)).fast[0]);
                 const bool weak = (flags & 2) != 0, lo = (flags & 4) == 0;
                 if constexpr (NU >= 6 || NU == 1) {
-                    walk_advance<true, true>(acc[j], bf, bufs, b, weak, lo);
-                } else if (lo) {
-                    walk_advance<true, false>(acc[j], bf, bufs, b, weak, true);
+                    walk_advance<true, true, 0>(acc[j], bf, bufs, b, weak, lo);
                 } else {
-                    walk_advance<false, false>(acc[j], bf, bufs, b, weak, false);
+                    // leading blocks that leave the advance: four or none (one
+                    // loop start per case; starts at every second block spilled
+                    // more registers and measured no faster)
+                    const int* fl = walk_tables(bufs.stage(b)).fast;
+                    int skip = 0;
+#pragma unroll
+                    for (int jb = 0; jb < kNTI; ++jb)
+                        skip += (__builtin_amdgcn_readfirstlane(fl[jb]) >> 3) & 1;  // the flags are monotone in jb
+                    skip = skip >= 4 ? 4 : 0;
+                    if (lo) {
+                        if (skip == 0) walk_advance<true, false, 0>(acc[j], bf, bufs, b, weak, true);
+                        else walk_advance<true, false, 4>(acc[j], bf, bufs, b, weak, true);
+                    } else {
+                        if (skip == 0) walk_advance<false, false, 0>(acc[j], bf, bufs, b, weak, false);
+                        else walk_advance<false, false, 4>(acc[j], bf, bufs, b, weak, false);
+                    }
                 }
                 if (more && j + 1 == nu) put_state(acc[0], bufs, b ^ 1, nt);
                 // sn's loads, issued at the step's start, are waited for here
