@@ -63,6 +63,7 @@ constexpr float kFastDecay = 60.f;  // same bound as the chunk scan's Horner sch
 constexpr float kWeakDecay = 60.f;  // whole-chunk decay below which the weights go to the chunk's end
 constexpr float kLoSkipDecay = 8.f;  // decay after a chunk from which its advance drops the lo half
 constexpr float kBlockSkipDecay = 16.f;  // decay to the chunk's end past which a block leaves the advance
+constexpr float kStateSkipDecay = 16.f;  // decay since the chunk's start past which a block of y drops the state term
 
 // One staging buffer: tables | (x wb)^T hi | (x wb)^T lo | x^T, the tiles
 // [32 columns p][kLP tokens] in bf16.
@@ -490,7 +491,7 @@ __device__ void walk_states(const Plan& pl, const Walk& w, const WalkBufs& bufs,
 // diagonal block inside the scheme when its decay is below kFastDecay (then
 // scaled by ue), else added with exact per-element factors after scaling by
 // ul.  y leaves through the wave's LDS tile as 16-byte row pieces.
-template <typename TY, int TI>
+template <typename TY, int TI, bool SKIP>
 __device__ __forceinline__ void walk_block(const bf16x8 (&ga)[TI + 1][2], const bf16x8 (&ca)[kNT / 16],
                                            bool has_state, const bf16_t* shrow, const bf16_t* slrow,
                                            const WalkTables& tb, const bf16_t* xhrow, const bf16_t* xrrow,
@@ -500,7 +501,9 @@ __device__ __forceinline__ void walk_block(const bf16x8 (&ga)[TI + 1][2], const 
     // the state term C_rows . h_c^T, a chain of its own: hi and lo, or hi
     // alone once the block's first token has decayed by kLoSkipDecay since
     // the chunk's start (every row of the term is then scaled by less than
-    // exp(-kLoSkipDecay); a NaN keeps both)
+    // exp(-kLoSkipDecay)), or none once it has decayed by kStateSkipDecay
+    // (the term is then below the hi half's rounding at kLoSkipDecay), where
+    // SKIP is set; a NaN keeps both halves
     f32x16 sacc = {};
     if (has_state) {
         const float cs0 = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(
@@ -511,7 +514,7 @@ __device__ __forceinline__ void walk_block(const bf16x8 (&ga)[TI + 1][2], const 
                 mma16(sacc, ca[s], Tr<bf16_t>::ld8(shrow + 16 * s));
                 mma16(sacc, ca[s], Tr<bf16_t>::ld8(slrow + 16 * s));
             }
-        } else {
+        } else if (!SKIP || !(cs0 <= -kStateSkipDecay)) {
 #pragma unroll
             for (int s = 0; s < kNT / 16; ++s) mma16(sacc, ca[s], Tr<bf16_t>::ld8(shrow + 16 * s));
         }
@@ -611,7 +614,7 @@ __device__ __forceinline__ void walk_block(const bf16x8 (&ga)[TI + 1][2], const 
     __builtin_amdgcn_wave_barrier();
 }
 
-template <typename TY, int TA, int TB>
+template <typename TY, int TA, int TB, bool SKIP>
 __device__ void walk_outputs(const Plan& pl, const Walk& w, const WalkBufs& bufs, const bf16_t* __restrict__ Cm,
                              const bf16_t* __restrict__ cb, const float* __restrict__ D, bool has_init,
                              TY* __restrict__ y) {
@@ -689,13 +692,13 @@ __device__ void walk_outputs(const Plan& pl, const Walk& w, const WalkBufs& bufs
             // arrived.  Without it the wait before their first use has to
             // hold on the path without this reload too, and on the reload
             // path it then also waits for most of the younger reload loads.
-            walk_block<TY, TA>(ga_a, ca_a, has_state, shrow, slrow, tb, xhrow, xrrow, ep, ry, yb0, rowb, d.len,
+            walk_block<TY, TA, SKIP>(ga_a, ca_a, has_state, shrow, slrow, tb, xhrow, xrrow, ep, ry, yb0, rowb, d.len,
                                pcols, Dh);
             __builtin_amdgcn_sched_barrier(0);
             __builtin_amdgcn_s_waitcnt(kWaitVmcnt4);
             if (reload) load_block(c + 1, IA{}, ga_a, ca_a);
             __builtin_amdgcn_sched_barrier(0);
-            walk_block<TY, TB>(ga_b, ca_b, has_state, shrow, slrow, tb, xhrow, xrrow, ep, ry, yb0, rowb, d.len,
+            walk_block<TY, TB, SKIP>(ga_b, ca_b, has_state, shrow, slrow, tb, xhrow, xrrow, ep, ry, yb0, rowb, d.len,
                                pcols, Dh);
             __builtin_amdgcn_sched_barrier(0);
             __builtin_amdgcn_s_waitcnt(kWaitVmcnt4);
@@ -750,14 +753,24 @@ __global__ __launch_bounds__(512, 1) void ssd_scan_walk_kernel(
     // block's reload is needed only after the larger block's work in the next
     // step.  With one unit every step switches chunks, and the smaller block
     // goes first, so that the larger block's reload has the smaller block's
-    // work, not its own, to hide behind.
+    // work, not its own, to hide behind.  The state term's skip in blocks
+    // that have decayed by kStateSkipDecay follows the same split: it gains
+    // with two or more units and measured slower with one.
     constexpr bool kLargeFirst = NU > 1;
     const bool has_init = init != nullptr;
     switch (wave) {
-        case 0: walk_outputs<TY, kLargeFirst ? 7 : 0, kLargeFirst ? 0 : 7>(pl, w, bufs, Cm, cb, D, has_init, y); break;
-        case 1: walk_outputs<TY, kLargeFirst ? 6 : 1, kLargeFirst ? 1 : 6>(pl, w, bufs, Cm, cb, D, has_init, y); break;
-        case 2: walk_outputs<TY, kLargeFirst ? 5 : 2, kLargeFirst ? 2 : 5>(pl, w, bufs, Cm, cb, D, has_init, y); break;
-        case 3: walk_outputs<TY, kLargeFirst ? 4 : 3, kLargeFirst ? 3 : 4>(pl, w, bufs, Cm, cb, D, has_init, y); break;
+        case 0:
+            walk_outputs<TY, kLargeFirst ? 7 : 0, kLargeFirst ? 0 : 7, kLargeFirst>(pl, w, bufs, Cm, cb, D, has_init, y);
+            break;
+        case 1:
+            walk_outputs<TY, kLargeFirst ? 6 : 1, kLargeFirst ? 1 : 6, kLargeFirst>(pl, w, bufs, Cm, cb, D, has_init, y);
+            break;
+        case 2:
+            walk_outputs<TY, kLargeFirst ? 5 : 2, kLargeFirst ? 2 : 5, kLargeFirst>(pl, w, bufs, Cm, cb, D, has_init, y);
+            break;
+        case 3:
+            walk_outputs<TY, kLargeFirst ? 4 : 3, kLargeFirst ? 3 : 4, kLargeFirst>(pl, w, bufs, Cm, cb, D, has_init, y);
+            break;
         default: walk_states<NU>(pl, w, bufs, x, cs, dtc, tail, bt, init, fin); break;
     }
 }
